@@ -1,0 +1,227 @@
+"""Benchmark: RESOLVE + top-k sparse attention per decode layer on one MI355X.
+
+Workload (default): batch 8 requests, 1 layer, context 131072 each, MLA-style
+576-element bf16 latent records shared by 64 query heads, k = 2048 selected
+positions, B = 4096 buffer slots, synthetic 13% Zipf(1.1)-recency drift
+traces. A step is one decode step: per layer, hs_resolve (hash, probe,
+victim select, in-place update, host-to-device miss fetch) then
+hs_sparse_attn (+ split-k combine), all captured once per step in a hipGraph
+and replayed with no host synchronisation. Inputs (pool, selections,
+queries) are resident before the timed region.
+
+Prints one JSON line with the time per layer, the live event-timed duration
+of each kernel class, the roofline of the dominant kernel, the attention
+kernel's HBM roofline, the miss fetch's host-link rate, and the CPU oracle
+timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+HOST_LINK_PEAK_GBS = 63.0      # PCIe Gen5 x16, one direction, nominal
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "resolve+sparse-attn µs/layer at batch 8, k=2048; achieved HBM and host GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=120)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", type=int, default=3, help="workload 1..5 (3 = batch-8 MLA)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate budget of the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+def attn_bytes(w, n_units):
+    """Algorithmic HBM bytes of one attention launch over n_units units:
+    the k selected rows read once, the queries read, the outputs written."""
+    rows = n_units * w.k * w.rec_bytes
+    q = n_units * w.n_q_heads * w.q_dim * (4 if w.q_dtype == 0 else 2)
+    out = n_units * w.n_q_heads * w.out_dim * 4
+    return rows + q + out
+
+
+def attn_flops(w, n_units):
+    if w.kind == "mha":
+        return n_units * 4.0 * w.n_q_heads * w.head_dim * w.k
+    return n_units * 2.0 * w.n_q_heads * w.k * (w.q_dim + w.out_dim)
+
+
+def cpu_baseline(w, traces, budget_s):
+    """The oracle (resolve + fp64 attention) on the first steps of the same
+    trace, all units of each step in parallel over the host cores, until
+    the time budget is spent. Returns (us per layer-step, steps, threads)."""
+    import oracle
+    from tiered_kv_cache_hs_amd import inputs as I
+
+    R, L = w.n_requests, w.n_layers
+    pools, bufs, lens = {}, {}, {}
+    max_steps = traces.shape[0]
+    for r in range(R):
+        for l in range(L):
+            u = r * L + l
+            pool = np.zeros((w.capacity(r, max_steps), w.rec_bytes), dtype=np.uint8)
+            pos = np.unique(traces[:, u, :].astype(np.int64))
+            pos = pos[(pos >= 0) & (pos < w.ctx[r])]
+            I.fill_records(w, pool.ctypes.data, r, l, positions=pos)
+            pools[u], lens[u] = pool, w.ctx[r]
+            bufs[u] = oracle.OracleBuffer(w.B[r], w.rec_bytes, with_rows=True)
+    slots = np.empty((R * L, w.k), np.int32)
+    miss = np.empty(R * L, np.int32)
+    out = np.empty((R * L, w.n_q_heads, w.out_dim), np.float32)
+    step_times, threads = [], 1
+    t_start = time.perf_counter()
+    for t in range(max_steps):
+        q = I.gen_queries(w, t)
+        units = []
+        for u in range(R * L):
+            b = bufs[u]
+            x = oracle.OracleUnitC()
+            x.B, x.k = b.B, w.k
+            x.pos, x.stamp, x.clock = b.pos.ctypes.data, b.stamp.ctypes.data, b.clock.ctypes.data
+            x.err, x.rows, x.rec_bytes = b.err.ctypes.data, b.rows.ctypes.data, w.rec_bytes
+            x.pool, x.pool_len = pools[u].ctypes.data, lens[u]
+            x.topk = traces[t, u].ctypes.data
+            x.slots, x.miss = slots[u].ctypes.data, miss[u:].ctypes.data
+            x.kind = 0 if w.kind == "mha" else 1
+            x.Hq, x.Hkv, x.D, x.Dl, x.Dr = w.n_q_heads, w.n_kv_heads, w.head_dim, w.latent_dim, w.rope_dim
+            x.kv_dtype, x.q_dtype, x.sm_scale = w.dtype, w.q_dtype, np.float32(w.sm_scale)
+            x.q, x.out = q[u].ctypes.data, out[u].ctypes.data
+            units.append(x)
+        t0 = time.perf_counter()
+        threads = oracle.step_batch(units, 0)
+        step_times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s and len(step_times) >= 2:
+            break
+    # step 0 is the cold all-miss step; report the warm steps when there are any
+    warm = step_times[1:] if len(step_times) > 1 else step_times
+    return 1e6 * float(np.median(warm)) / L, len(step_times), threads
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path runs on a "
+              "single MI355X; multi-GPU sharding is described in the design notes only)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from tiered_kv_cache_hs_amd import hisparse as H
+    from tiered_kv_cache_hs_amd import inputs as I
+    from tiered_kv_cache_hs_amd.session import Session
+
+    H.lib()
+    w = I.workload(args.workload)
+    W, K = args.warmup, args.steps
+    total = W + K
+    print(f"[bench] workload {w.name}: building session ({total} steps)", file=sys.stderr, flush=True)
+    fill = "full" if w.n_units * max(w.ctx) * w.rec_bytes <= (8 << 30) else "touched"
+    sess = Session(w, total, fill=fill)
+    sess.capture()
+    print("[bench] graphs captured", file=sys.stderr, flush=True)
+
+    # ---- timed region: graph replays of steps W .. W+K-1
+    for t in range(W):
+        sess.replay(t)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for t in range(W, total):
+        sess.replay(t)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev0.elapsed_time(ev1) / K
+    print(f"[bench] timed {K} steps: {ms_step * 1000:.1f} us/step (wall {wall * 1e3 / K:.3f} ms/step)",
+          file=sys.stderr, flush=True)
+
+    # ---- the same steps again, eagerly, with each kernel bracketed by events
+    sess.reset()
+    miss_hist = torch.zeros((total, w.n_layers, w.n_requests), dtype=torch.int32, device="cuda")
+    for t in range(total):
+        if t == W:
+            torch.cuda.synchronize()
+            H.hs_trace_enable(True)
+            H.hs_trace_read()
+        sess.step(t)
+        miss_hist[t].copy_(sess.miss)
+    tr = H.hs_trace_read()
+    H.hs_trace_enable(False)
+    misses = miss_hist[W:].cpu().numpy().astype(np.int64)
+    per = {c: (tr[c][0] / tr[c][1] if tr[c][1] else 0.0) for c in H.TRACE_CLASSES}
+
+    n_launch_units = w.n_requests  # one batch (one layer's requests) per launch
+    a_bytes = attn_bytes(w, n_launch_units)
+    a_flops = attn_flops(w, n_launch_units)
+    attn_us = per["attn"]
+    attn_gbs = a_bytes / (attn_us * 1e-6) / 1e9 if attn_us else 0.0
+    miss_bytes_launch = misses.sum() * w.rec_bytes / max(1, tr["gather"][1])
+    gather_us = per["gather"]
+    host_gbs = miss_bytes_launch / (gather_us * 1e-6) / 1e9 if gather_us else 0.0
+    miss_rate = float(misses.sum()) / (K * w.n_units * w.k)
+
+    roof_attn = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                 "kernel": "hs_k_attn_latent" if w.kind == "latent" else "hs_k_attn_mha",
+                 "avg_us": round(attn_us, 2), "bytes_per_launch": int(a_bytes),
+                 "tflops": round(a_flops / (attn_us * 1e-6) / 1e12, 2) if attn_us else 0.0}
+    roof_gather = {"bound": "host_link", "achieved": round(host_gbs, 2),
+                   "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                   "frac": round(host_gbs / HOST_LINK_PEAK_GBS, 4), "traffic": None,
+                   "kernel": "hs_k_gather", "avg_us": round(gather_us, 2),
+                   "bytes_per_launch": int(miss_bytes_launch)}
+    dominant = roof_gather if gather_us >= attn_us else roof_attn
+
+    result = {
+        "metric": METRIC,
+        "value": round(ms_step * 1000.0 / w.n_layers, 2),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == I.BF16 else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "requests": w.n_requests, "layers": w.n_layers,
+                   "context": w.ctx[0] if len(set(w.ctx)) == 1 else "per-request",
+                   "k": w.k, "B": w.B[0] if len(set(w.B)) == 1 else "per-request",
+                   "q_heads": w.n_q_heads, "record_bytes": w.rec_bytes, "kind": w.kind,
+                   "graph": "one hipGraph per step"},
+        "roofline": dominant,
+        "roofline_attn": roof_attn,
+        "host_link": roof_gather,
+        "kernels_us": {c: round(per[c], 2) for c in H.TRACE_CLASSES},
+        "miss_rate": round(miss_rate, 4),
+        "miss_bytes_per_step": int(misses.sum() * w.rec_bytes / K),
+    }
+    sess.close()
+
+    if not args.no_cpu:
+        print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
+        traces = I.gen_traces(w, total)
+        us, n_steps, threads = cpu_baseline(w, traces, args.cpu_seconds)
+        result["cpu_baseline"] = {
+            "value": round(us, 1), "unit": "us/layer", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_steps} steps of the same trace (step 0 cold, median of the rest), "
+                      f"all {w.n_units} units per step, resolve + fp64 attention"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

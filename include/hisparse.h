@@ -1,0 +1,266 @@
+/* hisparse.h - C ABI of the HiSparse decode hot path on AMD Instinct MI355X
+ * (gfx950): a pinned host KV pool, per-(request, layer) device buffers, the
+ * fused RESOLVE step and top-k sparse attention over the resolved slots.
+ *
+ * Source of the operations: "HiSparse: Scaling Sparse-Attention Decoding
+ * with Hierarchical KV Cache Management", as summarised on the
+ * marsggbo.github.io page of 2026-09-23 ("HiSparse | 稀疏注意力省了算力却没省
+ * 显存…"), cited below as "HiSparse summary" with the page's own section
+ * numbers:
+ *   section 3 - the architecture: the host pool is the authoritative copy of
+ *     every record; each request and layer owns a fixed B-slot device buffer
+ *     with a page table and LRU metadata; per decode step the indexer's k
+ *     selected positions are resolved against the buffer (hits used in
+ *     place, misses swapped in from host in one batch, LRU victims evicted);
+ *     the physical slots feed the sparse-attention backend; the new token's
+ *     record is written through to the host pool. The result is exact.
+ *   section 4 - the LRU state is kept and updated in place across steps.
+ *   section 5 - the fused resolve: an on-chip hash table of the selection,
+ *     a parallel probe of every buffer slot, a parallel scan that picks the
+ *     victims (hits to most-recently-used, misses right after the hits),
+ *     GPU threads loading the missing records straight from pinned host
+ *     memory, and a published slot vector aligned with the selection; the
+ *     whole step is capturable in a graph (no host synchronisation).
+ *   section 8 - the knobs: top_k (k per call) and device_buffer_size (B).
+ *
+ * Conventions
+ *   - Every call returns hs_status. HS_OK is 0; errors are negative.
+ *     hs_last_error() gives a message for the last failing call on the
+ *     calling thread.
+ *   - Handles are opaque and not thread-safe. A stream argument is a
+ *     hipStream_t passed as void* (NULL is the default stream).
+ *   - "Enqueue only" calls validate their arguments on the host, enqueue
+ *     GPU work on the stream and return; they never synchronise and are
+ *     safe inside hipStreamBeginCapture/EndCapture. Calls marked
+ *     "synchronous" block until their work is done and must not be called
+ *     while the stream is being captured.
+ *   - Device pointers (d_*) are caller-owned HIP device memory. Host
+ *     pointers are plain host memory.
+ *   - Units: a batch is an ordered list of n buffers ("units"); per-unit
+ *     arrays are unit-major: topk/slots [n][k], miss [n], queries
+ *     [n][n_q_heads][q_dim], outputs [n][n_q_heads][v_dim].
+ *
+ * Data errors found on the device (a selection or slot that the host cannot
+ * check without synchronising) are reported in the unit's sticky error word
+ * (read with hs_buffer_state_get): bits accumulate and are cleared only by
+ * hs_buffer_reset or hs_buffer_state_set.
+ */
+#ifndef HISPARSE_H
+#define HISPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t hs_status;
+#define HS_OK 0
+#define HS_E_INVAL (-1)  /* malformed argument (null, size, shape, k vs B) */
+#define HS_E_RANGE (-2)  /* request/layer/position outside the pool */
+#define HS_E_NOMEM (-3)  /* host or device allocation failed */
+#define HS_E_HIP (-4)    /* a HIP runtime call failed */
+#define HS_E_STATE (-5)  /* state given to hs_buffer_state_set is not valid */
+
+/* Bits of a unit's device error word. */
+#define HS_ERR_RANGE 1u  /* a selected position was outside [0, pool length) */
+#define HS_ERR_DUP 2u    /* an in-range position was selected twice */
+#define HS_ERR_CLOCK 4u  /* the buffer's clock is exhausted (2^31 - 1 steps) */
+#define HS_ERR_SLOT 8u   /* attention got a slot outside [0, B) */
+#define HS_ERR_INTERNAL 16u /* resolve found its victim count inconsistent with
+                               the miss count (never expected; state untouched) */
+
+/* Record layouts. HS_KV_MHA: one record per token holds
+ * [K: n_kv_heads x head_dim][V: n_kv_heads x head_dim]. HS_KV_LATENT
+ * (MLA-style shared latent): [latent: latent_dim][rope: rope_dim]; the key is
+ * the whole record and the value is the latent part. */
+#define HS_KV_MHA 0
+#define HS_KV_LATENT 1
+
+#define HS_F32 0
+#define HS_BF16 1
+
+/* Limits of this implementation. */
+#define HS_MAX_K 4096          /* selected positions per unit and call */
+#define HS_MAX_B 16384         /* slots of a buffer that hs_resolve accepts */
+
+typedef struct hs_pool_s *hs_pool_t;
+typedef struct hs_buffer_s *hs_buffer_t;
+typedef struct hs_batch_s *hs_batch_t;
+
+typedef struct hs_pool_desc {
+  int32_t n_requests;             /* >= 1 */
+  int32_t n_layers;               /* >= 1 */
+  int32_t kind;                   /* HS_KV_MHA or HS_KV_LATENT */
+  int32_t dtype;                  /* HS_F32 or HS_BF16 (records) */
+  int32_t n_kv_heads;             /* HS_KV_MHA */
+  int32_t head_dim;               /* HS_KV_MHA */
+  int32_t latent_dim;             /* HS_KV_LATENT: value part */
+  int32_t rope_dim;               /* HS_KV_LATENT: key-only part */
+  const int64_t *capacity_tokens; /* [n_requests] records per layer, host */
+} hs_pool_desc;
+
+/* Tuning knobs (library-wide; 0 = choose automatically). */
+typedef struct hs_tuning {
+  int32_t gather_wgs_per_unit;  /* workgroups copying one unit's misses */
+  int32_t attn_splits;          /* split-k factor of sparse attention */
+  int32_t reserved[6];
+} hs_tuning;
+
+const char *hs_status_str(hs_status s);
+const char *hs_last_error(void);
+
+hs_status hs_set_tuning(const hs_tuning *t);
+hs_status hs_get_tuning(hs_tuning *t);
+
+/* ---------------- host KV pool (HiSparse summary, section 3) ---------------
+ * hs_pool_create: allocates, for every request, n_layers x capacity records
+ * of pinned host memory mapped into the current device's address space
+ * (hipHostMalloc), plus a small device table of per-unit lengths (all 0).
+ * The library owns that memory until hs_pool_destroy. Synchronous.
+ * Errors: HS_E_INVAL (bad descriptor), HS_E_NOMEM (allocation failed). */
+hs_status hs_pool_create(const hs_pool_desc *desc, hs_pool_t *out);
+/* The caller must have synchronised every stream that used the pool. */
+hs_status hs_pool_destroy(hs_pool_t pool);
+/* Bytes of one record. */
+hs_status hs_pool_record_bytes(hs_pool_t pool, size_t *rec_bytes);
+/* Host pointer of unit (req, layer)'s record array: record p is at
+ * host_ptr + p * rec_bytes for 0 <= p < capacity. Used to write prefill
+ * records directly. HS_E_RANGE for a bad req/layer. */
+hs_status hs_pool_unit_ptr(hs_pool_t pool, int32_t req, int32_t layer,
+                           void **host_ptr, int64_t *capacity);
+/* Current length (records valid for selection) of unit (req, layer).
+ * Synchronous (reads the device table). */
+hs_status hs_pool_length(hs_pool_t pool, int32_t req, int32_t layer,
+                         int64_t *len);
+/* Declare that records [0, len) of the unit were written through
+ * hs_pool_unit_ptr (prefill). Synchronous. HS_E_RANGE if len > capacity. */
+hs_status hs_pool_set_length(hs_pool_t pool, int32_t req, int32_t layer,
+                             int64_t len);
+/* Write-through append (HiSparse summary, section 3, arrow 5): write n
+ * records from src to positions [pos, pos + n) of unit (req, layer) and set
+ * its length to max(length, pos + n). The pool stays contiguous: pos must
+ * not exceed the length as of the calls made so far (appends enqueued but
+ * not yet run count). Only the pool is written; device buffers see the new
+ * records only through later misses.
+ * src_on_device = 0: src is host memory; copied synchronously.
+ * src_on_device = 1: src is device memory; enqueued on stream (capture-safe).
+ * Errors: HS_E_RANGE (pos > length or pos + n > capacity), HS_E_INVAL. */
+hs_status hs_pool_append(hs_pool_t pool, int32_t req, int32_t layer,
+                         int64_t pos, int64_t n, const void *src,
+                         int32_t src_on_device, void *stream);
+
+/* ------------- hot device buffer (HiSparse summary, sections 3-4) ----------
+ * A buffer of B record slots for unit (req, layer) with its page table
+ * (slot -> logical position, -1 when empty), LRU stamps, clock and error
+ * word. The memory is caller-owned device memory of at least
+ * hs_buffer_bytes(pool, B) bytes, 256-byte aligned; the library only writes
+ * into it and never frees it. */
+size_t hs_buffer_bytes(hs_pool_t pool, int32_t B);
+/* Enqueues the empty state (every slot empty, clock 0, error 0) on stream.
+ * HS_E_INVAL for B < 1, too few bytes or misaligned memory; HS_E_RANGE for
+ * a bad req/layer. */
+hs_status hs_buffer_create(hs_pool_t pool, int32_t req, int32_t layer,
+                           int32_t B, void *d_mem, size_t bytes, void *stream,
+                           hs_buffer_t *out);
+/* Frees the handle only (not d_mem). */
+hs_status hs_buffer_destroy(hs_buffer_t buf);
+/* Enqueues the empty state again (also clears the error word). */
+hs_status hs_buffer_reset(hs_buffer_t buf, void *stream);
+/* Device pointer and size of the rows region: row s (the record held by
+ * slot s) is at *d_rows + s * rec_bytes. */
+hs_status hs_buffer_rows(hs_buffer_t buf, void **d_rows, size_t *rec_bytes);
+/* Copies the buffer's metadata to host arrays pos[B], stamp[B] and scalars
+ * (any pointer may be NULL). Synchronises stream. */
+hs_status hs_buffer_state_get(hs_buffer_t buf, int32_t *pos, uint32_t *stamp,
+                              uint32_t *clock, int32_t *err, void *stream);
+/* Replaces the metadata (checkpoint restore) and re-gathers every occupied
+ * row from the host pool; the error word is set to err. The state must be
+ * valid: every pos in [-1, pool length), occupied positions distinct,
+ * stamp 0 exactly for empty slots, stamps <= 2 * clock, clock < 2^31 - 1;
+ * otherwise HS_E_STATE and nothing changes. Synchronous. */
+hs_status hs_buffer_state_set(hs_buffer_t buf, const int32_t *pos,
+                              const uint32_t *stamp, uint32_t clock,
+                              int32_t err, void *stream);
+
+/* ------------------------------- batches -----------------------------------
+ * An ordered list of n units (buffers of one pool; buffer sizes may
+ * differ). Uploads a device descriptor table. Synchronous; create batches
+ * before graph capture. */
+hs_status hs_batch_create(const hs_buffer_t *bufs, int32_t n,
+                          hs_batch_t *out);
+hs_status hs_batch_destroy(hs_batch_t batch);
+
+/* --------------- RESOLVE (HiSparse summary, sections 4-5) ------------------
+ * For every unit u, resolves the selection d_topk[u][0..k) (logical
+ * positions) against u's buffer in place, and writes d_slots[u][i], the
+ * slot that now holds position d_topk[u][i] (aligned with the selection),
+ * and d_miss[u], the number of positions fetched from the host pool
+ * (d_miss may be NULL). Semantics, per unit, with c = clock + 1:
+ *   hits   - slots whose position is selected; their stamp becomes 2c;
+ *   misses - selected positions held by no slot, in selection order;
+ *   victims- the m = #misses non-hit slots with the smallest key
+ *            (stamp, position, slot) (empty slots: stamp 0, position -1,
+ *            so they are used first, lowest slot first; equal stamps leave
+ *            in ascending position), sorted by ascending slot; the j-th miss
+ *            goes into the j-th victim with stamp 2c - 1, and its record is
+ *            copied from the host pool into the slot's row;
+ *   clock  - becomes c.
+ * Host checks (HS_E_INVAL): 1 <= k <= min B, k <= HS_MAX_K, every B <=
+ * HS_MAX_B, null pointers. Device data errors (a position outside
+ * [0, length), a repeated position, an exhausted clock) set the unit's
+ * error bits, write slots = -1 and miss = -1 and leave its state unchanged;
+ * other units proceed. Enqueue only; capture-safe. */
+hs_status hs_resolve(hs_batch_t batch, const int32_t *d_topk, int32_t k,
+                     int32_t *d_slots, int32_t *d_miss, void *stream);
+
+/* ------------- sparse attention (HiSparse summary, sections 3, 5) ----------
+ * Decode attention of each unit's queries over the k rows named by
+ * d_slots[u][0..k) in its buffer:
+ *   out[u][h] = sum_i softmax_i(sm_scale * q[u][h] . K_i) V_i
+ * HS_KV_MHA: q [n][n_q_heads][head_dim] of the pool's dtype; query head h
+ *   reads KV head h / (n_q_heads / n_kv_heads); out [n][n_q_heads][head_dim].
+ *   Supported: head_dim 64 or 128, n_q_heads / n_kv_heads in {1, 2, 4, 8}.
+ * HS_KV_LATENT: q [n][n_q_heads][latent_dim + rope_dim] bf16; K is the whole
+ *   record, V its latent part; out [n][n_q_heads][latent_dim]. Supported:
+ *   bf16, latent_dim 512, rope_dim 64, n_q_heads a multiple of 16.
+ * Outputs are fp32 (accumulation is fp32). A slot outside [0, B) makes the
+ * unit's output NaN and sets HS_ERR_SLOT. d_ws is scratch of at least
+ * hs_sparse_attn_workspace(...) bytes (may be NULL when that is 0); its
+ * contents need no initialisation. Enqueue only; capture-safe.
+ * HS_E_INVAL for unsupported shapes or a small workspace. */
+size_t hs_sparse_attn_workspace(hs_batch_t batch, int32_t n_q_heads,
+                                int32_t k);
+hs_status hs_sparse_attn(hs_batch_t batch, const void *d_q, int32_t n_q_heads,
+                         const int32_t *d_slots, int32_t k, float sm_scale,
+                         float *d_out, void *d_ws, size_t ws_bytes,
+                         void *stream);
+
+/* ------------------------------- tracing -----------------------------------
+ * Event timing of individual kernels, for measurement. While enabled, every
+ * kernel that hs_resolve and hs_sparse_attn enqueue is bracketed by a pair
+ * of HIP events recorded on the same stream (do not enable it around graph
+ * capture). hs_trace_read synchronises the device, adds up the elapsed time
+ * of every completed pair per kernel class and clears the record. Classes:
+ * HS_TRACE_SELECT (hash, probe, victim select, update), HS_TRACE_GATHER
+ * (host-to-device miss fetch), HS_TRACE_ATTN (sparse attention),
+ * HS_TRACE_COMBINE (split-k merge). At most 4096 launches are recorded
+ * between reads; later ones are counted in `dropped`. */
+#define HS_TRACE_SELECT 0
+#define HS_TRACE_GATHER 1
+#define HS_TRACE_ATTN 2
+#define HS_TRACE_COMBINE 3
+#define HS_TRACE_CLASSES 4
+typedef struct hs_trace {
+  double total_us[HS_TRACE_CLASSES];
+  int64_t launches[HS_TRACE_CLASSES];
+  int64_t dropped;
+} hs_trace;
+hs_status hs_trace_enable(int32_t on);
+hs_status hs_trace_read(hs_trace *out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HISPARSE_H */

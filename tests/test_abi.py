@@ -1,0 +1,60 @@
+"""The C-ABI library loads and exports every entry point include/*.h declares.
+
+No compute calls (no GPU here): loading libhisparse.so only needs the HIP
+runtime library, and the host-side argument checks that touch no device
+state can run too.
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+from tiered_kv_cache_hs_amd import hisparse as H
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    names = set()
+    for hdr in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(hdr).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        for m in re.finditer(r"\b(hs_[a-z_0-9]+)\s*\(", text):
+            names.add(m.group(1))
+    return names
+
+
+def test_header_declares_the_binding_names():
+    assert declared_functions() == set(H.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = H.lib()
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def test_status_strings_and_tuning_roundtrip():
+    assert H.hs_status_str(H.HS_OK) == "ok"
+    assert H.hs_status_str(H.HS_E_STATE) == "invalid buffer state"
+    H.hs_set_tuning(8, 4)
+    assert H.hs_get_tuning() == {"gather_wgs_per_unit": 8, "attn_splits": 4}
+    H.hs_set_tuning(0, 0)
+    with pytest.raises(H.HsError):
+        H.hs_set_tuning(-1, 0)
+
+
+def test_null_and_shape_checks_without_device():
+    L = H.lib()
+    assert L.hs_pool_create(None, None) == H.HS_E_INVAL
+    assert L.hs_batch_create(None, 0, None) == H.HS_E_INVAL
+    assert L.hs_resolve(None, None, 1, None, None, None) == H.HS_E_INVAL
+    assert L.hs_buffer_bytes(None, 4) == 0
+    d = H.PoolDesc(1, 1, 7, H.HS_BF16, 1, 64, 0, 0, (ctypes.c_int64 * 1)(100))
+    out = ctypes.c_void_p()
+    assert L.hs_pool_create(ctypes.byref(d), ctypes.byref(out)) == H.HS_E_INVAL
+    d = H.PoolDesc(1, 1, H.HS_KV_MHA, H.HS_BF16, 1, 3, 0, 0, (ctypes.c_int64 * 1)(100))
+    assert L.hs_pool_create(ctypes.byref(d), ctypes.byref(out)) == H.HS_E_INVAL  # 12-byte record
+    assert "multiple of 16" in H.hs_last_error()

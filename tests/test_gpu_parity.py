@@ -1,0 +1,303 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Slot ids, victim choices, LRU state (page table, stamps, clock), error words,
+miss counts and resident row bytes must match bit for bit; attention within
+max abs 1e-5 (fp32 records) or max abs 1e-2 and relative L2 4e-3 (bf16).
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+from tests.parity import OracleRun, check_attn  # noqa: E402
+from tiered_kv_cache_hs_amd import hisparse as H  # noqa: E402
+from tiered_kv_cache_hs_amd import inputs as I  # noqa: E402
+from tiered_kv_cache_hs_amd.session import Session  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    H.lib()
+    H.hs_set_tuning(0, 0)
+    yield
+    H.hs_set_tuning(0, 0)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def compare_run(w, steps, traces=None, attn_every=1, rows_every=1, attn_units=None,
+                graph=False, fill="touched"):
+    sess = Session(w, steps, fill=fill, traces=traces)
+    orc = OracleRun(w, sess.traces, steps)
+    if graph:
+        sess.capture()
+    stats = []
+    try:
+        for t in range(steps):
+            if graph:
+                sess.replay(t)
+            else:
+                sess.step(t)
+            torch.cuda.synchronize()
+            slots_g = sess.slots.cpu().numpy()
+            miss_g = sess.miss.cpu().numpy()
+            out_g = sess.out.cpu().numpy()
+            for l in range(w.n_layers):
+                for r in range(w.n_requests):
+                    so, mo = orc.resolve(t, r, l)
+                    assert np.array_equal(slots_g[l, r], so), f"slots t={t} r={r} l={l}"
+                    assert int(miss_g[l, r]) == mo, f"miss t={t} r={r} l={l}"
+                    pos, stamp, clock, err = sess.state(l, r)
+                    ob = orc.bufs[(r, l)]
+                    assert np.array_equal(pos, ob.pos), f"pos t={t} r={r} l={l}"
+                    assert np.array_equal(stamp, ob.stamp), f"stamp t={t} r={r} l={l}"
+                    assert clock == int(ob.clock[0]) and err == int(ob.err[0])
+                    if rows_every and t % rows_every == 0:
+                        rows = sess.rows(l, r)
+                        occ = ob.pos >= 0
+                        assert np.array_equal(rows[occ], ob.rows[occ]), f"rows t={t} r={r} l={l}"
+                    if attn_every and t % attn_every == 0 and (attn_units is None or (r, l) in attn_units):
+                        want = orc.attend(t, r, l, so)
+                        stats.append(check_attn(w, out_g[l, r], want, f"attn t={t} r={r} l={l}"))
+                    if w.append:
+                        orc.append(t, r, l)
+    finally:
+        sess.close()
+    return stats
+
+
+def test_tiny_fp32_every_step():
+    w = I.workload(1)
+    say("workload 1 (tiny fp32), 32 steps")
+    st = compare_run(w, w.steps)
+    say("worst max abs", max(s["max_abs"] for s in st))
+
+
+def test_tiny_fp32_graph_replay():
+    w = I.workload(1)
+    compare_run(w, w.steps, graph=True)
+
+
+def test_gqa32k_append_prefix():
+    w = I.workload(2)
+    say("workload 2 (GQA 32K bf16, appends), 48 steps")
+    st = compare_run(w, 48, attn_every=4, rows_every=8)
+    say("worst", max(s["max_abs"] for s in st), max(s["rel_l2"] for s in st))
+
+
+def test_mla_b8_prefix():
+    w = I.workload(3)
+    say("workload 3 (MLA batch 8), 12 steps")
+    st = compare_run(w, 12, attn_every=4, rows_every=6, attn_units=[(0, 0), (5, 0)])
+    say("worst", max(s["max_abs"] for s in st), max(s["rel_l2"] for s in st))
+
+
+def _small(kind, dtype, B, k, ctx, steps, n_new, R=1, L=1, seed=0, Hkv=1, D=64, Hq=1):
+    if kind == "mha":
+        w = I.Workload(f"small_{seed}", R, L, "mha", dtype, dtype, Hkv, D, 0, 0, Hq, k, steps,
+                       n_new, (("uniform", 0.5), ("window", 0.5)), 1.0, 1000 + seed)
+    else:
+        w = I.Workload(f"small_{seed}", R, L, "latent", I.BF16, I.BF16, 1, 0, 512, 64, Hq, k,
+                       steps, n_new, (("uniform", 1.0),), 0.5, 1000 + seed)
+    w.ctx = [ctx] * R
+    w.B = [B] * R
+    return w
+
+
+SMALL = [
+    # kind, dtype, B, k, ctx, steps, n_new
+    ("mha", I.F32, 1, 1, 5, 6, 1),
+    ("mha", I.F32, 7, 7, 40, 8, 3),
+    ("mha", I.F32, 33, 17, 100, 10, 9),
+    ("mha", I.F32, 1000, 300, 5000, 6, 77),
+    ("mha", I.F32, 1024, 1024, 3000, 4, 100),
+    ("mha", I.F32, 1025, 1000, 6000, 5, 333),
+    ("mha", I.BF16, 3000, 2049, 9000, 5, 500),
+    ("mha", I.F32, 16384, 4096, 40000, 4, 1000),
+    ("latent", I.BF16, 97, 33, 500, 6, 10),
+    ("latent", I.BF16, 2048, 2048, 9000, 4, 614),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_small_shapes(case):
+    kind, dt, B, k, ctx, steps, n_new = SMALL[case]
+    if kind == "mha":
+        w = _small(kind, dt, B, k, ctx, steps, n_new, seed=case,
+                   Hkv=2 if dt == I.BF16 else 1, D=128 if dt == I.BF16 else 64,
+                   Hq=4 if dt == I.BF16 else 1)
+    else:
+        w = _small(kind, dt, B, k, ctx, steps, n_new, seed=case, Hq=32)
+    say(f"small case {case}: {SMALL[case]}")
+    compare_run(w, steps, fill="full")
+
+
+def test_multi_request_multi_layer_small():
+    w = _small("mha", I.BF16, 600, 200, 3000, 6, 50, R=3, L=2, seed=77, Hkv=2, D=128, Hq=16)
+    compare_run(w, 6, fill="full")
+
+
+def test_stamp_ties_break_by_position():
+    # hand-made state: every slot holds the same stamp; the victims must be
+    # the smallest positions (then ascending slot pairing with the misses)
+    w = _small("mha", I.F32, 8, 3, 64, 1, 1, seed=5)
+    sess = Session(w, 1, fill="full", traces=np.array([[[60, 61, 62]]], dtype=np.int32))
+    try:
+        pos = np.array([40, 3, 22, 7, 50, 9, 31, 18], dtype=np.int32)
+        stamp = np.full(8, 5, dtype=np.uint32)
+        H.hs_buffer_state_set(sess.bufs[0][0], pos, stamp, 3)
+        ob = oracle.OracleBuffer(8, w.rec_bytes, with_rows=False)
+        ob.pos[:] = pos
+        ob.stamp[:] = stamp
+        ob.clock[0] = 3
+        sess.step(0)
+        torch.cuda.synchronize()
+        so, mo = oracle.resolve(ob, np.array([60, 61, 62]), None, 64)
+        g_pos, g_stamp, g_clock, g_err = sess.state(0, 0)
+        assert mo == 3 and int(sess.miss[0, 0]) == 3
+        # positions 3, 7, 9 (slots 1, 3, 5) are evicted
+        assert sorted(set(pos) - set(g_pos.tolist())) == [3, 7, 9]
+        assert np.array_equal(sess.slots[0, 0].cpu().numpy(), so)
+        assert np.array_equal(g_pos, ob.pos) and np.array_equal(g_stamp, ob.stamp)
+    finally:
+        sess.close()
+
+
+def test_data_errors_leave_state_unchanged():
+    w = _small("mha", I.F32, 16, 4, 64, 4, 2, seed=9)
+    tr = np.array([[[1, 2, 3, 4]], [[5, 64, 6, 7]], [[8, 9, 8, 10]], [[11, 12, 13, -3]]],
+                  dtype=np.int32)
+    sess = Session(w, 4, fill="full", traces=tr)
+    try:
+        sess.step(0)
+        torch.cuda.synchronize()
+        p0, s0, c0, e0 = sess.state(0, 0)
+        out0 = sess.out.cpu().numpy()
+        assert e0 == 0 and c0 == 1
+        for t, bits in ((1, H.HS_ERR_RANGE), (2, H.HS_ERR_DUP), (3, H.HS_ERR_RANGE)):
+            sess.step(t)
+            torch.cuda.synchronize()
+            p, s, c, e = sess.state(0, 0)
+            assert np.array_equal(p, p0) and np.array_equal(s, s0) and c == c0
+            assert e & bits and e & H.HS_ERR_SLOT  # attention saw slots of -1
+            assert (sess.slots.cpu().numpy() == -1).all() and int(sess.miss[0, 0]) == -1
+            assert np.isnan(sess.out.cpu().numpy()).all()
+        # a valid selection still resolves; the sticky bits stay
+        H.hs_resolve(sess.batches[0], sess.topk[0, 0], 4, sess.slots[0], sess.miss[0])
+        torch.cuda.synchronize()
+        p, s, c, e = sess.state(0, 0)
+        assert c == 2 and int(sess.miss[0, 0]) == 0
+        assert e == (H.HS_ERR_RANGE | H.HS_ERR_DUP | H.HS_ERR_SLOT)
+        assert np.isfinite(out0).all()
+    finally:
+        sess.close()
+
+
+def test_clock_exhaustion_and_state_validation():
+    w = _small("mha", I.F32, 4, 1, 16, 2, 1, seed=11)
+    sess = Session(w, 2, fill="full", traces=np.array([[[1]], [[1]]], dtype=np.int32))
+    try:
+        buf = sess.bufs[0][0]
+        pos = np.array([1, -1, -1, -1], np.int32)
+        with pytest.raises(H.HsError):  # stamp must be 0 exactly for empty slots
+            H.hs_buffer_state_set(buf, pos, np.array([0, 0, 0, 0], np.uint32), 5)
+        with pytest.raises(H.HsError):  # duplicate position
+            H.hs_buffer_state_set(buf, np.array([1, 1, -1, -1], np.int32),
+                                  np.array([3, 4, 0, 0], np.uint32), 5)
+        with pytest.raises(H.HsError):  # position beyond the pool length
+            H.hs_buffer_state_set(buf, np.array([16, -1, -1, -1], np.int32),
+                                  np.array([3, 0, 0, 0], np.uint32), 5)
+        H.hs_buffer_state_set(buf, pos, np.array([9, 0, 0, 0], np.uint32), 0x7FFFFFFE)
+        sess.step(0)
+        torch.cuda.synchronize()
+        p, s, c, e = sess.state(0, 0)
+        assert c == 0x7FFFFFFF and e == 0 and s[0] == 2 * 0x7FFFFFFF
+        sess.step(1)
+        torch.cuda.synchronize()
+        p, s, c, e = sess.state(0, 0)
+        assert c == 0x7FFFFFFF and e & H.HS_ERR_CLOCK
+    finally:
+        sess.close()
+
+
+def test_host_argument_checks():
+    w = _small("mha", I.F32, 8, 4, 64, 1, 1, seed=12)
+    sess = Session(w, 1, fill="full")
+    try:
+        b = sess.batches[0]
+        with pytest.raises(H.HsError):
+            H.hs_resolve(b, sess.topk[0, 0], 9, sess.slots[0], sess.miss[0])  # k > B
+        with pytest.raises(H.HsError):
+            H.hs_resolve(b, sess.topk[0, 0], 0, sess.slots[0], sess.miss[0])
+        with pytest.raises(H.HsError):
+            H.hs_pool_append(sess.pool, 0, 0, 70, np.zeros((1, w.rec_bytes), np.uint8))
+        with pytest.raises(H.HsError):
+            H.hs_pool_append(sess.pool, 1, 0, 0, np.zeros((1, w.rec_bytes), np.uint8))
+        with pytest.raises(H.HsError):
+            H.hs_sparse_attn(b, sess.q[0, 0], 3, sess.slots[0], 4, 0.1, sess.out[0], sess.ws)
+    finally:
+        sess.close()
+
+
+def test_invalid_slot_gives_nan_and_error_bit():
+    w = _small("mha", I.BF16, 64, 40, 500, 1, 1, seed=13, Hkv=2, D=128, Hq=4)
+    sess = Session(w, 1, fill="full")
+    try:
+        sess.step(0)
+        torch.cuda.synchronize()
+        bad = sess.slots.clone()
+        bad[0, 0, 17] = 64  # == B
+        H.hs_sparse_attn(sess.batches[0], sess.q[0, 0], 4, bad[0], 40, 0.1, sess.out[0], sess.ws)
+        torch.cuda.synchronize()
+        assert np.isnan(sess.out.cpu().numpy()).all()
+        assert sess.state(0, 0)[3] & H.HS_ERR_SLOT
+    finally:
+        sess.close()
+
+
+@pytest.mark.parametrize("wl", [1, 3])
+def test_exactness_against_full_kv_buffer(wl):
+    # attention through the resolved slots equals the same kernel over a
+    # full-KV buffer (slot = position), bit for bit
+    w = I.workload(wl)
+    steps = 4
+    sess = Session(w, steps, fill="full")
+    try:
+        full_B = w.ctx[0]
+        t_mem = torch.empty(H.hs_buffer_bytes(sess.pool, full_B), dtype=torch.uint8, device="cuda")
+        fb = H.hs_buffer_create(sess.pool, 0, 0, full_B, t_mem)
+        H.hs_buffer_state_set(fb, np.arange(full_B, dtype=np.int32),
+                              np.ones(full_B, dtype=np.uint32), 1)
+        fbatch = H.hs_batch_create([fb])
+        # single-unit batches on both sides, so the split plans are the same
+        b1 = H.hs_batch_create([sess.bufs[0][0]])
+        out_res = torch.empty_like(sess.out[0, :1])
+        out_full = torch.empty_like(sess.out[0, :1])
+        ws = torch.empty(max(256, H.hs_sparse_attn_workspace(fbatch, w.n_q_heads, w.k)),
+                         dtype=torch.uint8, device="cuda")
+        for t in range(steps):
+            sess.step(t)
+            H.hs_sparse_attn(b1, sess.q[t, 0, :1], w.n_q_heads, sess.slots[0, :1], w.k,
+                             w.sm_scale, out_res, ws)
+            H.hs_sparse_attn(fbatch, sess.q[t, 0, :1], w.n_q_heads, sess.topk[t, 0, :1], w.k,
+                             w.sm_scale, out_full, ws)
+            torch.cuda.synchronize()
+            a = out_res.cpu().numpy().view(np.uint32)
+            b = out_full.cpu().numpy().view(np.uint32)
+            assert np.array_equal(a, b), f"step {t}"
+        H.hs_batch_destroy(b1)
+        H.hs_batch_destroy(fbatch)
+        H.hs_buffer_destroy(fb)
+    finally:
+        sess.close()

@@ -1,0 +1,288 @@
+// Top-k sparse decode attention over resolved slots, MHA/GQA record layout
+// ([K: Hkv x D][V: Hkv x D] per row), plus the split-k combine.
+//
+// HiSparse summary (marsggbo.github.io, 2026-09-23), section 3, arrow 4:
+// the physical slots go to the sparse-attention backend, which gathers the
+// selected rows from the device buffer; the output equals full-KV attention
+// at the selected positions. The page does not describe the backend; this
+// one is written for gfx950.
+//
+// Design: the work is HBM-bound (about 1 flop per byte), so it stays on the
+// vector ALUs. A group of LPS lanes owns one slot's K (or V) slice of one KV
+// head (16 bytes per lane, LPS = D * sizeof(T) / 16), so a wave reads
+// 64 / LPS whole slices per load instruction. Every lane keeps the online
+// softmax state (running max and sum in log2 units, and its 16-byte share of
+// the value accumulator) for the GQ query heads of its KV head. Loads of
+// UNROLL slots are issued before any of them is used. The split-k factor
+// spreads a unit's k slots over enough workgroups to fill 256 CUs; each
+// workgroup writes (m, l, acc) partials that hs_k_combine merges. The split
+// boundaries depend only on the index in the selection, never on the slot,
+// so the slot-indirected result is bit-identical to the same computation
+// over a full-KV copy.
+#include "hs_device.h"
+
+namespace hs {
+
+namespace {
+
+constexpr int MHA_THREADS = 256;
+constexpr int MHA_WAVES = MHA_THREADS / 64;
+constexpr int MHA_UNROLL = 4;
+constexpr float NEG_INF = -__builtin_huge_valf();
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+template <typename T>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int EPL = 4;  // elements per 16 bytes
+  __device__ static void unpack(const v4u &w, float *f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(w[e]);
+  }
+};
+template <>
+struct Elem<uint16_t> {  // bfloat16 bits
+  static constexpr int EPL = 8;
+  __device__ static void unpack(const v4u &w, float *f) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f[2 * e] = __uint_as_float(w[e] << 16);
+      f[2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+    }
+  }
+};
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Merge state (m2, l2, a2) into (m, l, a); m in log2 units, -inf = empty.
+template <int EPL>
+__device__ __forceinline__ void merge_state(float &m, float &l, float *a, float m2, float l2,
+                                            const float *a2) {
+  const float mn = fmaxf(m, m2);
+  const float f1 = (m == NEG_INF) ? 0.f : exp2_fast(m - mn);
+  const float f2 = (m2 == NEG_INF) ? 0.f : exp2_fast(m2 - mn);
+  l = l * f1 + l2 * f2;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) a[e] = a[e] * f1 + a2[e] * f2;
+  m = mn;
+}
+
+template <typename T, int D, int GQ>
+__global__ __launch_bounds__(MHA_THREADS) void hs_k_attn_mha(
+    const UnitDesc *__restrict__ units, const T *__restrict__ q_all,
+    const int32_t *__restrict__ slots_all, int k, int Hq, int Hkv, float scale_log2,
+    int S, int chunk, int rec_bytes, float *__restrict__ ws_o, float *__restrict__ ws_ml,
+    float *__restrict__ out) {
+  constexpr int EPL = Elem<T>::EPL;
+  constexpr int LPS = D / EPL;          // lanes per slice
+  constexpr int NG = 64 / LPS;          // slice groups per wave
+  constexpr int NGW = NG * MHA_WAVES;   // slice groups per workgroup
+  static_assert(LPS >= 1 && LPS <= 64 && (64 % LPS) == 0, "bad slice width");
+
+  __shared__ float s_acc[MHA_WAVES][GQ][D];
+  __shared__ float s_ml[MHA_WAVES][GQ][2];
+
+  const int b = blockIdx.x;
+  const int s = b % S;
+  const int rest = b / S;
+  const int g = rest % Hkv;
+  const int u = rest / Hkv;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int grp = wave * NG + lane / LPS;
+  const int gl = lane % LPS;
+
+  const UnitDesc d = units[u];
+  const int B = d.B;
+  const int i_begin = s * chunk;
+  const int i_end = min(k, i_begin + chunk);
+  const int32_t *slots = slots_all + (size_t)u * k;
+
+  float qf[GQ][EPL];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    const v4u w = *(const v4u *)(q_all + ((size_t)u * Hq + g * GQ + h) * D + gl * EPL);
+    Elem<T>::unpack(w, qf[h]);
+  }
+  const size_t koff = (size_t)g * D * sizeof(T) + (size_t)gl * 16;
+  const size_t voff = (size_t)(Hkv + g) * D * sizeof(T) + (size_t)gl * 16;
+
+  float m_run[GQ], l_run[GQ], acc[GQ][EPL];
+#pragma unroll
+  for (int h = 0; h < GQ; ++h) {
+    m_run[h] = NEG_INF;
+    l_run[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
+  }
+  bool bad = false;
+
+  for (int i0 = i_begin + grp; i0 < i_end; i0 += MHA_UNROLL * NGW) {
+    v4u kw[MHA_UNROLL], vw[MHA_UNROLL];
+    bool valid[MHA_UNROLL];
+#pragma unroll
+    for (int uu = 0; uu < MHA_UNROLL; ++uu) {
+      const int i = i0 + uu * NGW;
+      valid[uu] = i < i_end;
+      int slot = valid[uu] ? slots[i] : 0;
+      if ((unsigned)slot >= (unsigned)B) {
+        bad = true;
+        slot = 0;
+      }
+      const uint8_t *row = d.rows + (size_t)slot * rec_bytes;
+      if (valid[uu]) {
+        kw[uu] = *(const v4u *)(row + koff);
+        vw[uu] = *(const v4u *)(row + voff);
+      } else {
+        kw[uu] = v4u{0, 0, 0, 0};
+        vw[uu] = v4u{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int uu = 0; uu < MHA_UNROLL; ++uu) {
+      float kf[EPL], vf[EPL];
+      Elem<T>::unpack(kw[uu], kf);
+      Elem<T>::unpack(vw[uu], vf);
+#pragma unroll
+      for (int h = 0; h < GQ; ++h) {
+        float dot = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dot = fmaf(qf[h][e], kf[e], dot);
+#pragma unroll
+        for (int o = LPS / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
+        if (valid[uu]) {
+          const float sc = dot * scale_log2;
+          const float mn = fmaxf(m_run[h], sc);
+          const float a = exp2_fast(m_run[h] - mn);
+          const float p = exp2_fast(sc - mn);
+          l_run[h] = l_run[h] * a + p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) acc[h][e] = fmaf(acc[h][e], a, p * vf[e]);
+          m_run[h] = mn;
+        }
+      }
+    }
+  }
+
+  // merge the slice groups of a wave (butterfly over lane offsets >= LPS)
+#pragma unroll
+  for (int o = LPS; o < 64; o <<= 1) {
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+      const float m2 = __shfl_xor(m_run[h], o, 64);
+      const float l2 = __shfl_xor(l_run[h], o, 64);
+      float a2[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a2[e] = __shfl_xor(acc[h][e], o, 64);
+      merge_state<EPL>(m_run[h], l_run[h], acc[h], m2, l2, a2);
+    }
+  }
+  if (lane < LPS) {
+#pragma unroll
+    for (int h = 0; h < GQ; ++h) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) s_acc[wave][h][gl * EPL + e] = acc[h][e];
+      if (lane == 0) {
+        s_ml[wave][h][0] = m_run[h];
+        s_ml[wave][h][1] = l_run[h];
+      }
+    }
+  }
+  const int any_bad = __syncthreads_or(bad ? 1 : 0);
+  if (any_bad && tid == 0) atomicOr(&d.ctl[CTL_ERR], HS_ERR_SLOT);
+
+  // merge the waves; threads index (head, element)
+  for (int t = tid; t < GQ * D; t += MHA_THREADS) {
+    const int h = t / D, e = t - h * D;
+    float m = s_ml[0][h][0], l = s_ml[0][h][1], a = s_acc[0][h][e];
+#pragma unroll
+    for (int w = 1; w < MHA_WAVES; ++w)
+      merge_state<1>(m, l, &a, s_ml[w][h][0], s_ml[w][h][1], &s_acc[w][h][e]);
+    const size_t row = (size_t)u * Hq + g * GQ + h;
+    if (S == 1) {
+      out[row * D + e] = any_bad ? __builtin_nanf("") : a / l;
+    } else {
+      ws_o[(row * S + s) * D + e] = a;
+      if (e == 0) {
+        ws_ml[(row * S + s) * 2] = any_bad ? __builtin_nanf("") : m;
+        ws_ml[(row * S + s) * 2 + 1] = l;
+      }
+    }
+  }
+}
+
+// Merge S split partials per output row. Grid: rows; block: 256 threads.
+__global__ __launch_bounds__(256) void hs_k_combine(const float *__restrict__ ws_o,
+                                                    const float *__restrict__ ws_ml, int S,
+                                                    int dv, float *__restrict__ out) {
+  const size_t row = blockIdx.x;
+  const float *ml = ws_ml + row * S * 2;
+  float M = NEG_INF;
+  bool nan = false;
+  for (int s = 0; s < S; ++s) {
+    const float m = ml[2 * s];
+    nan |= (m != m);
+    M = fmaxf(M, m);
+  }
+  float L = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float m = ml[2 * s];
+    if (m != NEG_INF) L += exp2_fast(m - M) * ml[2 * s + 1];
+  }
+  for (int e = threadIdx.x; e < dv; e += blockDim.x) {
+    float o = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float m = ml[2 * s];
+      if (m != NEG_INF) o = fmaf(exp2_fast(m - M), ws_o[(row * S + s) * dv + e], o);
+    }
+    out[row * dv + e] = nan ? __builtin_nanf("") : o / L;
+  }
+}
+
+template <typename T, int D, int GQ>
+hipError_t launch_mha_t(const AttnMhaArgs &a, hipStream_t stream) {
+  const int grid = a.n_units * a.Hkv * a.splits;
+  trace_begin(HS_TRACE_ATTN, stream);
+  hipLaunchKernelGGL((hs_k_attn_mha<T, D, GQ>), dim3(grid), dim3(MHA_THREADS), 0, stream,
+                     a.units, (const T *)a.q, a.slots, a.k, a.Hq, a.Hkv, a.scale_log2,
+                     a.splits, a.chunk, a.rec_bytes, a.ws_o, a.ws_ml, a.out);
+  trace_end(stream);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_mha_d(const AttnMhaArgs &a, hipStream_t stream) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_mha_t<T, D, 1>(a, stream);
+    case 2: return launch_mha_t<T, D, 2>(a, stream);
+    case 4: return launch_mha_t<T, D, 4>(a, stream);
+    case 8: return launch_mha_t<T, D, 8>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_mha(const AttnMhaArgs &a, hipStream_t stream) {
+  hipError_t e;
+  if (a.dtype == HS_F32)
+    e = a.D == 64 ? launch_mha_d<float, 64>(a, stream) : launch_mha_d<float, 128>(a, stream);
+  else
+    e = a.D == 64 ? launch_mha_d<uint16_t, 64>(a, stream)
+                  : launch_mha_d<uint16_t, 128>(a, stream);
+  if (e != hipSuccess || a.splits == 1) return e;
+  return launch_combine(a.ws_o, a.ws_ml, a.n_units * a.Hq, a.splits, a.D, a.out, stream);
+}
+
+hipError_t launch_combine(const float *ws_o, const float *ws_ml, int rows, int splits, int dv,
+                          float *out, hipStream_t stream) {
+  trace_begin(HS_TRACE_COMBINE, stream);
+  hipLaunchKernelGGL(hs_k_combine, dim3(rows), dim3(256), 0, stream, ws_o, ws_ml, splits, dv,
+                     out);
+  trace_end(stream);
+  return hipGetLastError();
+}
+
+}  // namespace hs

@@ -1,0 +1,515 @@
+// RESOLVE on gfx950: hit detection, LRU victim selection, in-place update and
+// the batched fetch of missing records from pinned host memory.
+//
+// HiSparse summary (marsggbo.github.io, 2026-09-23), section 5: the selected
+// positions go into an on-chip hash table; every buffer slot probes it in
+// parallel and is marked hit or stale; a parallel scan picks the victims and
+// updates the LRU state in place (hits most recent, fetched misses right
+// after them); GPU threads then load the missing records straight from
+// pinned host memory into the slots they claimed; the slot vector published
+// for attention is aligned with the selection. Section 4: the state is kept
+// across steps, never rebuilt from the current selection.
+//
+// Design on MI355X:
+//  * hs_k_resolve: one 1024-thread workgroup per unit (request, layer).
+//    Thread t owns a contiguous run of SPT slots and KPT selection entries,
+//    so ranks in slot order and in selection order are one exclusive block
+//    scan of per-thread counts (wave64 shuffles + one LDS pass over waves).
+//    The hash table is open addressing with linear probing in LDS,
+//    capacity the power of two >= 2k, keys inserted with atomicCAS.
+//    Victims are the m smallest 64-bit keys (stamp << 32 | secondary) among
+//    non-hit slots, where secondary = slot for an empty slot and B + position
+//    otherwise; keys are distinct, so an MSB-first radix select with 8-bit
+//    digits (LDS histogram, one wave scans it) finds the exact threshold.
+//    Leading digits shared by every candidate are skipped, and the select
+//    stops at the first digit whose bucket is taken whole.
+//  * hs_k_gather: the fetch list is copied by many workgroups per unit with
+//    16-byte non-temporal loads from the device-mapped host pool, several
+//    loads in flight per lane, so the host link sees many outstanding reads
+//    even at small batch.
+#include "hs_device.h"
+
+namespace hs {
+
+namespace {
+
+constexpr int RES_THREADS = 1024;
+constexpr int RES_WAVES = RES_THREADS / 64;
+constexpr int EMPTY_KEY = -1;
+
+__device__ __forceinline__ uint32_t hash_pos(int32_t p, int hlog2) {
+  return ((uint32_t)p * 0x9E3779B1u) >> (32 - hlog2);
+}
+
+// Exclusive scan of one int per thread over the block; *total gets the sum.
+// buf: RES_WAVES ints of LDS. Ends with a barrier so buf can be reused.
+__device__ __forceinline__ int block_excl_scan(int v, int *total, int *buf) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) buf[wid] = x;
+  __syncthreads();
+  if (wid == 0) {
+    int w = lane < RES_WAVES ? buf[lane] : 0;
+#pragma unroll
+    for (int o = 1; o < RES_WAVES; o <<= 1) {
+      int y = __shfl_up(w, o, 64);
+      if (lane >= o) w += y;
+    }
+    if (lane < RES_WAVES) buf[lane] = w;
+  }
+  __syncthreads();
+  const int before = wid ? buf[wid - 1] : 0;
+  *total = buf[RES_WAVES - 1];
+  __syncthreads();
+  return before + x - v;
+}
+
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    uint64_t y = __shfl_xor(v, o, 64);
+    v = y < v ? y : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    uint64_t y = __shfl_xor(v, o, 64);
+    v = y > v ? y : v;
+  }
+  return v;
+}
+
+template <int SPT, int KPT>
+__global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
+    const UnitDesc *__restrict__ units, const int32_t *__restrict__ topk_all,
+    int k, int hlog2, int32_t *__restrict__ slots_all,
+    int32_t *__restrict__ miss_all) {
+  // LDS: region A holds the hash table (keys, values: 2H ints) during build
+  // and probe, then the miss and victim lists (2k ints); region B holds
+  // slot_of[k].
+  extern __shared__ int lds[];
+  __shared__ int scan_buf[RES_WAVES];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t s_flag;
+  __shared__ unsigned long long s_min, s_max;
+  __shared__ int s_digit, s_below, s_bucket;
+
+  const int H = 1 << hlog2;
+  int *hkey = lds;
+  int *hval = lds + H;
+  int *miss_list = lds;
+  int *victim_list = lds + k;
+  const int regionA = (2 * H > 2 * k) ? 2 * H : 2 * k;
+  int *slot_of = lds + regionA;
+
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x;
+  const UnitDesc d = units[u];
+  const int B = d.B;
+  const int32_t *topk = topk_all + (size_t)u * k;
+  int32_t *slots = slots_all + (size_t)u * k;
+  const int64_t len = *d.len;
+  const uint32_t clock = d.ctl[CTL_CLOCK];
+
+  for (int i = tid; i < H; i += RES_THREADS) hkey[i] = EMPTY_KEY;
+  for (int i = tid; i < k; i += RES_THREADS) slot_of[i] = -1;
+  if (tid == 0) {
+    s_flag = clock >= 0x7FFFFFFFu ? HS_ERR_CLOCK : 0u;
+    s_min = ~0ull;
+    s_max = 0ull;
+  }
+  __syncthreads();
+
+  // ---- 1. hash build of the selection (and range / duplicate checks)
+  const int k0 = tid * KPT;
+  uint32_t myflag = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int i = k0 + j;
+    if (i >= k) break;
+    const int32_t p = topk[i];
+    if (p < 0 || (int64_t)p >= len) {
+      myflag |= HS_ERR_RANGE;
+      continue;
+    }
+    uint32_t h = hash_pos(p, hlog2);
+    while (true) {
+      const int old = atomicCAS(&hkey[h], EMPTY_KEY, p);
+      if (old == EMPTY_KEY) {
+        hval[h] = i;
+        break;
+      }
+      if (old == p) {
+        myflag |= HS_ERR_DUP;
+        break;
+      }
+      h = (h + 1) & (uint32_t)(H - 1);
+    }
+  }
+  if (myflag) atomicOr(&s_flag, myflag);
+  __syncthreads();
+  const uint32_t flag = s_flag;
+  if (flag) {
+    for (int i = tid; i < k; i += RES_THREADS) slots[i] = -1;
+    if (tid == 0) {
+      d.ctl[CTL_ERR] |= flag;
+      d.ctl[CTL_FETCH] = 0;
+      if (miss_all) miss_all[u] = -1;
+    }
+    return;
+  }
+
+  // ---- 2. probe every slot of the buffer
+  const int s0 = tid * SPT;
+  int32_t sp[SPT];
+  uint32_t st[SPT];
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int s = s0 + j;
+    sp[j] = s < B ? d.pos[s] : -1;
+    st[j] = s < B ? d.stamp[s] : 0u;
+  }
+  uint32_t hitmask = 0;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int32_t p = sp[j];
+    if (s0 + j >= B || p < 0) continue;
+    uint32_t h = hash_pos(p, hlog2);
+    while (true) {
+      const int kk = hkey[h];
+      if (kk == p) {
+        slot_of[hval[h]] = s0 + j;
+        hitmask |= 1u << j;
+        break;
+      }
+      if (kk == EMPTY_KEY) break;
+      h = (h + 1) & (uint32_t)(H - 1);
+    }
+  }
+  __syncthreads();  // slot_of complete; the hash table is dead from here on
+
+  // ---- 3. misses in selection order
+  int my_miss = 0;
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int i = k0 + j;
+    if (i < k && slot_of[i] < 0) ++my_miss;
+  }
+  int m;
+  int mrank = block_excl_scan(my_miss, &m, scan_buf);
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int i = k0 + j;
+    if (i < k && slot_of[i] < 0) miss_list[mrank++] = i;
+  }
+  const int n_cand = B - (k - m);
+
+  // ---- 4. victims: the m smallest keys among non-hit slots
+  uint64_t key[SPT];
+  uint32_t candmask = 0;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int s = s0 + j;
+    const uint32_t second = sp[j] < 0 ? (uint32_t)s : (uint32_t)(B + sp[j]);
+    key[j] = ((uint64_t)st[j] << 32) | second;
+    if (s < B && !((hitmask >> j) & 1u)) candmask |= 1u << j;
+  }
+  uint32_t vmask = 0;
+  if (m == n_cand) {
+    vmask = candmask;
+  } else if (m > 0) {
+    uint64_t lo = ~0ull, hi = 0ull;
+#pragma unroll
+    for (int j = 0; j < SPT; ++j)
+      if ((candmask >> j) & 1u) {
+        lo = key[j] < lo ? key[j] : lo;
+        hi = key[j] > hi ? key[j] : hi;
+      }
+    lo = wave_min_u64(lo);
+    hi = wave_max_u64(hi);
+    if ((tid & 63) == 0) {
+      atomicMin(&s_min, (unsigned long long)lo);
+      atomicMax(&s_max, (unsigned long long)hi);
+    }
+    __syncthreads();
+    const uint64_t kmin = s_min, kmax = s_max;
+    const int hb = 63 - __clzll((long long)(kmin ^ kmax));  // n_cand >= 2, keys distinct
+    int sh = (hb / 8) * 8;
+    uint64_t prefix = kmin;
+    int need = m;
+    int final_sh = 0;
+    while (true) {
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < SPT; ++j) {
+        if (!((candmask >> j) & 1u)) continue;
+        const bool match = (sh + 8 >= 64) || ((key[j] >> (sh + 8)) == (prefix >> (sh + 8)));
+        if (match) atomicAdd(&hist[(key[j] >> sh) & 255u], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        const uint32_t c0 = hist[4 * tid], c1 = hist[4 * tid + 1];
+        const uint32_t c2 = hist[4 * tid + 2], c3 = hist[4 * tid + 3];
+        const int tot = (int)(c0 + c1 + c2 + c3);
+        int incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          int y = __shfl_up(incl, o, 64);
+          if (tid >= o) incl += y;
+        }
+        const int excl = incl - tot;
+        if (excl < need && need <= incl) {
+          const uint32_t c[4] = {c0, c1, c2, c3};
+          int run = excl;
+          for (int b = 0; b < 4; ++b) {
+            if (run + (int)c[b] >= need) {
+              s_digit = 4 * tid + b;
+              s_below = run;
+              s_bucket = (int)c[b];
+              break;
+            }
+            run += (int)c[b];
+          }
+        }
+      }
+      __syncthreads();
+      const int dg = s_digit;
+      need -= s_below;
+      const uint64_t mask_low = (sh + 8 >= 64) ? ~0ull : ((1ull << (sh + 8)) - 1ull);
+      prefix = (prefix & ~mask_low) | ((uint64_t)dg << sh);
+      if (need == s_bucket || sh == 0) {
+        final_sh = sh;
+        break;
+      }
+      sh -= 8;
+    }
+    const uint64_t lim = prefix >> final_sh;
+#pragma unroll
+    for (int j = 0; j < SPT; ++j)
+      if (((candmask >> j) & 1u) && (key[j] >> final_sh) <= lim) vmask |= 1u << j;
+  }
+
+  // ---- 5. rank victims in ascending slot order and pair them with misses
+  int vtot;
+  int vrank = block_excl_scan(__popc(vmask), &vtot, scan_buf);
+  if (vtot != m) {
+    // cannot happen for a valid state (keys are distinct); refuse to update
+    for (int i = tid; i < k; i += RES_THREADS) slots[i] = -1;
+    if (tid == 0) {
+      d.ctl[CTL_ERR] |= HS_ERR_INTERNAL;
+      d.ctl[CTL_FETCH] = 0;
+      if (miss_all) miss_all[u] = -1;
+    }
+    return;
+  }
+#pragma unroll
+  for (int j = 0; j < SPT; ++j)
+    if ((vmask >> j) & 1u) victim_list[vrank++] = s0 + j;
+  __syncthreads();
+
+  // ---- 6. in-place update: fills get 2c - 1, hits get 2c
+  const uint32_t c = clock + 1u;
+  for (int r = tid; r < m; r += RES_THREADS) {
+    const int s = victim_list[r];
+    const int i = miss_list[r];
+    const int32_t p = topk[i];
+    d.pos[s] = p;
+    d.stamp[s] = 2u * c - 1u;
+    slot_of[i] = s;
+    d.work[r] = make_int2(s, p);
+  }
+#pragma unroll
+  for (int j = 0; j < SPT; ++j)
+    if ((hitmask >> j) & 1u) d.stamp[s0 + j] = 2u * c;
+  __syncthreads();
+
+  // ---- 7. publish the slot vector, aligned with the selection
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) {
+    const int i = k0 + j;
+    if (i < k) slots[i] = slot_of[i];
+  }
+  if (tid == 0) {
+    d.ctl[CTL_CLOCK] = c;
+    d.ctl[CTL_FETCH] = (uint32_t)m;
+    if (miss_all) miss_all[u] = m;
+  }
+}
+
+// Copy each unit's fetch list from host records into device rows.
+// Grid: n_units * G workgroups of 256 threads; workgroup g of unit u walks
+// the unit's 16-byte chunks g*256 + tid, stepping by G*256.
+constexpr int GATHER_THREADS = 256;
+constexpr int GATHER_UNROLL = 4;
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(GATHER_THREADS) void hs_k_gather(
+    const UnitDesc *__restrict__ units, int G, int rec16) {
+  const int u = blockIdx.x / G;
+  const int g = blockIdx.x - u * G;
+  const UnitDesc d = units[u];
+  const int m = (int)d.ctl[CTL_FETCH];
+  if (m <= 0 || m > d.B) return;
+  const int total = m * rec16;
+  const int stride = G * GATHER_THREADS;
+  const size_t rec = (size_t)rec16 * 16;
+  for (int c0 = g * GATHER_THREADS + (int)threadIdx.x; c0 < total;
+       c0 += stride * GATHER_UNROLL) {
+    v4u v[GATHER_UNROLL];
+    v4u *dst[GATHER_UNROLL];
+#pragma unroll
+    for (int uu = 0; uu < GATHER_UNROLL; ++uu) {
+      const int c = c0 + uu * stride;
+      dst[uu] = nullptr;
+      if (c < total) {
+        const int r = c / rec16;
+        const int off = c - r * rec16;
+        const int2 w = d.work[r];
+        const v4u *src = (const v4u *)(d.pool + (size_t)w.y * rec) + off;
+        v[uu] = __builtin_nontemporal_load(src);
+        dst[uu] = (v4u *)(d.rows + (size_t)w.x * rec) + off;
+      }
+    }
+#pragma unroll
+    for (int uu = 0; uu < GATHER_UNROLL; ++uu)
+      if (dst[uu]) *dst[uu] = v[uu];
+  }
+}
+
+// Re-gather every occupied row of one buffer (checkpoint restore).
+__global__ __launch_bounds__(256) void hs_k_regather(const UnitDesc *__restrict__ unit,
+                                                     int B, int rec16) {
+  const UnitDesc d = *unit;
+  const size_t rec = (size_t)rec16 * 16;
+  const int64_t total = (int64_t)B * rec16;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int s = (int)(c / rec16);
+    const int off = (int)(c - (int64_t)s * rec16);
+    const int32_t p = d.pos[s];
+    if (p < 0) continue;
+    const v4u *src = (const v4u *)(d.pool + (size_t)p * rec) + off;
+    ((v4u *)(d.rows + (size_t)s * rec))[off] = __builtin_nontemporal_load(src);
+  }
+}
+
+__global__ void hs_k_buffer_init(int32_t *pos, uint32_t *stamp, uint32_t *ctl, int B) {
+  for (int s = blockIdx.x * blockDim.x + threadIdx.x; s < B; s += gridDim.x * blockDim.x) {
+    pos[s] = -1;
+    stamp[s] = 0u;
+  }
+  if (blockIdx.x == 0 && threadIdx.x < CTL_WORDS) ctl[threadIdx.x] = 0u;
+}
+
+// Write-through append from device memory into the mapped host pool, then
+// extend the unit's length.
+__global__ __launch_bounds__(256) void hs_k_append(uint8_t *dst, const uint8_t *src,
+                                                   int64_t n16, int64_t *len,
+                                                   int64_t new_len) {
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n16;
+       c += (int64_t)gridDim.x * blockDim.x)
+    ((v4u *)dst)[c] = ((const v4u *)src)[c];
+  if (blockIdx.x == 0 && threadIdx.x == 0 && *len < new_len) *len = new_len;
+}
+
+template <int SPT, int KPT>
+hipError_t launch_select(const UnitDesc *d_units, int n, const int32_t *d_topk, int k,
+                         int hlog2, size_t lds, int32_t *d_slots, int32_t *d_miss,
+                         hipStream_t stream) {
+  trace_begin(HS_TRACE_SELECT, stream);
+  hipLaunchKernelGGL((hs_k_resolve<SPT, KPT>), dim3(n), dim3(RES_THREADS), lds, stream,
+                     d_units, d_topk, k, hlog2, d_slots, d_miss);
+  trace_end(stream);
+  return hipGetLastError();
+}
+
+template <int SPT>
+hipError_t launch_select_k(const UnitDesc *d_units, int n, const int32_t *d_topk, int k,
+                           int hlog2, size_t lds, int32_t *d_slots, int32_t *d_miss,
+                           hipStream_t stream) {
+  if (k <= RES_THREADS)
+    return launch_select<SPT, 1>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+  if (k <= 2 * RES_THREADS)
+    return launch_select<SPT, 2>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+  return launch_select<SPT, 4>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+}
+
+int hash_log2(int k) {
+  int h = 1;
+  while ((1 << h) < 2 * k) ++h;
+  return h;
+}
+
+}  // namespace
+
+size_t resolve_lds_bytes(int k) {
+  const int H = 1 << hash_log2(k);
+  const int regionA = (2 * H > 2 * k) ? 2 * H : 2 * k;
+  return (size_t)(regionA + k) * sizeof(int);
+}
+
+hipError_t launch_resolve(const UnitDesc *d_units, int n, int max_B, const int32_t *d_topk,
+                          int k, int32_t *d_slots, int32_t *d_miss, int gather_wgs,
+                          int rec_bytes, hipStream_t stream) {
+  const int hlog2 = hash_log2(k);
+  const size_t lds = resolve_lds_bytes(k);
+  hipError_t e;
+  if (max_B <= RES_THREADS)
+    e = launch_select_k<1>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+  else if (max_B <= 2 * RES_THREADS)
+    e = launch_select_k<2>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+  else if (max_B <= 4 * RES_THREADS)
+    e = launch_select_k<4>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+  else if (max_B <= 8 * RES_THREADS)
+    e = launch_select_k<8>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+  else
+    e = launch_select_k<16>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+  if (e != hipSuccess) return e;
+  trace_begin(HS_TRACE_GATHER, stream);
+  hipLaunchKernelGGL(hs_k_gather, dim3(n * gather_wgs), dim3(GATHER_THREADS), 0, stream,
+                     d_units, gather_wgs, rec_bytes / 16);
+  trace_end(stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_regather(const UnitDesc *d_unit, int B, int rec_bytes, hipStream_t stream) {
+  const int64_t total = (int64_t)B * (rec_bytes / 16);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(hs_k_regather, dim3((unsigned)blocks), dim3(256), 0, stream, d_unit, B,
+                     rec_bytes / 16);
+  return hipGetLastError();
+}
+
+hipError_t launch_buffer_init(int32_t *pos, uint32_t *stamp, uint32_t *ctl, int B,
+                              hipStream_t stream) {
+  int blocks = (B + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(hs_k_buffer_init, dim3(blocks), dim3(256), 0, stream, pos, stamp, ctl, B);
+  return hipGetLastError();
+}
+
+hipError_t launch_append(uint8_t *dst_dev, const uint8_t *src, int64_t bytes, int64_t *d_len,
+                         int64_t new_len, hipStream_t stream) {
+  const int64_t n16 = bytes / 16;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(hs_k_append, dim3((unsigned)blocks), dim3(256), 0, stream, dst_dev, src,
+                     n16, d_len, new_len);
+  return hipGetLastError();
+}
+
+}  // namespace hs

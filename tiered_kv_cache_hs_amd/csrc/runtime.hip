@@ -1,0 +1,664 @@
+// Host runtime of libhisparse: the C ABI declared in include/hisparse.h.
+//
+// Owns the pinned host pool (HiSparse summary, marsggbo.github.io
+// 2026-09-23, section 3: the host copy is authoritative and holds every
+// record), validates arguments, lays out caller-owned device buffers, uploads
+// batch descriptor tables and enqueues the kernels of resolve.hip,
+// attn_mha.hip and attn_latent.hip. Nothing on the enqueue paths allocates
+// or synchronises, so hs_resolve and hs_sparse_attn can be captured in a
+// hipGraph (section 5: the resolve step lives inside the decode graph).
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "hs_device.h"
+
+using hs::UnitDesc;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hs_status fail(hs_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+hs_status hip_fail(hipError_t e, const char *what) {
+  return fail(HS_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HS_HIP(call)                              \
+  do {                                            \
+    hipError_t e_ = (call);                       \
+    if (e_ != hipSuccess) return hip_fail(e_, #call); \
+  } while (0)
+
+hs_tuning g_tuning = {0, 0, {0, 0, 0, 0, 0, 0}};
+
+inline hipStream_t S(void *s) { return (hipStream_t)s; }
+
+// Event pairs of the kernel tracer.
+constexpr int TRACE_CAP = 4096;
+struct TraceState {
+  bool on = false;
+  std::vector<hipEvent_t> begin, end;
+  std::vector<int> cls;
+  int n = 0;        // completed pairs recorded
+  int pending = -1; // class of the open pair, -1 if none
+  int64_t dropped = 0;
+};
+TraceState g_trace;
+
+}  // namespace
+
+namespace hs {
+
+void trace_begin(int cls, hipStream_t stream) {
+  if (!g_trace.on) return;
+  if (g_trace.n >= TRACE_CAP) {
+    ++g_trace.dropped;
+    g_trace.pending = -1;
+    return;
+  }
+  if (hipEventRecord(g_trace.begin[g_trace.n], stream) != hipSuccess) {
+    g_trace.pending = -1;
+    return;
+  }
+  g_trace.pending = cls;
+}
+
+void trace_end(hipStream_t stream) {
+  if (!g_trace.on || g_trace.pending < 0) return;
+  if (hipEventRecord(g_trace.end[g_trace.n], stream) == hipSuccess) {
+    g_trace.cls[g_trace.n] = g_trace.pending;
+    ++g_trace.n;
+  }
+  g_trace.pending = -1;
+}
+
+}  // namespace hs
+
+struct hs_pool_s {
+  int32_t R = 0, L = 0, kind = 0, dtype = 0, Hkv = 0, D = 0, Dl = 0, Dr = 0;
+  size_t rec = 0;
+  std::vector<int64_t> cap;
+  std::vector<uint8_t *> host;  // per request: L * cap[r] records
+  std::vector<uint8_t *> dev;   // device-visible address of host[r]
+  int64_t *d_len = nullptr;     // [R * L]
+  std::vector<int64_t> shadow;  // lengths as of the calls made so far
+  int device = 0;
+};
+
+struct hs_buffer_s {
+  hs_pool_t pool = nullptr;
+  int32_t req = 0, layer = 0, B = 0;
+  uint8_t *mem = nullptr;
+  hs::BufferLayout lay{};
+  UnitDesc desc{};
+  UnitDesc *d_desc = nullptr;  // single-unit table (state restore)
+};
+
+struct hs_batch_s {
+  hs_pool_t pool = nullptr;
+  int32_t n = 0, min_B = 0, max_B = 0;
+  UnitDesc *d_units = nullptr;
+};
+
+extern "C" {
+
+const char *hs_status_str(hs_status s) {
+  switch (s) {
+    case HS_OK: return "ok";
+    case HS_E_INVAL: return "invalid argument";
+    case HS_E_RANGE: return "out of range";
+    case HS_E_NOMEM: return "out of memory";
+    case HS_E_HIP: return "HIP runtime error";
+    case HS_E_STATE: return "invalid buffer state";
+    default: return "unknown status";
+  }
+}
+
+const char *hs_last_error(void) { return g_last_error.c_str(); }
+
+hs_status hs_set_tuning(const hs_tuning *t) {
+  if (!t) return fail(HS_E_INVAL, "null tuning");
+  if (t->gather_wgs_per_unit < 0 || t->gather_wgs_per_unit > 4096 || t->attn_splits < 0 ||
+      t->attn_splits > 4096)
+    return fail(HS_E_INVAL, "tuning value out of range");
+  g_tuning = *t;
+  return HS_OK;
+}
+
+hs_status hs_get_tuning(hs_tuning *t) {
+  if (!t) return fail(HS_E_INVAL, "null tuning");
+  *t = g_tuning;
+  return HS_OK;
+}
+
+// ------------------------------------------------------------------- pool
+
+hs_status hs_pool_create(const hs_pool_desc *d, hs_pool_t *out) {
+  if (!d || !out) return fail(HS_E_INVAL, "null argument");
+  *out = nullptr;
+  if (d->n_requests < 1 || d->n_layers < 1 || !d->capacity_tokens)
+    return fail(HS_E_INVAL, "need n_requests, n_layers >= 1 and capacities");
+  if (d->dtype != HS_F32 && d->dtype != HS_BF16) return fail(HS_E_INVAL, "bad dtype");
+  const size_t es = d->dtype == HS_F32 ? 4 : 2;
+  size_t rec;
+  if (d->kind == HS_KV_MHA) {
+    if (d->n_kv_heads < 1 || d->head_dim < 1) return fail(HS_E_INVAL, "bad MHA shape");
+    rec = 2 * (size_t)d->n_kv_heads * d->head_dim * es;
+  } else if (d->kind == HS_KV_LATENT) {
+    if (d->latent_dim < 1 || d->rope_dim < 0) return fail(HS_E_INVAL, "bad latent shape");
+    rec = ((size_t)d->latent_dim + d->rope_dim) * es;
+  } else {
+    return fail(HS_E_INVAL, "bad kind");
+  }
+  if (rec % 16) return fail(HS_E_INVAL, "record bytes %zu not a multiple of 16", rec);
+  for (int r = 0; r < d->n_requests; ++r)
+    if (d->capacity_tokens[r] < 1 || d->capacity_tokens[r] > 0x7FFFFFFF)
+      return fail(HS_E_INVAL, "capacity of request %d outside [1, 2^31)", r);
+
+  hs_pool_s *p = new (std::nothrow) hs_pool_s;
+  if (!p) return fail(HS_E_NOMEM, "pool handle");
+  p->R = d->n_requests;
+  p->L = d->n_layers;
+  p->kind = d->kind;
+  p->dtype = d->dtype;
+  p->Hkv = d->n_kv_heads;
+  p->D = d->head_dim;
+  p->Dl = d->latent_dim;
+  p->Dr = d->rope_dim;
+  p->rec = rec;
+  p->cap.assign(d->capacity_tokens, d->capacity_tokens + d->n_requests);
+  p->host.assign(p->R, nullptr);
+  p->dev.assign(p->R, nullptr);
+  p->shadow.assign((size_t)p->R * p->L, 0);
+  (void)hipGetDevice(&p->device);
+  auto cleanup = [p]() {
+    for (auto h : p->host)
+      if (h) (void)hipHostFree(h);
+    if (p->d_len) (void)hipFree(p->d_len);
+    delete p;
+  };
+  for (int r = 0; r < p->R; ++r) {
+    const size_t bytes = (size_t)p->L * (size_t)p->cap[r] * rec;
+    void *h = nullptr;
+    hipError_t e = hipHostMalloc(&h, bytes, hipHostMallocMapped | hipHostMallocCoherent);
+    if (e != hipSuccess || !h) {
+      cleanup();
+      return fail(HS_E_NOMEM, "hipHostMalloc(%zu bytes) for request %d: %s", bytes, r,
+                  hipGetErrorString(e));
+    }
+    p->host[r] = (uint8_t *)h;
+    void *dp = nullptr;
+    e = hipHostGetDevicePointer(&dp, h, 0);
+    if (e != hipSuccess) {
+      cleanup();
+      return hip_fail(e, "hipHostGetDevicePointer");
+    }
+    p->dev[r] = (uint8_t *)dp;
+  }
+  hipError_t e = hipMalloc(&p->d_len, sizeof(int64_t) * p->R * p->L);
+  if (e != hipSuccess) {
+    cleanup();
+    return fail(HS_E_NOMEM, "hipMalloc lengths: %s", hipGetErrorString(e));
+  }
+  e = hipMemset(p->d_len, 0, sizeof(int64_t) * p->R * p->L);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    cleanup();
+    return hip_fail(e, "hipMemset lengths");
+  }
+  *out = p;
+  return HS_OK;
+}
+
+hs_status hs_pool_destroy(hs_pool_t p) {
+  if (!p) return fail(HS_E_INVAL, "null pool");
+  for (auto h : p->host)
+    if (h) (void)hipHostFree(h);
+  if (p->d_len) (void)hipFree(p->d_len);
+  delete p;
+  return HS_OK;
+}
+
+hs_status hs_pool_record_bytes(hs_pool_t p, size_t *rec) {
+  if (!p || !rec) return fail(HS_E_INVAL, "null argument");
+  *rec = p->rec;
+  return HS_OK;
+}
+
+static hs_status check_unit(hs_pool_t p, int32_t req, int32_t layer) {
+  if (!p) return fail(HS_E_INVAL, "null pool");
+  if (req < 0 || req >= p->R || layer < 0 || layer >= p->L)
+    return fail(HS_E_RANGE, "unit (%d, %d) outside %d x %d", req, layer, p->R, p->L);
+  return HS_OK;
+}
+
+static size_t unit_offset(hs_pool_t p, int32_t req, int32_t layer) {
+  return (size_t)layer * (size_t)p->cap[req] * p->rec;
+}
+
+hs_status hs_pool_unit_ptr(hs_pool_t p, int32_t req, int32_t layer, void **host_ptr,
+                           int64_t *capacity) {
+  hs_status s = check_unit(p, req, layer);
+  if (s) return s;
+  if (host_ptr) *host_ptr = p->host[req] + unit_offset(p, req, layer);
+  if (capacity) *capacity = p->cap[req];
+  return HS_OK;
+}
+
+hs_status hs_pool_length(hs_pool_t p, int32_t req, int32_t layer, int64_t *len) {
+  hs_status s = check_unit(p, req, layer);
+  if (s) return s;
+  if (!len) return fail(HS_E_INVAL, "null len");
+  HS_HIP(hipDeviceSynchronize());
+  HS_HIP(hipMemcpy(len, p->d_len + (size_t)req * p->L + layer, sizeof(int64_t),
+                   hipMemcpyDeviceToHost));
+  return HS_OK;
+}
+
+hs_status hs_pool_set_length(hs_pool_t p, int32_t req, int32_t layer, int64_t len) {
+  hs_status s = check_unit(p, req, layer);
+  if (s) return s;
+  if (len < 0 || len > p->cap[req])
+    return fail(HS_E_RANGE, "length %lld outside [0, %lld]", (long long)len,
+                (long long)p->cap[req]);
+  HS_HIP(hipDeviceSynchronize());
+  HS_HIP(hipMemcpy(p->d_len + (size_t)req * p->L + layer, &len, sizeof(int64_t),
+                   hipMemcpyHostToDevice));
+  HS_HIP(hipDeviceSynchronize());
+  p->shadow[(size_t)req * p->L + layer] = len;
+  return HS_OK;
+}
+
+hs_status hs_pool_append(hs_pool_t p, int32_t req, int32_t layer, int64_t pos, int64_t n,
+                         const void *src, int32_t src_on_device, void *stream) {
+  hs_status s = check_unit(p, req, layer);
+  if (s) return s;
+  if (n < 0 || (n > 0 && !src)) return fail(HS_E_INVAL, "bad source");
+  const size_t ui = (size_t)req * p->L + layer;
+  if (pos < 0 || pos > p->shadow[ui] || pos + n > p->cap[req])
+    return fail(HS_E_RANGE, "append [%lld, %lld) with length %lld, capacity %lld",
+                (long long)pos, (long long)(pos + n), (long long)p->shadow[ui],
+                (long long)p->cap[req]);
+  if (n == 0) return HS_OK;
+  const size_t off = unit_offset(p, req, layer) + (size_t)pos * p->rec;
+  const int64_t new_len = std::max(p->shadow[ui], pos + n);
+  if (src_on_device) {
+    if ((uintptr_t)src % 16) return fail(HS_E_INVAL, "device source must be 16-byte aligned");
+    hipError_t e = hs::launch_append(p->dev[req] + off, (const uint8_t *)src,
+                                     (int64_t)n * (int64_t)p->rec, p->d_len + ui, new_len,
+                                     S(stream));
+    if (e != hipSuccess) return hip_fail(e, "append launch");
+  } else {
+    HS_HIP(hipStreamSynchronize(S(stream)));
+    memcpy(p->host[req] + off, src, (size_t)n * p->rec);
+    HS_HIP(hipMemcpyAsync(p->d_len + ui, &new_len, sizeof(int64_t), hipMemcpyHostToDevice,
+                          S(stream)));
+    HS_HIP(hipStreamSynchronize(S(stream)));
+  }
+  p->shadow[ui] = new_len;
+  return HS_OK;
+}
+
+// ----------------------------------------------------------------- buffers
+
+size_t hs_buffer_bytes(hs_pool_t p, int32_t B) {
+  if (!p || B < 1) return 0;
+  return hs::buffer_layout(p->rec, B).total;
+}
+
+hs_status hs_buffer_create(hs_pool_t p, int32_t req, int32_t layer, int32_t B, void *d_mem,
+                           size_t bytes, void *stream, hs_buffer_t *out) {
+  hs_status s = check_unit(p, req, layer);
+  if (s) return s;
+  if (!out || !d_mem) return fail(HS_E_INVAL, "null argument");
+  *out = nullptr;
+  if (B < 1) return fail(HS_E_INVAL, "B must be >= 1");
+  if ((uintptr_t)d_mem % 256) return fail(HS_E_INVAL, "buffer memory must be 256-byte aligned");
+  const hs::BufferLayout lay = hs::buffer_layout(p->rec, B);
+  if (bytes < lay.total)
+    return fail(HS_E_INVAL, "buffer needs %zu bytes, got %zu", lay.total, bytes);
+  hs_buffer_s *b = new (std::nothrow) hs_buffer_s;
+  if (!b) return fail(HS_E_NOMEM, "buffer handle");
+  b->pool = p;
+  b->req = req;
+  b->layer = layer;
+  b->B = B;
+  b->mem = (uint8_t *)d_mem;
+  b->lay = lay;
+  UnitDesc &d = b->desc;
+  d.rows = b->mem + lay.rows;
+  d.pos = (int32_t *)(b->mem + lay.pos);
+  d.stamp = (uint32_t *)(b->mem + lay.stamp);
+  d.work = (int2 *)(b->mem + lay.work);
+  d.ctl = (uint32_t *)(b->mem + lay.ctl);
+  d.pool = p->dev[req] + unit_offset(p, req, layer);
+  d.len = p->d_len + (size_t)req * p->L + layer;
+  d.B = B;
+  d.pad = 0;
+  hipError_t e = hipMalloc(&b->d_desc, sizeof(UnitDesc));
+  if (e == hipSuccess)
+    e = hipMemcpy(b->d_desc, &b->desc, sizeof(UnitDesc), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hs::launch_buffer_init(d.pos, d.stamp, d.ctl, B, S(stream));
+  if (e != hipSuccess) {
+    if (b->d_desc) (void)hipFree(b->d_desc);
+    delete b;
+    return hip_fail(e, "buffer create");
+  }
+  *out = b;
+  return HS_OK;
+}
+
+hs_status hs_buffer_destroy(hs_buffer_t b) {
+  if (!b) return fail(HS_E_INVAL, "null buffer");
+  if (b->d_desc) (void)hipFree(b->d_desc);
+  delete b;
+  return HS_OK;
+}
+
+hs_status hs_buffer_reset(hs_buffer_t b, void *stream) {
+  if (!b) return fail(HS_E_INVAL, "null buffer");
+  hipError_t e = hs::launch_buffer_init(b->desc.pos, b->desc.stamp, b->desc.ctl, b->B, S(stream));
+  if (e != hipSuccess) return hip_fail(e, "buffer reset");
+  return HS_OK;
+}
+
+hs_status hs_buffer_rows(hs_buffer_t b, void **d_rows, size_t *rec_bytes) {
+  if (!b) return fail(HS_E_INVAL, "null buffer");
+  if (d_rows) *d_rows = b->desc.rows;
+  if (rec_bytes) *rec_bytes = b->pool->rec;
+  return HS_OK;
+}
+
+hs_status hs_buffer_state_get(hs_buffer_t b, int32_t *pos, uint32_t *stamp, uint32_t *clock,
+                              int32_t *err, void *stream) {
+  if (!b) return fail(HS_E_INVAL, "null buffer");
+  uint32_t ctl[4];
+  if (pos)
+    HS_HIP(hipMemcpyAsync(pos, b->desc.pos, sizeof(int32_t) * b->B, hipMemcpyDeviceToHost,
+                          S(stream)));
+  if (stamp)
+    HS_HIP(hipMemcpyAsync(stamp, b->desc.stamp, sizeof(uint32_t) * b->B, hipMemcpyDeviceToHost,
+                          S(stream)));
+  HS_HIP(hipMemcpyAsync(ctl, b->desc.ctl, sizeof ctl, hipMemcpyDeviceToHost, S(stream)));
+  HS_HIP(hipStreamSynchronize(S(stream)));
+  if (clock) *clock = ctl[hs::CTL_CLOCK];
+  if (err) *err = (int32_t)ctl[hs::CTL_ERR];
+  return HS_OK;
+}
+
+hs_status hs_buffer_state_set(hs_buffer_t b, const int32_t *pos, const uint32_t *stamp,
+                              uint32_t clock, int32_t err, void *stream) {
+  if (!b || !pos || !stamp) return fail(HS_E_INVAL, "null argument");
+  int64_t len = 0;
+  hs_status s = hs_pool_length(b->pool, b->req, b->layer, &len);
+  if (s) return s;
+  if (clock >= 0x7FFFFFFFu) return fail(HS_E_STATE, "clock %u exhausted", clock);
+  std::vector<int32_t> seen;
+  seen.reserve(b->B);
+  for (int32_t i = 0; i < b->B; ++i) {
+    if (pos[i] < -1 || (int64_t)pos[i] >= len)
+      return fail(HS_E_STATE, "slot %d: position %d outside [-1, %lld)", i, pos[i],
+                  (long long)len);
+    if ((pos[i] < 0) != (stamp[i] == 0))
+      return fail(HS_E_STATE, "slot %d: stamp must be 0 exactly when empty", i);
+    if ((uint64_t)stamp[i] > 2ull * clock)
+      return fail(HS_E_STATE, "slot %d: stamp %u newer than clock %u", i, stamp[i], clock);
+    if (pos[i] >= 0) seen.push_back(pos[i]);
+  }
+  std::sort(seen.begin(), seen.end());
+  if (std::adjacent_find(seen.begin(), seen.end()) != seen.end())
+    return fail(HS_E_STATE, "a position is held by two slots");
+  uint32_t ctl[hs::CTL_WORDS] = {0};
+  ctl[hs::CTL_CLOCK] = clock;
+  ctl[hs::CTL_ERR] = (uint32_t)err;
+  HS_HIP(hipMemcpyAsync(b->desc.pos, pos, sizeof(int32_t) * b->B, hipMemcpyHostToDevice,
+                        S(stream)));
+  HS_HIP(hipMemcpyAsync(b->desc.stamp, stamp, sizeof(uint32_t) * b->B, hipMemcpyHostToDevice,
+                        S(stream)));
+  HS_HIP(hipMemcpyAsync(b->desc.ctl, ctl, sizeof ctl, hipMemcpyHostToDevice, S(stream)));
+  hipError_t e = hs::launch_regather(b->d_desc, b->B, (int)b->pool->rec, S(stream));
+  if (e != hipSuccess) return hip_fail(e, "regather");
+  HS_HIP(hipStreamSynchronize(S(stream)));
+  return HS_OK;
+}
+
+// ----------------------------------------------------------------- batches
+
+hs_status hs_batch_create(const hs_buffer_t *bufs, int32_t n, hs_batch_t *out) {
+  if (!bufs || !out || n < 1) return fail(HS_E_INVAL, "need n >= 1 buffers");
+  *out = nullptr;
+  std::vector<UnitDesc> h(n);
+  hs_pool_t pool = bufs[0] ? bufs[0]->pool : nullptr;
+  int min_B = 0x7FFFFFFF, max_B = 0;
+  for (int i = 0; i < n; ++i) {
+    if (!bufs[i]) return fail(HS_E_INVAL, "null buffer %d", i);
+    if (bufs[i]->pool != pool) return fail(HS_E_INVAL, "buffers of different pools");
+    h[i] = bufs[i]->desc;
+    min_B = std::min(min_B, bufs[i]->B);
+    max_B = std::max(max_B, bufs[i]->B);
+  }
+  hs_batch_s *bt = new (std::nothrow) hs_batch_s;
+  if (!bt) return fail(HS_E_NOMEM, "batch handle");
+  bt->pool = pool;
+  bt->n = n;
+  bt->min_B = min_B;
+  bt->max_B = max_B;
+  hipError_t e = hipMalloc(&bt->d_units, sizeof(UnitDesc) * n);
+  if (e == hipSuccess)
+    e = hipMemcpy(bt->d_units, h.data(), sizeof(UnitDesc) * n, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    if (bt->d_units) (void)hipFree(bt->d_units);
+    delete bt;
+    return hip_fail(e, "batch table");
+  }
+  *out = bt;
+  return HS_OK;
+}
+
+hs_status hs_batch_destroy(hs_batch_t b) {
+  if (!b) return fail(HS_E_INVAL, "null batch");
+  if (b->d_units) (void)hipFree(b->d_units);
+  delete b;
+  return HS_OK;
+}
+
+// ----------------------------------------------------------------- resolve
+
+static int gather_wgs_for(int n_units) {
+  if (g_tuning.gather_wgs_per_unit > 0) return g_tuning.gather_wgs_per_unit;
+  int g = (512 + n_units - 1) / n_units;
+  return std::max(1, std::min(64, g));
+}
+
+hs_status hs_resolve(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_t *d_slots,
+                     int32_t *d_miss, void *stream) {
+  if (!b || !d_topk || !d_slots) return fail(HS_E_INVAL, "null argument");
+  if (k < 1 || k > HS_MAX_K || k > b->min_B)
+    return fail(HS_E_INVAL, "k = %d outside [1, min(%d, smallest B = %d)]", k, HS_MAX_K,
+                b->min_B);
+  if (b->max_B > HS_MAX_B) return fail(HS_E_INVAL, "B = %d above %d", b->max_B, HS_MAX_B);
+  static int lds_limit = -1;
+  if (lds_limit < 0) {
+    int dev = 0, v = 0;
+    HS_HIP(hipGetDevice(&dev));
+    HS_HIP(hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
+    lds_limit = v;
+  }
+  if (hs::resolve_lds_bytes(k) + 2048 > (size_t)lds_limit)
+    return fail(HS_E_INVAL, "k = %d needs %zu bytes of LDS; the device allows %d", k,
+                hs::resolve_lds_bytes(k) + 2048, lds_limit);
+  hipError_t e = hs::launch_resolve(b->d_units, b->n, b->max_B, d_topk, k, d_slots, d_miss,
+                                    gather_wgs_for(b->n), (int)b->pool->rec, S(stream));
+  if (e != hipSuccess) return hip_fail(e, "resolve launch");
+  return HS_OK;
+}
+
+// --------------------------------------------------------------- attention
+
+struct AttnPlan {
+  int splits, chunk, dv;
+  size_t ws_o_floats, ws_ml_floats, ws_bytes;
+};
+
+static hs_status plan_attn(hs_batch_t b, int32_t Hq, int32_t k, AttnPlan *pl) {
+  const hs_pool_s *p = b->pool;
+  if (k < 1 || k > HS_MAX_K) return fail(HS_E_INVAL, "k = %d outside [1, %d]", k, HS_MAX_K);
+  int base, min_chunk, target;
+  if (p->kind == HS_KV_MHA) {
+    if (p->D != 64 && p->D != 128) return fail(HS_E_INVAL, "head_dim %d unsupported", p->D);
+    if (Hq < p->Hkv || Hq % p->Hkv) return fail(HS_E_INVAL, "n_q_heads %% n_kv_heads != 0");
+    const int gq = Hq / p->Hkv;
+    if (gq != 1 && gq != 2 && gq != 4 && gq != 8)
+      return fail(HS_E_INVAL, "GQA group %d unsupported", gq);
+    base = b->n * p->Hkv;
+    min_chunk = 64;
+    target = 1024;
+    pl->dv = p->D;
+  } else {
+    if (p->dtype != HS_BF16 || p->Dl != 512 || p->Dr != 64)
+      return fail(HS_E_INVAL, "latent attention needs bf16, 512 + 64");
+    if (Hq < 16 || Hq % 16) return fail(HS_E_INVAL, "n_q_heads must be a multiple of 16");
+    base = b->n * (Hq / 16);
+    min_chunk = 64;
+    target = 512;
+    pl->dv = p->Dl;
+  }
+  int splits = g_tuning.attn_splits > 0 ? g_tuning.attn_splits : (target + base - 1) / base;
+  const int max_splits = std::max(1, k / min_chunk);
+  if (g_tuning.attn_splits <= 0) splits = std::min(splits, max_splits);
+  splits = std::max(1, std::min(splits, k));
+  int chunk = (k + splits - 1) / splits;
+  if (p->kind == HS_KV_LATENT) chunk = (chunk + 31) / 32 * 32;
+  splits = (k + chunk - 1) / chunk;  // every split has at least one slot
+  pl->splits = splits;
+  pl->chunk = chunk;
+  if (splits == 1) {
+    pl->ws_o_floats = pl->ws_ml_floats = 0;
+    pl->ws_bytes = 0;
+  } else {
+    const size_t rows = (size_t)b->n * Hq;
+    pl->ws_o_floats = rows * splits * pl->dv;
+    pl->ws_ml_floats = rows * splits * 2;
+    pl->ws_bytes = hs::align_up(pl->ws_o_floats * 4, 256) + pl->ws_ml_floats * 4;
+  }
+  return HS_OK;
+}
+
+size_t hs_sparse_attn_workspace(hs_batch_t b, int32_t n_q_heads, int32_t k) {
+  AttnPlan pl;
+  if (!b || plan_attn(b, n_q_heads, k, &pl) != HS_OK) return 0;
+  return pl.ws_bytes;
+}
+
+hs_status hs_sparse_attn(hs_batch_t b, const void *d_q, int32_t Hq, const int32_t *d_slots,
+                         int32_t k, float sm_scale, float *d_out, void *d_ws, size_t ws_bytes,
+                         void *stream) {
+  if (!b || !d_q || !d_slots || !d_out) return fail(HS_E_INVAL, "null argument");
+  if (k > b->min_B) return fail(HS_E_INVAL, "k = %d above smallest B = %d", k, b->min_B);
+  if (!(sm_scale > 0.f) || sm_scale == __builtin_huge_valf())
+    return fail(HS_E_INVAL, "sm_scale must be positive and finite");
+  if ((uintptr_t)d_q % 16 || (uintptr_t)d_out % 16)
+    return fail(HS_E_INVAL, "q and out must be 16-byte aligned");
+  AttnPlan pl;
+  hs_status s = plan_attn(b, Hq, k, &pl);
+  if (s) return s;
+  if (pl.ws_bytes > 0 && (!d_ws || ws_bytes < pl.ws_bytes))
+    return fail(HS_E_INVAL, "workspace needs %zu bytes, got %zu", pl.ws_bytes, ws_bytes);
+  if (d_ws && (uintptr_t)d_ws % 256) return fail(HS_E_INVAL, "workspace must be 256-byte aligned");
+  float *ws_o = (float *)d_ws;
+  float *ws_ml = pl.ws_bytes ? (float *)((uint8_t *)d_ws + hs::align_up(pl.ws_o_floats * 4, 256))
+                             : nullptr;
+  const float scale_log2 = sm_scale * 1.4426950408889634f;
+  const hs_pool_s *p = b->pool;
+  hipError_t e;
+  if (p->kind == HS_KV_MHA) {
+    hs::AttnMhaArgs a;
+    a.units = b->d_units;
+    a.q = d_q;
+    a.slots = d_slots;
+    a.n_units = b->n;
+    a.k = k;
+    a.Hq = Hq;
+    a.Hkv = p->Hkv;
+    a.D = p->D;
+    a.dtype = p->dtype;
+    a.splits = pl.splits;
+    a.chunk = pl.chunk;
+    a.rec_bytes = (int)p->rec;
+    a.scale_log2 = scale_log2;
+    a.ws_o = ws_o;
+    a.ws_ml = ws_ml;
+    a.out = d_out;
+    e = hs::launch_attn_mha(a, S(stream));
+  } else {
+    hs::AttnLatentArgs a;
+    a.units = b->d_units;
+    a.q = (const uint16_t *)d_q;
+    a.slots = d_slots;
+    a.n_units = b->n;
+    a.k = k;
+    a.Hq = Hq;
+    a.splits = pl.splits;
+    a.chunk = pl.chunk;
+    a.scale_log2 = scale_log2;
+    a.ws_o = ws_o;
+    a.ws_ml = ws_ml;
+    a.out = d_out;
+    e = hs::launch_attn_latent(a, S(stream));
+  }
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return HS_OK;
+}
+
+// ------------------------------------------------------------------ tracing
+
+hs_status hs_trace_enable(int32_t on) {
+  if (on && g_trace.begin.empty()) {
+    g_trace.begin.resize(TRACE_CAP);
+    g_trace.end.resize(TRACE_CAP);
+    g_trace.cls.assign(TRACE_CAP, 0);
+    for (int i = 0; i < TRACE_CAP; ++i) {
+      HS_HIP(hipEventCreate(&g_trace.begin[i]));
+      HS_HIP(hipEventCreate(&g_trace.end[i]));
+    }
+  }
+  g_trace.on = on != 0;
+  g_trace.pending = -1;
+  return HS_OK;
+}
+
+hs_status hs_trace_read(hs_trace *out) {
+  if (!out) return fail(HS_E_INVAL, "null trace");
+  memset(out, 0, sizeof *out);
+  if (g_trace.n > 0) HS_HIP(hipDeviceSynchronize());
+  for (int i = 0; i < g_trace.n; ++i) {
+    float ms = 0.f;
+    HS_HIP(hipEventElapsedTime(&ms, g_trace.begin[i], g_trace.end[i]));
+    const int c = g_trace.cls[i];
+    if (c >= 0 && c < HS_TRACE_CLASSES) {
+      out->total_us[c] += 1000.0 * ms;
+      ++out->launches[c];
+    }
+  }
+  out->dropped = g_trace.dropped;
+  g_trace.n = 0;
+  g_trace.dropped = 0;
+  return HS_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,158 @@
+"""Set up one decode workload on the GPU and run its steps.
+
+A Session owns, for one Workload: the pinned host pool (prefill records
+written from the seeded generators), one device buffer per (request, layer)
+unit, one batch per layer (layers run in sequence within a step, requests of
+a layer together), the per-step selections and queries staged in HBM, and
+the appended-token records for write-through workloads. A decode step is,
+for each layer in order: hs_resolve -> hs_sparse_attn -> (write-through)
+hs_pool_append of that layer's new token. Steps can run eagerly or be
+captured once each into a hipGraph (torch.cuda.CUDAGraph) and replayed with
+no host synchronisation.
+
+Only the library's entry points do work here; this module allocates and
+orders. Unit order inside the session is layer-major: index l * R + r.
+"""
+from __future__ import annotations
+
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+from . import hisparse as H
+from . import inputs as I
+
+
+class Session:
+    def __init__(self, w: I.Workload, steps: Optional[int] = None, device: str = "cuda",
+                 fill: str = "touched", traces: Optional[np.ndarray] = None):
+        self.w = w
+        self.steps = w.steps if steps is None else steps
+        self.device = torch.device(device)
+        R, L, k = w.n_requests, w.n_layers, w.k
+        self.R, self.L, self.k = R, L, k
+        # traces [steps][n_units (request-major)][k] -> layer-major device copy
+        self.traces = I.gen_traces(w, self.steps) if traces is None else traces
+        lm = self.traces.reshape(self.steps, R, L, k).transpose(0, 2, 1, 3)
+        self.topk = torch.from_numpy(np.ascontiguousarray(lm)).to(self.device)  # [T][L][R][k]
+
+        kind = H.HS_KV_MHA if w.kind == "mha" else H.HS_KV_LATENT
+        self.pool = H.hs_pool_create(R, L, kind, w.dtype,
+                                     [w.capacity(r, self.steps) for r in range(R)],
+                                     n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
+                                     latent_dim=w.latent_dim, rope_dim=w.rope_dim)
+        self.rec = H.hs_pool_record_bytes(self.pool)
+        for r in range(R):
+            for l in range(L):
+                addr, _ = H.hs_pool_unit_ptr(self.pool, r, l)
+                if fill == "full":
+                    I.fill_records(w, addr, r, l, p0=0, p1=w.ctx[r])
+                else:  # only the positions the trace ever selects are written
+                    u = r * L + l
+                    pos = np.unique(self.traces[:, u, :].astype(np.int64))
+                    pos = pos[(pos >= 0) & (pos < w.ctx[r])]
+                    I.fill_records(w, addr, r, l, positions=pos)
+                H.hs_pool_set_length(self.pool, r, l, w.ctx[r])
+
+        # device buffers, one allocation per unit
+        self.mem: List[torch.Tensor] = []
+        self.bufs: List[List[int]] = [[0] * R for _ in range(L)]
+        for l in range(L):
+            for r in range(R):
+                nbytes = H.hs_buffer_bytes(self.pool, w.B[r])
+                t = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+                self.mem.append(t)
+                self.bufs[l][r] = H.hs_buffer_create(self.pool, r, l, w.B[r], t)
+        self.batches = [H.hs_batch_create(self.bufs[l]) for l in range(L)]
+
+        # queries [T][L][R][Hq][qdim] (bf16 bits as int16, or fp32)
+        qdt = torch.float32 if w.q_dtype == I.F32 else torch.int16
+        q = np.stack([I.gen_queries(w, t) for t in range(self.steps)])  # [T][n(req-major)]...
+        q = q.reshape(self.steps, R, L, w.n_q_heads, w.q_dim).transpose(0, 2, 1, 3, 4)
+        q = np.ascontiguousarray(q)
+        self.q = torch.from_numpy(q.view(np.int16) if qdt == torch.int16 else q).to(self.device)
+
+        # appended-token records [T][L][R][rec] (write-through workloads)
+        self.app = None
+        if w.append:
+            app = np.empty((self.steps, L, R, self.rec), dtype=np.uint8)
+            for r in range(R):
+                for l in range(L):
+                    pos = np.array([w.ctx[r] + t for t in range(self.steps)], dtype=np.int64)
+                    app[:, l, r, :] = I.record_array(w, r, l, pos)
+            self.app = torch.from_numpy(app).to(self.device)
+
+        self.slots = torch.empty((L, R, k), dtype=torch.int32, device=self.device)
+        self.miss = torch.empty((L, R), dtype=torch.int32, device=self.device)
+        self.out = torch.empty((L, R, w.n_q_heads, w.out_dim), dtype=torch.float32,
+                               device=self.device)
+        wsb = max(H.hs_sparse_attn_workspace(self.batches[l], w.n_q_heads, k) for l in range(L))
+        self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=self.device)
+        self.scale = w.sm_scale
+        self.graphs: List[torch.cuda.CUDAGraph] = []
+        torch.cuda.synchronize()
+
+    # -------------------------------------------------------------- steps
+    def layer(self, t: int, l: int) -> None:
+        """Enqueue step t of layer l on the current stream."""
+        w = self.w
+        H.hs_resolve(self.batches[l], self.topk[t, l], self.k, self.slots[l], self.miss[l])
+        H.hs_sparse_attn(self.batches[l], self.q[t, l], w.n_q_heads, self.slots[l], self.k,
+                         self.scale, self.out[l], self.ws)
+        if self.app is not None:
+            for r in range(self.R):
+                H.hs_pool_append(self.pool, r, l, w.ctx[r] + t, self.app[t, l, r], n=1)
+
+    def step(self, t: int) -> None:
+        for l in range(self.L):
+            self.layer(t, l)
+
+    def capture(self, steps: Optional[range] = None) -> None:
+        """Capture one graph per step (arguments of step t baked in)."""
+        steps = range(self.steps) if steps is None else steps
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        self.graphs = [None] * self.steps
+        for t in steps:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                self.step(t)
+            self.graphs[t] = g
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+
+    def replay(self, t: int) -> None:
+        self.graphs[t].replay()
+
+    def reset(self) -> None:
+        """Every buffer back to empty; pool lengths back to the prefill."""
+        torch.cuda.synchronize()
+        for l in range(self.L):
+            for r in range(self.R):
+                H.hs_buffer_reset(self.bufs[l][r])
+        for r in range(self.R):
+            for l in range(self.L):
+                H.hs_pool_set_length(self.pool, r, l, self.w.ctx[r])
+        torch.cuda.synchronize()
+
+    # -------------------------------------------------------------- state
+    def state(self, l: int, r: int):
+        return H.hs_buffer_state_get(self.bufs[l][r], self.w.B[r])
+
+    def rows(self, l: int, r: int) -> np.ndarray:
+        addr, rec = H.hs_buffer_rows(self.bufs[l][r])
+        B = self.w.B[r]
+        t = self.mem[l * self.R + r][: B * rec]
+        return t.cpu().numpy().reshape(B, rec)
+
+    def close(self) -> None:
+        torch.cuda.synchronize()
+        self.graphs = []
+        for b in self.batches:
+            H.hs_batch_destroy(b)
+        for l in range(self.L):
+            for r in range(self.R):
+                H.hs_buffer_destroy(self.bufs[l][r])
+        H.hs_pool_destroy(self.pool)
+        self.batches, self.bufs, self.pool = [], [], None
