@@ -1,0 +1,93 @@
+"""GPU parity at the five workloads' full sizes, in the benchmark's launch
+configuration (one captured hipGraph per decode step, replayed in order).
+
+Every step: slot vectors, miss counts, page tables, LRU stamps, clocks and
+error words of every unit are compared bit for bit with the oracle. Sampled
+steps: the resident row bytes of sampled units, and attention outputs of
+sampled units (max abs 1e-5 for fp32 records; max abs 1e-2 and relative L2
+4e-3 for bf16 records), the oracle computing them one unit at a time.
+"""
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from tests.parity import OracleRun, check_attn  # noqa: E402
+from tiered_kv_cache_hs_amd import hisparse as H  # noqa: E402
+from tiered_kv_cache_hs_amd import inputs as I  # noqa: E402
+from tiered_kv_cache_hs_amd.session import Session  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    H.lib()
+    H.hs_set_tuning(0, 0)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# workload -> (attention-check steps, attention-check units (r, l), row-check every)
+PLAN = {
+    1: (range(0, 32, 1), None, 1),
+    2: (range(0, 256, 32), None, 64),
+    3: (range(0, 128, 32), [(0, 0), (7, 0)], 64),
+    4: (range(0, 64, 32), [(0, 0), (31, 1)], 32),
+    5: (range(0, 64, 32), [(0, 0), (63, 0)], 32),
+}
+
+
+@pytest.mark.parametrize("wl", [1, 2, 3, 4, 5])
+def test_full_size_workload(wl):
+    w = I.workload(wl)
+    attn_steps, attn_units, rows_every = PLAN[wl]
+    t0 = time.time()
+    sess = Session(w, w.steps, fill="touched")
+    orc = OracleRun(w, sess.traces, w.steps)
+    sess.capture()
+    say(f"workload {wl} {w.name}: setup {time.time() - t0:.1f}s")
+    worst = {"max_abs": 0.0, "rel_l2": 0.0}
+    try:
+        for t in range(w.steps):
+            sess.replay(t)
+            torch.cuda.synchronize()
+            slots_g = sess.slots.cpu().numpy()
+            miss_g = sess.miss.cpu().numpy()
+            out_g = sess.out.cpu().numpy() if t in attn_steps else None
+            for l in range(w.n_layers):
+                for r in range(w.n_requests):
+                    so, mo = orc.resolve(t, r, l)
+                    assert np.array_equal(slots_g[l, r], so), f"slots t={t} r={r} l={l}"
+                    assert int(miss_g[l, r]) == mo, f"miss t={t} r={r} l={l}"
+                    pos, stamp, clock, err = sess.state(l, r)
+                    ob = orc.bufs[(r, l)]
+                    assert np.array_equal(pos, ob.pos), f"pos t={t} r={r} l={l}"
+                    assert np.array_equal(stamp, ob.stamp), f"stamp t={t} r={r} l={l}"
+                    assert clock == int(ob.clock[0]) and err == 0 == int(ob.err[0])
+                    sampled = attn_units is None or (r, l) in attn_units
+                    if sampled and t % rows_every == rows_every - 1:
+                        rows = sess.rows(l, r)
+                        occ = ob.pos >= 0
+                        assert np.array_equal(rows[occ], ob.rows[occ]), f"rows t={t} r={r} l={l}"
+                    if sampled and t in attn_steps:
+                        want = orc.attend(t, r, l, so)
+                        st = check_attn(w, out_g[l, r], want, f"attn t={t} r={r} l={l}")
+                        worst = {kk: max(worst[kk], st[kk]) for kk in worst}
+                    if w.append:
+                        orc.append(t, r, l)
+            if t % 16 == 15:
+                say(f"  step {t + 1}/{w.steps} ok ({time.time() - t0:.1f}s)")
+    finally:
+        sess.close()
+    say(f"workload {wl}: all {w.steps} steps bit-exact; worst attention {worst}; "
+        f"{time.time() - t0:.1f}s")

@@ -266,6 +266,25 @@ def test_invalid_slot_gives_nan_and_error_bit():
         sess.close()
 
 
+@pytest.mark.parametrize("bad_index,bad_slot", [(0, -1), (37, 96), (95, 10**6)])
+def test_latent_invalid_slot_gives_nan_and_error_bit(bad_index, bad_slot):
+    w = _small("latent", I.BF16, 96, 96, 700, 1, 1, seed=14, Hq=32)
+    sess = Session(w, 1, fill="full")
+    try:
+        sess.step(0)
+        torch.cuda.synchronize()
+        assert np.isfinite(sess.out.cpu().numpy()).all()
+        assert sess.state(0, 0)[3] == 0
+        bad = sess.slots.clone()
+        bad[0, 0, bad_index] = bad_slot
+        H.hs_sparse_attn(sess.batches[0], sess.q[0, 0], 32, bad[0], 96, 0.1, sess.out[0], sess.ws)
+        torch.cuda.synchronize()
+        assert np.isnan(sess.out.cpu().numpy()).all()
+        assert sess.state(0, 0)[3] & H.HS_ERR_SLOT
+    finally:
+        sess.close()
+
+
 @pytest.mark.parametrize("wl", [1, 3])
 def test_exactness_against_full_kv_buffer(wl):
     # attention through the resolved slots equals the same kernel over a

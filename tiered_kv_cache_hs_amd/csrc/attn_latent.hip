@@ -46,7 +46,8 @@ constexpr int LAT_DL = 512;
 constexpr int LAT_DR = 64;
 constexpr int LAT_DK = LAT_DL + LAT_DR;   // 576
 constexpr int LAT_REC = LAT_DK * 2;       // 1152 bytes
-constexpr int LAT_VT_WORDS = 16 * (128 + 16);  // per wave: 128 value rows of 16 words, padded
+constexpr int LAT_VT_STRIDE = 20;                 // words per value row (16 used)
+constexpr int LAT_VT_WORDS = 128 * LAT_VT_STRIDE;  // per wave: 128 value rows
 constexpr float NEG_INF = -__builtin_huge_valf();
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -61,10 +62,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even (finite inputs)
 }
 
-// Word address of value row v (0..127) of a wave's transposed-value area:
-// 16 words per row, plus 16 words of padding after every 8 rows, so that the
-// 64 lanes of one packed write hit 64 distinct banks.
-__device__ __forceinline__ int vt_row(int v) { return 16 * (v + (v >> 3)); }
+// Word address of value row v (0..127) of a wave's transposed-value area.
+// Rows are 20 words apart (16 used): 16-byte aligned, and 8 (or 16)
+// consecutive rows start in distinct groups of 4 banks, so the 16-byte reads
+// of the PV operand (one row per lane) are free of bank conflicts.
+__device__ __forceinline__ int vt_row(int v) { return LAT_VT_STRIDE * v; }
 
 __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
     const UnitDesc *__restrict__ units, const uint16_t *__restrict__ q_all,

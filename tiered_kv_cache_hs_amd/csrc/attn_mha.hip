@@ -213,31 +213,41 @@ __global__ __launch_bounds__(MHA_THREADS) void hs_k_attn_mha(
   }
 }
 
-// Merge S split partials per output row. Grid: rows; block: 256 threads.
+// Merge S <= COMBINE_MAX_S split partials per output row.
+// Grid: rows; block: 256 threads. Wave 0 turns the S (m, l) pairs into
+// weights w_s = 2^(m_s - max m) and L = sum w_s l_s; then every thread sums
+// its output elements over the splits with the loads of 8 splits in flight.
+constexpr int COMBINE_MAX_S = 64;
+
 __global__ __launch_bounds__(256) void hs_k_combine(const float *__restrict__ ws_o,
                                                     const float *__restrict__ ws_ml, int S,
                                                     int dv, float *__restrict__ out) {
+  __shared__ float s_w[COMBINE_MAX_S];
+  __shared__ float s_inv;
   const size_t row = blockIdx.x;
-  const float *ml = ws_ml + row * S * 2;
-  float M = NEG_INF;
-  bool nan = false;
-  for (int s = 0; s < S; ++s) {
-    const float m = ml[2 * s];
-    nan |= (m != m);
-    M = fmaxf(M, m);
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const float m = tid < S ? ws_ml[(row * S + tid) * 2] : NEG_INF;
+    const float l = tid < S ? ws_ml[(row * S + tid) * 2 + 1] : 0.f;
+    const bool nan = __any(m != m);
+    float M = m;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float wgt = (m == NEG_INF) ? 0.f : exp2_fast(m - M);
+    float L = wgt * l;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+    if (tid < S) s_w[tid] = wgt;
+    if (tid == 0) s_inv = nan ? __builtin_nanf("") : 1.f / L;
   }
-  float L = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float m = ml[2 * s];
-    if (m != NEG_INF) L += exp2_fast(m - M) * ml[2 * s + 1];
-  }
-  for (int e = threadIdx.x; e < dv; e += blockDim.x) {
+  __syncthreads();
+  const float inv = s_inv;
+  const float *src = ws_o + row * S * dv;
+  for (int e = tid; e < dv; e += blockDim.x) {
     float o = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const float m = ml[2 * s];
-      if (m != NEG_INF) o = fmaf(exp2_fast(m - M), ws_o[(row * S + s) * dv + e], o);
-    }
-    out[row * dv + e] = nan ? __builtin_nanf("") : o / L;
+#pragma unroll 8
+    for (int s = 0; s < S; ++s) o = fmaf(s_w[s], src[(size_t)s * dv + e], o);
+    out[row * dv + e] = o * inv;
   }
 }
 

@@ -26,6 +26,16 @@ constexpr int CTL_ERR = 1;    // sticky HS_ERR_* bits
 constexpr int CTL_FETCH = 2;  // records the last resolve must fetch
 constexpr int CTL_WORDS = 64; // control block size in words (256 bytes)
 
+// Workgroup barrier that orders LDS accesses only. A plain __syncthreads()
+// also waits for every outstanding global load and store of the wave
+// (s_waitcnt vmcnt(0)); where threads exchange data only through LDS, this
+// one lets global traffic stay in flight across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Byte layout of a buffer's caller-owned memory.
 struct BufferLayout {
   size_t rows, pos, stamp, work, ctl, total;

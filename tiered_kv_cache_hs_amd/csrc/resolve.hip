@@ -12,6 +12,8 @@
 //
 // Design on MI355X:
 //  * hs_k_resolve: one 1024-thread workgroup per unit (request, layer).
+//    Threads exchange data through LDS only, so its barriers order LDS only
+//    and every global read is issued before the first one.
 //    Thread t owns a contiguous run of SPT slots and KPT selection entries,
 //    so ranks in slot order and in selection order are one exclusive block
 //    scan of per-thread counts (wave64 shuffles + one LDS pass over waves).
@@ -41,31 +43,36 @@ __device__ __forceinline__ uint32_t hash_pos(int32_t p, int hlog2) {
   return ((uint32_t)p * 0x9E3779B1u) >> (32 - hlog2);
 }
 
-// Exclusive scan of one int per thread over the block; *total gets the sum.
-// buf: RES_WAVES ints of LDS. Ends with a barrier so buf can be reused.
-__device__ __forceinline__ int block_excl_scan(int v, int *total, int *buf) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  int x = v;
+// Wave-wide inclusive prefix sum.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    int y = __shfl_up(x, o, 64);
+    const int y = __shfl_up(x, o, 64);
     if (lane >= o) x += y;
   }
-  if (lane == 63) buf[wid] = x;
-  __syncthreads();
-  if (wid == 0) {
-    int w = lane < RES_WAVES ? buf[lane] : 0;
+  return x;
+}
+
+// Exclusive scan of one int per thread over the block with one barrier:
+// every wave publishes its total in buf (one of two alternating rows, so a
+// fast wave of the next scan cannot overwrite totals still being read), then
+// each lane adds up the totals of the waves before its own.
+__device__ __forceinline__ int block_excl_scan(int v, int *total, int (*buf)[RES_WAVES],
+                                               int &parity) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int x = wave_incl_scan(v);
+  if (lane == 63) buf[parity][wid] = x;
+  lds_barrier();
+  int before = 0, tot = 0;
 #pragma unroll
-    for (int o = 1; o < RES_WAVES; o <<= 1) {
-      int y = __shfl_up(w, o, 64);
-      if (lane >= o) w += y;
-    }
-    if (lane < RES_WAVES) buf[lane] = w;
+  for (int w = 0; w < RES_WAVES; ++w) {
+    const int t = buf[parity][w];
+    tot += t;
+    before += w < wid ? t : 0;
   }
-  __syncthreads();
-  const int before = wid ? buf[wid - 1] : 0;
-  *total = buf[RES_WAVES - 1];
-  __syncthreads();
+  parity ^= 1;
+  *total = tot;
   return before + x - v;
 }
 
@@ -96,11 +103,10 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
   // and probe, then the miss and victim lists (2k ints); region B holds
   // slot_of[k].
   extern __shared__ int lds[];
-  __shared__ int scan_buf[RES_WAVES];
-  __shared__ uint32_t hist[256];
+  __shared__ int scan_buf[2][RES_WAVES];
+  __shared__ uint32_t hist[3][256];
   __shared__ uint32_t s_flag;
   __shared__ unsigned long long s_min, s_max;
-  __shared__ int s_digit, s_below, s_bucket;
 
   const int H = 1 << hlog2;
   int *hkey = lds;
@@ -112,30 +118,51 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
 
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const UnitDesc d = units[u];
   const int B = d.B;
   const int32_t *topk = topk_all + (size_t)u * k;
   int32_t *slots = slots_all + (size_t)u * k;
+
+  // ---- 0. every global read of the kernel is issued here, before the first
+  // barrier, so the whole kernel waits for memory once
   const int64_t len = *d.len;
   const uint32_t clock = d.ctl[CTL_CLOCK];
+  const int k0 = tid * KPT;
+  const int s0 = tid * SPT;
+  int32_t tk[KPT];
+#pragma unroll
+  for (int j = 0; j < KPT; ++j) tk[j] = k0 + j < k ? topk[k0 + j] : 0;
+  int32_t sp[SPT];
+  uint32_t st[SPT];
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int s = s0 + j;
+    sp[j] = s < B ? d.pos[s] : -1;
+    st[j] = s < B ? d.stamp[s] : 0u;
+  }
 
   for (int i = tid; i < H; i += RES_THREADS) hkey[i] = EMPTY_KEY;
   for (int i = tid; i < k; i += RES_THREADS) slot_of[i] = -1;
+  if (tid < 256) {
+    hist[0][tid] = 0;
+    hist[1][tid] = 0;
+  }
   if (tid == 0) {
     s_flag = clock >= 0x7FFFFFFFu ? HS_ERR_CLOCK : 0u;
     s_min = ~0ull;
     s_max = 0ull;
   }
-  __syncthreads();
+  int parity = 0;
+  lds_barrier();
 
   // ---- 1. hash build of the selection (and range / duplicate checks)
-  const int k0 = tid * KPT;
   uint32_t myflag = 0;
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = k0 + j;
     if (i >= k) break;
-    const int32_t p = topk[i];
+    const int32_t p = tk[j];
     if (p < 0 || (int64_t)p >= len) {
       myflag |= HS_ERR_RANGE;
       continue;
@@ -155,7 +182,7 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
     }
   }
   if (myflag) atomicOr(&s_flag, myflag);
-  __syncthreads();
+  lds_barrier();
   const uint32_t flag = s_flag;
   if (flag) {
     for (int i = tid; i < k; i += RES_THREADS) slots[i] = -1;
@@ -168,15 +195,6 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
   }
 
   // ---- 2. probe every slot of the buffer
-  const int s0 = tid * SPT;
-  int32_t sp[SPT];
-  uint32_t st[SPT];
-#pragma unroll
-  for (int j = 0; j < SPT; ++j) {
-    const int s = s0 + j;
-    sp[j] = s < B ? d.pos[s] : -1;
-    st[j] = s < B ? d.stamp[s] : 0u;
-  }
   uint32_t hitmask = 0;
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
@@ -194,7 +212,29 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
       h = (h + 1) & (uint32_t)(H - 1);
     }
   }
-  __syncthreads();  // slot_of complete; the hash table is dead from here on
+  // candidate keys: (stamp << 32) | secondary, secondary = slot when empty,
+  // B + position otherwise
+  uint64_t key[SPT];
+  uint32_t candmask = 0;
+  uint64_t lo = ~0ull, hi = 0ull;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int s = s0 + j;
+    const uint32_t second = sp[j] < 0 ? (uint32_t)s : (uint32_t)(B + sp[j]);
+    key[j] = ((uint64_t)st[j] << 32) | second;
+    if (s < B && !((hitmask >> j) & 1u)) {
+      candmask |= 1u << j;
+      lo = key[j] < lo ? key[j] : lo;
+      hi = key[j] > hi ? key[j] : hi;
+    }
+  }
+  lo = wave_min_u64(lo);
+  hi = wave_max_u64(hi);
+  if (lane == 0) {
+    atomicMin(&s_min, (unsigned long long)lo);
+    atomicMax(&s_max, (unsigned long long)hi);
+  }
+  lds_barrier();  // slot_of complete; the hash table is dead from here on
 
   // ---- 3. misses in selection order
   int my_miss = 0;
@@ -204,7 +244,7 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
     if (i < k && slot_of[i] < 0) ++my_miss;
   }
   int m;
-  int mrank = block_excl_scan(my_miss, &m, scan_buf);
+  int mrank = block_excl_scan(my_miss, &m, scan_buf, parity);
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = k0 + j;
@@ -212,85 +252,72 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
   }
   const int n_cand = B - (k - m);
 
-  // ---- 4. victims: the m smallest keys among non-hit slots
-  uint64_t key[SPT];
-  uint32_t candmask = 0;
-#pragma unroll
-  for (int j = 0; j < SPT; ++j) {
-    const int s = s0 + j;
-    const uint32_t second = sp[j] < 0 ? (uint32_t)s : (uint32_t)(B + sp[j]);
-    key[j] = ((uint64_t)st[j] << 32) | second;
-    if (s < B && !((hitmask >> j) & 1u)) candmask |= 1u << j;
-  }
+  // ---- 4. victims: the m smallest keys among non-hit slots, by an MSB-first
+  // radix select over 8-bit digits; one barrier per digit (histograms rotate
+  // through three buffers: the one two passes ahead is cleared while the
+  // current one is read)
   uint32_t vmask = 0;
   if (m == n_cand) {
     vmask = candmask;
   } else if (m > 0) {
-    uint64_t lo = ~0ull, hi = 0ull;
-#pragma unroll
-    for (int j = 0; j < SPT; ++j)
-      if ((candmask >> j) & 1u) {
-        lo = key[j] < lo ? key[j] : lo;
-        hi = key[j] > hi ? key[j] : hi;
-      }
-    lo = wave_min_u64(lo);
-    hi = wave_max_u64(hi);
-    if ((tid & 63) == 0) {
-      atomicMin(&s_min, (unsigned long long)lo);
-      atomicMax(&s_max, (unsigned long long)hi);
-    }
-    __syncthreads();
     const uint64_t kmin = s_min, kmax = s_max;
     const int hb = 63 - __clzll((long long)(kmin ^ kmax));  // n_cand >= 2, keys distinct
+    // secondaries are below B + len: digits of the low word above that are 0
+    const uint64_t sec_lim = (uint64_t)B + (uint64_t)len;
+    const int sec_top = 64 - __clzll((long long)sec_lim);  // bits needed
     int sh = (hb / 8) * 8;
     uint64_t prefix = kmin;
     int need = m;
     int final_sh = 0;
+    int pass = 0;
     while (true) {
-      if (tid < 256) hist[tid] = 0;
-      __syncthreads();
+      uint32_t *hcur = hist[pass % 3];
 #pragma unroll
       for (int j = 0; j < SPT; ++j) {
         if (!((candmask >> j) & 1u)) continue;
         const bool match = (sh + 8 >= 64) || ((key[j] >> (sh + 8)) == (prefix >> (sh + 8)));
-        if (match) atomicAdd(&hist[(key[j] >> sh) & 255u], 1u);
+        if (match) atomicAdd(&hcur[(key[j] >> sh) & 255u], 1u);
       }
-      __syncthreads();
-      if (tid < 64) {
-        const uint32_t c0 = hist[4 * tid], c1 = hist[4 * tid + 1];
-        const uint32_t c2 = hist[4 * tid + 2], c3 = hist[4 * tid + 3];
-        const int tot = (int)(c0 + c1 + c2 + c3);
-        int incl = tot;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          int y = __shfl_up(incl, o, 64);
-          if (tid >= o) incl += y;
-        }
-        const int excl = incl - tot;
-        if (excl < need && need <= incl) {
-          const uint32_t c[4] = {c0, c1, c2, c3};
-          int run = excl;
-          for (int b = 0; b < 4; ++b) {
-            if (run + (int)c[b] >= need) {
-              s_digit = 4 * tid + b;
-              s_below = run;
-              s_bucket = (int)c[b];
-              break;
-            }
-            run += (int)c[b];
+      lds_barrier();
+      if (tid < 256) hist[(pass + 2) % 3][tid] = 0;
+      // every wave finds the digit on its own (no broadcast barrier)
+      const uint32_t c0 = hcur[4 * lane], c1 = hcur[4 * lane + 1];
+      const uint32_t c2 = hcur[4 * lane + 2], c3 = hcur[4 * lane + 3];
+      const int tot = (int)(c0 + c1 + c2 + c3);
+      const int incl = wave_incl_scan(tot);
+      const int excl = incl - tot;
+      const bool here = excl < need && need <= incl;
+      int dg = 0, below = 0, bucket = 0;
+      if (here) {
+        int run = excl;
+        const int cc[4] = {(int)c0, (int)c1, (int)c2, (int)c3};
+        for (int b = 0; b < 4; ++b) {
+          if (run + cc[b] >= need) {
+            dg = 4 * lane + b;
+            below = run;
+            bucket = cc[b];
+            break;
           }
+          run += cc[b];
         }
       }
-      __syncthreads();
-      const int dg = s_digit;
-      need -= s_below;
+      const unsigned long long ball = __ballot(here);
+      const int src = __ffsll(ball) - 1;
+      dg = __shfl(dg, src, 64);
+      below = __shfl(below, src, 64);
+      bucket = __shfl(bucket, src, 64);
+      need -= below;
       const uint64_t mask_low = (sh + 8 >= 64) ? ~0ull : ((1ull << (sh + 8)) - 1ull);
       prefix = (prefix & ~mask_low) | ((uint64_t)dg << sh);
-      if (need == s_bucket || sh == 0) {
+      ++pass;
+      if (need == bucket || sh == 0) {
         final_sh = sh;
         break;
       }
+      // next digit; inside the low word skip the digits above the secondary's
+      // highest possible bit (they are 0 for every key)
       sh -= 8;
+      if (sh < 32 && sh >= sec_top) sh = ((sec_top - 1) / 8) * 8;
     }
     const uint64_t lim = prefix >> final_sh;
 #pragma unroll
@@ -300,7 +327,7 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
 
   // ---- 5. rank victims in ascending slot order and pair them with misses
   int vtot;
-  int vrank = block_excl_scan(__popc(vmask), &vtot, scan_buf);
+  int vrank = block_excl_scan(__popc(vmask), &vtot, scan_buf, parity);
   if (vtot != m) {
     // cannot happen for a valid state (keys are distinct); refuse to update
     for (int i = tid; i < k; i += RES_THREADS) slots[i] = -1;
@@ -314,7 +341,7 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
     if ((vmask >> j) & 1u) victim_list[vrank++] = s0 + j;
-  __syncthreads();
+  lds_barrier();
 
   // ---- 6. in-place update: fills get 2c - 1, hits get 2c
   const uint32_t c = clock + 1u;
@@ -330,7 +357,7 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
     if ((hitmask >> j) & 1u) d.stamp[s0 + j] = 2u * c;
-  __syncthreads();
+  lds_barrier();
 
   // ---- 7. publish the slot vector, aligned with the selection
 #pragma unroll

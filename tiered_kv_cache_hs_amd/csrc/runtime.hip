@@ -541,7 +541,7 @@ static hs_status plan_attn(hs_batch_t b, int32_t Hq, int32_t k, AttnPlan *pl) {
   int splits = g_tuning.attn_splits > 0 ? g_tuning.attn_splits : (target + base - 1) / base;
   const int max_splits = std::max(1, k / min_chunk);
   if (g_tuning.attn_splits <= 0) splits = std::min(splits, max_splits);
-  splits = std::max(1, std::min(splits, k));
+  splits = std::max(1, std::min(std::min(splits, k), 64));  // the combine merges <= 64
   int chunk = (k + splits - 1) / splits;
   if (p->kind == HS_KV_LATENT) chunk = (chunk + 31) / 32 * 32;
   splits = (k + chunk - 1) / chunk;  // every split has at least one slot
