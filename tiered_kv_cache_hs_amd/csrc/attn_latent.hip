@@ -162,8 +162,9 @@ __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
       for (int e = 0; e < 4; ++e) {
         const uint32_t a = ka[jj][e], c = kb[jj][e];
         const int v = 32 * jj + 8 * q4 + 2 * e;
-        vt[vt_row(v) + r] = (a & 0xFFFFu) | (c << 16);
-        vt[vt_row(v + 1) + r] = (a >> 16) | (c & 0xFFFF0000u);
+        // v_perm_b32: bytes of (c:a) -> {a.lo, c.lo} and {a.hi, c.hi}
+        vt[vt_row(v) + r] = __builtin_amdgcn_perm(c, a, 0x05040100u);
+        vt[vt_row(v + 1) + r] = __builtin_amdgcn_perm(c, a, 0x07060302u);
       }
     }
     // sum the four waves' partial scores in a fixed order
@@ -205,9 +206,12 @@ __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
     const v4u pw = {pbits[0] | (pbits[1] << 16), pbits[2] | (pbits[3] << 16),
                     pbits[4] | (pbits[5] << 16), pbits[6] | (pbits[7] << 16)};
     const bf16x8 pB = __builtin_bit_cast(bf16x8, pw);
+    if (__any(alpha != 1.f)) {  // the running max moved for some head
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) o[jj] *= alpha;
+    }
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
-      o[jj] *= alpha;
       const v4u a = *(const v4u *)(vt + vt_row(16 * jj + r) + 4 * q4);
       o[jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pB, o[jj],
                                                        0, 0, 0);

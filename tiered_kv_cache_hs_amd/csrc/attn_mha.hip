@@ -56,6 +56,27 @@ struct Elem<uint16_t> {  // bfloat16 bits
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+template <int CTRL>
+__device__ __forceinline__ float fdpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G lanes (G = 8, 16, 32 or 64); every lane of a
+// group gets the group's sum. Within a row of 16 lanes the steps are DPP lane
+// moves (quad swaps, half-row mirror, row mirror); wider groups add xor
+// shuffles across rows.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+  static_assert(G == 8 || G == 16 || G == 32 || G == 64, "group width");
+  x += fdpp<0xB1>(x);   // quad_perm [1,0,3,2]
+  x += fdpp<0x4E>(x);   // quad_perm [2,3,0,1]
+  x += fdpp<0x141>(x);  // row_half_mirror: the other quad of the half-row
+  if (G >= 16) x += fdpp<0x140>(x);  // row_mirror: the other half-row
+  if (G >= 32) x += __shfl_xor(x, 16, 64);
+  if (G >= 64) x += __shfl_xor(x, 32, 64);
+  return x;
+}
+
 // Merge state (m2, l2, a2) into (m, l, a); m in log2 units, -inf = empty.
 template <int EPL>
 __device__ __forceinline__ void merge_state(float &m, float &l, float *a, float m2, float l2,
@@ -150,8 +171,7 @@ __global__ __launch_bounds__(MHA_THREADS) void hs_k_attn_mha(
         float dot = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) dot = fmaf(qf[h][e], kf[e], dot);
-#pragma unroll
-        for (int o = LPS / 2; o >= 1; o >>= 1) dot += __shfl_xor(dot, o, 64);
+        dot = group_sum<LPS>(dot);
         if (valid[uu]) {
           const float sc = dot * scale_log2;
           const float mn = fmaxf(m_run[h], sc);

@@ -29,28 +29,41 @@
 //    16-byte non-temporal loads from the device-mapped host pool, several
 //    loads in flight per lane, so the host link sees many outstanding reads
 //    even at small batch.
+#include <type_traits>
+
 #include "hs_device.h"
 
 namespace hs {
 
 namespace {
 
-constexpr int RES_THREADS = 1024;
-constexpr int RES_WAVES = RES_THREADS / 64;
+constexpr int RES_MAX_WAVES = 16;  // resolve workgroups have up to 1024 threads
 constexpr int EMPTY_KEY = -1;
 
 __device__ __forceinline__ uint32_t hash_pos(int32_t p, int hlog2) {
   return ((uint32_t)p * 0x9E3779B1u) >> (32 - hlog2);
 }
 
-// Wave-wide inclusive prefix sum.
+// Cross-lane steps use DPP (VALU lane moves) rather than ds_bpermute, which
+// goes through the LDS pipe with its latency. Controls for gfx9-family DPP:
+constexpr int DPP_ROW_SHR1 = 0x111, DPP_ROW_SHR2 = 0x112, DPP_ROW_SHR4 = 0x114,
+              DPP_ROW_SHR8 = 0x118, DPP_ROW_BCAST15 = 0x142, DPP_ROW_BCAST31 = 0x143;
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ int dpp(int x) {
+  // lanes without a source (or outside ROW_MASK) read 0
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Wave-wide inclusive prefix sum: Hillis-Steele within each row of 16 lanes,
+// then the row totals are carried across rows with row broadcasts.
 __device__ __forceinline__ int wave_incl_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  x += dpp<DPP_ROW_SHR1, 0xF>(x);
+  x += dpp<DPP_ROW_SHR2, 0xF>(x);
+  x += dpp<DPP_ROW_SHR4, 0xF>(x);
+  x += dpp<DPP_ROW_SHR8, 0xF>(x);
+  x += dpp<DPP_ROW_BCAST15, 0xA>(x);
+  x += dpp<DPP_ROW_BCAST31, 0xC>(x);
   return x;
 }
 
@@ -58,7 +71,8 @@ __device__ __forceinline__ int wave_incl_scan(int x) {
 // every wave publishes its total in buf (one of two alternating rows, so a
 // fast wave of the next scan cannot overwrite totals still being read), then
 // each lane adds up the totals of the waves before its own.
-__device__ __forceinline__ int block_excl_scan(int v, int *total, int (*buf)[RES_WAVES],
+template <int NW>
+__device__ __forceinline__ int block_excl_scan(int v, int *total, int (*buf)[RES_MAX_WAVES],
                                                int &parity) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int x = wave_incl_scan(v);
@@ -66,7 +80,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int *total, int (*buf)[RES
   lds_barrier();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < RES_WAVES; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int t = buf[parity][w];
     tot += t;
     before += w < wid ? t : 0;
@@ -76,26 +90,37 @@ __device__ __forceinline__ int block_excl_scan(int v, int *total, int (*buf)[RES
   return before + x - v;
 }
 
-__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    uint64_t y = __shfl_xor(v, o, 64);
-    v = y < v ? y : v;
-  }
-  return v;
+// Wave-wide min / max of unsigned 32-bit values (result in every lane):
+// prefix min/max with DPP, then lane 63 holds the answer.
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t v) {
+  const uint32_t id = MAX ? 0u : 0xFFFFFFFFu;
+  auto f = [](uint32_t a, uint32_t b) { return MAX ? (a > b ? a : b) : (a < b ? a : b); };
+  // inactive / sourceless lanes must contribute the identity, not 0
+  auto mv = [&](uint32_t x, auto ctrl, auto rmask) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)x, decltype(ctrl)::value,
+                                                 decltype(rmask)::value, 0xF, false);
+  };
+  using C1 = std::integral_constant<int, DPP_ROW_SHR1>;
+  using C2 = std::integral_constant<int, DPP_ROW_SHR2>;
+  using C4 = std::integral_constant<int, DPP_ROW_SHR4>;
+  using C8 = std::integral_constant<int, DPP_ROW_SHR8>;
+  using B15 = std::integral_constant<int, DPP_ROW_BCAST15>;
+  using B31 = std::integral_constant<int, DPP_ROW_BCAST31>;
+  using RA = std::integral_constant<int, 0xF>;
+  using RB = std::integral_constant<int, 0xA>;
+  using RC = std::integral_constant<int, 0xC>;
+  v = f(v, mv(v, C1{}, RA{}));
+  v = f(v, mv(v, C2{}, RA{}));
+  v = f(v, mv(v, C4{}, RA{}));
+  v = f(v, mv(v, C8{}, RA{}));
+  v = f(v, mv(v, B15{}, RB{}));
+  v = f(v, mv(v, B31{}, RC{}));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    uint64_t y = __shfl_xor(v, o, 64);
-    v = y > v ? y : v;
-  }
-  return v;
-}
-
-template <int SPT, int KPT>
-__global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
+template <int NT, int SPT, int KPT>
+__global__ __launch_bounds__(NT) void hs_k_resolve(
     const UnitDesc *__restrict__ units, const int32_t *__restrict__ topk_all,
     int k, int hlog2, int32_t *__restrict__ slots_all,
     int32_t *__restrict__ miss_all) {
@@ -103,10 +128,11 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
   // and probe, then the miss and victim lists (2k ints); region B holds
   // slot_of[k].
   extern __shared__ int lds[];
-  __shared__ int scan_buf[2][RES_WAVES];
+  constexpr int NW = NT / 64;
+  __shared__ int scan_buf[2][RES_MAX_WAVES];
   __shared__ uint32_t hist[3][256];
   __shared__ uint32_t s_flag;
-  __shared__ unsigned long long s_min, s_max;
+  __shared__ uint32_t s_smin, s_smax, s_cmin, s_cmax;  // stamp / secondary bounds
 
   const int H = 1 << hlog2;
   int *hkey = lds;
@@ -132,60 +158,86 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
   const int s0 = tid * SPT;
   int32_t tk[KPT];
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) tk[j] = k0 + j < k ? topk[k0 + j] : 0;
+  for (int j = 0; j < KPT; ++j) {
+    const int32_t v = topk[min(k0 + j, k - 1)];  // clamped address, value masked
+    tk[j] = k0 + j < k ? v : 0;
+  }
   int32_t sp[SPT];
   uint32_t st[SPT];
+  if (s0 + SPT <= B && (SPT % 4) == 0) {
+    // the whole run is in range: 16-byte loads, no per-slot branches
 #pragma unroll
-  for (int j = 0; j < SPT; ++j) {
-    const int s = s0 + j;
-    sp[j] = s < B ? d.pos[s] : -1;
-    st[j] = s < B ? d.stamp[s] : 0u;
+    for (int j = 0; j < SPT; j += 4) {
+      const int4 a = *(const int4 *)(d.pos + s0 + j);
+      const uint4 b = *(const uint4 *)(d.stamp + s0 + j);
+      sp[j] = a.x; sp[j + 1] = a.y; sp[j + 2] = a.z; sp[j + 3] = a.w;
+      st[j] = b.x; st[j + 1] = b.y; st[j + 2] = b.z; st[j + 3] = b.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int s = min(s0 + j, B - 1);  // clamped address, value masked below
+      const int32_t pv = d.pos[s];
+      const uint32_t sv = d.stamp[s];
+      sp[j] = s0 + j < B ? pv : -1;
+      st[j] = s0 + j < B ? sv : 0u;
+    }
   }
 
-  for (int i = tid; i < H; i += RES_THREADS) hkey[i] = EMPTY_KEY;
-  for (int i = tid; i < k; i += RES_THREADS) slot_of[i] = -1;
+  for (int i = tid; i < H; i += NT) hkey[i] = EMPTY_KEY;
+  for (int i = tid; i < k; i += NT) slot_of[i] = -1;
   if (tid < 256) {
     hist[0][tid] = 0;
     hist[1][tid] = 0;
   }
   if (tid == 0) {
     s_flag = clock >= 0x7FFFFFFFu ? HS_ERR_CLOCK : 0u;
-    s_min = ~0ull;
-    s_max = 0ull;
+    s_smin = 0xFFFFFFFFu;
+    s_smax = 0u;
+    s_cmin = 0xFFFFFFFFu;
+    s_cmax = 0u;
   }
   int parity = 0;
   lds_barrier();
 
-  // ---- 1. hash build of the selection (and range / duplicate checks)
+  // ---- 1. hash build of the selection (and range / duplicate checks); the
+  // KPT inserts of a thread advance together, one probe step per round
   uint32_t myflag = 0;
+  uint32_t hcur[KPT];
+  uint32_t pend = 0;  // inserts still probing
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
-    const int i = k0 + j;
-    if (i >= k) break;
-    const int32_t p = tk[j];
-    if (p < 0 || (int64_t)p >= len) {
+    hcur[j] = hash_pos(tk[j], hlog2);
+    if (k0 + j >= k) continue;
+    if (tk[j] < 0 || (int64_t)tk[j] >= len)
       myflag |= HS_ERR_RANGE;
-      continue;
-    }
-    uint32_t h = hash_pos(p, hlog2);
-    while (true) {
-      const int old = atomicCAS(&hkey[h], EMPTY_KEY, p);
-      if (old == EMPTY_KEY) {
-        hval[h] = i;
-        break;
-      }
-      if (old == p) {
+    else
+      pend |= 1u << j;
+  }
+  while (pend) {
+    int old[KPT];
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      if ((pend >> j) & 1u) old[j] = atomicCAS(&hkey[hcur[j]], EMPTY_KEY, tk[j]);
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (!((pend >> j) & 1u)) continue;
+      if (old[j] == EMPTY_KEY) {
+        hval[hcur[j]] = k0 + j;
+        pend &= ~(1u << j);
+      } else if (old[j] == tk[j]) {
         myflag |= HS_ERR_DUP;
-        break;
+        pend &= ~(1u << j);
+      } else {
+        hcur[j] = (hcur[j] + 1) & (uint32_t)(H - 1);
       }
-      h = (h + 1) & (uint32_t)(H - 1);
     }
   }
   if (myflag) atomicOr(&s_flag, myflag);
   lds_barrier();
   const uint32_t flag = s_flag;
   if (flag) {
-    for (int i = tid; i < k; i += RES_THREADS) slots[i] = -1;
+    for (int i = tid; i < k; i += NT) slots[i] = -1;
     if (tid == 0) {
       d.ctl[CTL_ERR] |= flag;
       d.ctl[CTL_FETCH] = 0;
@@ -194,29 +246,41 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
     return;
   }
 
-  // ---- 2. probe every slot of the buffer
+  // ---- 2. probe every slot of the buffer (SPT lookups advance together)
   uint32_t hitmask = 0;
+  {
+    uint32_t h[SPT];
+    uint32_t pend = 0;
 #pragma unroll
-  for (int j = 0; j < SPT; ++j) {
-    const int32_t p = sp[j];
-    if (s0 + j >= B || p < 0) continue;
-    uint32_t h = hash_pos(p, hlog2);
-    while (true) {
-      const int kk = hkey[h];
-      if (kk == p) {
-        slot_of[hval[h]] = s0 + j;
-        hitmask |= 1u << j;
-        break;
+    for (int j = 0; j < SPT; ++j) {
+      h[j] = hash_pos(sp[j], hlog2);
+      if (s0 + j < B && sp[j] >= 0) pend |= 1u << j;
+    }
+    while (pend) {
+      int kk[SPT];
+#pragma unroll
+      for (int j = 0; j < SPT; ++j)
+        if ((pend >> j) & 1u) kk[j] = hkey[h[j]];
+#pragma unroll
+      for (int j = 0; j < SPT; ++j) {
+        if (!((pend >> j) & 1u)) continue;
+        if (kk[j] == sp[j]) {
+          slot_of[hval[h[j]]] = s0 + j;
+          hitmask |= 1u << j;
+          pend &= ~(1u << j);
+        } else if (kk[j] == EMPTY_KEY) {
+          pend &= ~(1u << j);
+        } else {
+          h[j] = (h[j] + 1) & (uint32_t)(H - 1);
+        }
       }
-      if (kk == EMPTY_KEY) break;
-      h = (h + 1) & (uint32_t)(H - 1);
     }
   }
   // candidate keys: (stamp << 32) | secondary, secondary = slot when empty,
-  // B + position otherwise
+  // B + position otherwise; bounds of both halves over the candidates
   uint64_t key[SPT];
   uint32_t candmask = 0;
-  uint64_t lo = ~0ull, hi = 0ull;
+  uint32_t smin = 0xFFFFFFFFu, smax = 0u, cmin = 0xFFFFFFFFu, cmax = 0u;
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
     const int s = s0 + j;
@@ -224,15 +288,21 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
     key[j] = ((uint64_t)st[j] << 32) | second;
     if (s < B && !((hitmask >> j) & 1u)) {
       candmask |= 1u << j;
-      lo = key[j] < lo ? key[j] : lo;
-      hi = key[j] > hi ? key[j] : hi;
+      smin = st[j] < smin ? st[j] : smin;
+      smax = st[j] > smax ? st[j] : smax;
+      cmin = second < cmin ? second : cmin;
+      cmax = second > cmax ? second : cmax;
     }
   }
-  lo = wave_min_u64(lo);
-  hi = wave_max_u64(hi);
+  smin = wave_minmax_u32<false>(smin);
+  smax = wave_minmax_u32<true>(smax);
+  cmin = wave_minmax_u32<false>(cmin);
+  cmax = wave_minmax_u32<true>(cmax);
   if (lane == 0) {
-    atomicMin(&s_min, (unsigned long long)lo);
-    atomicMax(&s_max, (unsigned long long)hi);
+    atomicMin(&s_smin, smin);
+    atomicMax(&s_smax, smax);
+    atomicMin(&s_cmin, cmin);
+    atomicMax(&s_cmax, cmax);
   }
   lds_barrier();  // slot_of complete; the hash table is dead from here on
 
@@ -244,7 +314,7 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
     if (i < k && slot_of[i] < 0) ++my_miss;
   }
   int m;
-  int mrank = block_excl_scan(my_miss, &m, scan_buf, parity);
+  int mrank = block_excl_scan<NW>(my_miss, &m, scan_buf, parity);
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = k0 + j;
@@ -260,8 +330,14 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
   if (m == n_cand) {
     vmask = candmask;
   } else if (m > 0) {
-    const uint64_t kmin = s_min, kmax = s_max;
-    const int hb = 63 - __clzll((long long)(kmin ^ kmax));  // n_cand >= 2, keys distinct
+    // highest bit in which the candidates' keys differ: in the stamp half if
+    // the stamps differ, else in the secondary half (n_cand >= 2, keys are
+    // distinct); prefix starts as (smallest stamp, smallest secondary), whose
+    // bits above that position every candidate shares
+    const uint32_t smin_b = s_smin, smax_b = s_smax, cmin_b = s_cmin, cmax_b = s_cmax;
+    const int hb = smin_b != smax_b ? 63 - __clz((int)(smin_b ^ smax_b))
+                                    : 31 - __clz((int)(cmin_b ^ cmax_b));
+    const uint64_t kmin = ((uint64_t)smin_b << 32) | cmin_b;
     // secondaries are below B + len: digits of the low word above that are 0
     const uint64_t sec_lim = (uint64_t)B + (uint64_t)len;
     const int sec_top = 64 - __clzll((long long)sec_lim);  // bits needed
@@ -302,10 +378,10 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
         }
       }
       const unsigned long long ball = __ballot(here);
-      const int src = __ffsll(ball) - 1;
-      dg = __shfl(dg, src, 64);
-      below = __shfl(below, src, 64);
-      bucket = __shfl(bucket, src, 64);
+      const int src = __ffsll(ball) - 1;  // wave-uniform
+      dg = __builtin_amdgcn_readlane(dg, src);
+      below = __builtin_amdgcn_readlane(below, src);
+      bucket = __builtin_amdgcn_readlane(bucket, src);
       need -= below;
       const uint64_t mask_low = (sh + 8 >= 64) ? ~0ull : ((1ull << (sh + 8)) - 1ull);
       prefix = (prefix & ~mask_low) | ((uint64_t)dg << sh);
@@ -327,10 +403,10 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
 
   // ---- 5. rank victims in ascending slot order and pair them with misses
   int vtot;
-  int vrank = block_excl_scan(__popc(vmask), &vtot, scan_buf, parity);
+  int vrank = block_excl_scan<NW>(__popc(vmask), &vtot, scan_buf, parity);
   if (vtot != m) {
     // cannot happen for a valid state (keys are distinct); refuse to update
-    for (int i = tid; i < k; i += RES_THREADS) slots[i] = -1;
+    for (int i = tid; i < k; i += NT) slots[i] = -1;
     if (tid == 0) {
       d.ctl[CTL_ERR] |= HS_ERR_INTERNAL;
       d.ctl[CTL_FETCH] = 0;
@@ -345,7 +421,7 @@ __global__ __launch_bounds__(RES_THREADS) void hs_k_resolve(
 
   // ---- 6. in-place update: fills get 2c - 1, hits get 2c
   const uint32_t c = clock + 1u;
-  for (int r = tid; r < m; r += RES_THREADS) {
+  for (int r = tid; r < m; r += NT) {
     const int s = victim_list[r];
     const int i = miss_list[r];
     const int32_t p = topk[i];
@@ -449,26 +525,30 @@ __global__ __launch_bounds__(256) void hs_k_append(uint8_t *dst, const uint8_t *
   if (blockIdx.x == 0 && threadIdx.x == 0 && *len < new_len) *len = new_len;
 }
 
-template <int SPT, int KPT>
+template <int NT, int SPT, int KPT>
 hipError_t launch_select(const UnitDesc *d_units, int n, const int32_t *d_topk, int k,
                          int hlog2, size_t lds, int32_t *d_slots, int32_t *d_miss,
                          hipStream_t stream) {
   trace_begin(HS_TRACE_SELECT, stream);
-  hipLaunchKernelGGL((hs_k_resolve<SPT, KPT>), dim3(n), dim3(RES_THREADS), lds, stream,
-                     d_units, d_topk, k, hlog2, d_slots, d_miss);
+  hipLaunchKernelGGL((hs_k_resolve<NT, SPT, KPT>), dim3(n), dim3(NT), lds, stream, d_units,
+                     d_topk, k, hlog2, d_slots, d_miss);
   trace_end(stream);
   return hipGetLastError();
 }
 
-template <int SPT>
+// picks per thread: the power of two >= k / NT
+template <int NT, int SPT>
 hipError_t launch_select_k(const UnitDesc *d_units, int n, const int32_t *d_topk, int k,
                            int hlog2, size_t lds, int32_t *d_slots, int32_t *d_miss,
                            hipStream_t stream) {
-  if (k <= RES_THREADS)
-    return launch_select<SPT, 1>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
-  if (k <= 2 * RES_THREADS)
-    return launch_select<SPT, 2>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
-  return launch_select<SPT, 4>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+#define HS_SEL(KPT)                                                                        \
+  if (k <= NT * KPT)                                                                       \
+    return launch_select<NT, SPT, KPT>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, \
+                                       stream);
+  HS_SEL(1)
+  HS_SEL(2)
+#undef HS_SEL
+  return launch_select<NT, SPT, 4>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
 }
 
 int hash_log2(int k) {
@@ -491,16 +571,17 @@ hipError_t launch_resolve(const UnitDesc *d_units, int n, int max_B, const int32
   const int hlog2 = hash_log2(k);
   const size_t lds = resolve_lds_bytes(k);
   hipError_t e;
-  if (max_B <= RES_THREADS)
-    e = launch_select_k<1>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
-  else if (max_B <= 2 * RES_THREADS)
-    e = launch_select_k<2>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
-  else if (max_B <= 4 * RES_THREADS)
-    e = launch_select_k<4>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
-  else if (max_B <= 8 * RES_THREADS)
-    e = launch_select_k<8>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+  // 16 waves per unit; each thread owns SPT = B / 1024 consecutive slots
+  if (max_B <= 1024)
+    e = launch_select_k<1024, 1>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+  else if (max_B <= 2048)
+    e = launch_select_k<1024, 2>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+  else if (max_B <= 4096)
+    e = launch_select_k<1024, 4>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+  else if (max_B <= 8192)
+    e = launch_select_k<1024, 8>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
   else
-    e = launch_select_k<16>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+    e = launch_select_k<1024, 16>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
   if (e != hipSuccess) return e;
   trace_begin(HS_TRACE_GATHER, stream);
   hipLaunchKernelGGL(hs_k_gather, dim3(n * gather_wgs), dim3(GATHER_THREADS), 0, stream,
