@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--path", choices=("fused", "split"), default="fused",
+                    help="fused: hs_resolve_attn (misses fetched by the attention kernels); "
+                         "split: hs_resolve (with its gather kernel) then hs_sparse_attn")
     return ap.parse_args()
 
 
@@ -127,7 +130,8 @@ def main():
     total = W + K
     print(f"[bench] workload {w.name}: building session ({total} steps)", file=sys.stderr, flush=True)
     fill = "full" if w.n_units * max(w.ctx) * w.rec_bytes <= (8 << 30) else "touched"
-    sess = Session(w, total, fill=fill)
+    fused = args.path == "fused"
+    sess = Session(w, total, fill=fill, fused=fused)
     sess.capture()
     print("[bench] graphs captured", file=sys.stderr, flush=True)
 
@@ -168,22 +172,33 @@ def main():
     a_flops = attn_flops(w, n_launch_units)
     attn_us = per["attn"]
     attn_gbs = a_bytes / (attn_us * 1e-6) / 1e9 if attn_us else 0.0
-    miss_bytes_launch = misses.sum() * w.rec_bytes / max(1, tr["gather"][1])
-    gather_us = per["gather"]
-    host_gbs = miss_bytes_launch / (gather_us * 1e-6) / 1e9 if gather_us else 0.0
+    attn_kernel = "hs_k_attn_latent" if w.kind == "latent" else "hs_k_attn_mha"
+    # the kernel that moves the misses over the host link: the gather kernel,
+    # or in the fused path the attention kernel itself
+    fetch_class = "attn" if fused else "gather"
+    fetch_us = per[fetch_class]
+    miss_bytes_launch = misses.sum() * w.rec_bytes / max(1, tr[fetch_class][1])
+    host_gbs = miss_bytes_launch / (fetch_us * 1e-6) / 1e9 if fetch_us else 0.0
     miss_rate = float(misses.sum()) / (K * w.n_units * w.k)
 
     roof_attn = {"bound": "hbm", "achieved": round(attn_gbs, 1), "peak": HBM_PEAK_GBS,
                  "unit": "GB/s", "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": None,
-                 "kernel": "hs_k_attn_latent" if w.kind == "latent" else "hs_k_attn_mha",
-                 "avg_us": round(attn_us, 2), "bytes_per_launch": int(a_bytes),
+                 "kernel": attn_kernel, "avg_us": round(attn_us, 2),
+                 "bytes_per_launch": int(a_bytes),
                  "tflops": round(a_flops / (attn_us * 1e-6) / 1e12, 2) if attn_us else 0.0}
-    roof_gather = {"bound": "host_link", "achieved": round(host_gbs, 2),
-                   "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
-                   "frac": round(host_gbs / HOST_LINK_PEAK_GBS, 4), "traffic": None,
-                   "kernel": "hs_k_gather", "avg_us": round(gather_us, 2),
-                   "bytes_per_launch": int(miss_bytes_launch)}
-    dominant = roof_gather if gather_us >= attn_us else roof_attn
+    roof_host = {"bound": "host_link", "achieved": round(host_gbs, 2),
+                 "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
+                 "frac": round(host_gbs / HOST_LINK_PEAK_GBS, 4), "traffic": None,
+                 "kernel": attn_kernel if fused else "hs_k_gather", "avg_us": round(fetch_us, 2),
+                 "bytes_per_launch": int(miss_bytes_launch)}
+    if fused:
+        # one kernel moves both; its bound is the resource whose peak-rate
+        # time for the launch's bytes is longer
+        t_host = miss_bytes_launch / (HOST_LINK_PEAK_GBS * 1e9)
+        t_hbm = a_bytes / (HBM_PEAK_GBS * 1e9)
+        dominant = roof_host if t_host >= t_hbm else roof_attn
+    else:
+        dominant = roof_host if fetch_us >= attn_us else roof_attn
 
     result = {
         "metric": METRIC,
@@ -202,10 +217,11 @@ def main():
                    "context": w.ctx[0] if len(set(w.ctx)) == 1 else "per-request",
                    "k": w.k, "B": w.B[0] if len(set(w.B)) == 1 else "per-request",
                    "q_heads": w.n_q_heads, "record_bytes": w.rec_bytes, "kind": w.kind,
-                   "graph": "one hipGraph per step"},
+                   "graph": "one hipGraph per step",
+                   "path": "hs_resolve_attn" if fused else "hs_resolve + hs_sparse_attn"},
         "roofline": dominant,
         "roofline_attn": roof_attn,
-        "host_link": roof_gather,
+        "host_link": roof_host,
         "kernels_us": {c: round(per[c], 2) for c in H.TRACE_CLASSES},
         "miss_rate": round(miss_rate, 4),
         "miss_bytes_per_step": int(misses.sum() * w.rec_bytes / K),

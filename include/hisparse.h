@@ -224,7 +224,7 @@ hs_status hs_resolve(hs_batch_t batch, const int32_t *d_topk, int32_t k,
  *   Supported: head_dim 64 or 128, n_q_heads / n_kv_heads in {1, 2, 4, 8}.
  * HS_KV_LATENT: q [n][n_q_heads][latent_dim + rope_dim] bf16; K is the whole
  *   record, V its latent part; out [n][n_q_heads][latent_dim]. Supported:
- *   bf16, latent_dim 512, rope_dim 64, n_q_heads a multiple of 16.
+ *   bf16, latent_dim 512, rope_dim 64, n_q_heads 16, 32 or 64.
  * Outputs are fp32 (accumulation is fp32). A slot outside [0, B) makes the
  * unit's output NaN and sets HS_ERR_SLOT. d_ws is scratch of at least
  * hs_sparse_attn_workspace(...) bytes (may be NULL when that is 0); its
@@ -236,6 +236,22 @@ hs_status hs_sparse_attn(hs_batch_t batch, const void *d_q, int32_t n_q_heads,
                          const int32_t *d_slots, int32_t k, float sm_scale,
                          float *d_out, void *d_ws, size_t ws_bytes,
                          void *stream);
+
+/* ---------- RESOLVE + sparse attention, fused (HiSparse summary, §5) -------
+ * The same effect as hs_resolve followed by hs_sparse_attn on the same
+ * stream - identical page tables, stamps, clocks, error words, slot vectors,
+ * miss counts, row bytes and outputs, bit for bit - with one difference in
+ * how the misses travel: instead of a separate copy kernel, the attention
+ * workgroup that needs a just-resolved miss loads its record straight from
+ * the pinned host pool, uses it, and stores it into the slot the resolve
+ * assigned, so the host-link transfer overlaps the attention over the
+ * resident rows. Every missing byte still crosses the host link once.
+ * Arguments, checks and workspace as for the two calls. Enqueue only;
+ * capture-safe. */
+hs_status hs_resolve_attn(hs_batch_t batch, const int32_t *d_topk, int32_t k,
+                          int32_t *d_slots, int32_t *d_miss, const void *d_q,
+                          int32_t n_q_heads, float sm_scale, float *d_out,
+                          void *d_ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------- tracing -----------------------------------
  * Event timing of individual kernels, for measurement. While enabled, every

@@ -1,5 +1,6 @@
 """GPU parity at the five workloads' full sizes, in the benchmark's launch
-configuration (one captured hipGraph per decode step, replayed in order).
+configuration (one captured hipGraph per decode step, replayed in order, each
+layer one fused hs_resolve_attn).
 
 Every step: slot vectors, miss counts, page tables, LRU stamps, clocks and
 error words of every unit are compared bit for bit with the oracle. Sampled
@@ -52,7 +53,7 @@ def test_full_size_workload(wl):
     w = I.workload(wl)
     attn_steps, attn_units, rows_every = PLAN[wl]
     t0 = time.time()
-    sess = Session(w, w.steps, fill="touched")
+    sess = Session(w, w.steps, fill="touched", fused=True)
     orc = OracleRun(w, sess.traces, w.steps)
     sess.capture()
     say(f"workload {wl} {w.name}: setup {time.time() - t0:.1f}s")

@@ -37,8 +37,8 @@ def say(*a):
 
 
 def compare_run(w, steps, traces=None, attn_every=1, rows_every=1, attn_units=None,
-                graph=False, fill="touched"):
-    sess = Session(w, steps, fill=fill, traces=traces)
+                graph=False, fill="touched", fused=False):
+    sess = Session(w, steps, fill=fill, traces=traces, fused=fused)
     orc = OracleRun(w, sess.traces, steps)
     if graph:
         sess.capture()
@@ -320,3 +320,46 @@ def test_exactness_against_full_kv_buffer(wl):
         H.hs_buffer_destroy(fb)
     finally:
         sess.close()
+
+
+@pytest.mark.parametrize("case", [1, 3, 7, 8, 9])
+def test_small_shapes_fused(case):
+    kind, dt, B, k, ctx, steps, n_new = SMALL[case]
+    if kind == "mha":
+        w = _small(kind, dt, B, k, ctx, steps, n_new, seed=case,
+                   Hkv=2 if dt == I.BF16 else 1, D=128 if dt == I.BF16 else 64,
+                   Hq=4 if dt == I.BF16 else 1)
+    else:
+        w = _small(kind, dt, B, k, ctx, steps, n_new, seed=case, Hq=32)
+    compare_run(w, steps, fill="full", fused=True)
+
+
+@pytest.mark.parametrize("wl,steps,hq", [(1, 12, None), (2, 10, None), (3, 6, None), (3, 4, 16),
+                                         (5, 3, None)])
+def test_fused_equals_resolve_then_attention_bitwise(wl, steps, hq):
+    """hs_resolve_attn == hs_resolve + hs_sparse_attn: state, rows and outputs
+    bit for bit, step by step (workload 5 with its first 8 requests)."""
+    w = I.workload(wl)
+    if hq is not None:
+        w = dataclasses.replace(w, n_q_heads=hq)
+    if wl == 5:
+        w = dataclasses.replace(w, n_requests=8, ctx=w.ctx[:8], B=w.B[:8])
+    a = Session(w, steps, fill="touched", fused=False)
+    b = Session(w, steps, fill="touched", fused=True, traces=a.traces)
+    try:
+        for t in range(steps):
+            a.step(t)
+            b.step(t)
+            torch.cuda.synchronize()
+            assert np.array_equal(a.slots.cpu().numpy(), b.slots.cpu().numpy()), t
+            assert np.array_equal(a.miss.cpu().numpy(), b.miss.cpu().numpy()), t
+            assert np.array_equal(a.out.cpu().numpy().view(np.uint32),
+                                  b.out.cpu().numpy().view(np.uint32)), t
+            for l in range(w.n_layers):
+                for r in range(w.n_requests):
+                    sa, sb = a.state(l, r), b.state(l, r)
+                    assert all(np.array_equal(x, y) for x, y in zip(sa[:2], sb[:2])) and sa[2:] == sb[2:]
+                    assert np.array_equal(a.rows(l, r)[sa[0] >= 0], b.rows(l, r)[sb[0] >= 0])
+    finally:
+        a.close()
+        b.close()

@@ -90,7 +90,12 @@ __device__ __forceinline__ void merge_state(float &m, float &l, float *a, float 
   m = mn;
 }
 
-template <typename T, int D, int GQ>
+// FETCH: resolve + attention fused. A selected row that the resolve just
+// assigned to a victim slot is read from the host pool instead of the slot,
+// and the workgroup stores its head's K and V slices into the slot's row; the
+// workgroups of the Hkv heads together write the whole record, each byte
+// crossing the host link once.
+template <typename T, int D, int GQ, bool FETCH>
 __global__ __launch_bounds__(MHA_THREADS) void hs_k_attn_mha(
     const UnitDesc *__restrict__ units, const T *__restrict__ q_all,
     const int32_t *__restrict__ slots_all, int k, int Hq, int Hkv, float scale_log2,
@@ -139,21 +144,36 @@ __global__ __launch_bounds__(MHA_THREADS) void hs_k_attn_mha(
     for (int e = 0; e < EPL; ++e) acc[h][e] = 0.f;
   }
   bool bad = false;
+  const int64_t pool_len = FETCH ? *d.len : 0;
 
   for (int i0 = i_begin + grp; i0 < i_end; i0 += MHA_UNROLL * NGW) {
     v4u kw[MHA_UNROLL], vw[MHA_UNROLL];
     bool valid[MHA_UNROLL];
+    int slot_of[MHA_UNROLL];
+    int src[MHA_UNROLL];  // fetch mode: pool position of a just-resolved miss, else -1
 #pragma unroll
     for (int uu = 0; uu < MHA_UNROLL; ++uu) {
       const int i = i0 + uu * NGW;
       valid[uu] = i < i_end;
       int slot = valid[uu] ? slots[i] : 0;
+      src[uu] = (FETCH && valid[uu]) ? d.fsrc[i] : -1;
       if ((unsigned)slot >= (unsigned)B) {
         bad = true;
         slot = 0;
+        src[uu] = -1;
       }
-      const uint8_t *row = d.rows + (size_t)slot * rec_bytes;
-      if (valid[uu]) {
+      if (FETCH && src[uu] >= 0 && (int64_t)src[uu] >= pool_len) {
+        bad = true;
+        src[uu] = -1;
+      }
+      slot_of[uu] = slot;
+      const bool host = FETCH && src[uu] >= 0;
+      const uint8_t *row = host ? d.pool + (size_t)src[uu] * rec_bytes
+                                : d.rows + (size_t)slot * rec_bytes;
+      if (valid[uu] && host) {
+        kw[uu] = __builtin_nontemporal_load((const v4u *)(row + koff));
+        vw[uu] = __builtin_nontemporal_load((const v4u *)(row + voff));
+      } else if (valid[uu]) {
         kw[uu] = *(const v4u *)(row + koff);
         vw[uu] = *(const v4u *)(row + voff);
       } else {
@@ -163,6 +183,11 @@ __global__ __launch_bounds__(MHA_THREADS) void hs_k_attn_mha(
     }
 #pragma unroll
     for (int uu = 0; uu < MHA_UNROLL; ++uu) {
+      if (FETCH && src[uu] >= 0) {  // the fetched slices go to the slot's row
+        uint8_t *row = d.rows + (size_t)slot_of[uu] * rec_bytes;
+        *(v4u *)(row + koff) = kw[uu];
+        *(v4u *)(row + voff) = vw[uu];
+      }
       float kf[EPL], vf[EPL];
       Elem<T>::unpack(kw[uu], kf);
       Elem<T>::unpack(vw[uu], vf);
@@ -271,26 +296,31 @@ __global__ __launch_bounds__(256) void hs_k_combine(const float *__restrict__ ws
   }
 }
 
-template <typename T, int D, int GQ>
+template <typename T, int D, int GQ, bool FETCH>
 hipError_t launch_mha_t(const AttnMhaArgs &a, hipStream_t stream) {
   const int grid = a.n_units * a.Hkv * a.splits;
   trace_begin(HS_TRACE_ATTN, stream);
-  hipLaunchKernelGGL((hs_k_attn_mha<T, D, GQ>), dim3(grid), dim3(MHA_THREADS), 0, stream,
+  hipLaunchKernelGGL((hs_k_attn_mha<T, D, GQ, FETCH>), dim3(grid), dim3(MHA_THREADS), 0, stream,
                      a.units, (const T *)a.q, a.slots, a.k, a.Hq, a.Hkv, a.scale_log2,
                      a.splits, a.chunk, a.rec_bytes, a.ws_o, a.ws_ml, a.out);
   trace_end(stream);
   return hipGetLastError();
 }
 
-template <typename T, int D>
-hipError_t launch_mha_d(const AttnMhaArgs &a, hipStream_t stream) {
+template <typename T, int D, bool FETCH>
+hipError_t launch_mha_g(const AttnMhaArgs &a, hipStream_t stream) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_mha_t<T, D, 1>(a, stream);
-    case 2: return launch_mha_t<T, D, 2>(a, stream);
-    case 4: return launch_mha_t<T, D, 4>(a, stream);
-    case 8: return launch_mha_t<T, D, 8>(a, stream);
+    case 1: return launch_mha_t<T, D, 1, FETCH>(a, stream);
+    case 2: return launch_mha_t<T, D, 2, FETCH>(a, stream);
+    case 4: return launch_mha_t<T, D, 4, FETCH>(a, stream);
+    case 8: return launch_mha_t<T, D, 8, FETCH>(a, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <typename T, int D>
+hipError_t launch_mha_d(const AttnMhaArgs &a, hipStream_t stream) {
+  return a.fetch ? launch_mha_g<T, D, true>(a, stream) : launch_mha_g<T, D, false>(a, stream);
 }
 
 }  // namespace

@@ -8,17 +8,19 @@
 
 namespace hs {
 
-// Device view of one (request, layer) unit of a batch. 64 bytes.
-struct __attribute__((aligned(64))) UnitDesc {
+// Device view of one (request, layer) unit of a batch. 128 bytes.
+struct __attribute__((aligned(128))) UnitDesc {
   uint8_t *rows;        // B rows of rec_bytes (device memory)
   int32_t *pos;         // page table: slot -> logical position, -1 empty
   uint32_t *stamp;      // LRU stamps, 0 = never used
   int2 *work;           // last resolve's fetch list: (slot, position), B entries
+  int32_t *fsrc;        // last resolve, per selection index: its position if it
+                        // was a miss (fetched from the pool), else -1; B entries
   uint32_t *ctl;        // [CTL_CLOCK], [CTL_ERR], [CTL_FETCH]
   const uint8_t *pool;  // device-visible address of the unit's host records
   const int64_t *len;   // the unit's pool length (device memory)
   int32_t B;
-  int32_t pad;
+  int32_t pad[5];
 };
 
 constexpr int CTL_CLOCK = 0;  // resolve steps done
@@ -38,7 +40,7 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Byte layout of a buffer's caller-owned memory.
 struct BufferLayout {
-  size_t rows, pos, stamp, work, ctl, total;
+  size_t rows, pos, stamp, work, fsrc, ctl, total;
 };
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
@@ -49,7 +51,8 @@ inline BufferLayout buffer_layout(size_t rec_bytes, int B) {
   l.pos = align_up((size_t)B * rec_bytes, 256);
   l.stamp = l.pos + align_up((size_t)B * 4, 256);
   l.work = l.stamp + align_up((size_t)B * 4, 256);
-  l.ctl = l.work + align_up((size_t)B * 8, 256);
+  l.fsrc = l.work + align_up((size_t)B * 8, 256);
+  l.ctl = l.fsrc + align_up((size_t)B * 4, 256);
   l.total = l.ctl + CTL_WORDS * 4;
   return l;
 }
@@ -63,7 +66,7 @@ void trace_end(hipStream_t stream);
 // ---------------------------------------------------------------- launches
 // Declared here, defined in the .hip files; all enqueue on `stream` and
 // return the hipError_t of the launch.
-hipError_t launch_buffer_init(int32_t *pos, uint32_t *stamp, uint32_t *ctl,
+hipError_t launch_buffer_init(int32_t *pos, uint32_t *stamp, int32_t *fsrc, uint32_t *ctl,
                               int B, hipStream_t stream);
 hipError_t launch_resolve(const UnitDesc *d_units, int n_units, int max_B,
                           const int32_t *d_topk, int k, int32_t *d_slots,
@@ -80,6 +83,7 @@ struct AttnMhaArgs {
   const void *q;
   const int32_t *slots;
   int n_units, k, Hq, Hkv, D, dtype, splits, chunk, rec_bytes;
+  int fetch;  // fused resolve: read just-resolved misses from the host pool
   float scale_log2;
   float *ws_o, *ws_ml, *out;
 };
@@ -90,6 +94,7 @@ struct AttnLatentArgs {
   const uint16_t *q;
   const int32_t *slots;
   int n_units, k, Hq, splits, chunk;
+  int fetch;  // fused resolve: read just-resolved misses from the host pool
   float scale_log2;
   float *ws_o, *ws_ml, *out;
 };

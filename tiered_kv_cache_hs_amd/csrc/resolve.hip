@@ -237,7 +237,10 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   lds_barrier();
   const uint32_t flag = s_flag;
   if (flag) {
-    for (int i = tid; i < k; i += NT) slots[i] = -1;
+    for (int i = tid; i < k; i += NT) {
+      slots[i] = -1;
+      d.fsrc[i] = -1;
+    }
     if (tid == 0) {
       d.ctl[CTL_ERR] |= flag;
       d.ctl[CTL_FETCH] = 0;
@@ -308,18 +311,18 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
 
   // ---- 3. misses in selection order
   int my_miss = 0;
+  bool miss_here[KPT];
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = k0 + j;
-    if (i < k && slot_of[i] < 0) ++my_miss;
+    miss_here[j] = i < k && slot_of[i] < 0;
+    my_miss += miss_here[j] ? 1 : 0;
   }
   int m;
   int mrank = block_excl_scan<NW>(my_miss, &m, scan_buf, parity);
 #pragma unroll
-  for (int j = 0; j < KPT; ++j) {
-    const int i = k0 + j;
-    if (i < k && slot_of[i] < 0) miss_list[mrank++] = i;
-  }
+  for (int j = 0; j < KPT; ++j)
+    if (miss_here[j]) miss_list[mrank++] = k0 + j;
   const int n_cand = B - (k - m);
 
   // ---- 4. victims: the m smallest keys among non-hit slots, by an MSB-first
@@ -406,7 +409,10 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   int vrank = block_excl_scan<NW>(__popc(vmask), &vtot, scan_buf, parity);
   if (vtot != m) {
     // cannot happen for a valid state (keys are distinct); refuse to update
-    for (int i = tid; i < k; i += NT) slots[i] = -1;
+    for (int i = tid; i < k; i += NT) {
+      slots[i] = -1;
+      d.fsrc[i] = -1;
+    }
     if (tid == 0) {
       d.ctl[CTL_ERR] |= HS_ERR_INTERNAL;
       d.ctl[CTL_FETCH] = 0;
@@ -439,7 +445,10 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     const int i = k0 + j;
-    if (i < k) slots[i] = slot_of[i];
+    if (i < k) {
+      slots[i] = slot_of[i];
+      d.fsrc[i] = miss_here[j] ? tk[j] : -1;
+    }
   }
   if (tid == 0) {
     d.ctl[CTL_CLOCK] = c;
@@ -506,10 +515,12 @@ __global__ __launch_bounds__(256) void hs_k_regather(const UnitDesc *__restrict_
   }
 }
 
-__global__ void hs_k_buffer_init(int32_t *pos, uint32_t *stamp, uint32_t *ctl, int B) {
+__global__ void hs_k_buffer_init(int32_t *pos, uint32_t *stamp, int32_t *fsrc, uint32_t *ctl,
+                                 int B) {
   for (int s = blockIdx.x * blockDim.x + threadIdx.x; s < B; s += gridDim.x * blockDim.x) {
     pos[s] = -1;
     stamp[s] = 0u;
+    fsrc[s] = -1;
   }
   if (blockIdx.x == 0 && threadIdx.x < CTL_WORDS) ctl[threadIdx.x] = 0u;
 }
@@ -568,6 +579,7 @@ size_t resolve_lds_bytes(int k) {
 hipError_t launch_resolve(const UnitDesc *d_units, int n, int max_B, const int32_t *d_topk,
                           int k, int32_t *d_slots, int32_t *d_miss, int gather_wgs,
                           int rec_bytes, hipStream_t stream) {
+  // gather_wgs == 0: the fetch is left to the attention kernels
   const int hlog2 = hash_log2(k);
   const size_t lds = resolve_lds_bytes(k);
   hipError_t e;
@@ -582,7 +594,7 @@ hipError_t launch_resolve(const UnitDesc *d_units, int n, int max_B, const int32
     e = launch_select_k<1024, 8>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
   else
     e = launch_select_k<1024, 16>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || gather_wgs == 0) return e;
   trace_begin(HS_TRACE_GATHER, stream);
   hipLaunchKernelGGL(hs_k_gather, dim3(n * gather_wgs), dim3(GATHER_THREADS), 0, stream,
                      d_units, gather_wgs, rec_bytes / 16);
@@ -600,12 +612,13 @@ hipError_t launch_regather(const UnitDesc *d_unit, int B, int rec_bytes, hipStre
   return hipGetLastError();
 }
 
-hipError_t launch_buffer_init(int32_t *pos, uint32_t *stamp, uint32_t *ctl, int B,
+hipError_t launch_buffer_init(int32_t *pos, uint32_t *stamp, int32_t *fsrc, uint32_t *ctl, int B,
                               hipStream_t stream) {
   int blocks = (B + 255) / 256;
   if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(hs_k_buffer_init, dim3(blocks), dim3(256), 0, stream, pos, stamp, ctl, B);
+  hipLaunchKernelGGL(hs_k_buffer_init, dim3(blocks), dim3(256), 0, stream, pos, stamp, fsrc, ctl,
+                     B);
   return hipGetLastError();
 }
 

@@ -345,15 +345,15 @@ hs_status hs_buffer_create(hs_pool_t p, int32_t req, int32_t layer, int32_t B, v
   d.pos = (int32_t *)(b->mem + lay.pos);
   d.stamp = (uint32_t *)(b->mem + lay.stamp);
   d.work = (int2 *)(b->mem + lay.work);
+  d.fsrc = (int32_t *)(b->mem + lay.fsrc);
   d.ctl = (uint32_t *)(b->mem + lay.ctl);
   d.pool = p->dev[req] + unit_offset(p, req, layer);
   d.len = p->d_len + (size_t)req * p->L + layer;
   d.B = B;
-  d.pad = 0;
   hipError_t e = hipMalloc(&b->d_desc, sizeof(UnitDesc));
   if (e == hipSuccess)
     e = hipMemcpy(b->d_desc, &b->desc, sizeof(UnitDesc), hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hs::launch_buffer_init(d.pos, d.stamp, d.ctl, B, S(stream));
+  if (e == hipSuccess) e = hs::launch_buffer_init(d.pos, d.stamp, d.fsrc, d.ctl, B, S(stream));
   if (e != hipSuccess) {
     if (b->d_desc) (void)hipFree(b->d_desc);
     delete b;
@@ -372,7 +372,8 @@ hs_status hs_buffer_destroy(hs_buffer_t b) {
 
 hs_status hs_buffer_reset(hs_buffer_t b, void *stream) {
   if (!b) return fail(HS_E_INVAL, "null buffer");
-  hipError_t e = hs::launch_buffer_init(b->desc.pos, b->desc.stamp, b->desc.ctl, b->B, S(stream));
+  hipError_t e = hs::launch_buffer_init(b->desc.pos, b->desc.stamp, b->desc.fsrc, b->desc.ctl, b->B,
+                                         S(stream));
   if (e != hipSuccess) return hip_fail(e, "buffer reset");
   return HS_OK;
 }
@@ -485,8 +486,8 @@ static int gather_wgs_for(int n_units) {
   return std::max(1, std::min(64, g));
 }
 
-hs_status hs_resolve(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_t *d_slots,
-                     int32_t *d_miss, void *stream) {
+static hs_status check_resolve(hs_batch_t b, const int32_t *d_topk, int32_t k,
+                               const int32_t *d_slots) {
   if (!b || !d_topk || !d_slots) return fail(HS_E_INVAL, "null argument");
   if (k < 1 || k > HS_MAX_K || k > b->min_B)
     return fail(HS_E_INVAL, "k = %d outside [1, min(%d, smallest B = %d)]", k, HS_MAX_K,
@@ -502,6 +503,13 @@ hs_status hs_resolve(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_t *d_
   if (hs::resolve_lds_bytes(k) + 2048 > (size_t)lds_limit)
     return fail(HS_E_INVAL, "k = %d needs %zu bytes of LDS; the device allows %d", k,
                 hs::resolve_lds_bytes(k) + 2048, lds_limit);
+  return HS_OK;
+}
+
+hs_status hs_resolve(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_t *d_slots,
+                     int32_t *d_miss, void *stream) {
+  hs_status s = check_resolve(b, d_topk, k, d_slots);
+  if (s) return s;
   hipError_t e = hs::launch_resolve(b->d_units, b->n, b->max_B, d_topk, k, d_slots, d_miss,
                                     gather_wgs_for(b->n), (int)b->pool->rec, S(stream));
   if (e != hipSuccess) return hip_fail(e, "resolve launch");
@@ -532,10 +540,11 @@ static hs_status plan_attn(hs_batch_t b, int32_t Hq, int32_t k, AttnPlan *pl) {
   } else {
     if (p->dtype != HS_BF16 || p->Dl != 512 || p->Dr != 64)
       return fail(HS_E_INVAL, "latent attention needs bf16, 512 + 64");
-    if (Hq < 16 || Hq % 16) return fail(HS_E_INVAL, "n_q_heads must be a multiple of 16");
-    base = b->n * (Hq / 16);
+    if (Hq != 16 && Hq != 32 && Hq != 64)
+      return fail(HS_E_INVAL, "latent attention supports 16, 32 or 64 query heads");
+    base = (b->n + 7) / 8 * 8;  // one workgroup covers all heads of a (unit, split)
     min_chunk = 64;
-    target = 512;
+    target = 256;
     pl->dv = p->Dl;
   }
   int splits = g_tuning.attn_splits > 0 ? g_tuning.attn_splits : (target + base - 1) / base;
@@ -565,21 +574,26 @@ size_t hs_sparse_attn_workspace(hs_batch_t b, int32_t n_q_heads, int32_t k) {
   return pl.ws_bytes;
 }
 
-hs_status hs_sparse_attn(hs_batch_t b, const void *d_q, int32_t Hq, const int32_t *d_slots,
-                         int32_t k, float sm_scale, float *d_out, void *d_ws, size_t ws_bytes,
-                         void *stream) {
+static hs_status check_attn(hs_batch_t b, const void *d_q, int32_t Hq, const int32_t *d_slots,
+                            int32_t k, float sm_scale, float *d_out, void *d_ws, size_t ws_bytes,
+                            AttnPlan *pl) {
   if (!b || !d_q || !d_slots || !d_out) return fail(HS_E_INVAL, "null argument");
   if (k > b->min_B) return fail(HS_E_INVAL, "k = %d above smallest B = %d", k, b->min_B);
   if (!(sm_scale > 0.f) || sm_scale == __builtin_huge_valf())
     return fail(HS_E_INVAL, "sm_scale must be positive and finite");
   if ((uintptr_t)d_q % 16 || (uintptr_t)d_out % 16)
     return fail(HS_E_INVAL, "q and out must be 16-byte aligned");
-  AttnPlan pl;
-  hs_status s = plan_attn(b, Hq, k, &pl);
+  hs_status s = plan_attn(b, Hq, k, pl);
   if (s) return s;
-  if (pl.ws_bytes > 0 && (!d_ws || ws_bytes < pl.ws_bytes))
-    return fail(HS_E_INVAL, "workspace needs %zu bytes, got %zu", pl.ws_bytes, ws_bytes);
+  if (pl->ws_bytes > 0 && (!d_ws || ws_bytes < pl->ws_bytes))
+    return fail(HS_E_INVAL, "workspace needs %zu bytes, got %zu", pl->ws_bytes, ws_bytes);
   if (d_ws && (uintptr_t)d_ws % 256) return fail(HS_E_INVAL, "workspace must be 256-byte aligned");
+  return HS_OK;
+}
+
+static hs_status enqueue_attn(hs_batch_t b, const void *d_q, int32_t Hq, const int32_t *d_slots,
+                              int32_t k, float sm_scale, float *d_out, void *d_ws,
+                              const AttnPlan &pl, int fetch, void *stream) {
   float *ws_o = (float *)d_ws;
   float *ws_ml = pl.ws_bytes ? (float *)((uint8_t *)d_ws + hs::align_up(pl.ws_o_floats * 4, 256))
                              : nullptr;
@@ -600,6 +614,7 @@ hs_status hs_sparse_attn(hs_batch_t b, const void *d_q, int32_t Hq, const int32_
     a.splits = pl.splits;
     a.chunk = pl.chunk;
     a.rec_bytes = (int)p->rec;
+    a.fetch = fetch;
     a.scale_log2 = scale_log2;
     a.ws_o = ws_o;
     a.ws_ml = ws_ml;
@@ -615,6 +630,7 @@ hs_status hs_sparse_attn(hs_batch_t b, const void *d_q, int32_t Hq, const int32_
     a.Hq = Hq;
     a.splits = pl.splits;
     a.chunk = pl.chunk;
+    a.fetch = fetch;
     a.scale_log2 = scale_log2;
     a.ws_o = ws_o;
     a.ws_ml = ws_ml;
@@ -623,6 +639,30 @@ hs_status hs_sparse_attn(hs_batch_t b, const void *d_q, int32_t Hq, const int32_
   }
   if (e != hipSuccess) return hip_fail(e, "attention launch");
   return HS_OK;
+}
+
+hs_status hs_sparse_attn(hs_batch_t b, const void *d_q, int32_t Hq, const int32_t *d_slots,
+                         int32_t k, float sm_scale, float *d_out, void *d_ws, size_t ws_bytes,
+                         void *stream) {
+  AttnPlan pl;
+  hs_status s = check_attn(b, d_q, Hq, d_slots, k, sm_scale, d_out, d_ws, ws_bytes, &pl);
+  if (s) return s;
+  return enqueue_attn(b, d_q, Hq, d_slots, k, sm_scale, d_out, d_ws, pl, 0, stream);
+}
+
+hs_status hs_resolve_attn(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_t *d_slots,
+                          int32_t *d_miss, const void *d_q, int32_t Hq, float sm_scale,
+                          float *d_out, void *d_ws, size_t ws_bytes, void *stream) {
+  hs_status s = check_resolve(b, d_topk, k, d_slots);
+  if (s) return s;
+  AttnPlan pl;
+  s = check_attn(b, d_q, Hq, d_slots, k, sm_scale, d_out, d_ws, ws_bytes, &pl);
+  if (s) return s;
+  // resolve without the gather kernel: the attention kernels fetch the misses
+  hipError_t e = hs::launch_resolve(b->d_units, b->n, b->max_B, d_topk, k, d_slots, d_miss, 0,
+                                    (int)b->pool->rec, S(stream));
+  if (e != hipSuccess) return hip_fail(e, "resolve launch");
+  return enqueue_attn(b, d_q, Hq, d_slots, k, sm_scale, d_out, d_ws, pl, 1, stream);
 }
 
 // ------------------------------------------------------------------ tracing

@@ -45,7 +45,8 @@ EXPORTS = (
     "hs_buffer_bytes", "hs_buffer_create", "hs_buffer_destroy", "hs_buffer_reset",
     "hs_buffer_rows", "hs_buffer_state_get", "hs_buffer_state_set",
     "hs_batch_create", "hs_batch_destroy", "hs_resolve",
-    "hs_sparse_attn_workspace", "hs_sparse_attn", "hs_trace_enable", "hs_trace_read",
+    "hs_sparse_attn_workspace", "hs_sparse_attn", "hs_resolve_attn",
+    "hs_trace_enable", "hs_trace_read",
 )
 
 
@@ -115,6 +116,7 @@ def lib():
         "hs_resolve": ([vp, vp, i32, vp, vp, vp], i32),
         "hs_sparse_attn_workspace": ([vp, i32, i32], sz),
         "hs_sparse_attn": ([vp, vp, i32, vp, i32, ctypes.c_float, vp, vp, sz, vp], i32),
+        "hs_resolve_attn": ([vp, vp, i32, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz, vp], i32),
         "hs_trace_enable": ([i32], i32),
         "hs_trace_read": ([P(Trace)], i32),
     }
@@ -308,6 +310,16 @@ def hs_sparse_attn(batch: int, q, n_q_heads: int, slots, k: int, sm_scale: float
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().hs_sparse_attn(batch, _ptr(q), int(n_q_heads), _ptr(slots), int(k),
                                 float(sm_scale), _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def hs_resolve_attn(batch: int, topk, k: int, slots, miss, q, n_q_heads: int, sm_scale: float,
+                    out, ws=None, stream=None) -> None:
+    """hs_resolve + hs_sparse_attn with the miss fetch done by the attention
+    kernels (identical results)."""
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().hs_resolve_attn(batch, _ptr(topk), int(k), _ptr(slots), _ptr(miss), _ptr(q),
+                                 int(n_q_heads), float(sm_scale), _ptr(out), _ptr(ws), ws_bytes,
+                                 _stream(stream)))
 
 
 # ------------------------------------------------------------------ tracing

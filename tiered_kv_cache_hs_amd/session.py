@@ -5,8 +5,8 @@ written from the seeded generators), one device buffer per (request, layer)
 unit, one batch per layer (layers run in sequence within a step, requests of
 a layer together), the per-step selections and queries staged in HBM, and
 the appended-token records for write-through workloads. A decode step is,
-for each layer in order: hs_resolve -> hs_sparse_attn -> (write-through)
-hs_pool_append of that layer's new token. Steps can run eagerly or be
+for each layer in order: hs_resolve -> hs_sparse_attn (or the fused
+hs_resolve_attn) -> (write-through) hs_pool_append of that layer's new token. Steps can run eagerly or be
 captured once each into a hipGraph (torch.cuda.CUDAGraph) and replayed with
 no host synchronisation.
 
@@ -26,8 +26,10 @@ from . import inputs as I
 
 class Session:
     def __init__(self, w: I.Workload, steps: Optional[int] = None, device: str = "cuda",
-                 fill: str = "touched", traces: Optional[np.ndarray] = None):
+                 fill: str = "touched", traces: Optional[np.ndarray] = None,
+                 fused: bool = False):
         self.w = w
+        self.fused = fused  # hs_resolve_attn instead of hs_resolve + hs_sparse_attn
         self.steps = w.steps if steps is None else steps
         self.device = torch.device(device)
         R, L, k = w.n_requests, w.n_layers, w.k
@@ -97,9 +99,14 @@ class Session:
     def layer(self, t: int, l: int) -> None:
         """Enqueue step t of layer l on the current stream."""
         w = self.w
-        H.hs_resolve(self.batches[l], self.topk[t, l], self.k, self.slots[l], self.miss[l])
-        H.hs_sparse_attn(self.batches[l], self.q[t, l], w.n_q_heads, self.slots[l], self.k,
-                         self.scale, self.out[l], self.ws)
+        if self.fused:
+            H.hs_resolve_attn(self.batches[l], self.topk[t, l], self.k, self.slots[l],
+                              self.miss[l], self.q[t, l], w.n_q_heads, self.scale, self.out[l],
+                              self.ws)
+        else:
+            H.hs_resolve(self.batches[l], self.topk[t, l], self.k, self.slots[l], self.miss[l])
+            H.hs_sparse_attn(self.batches[l], self.q[t, l], w.n_q_heads, self.slots[l], self.k,
+                             self.scale, self.out[l], self.ws)
         if self.app is not None:
             for r in range(self.R):
                 H.hs_pool_append(self.pool, r, l, w.ctx[r] + t, self.app[t, l, r], n=1)
