@@ -105,7 +105,9 @@ typedef struct hs_pool_desc {
 typedef struct hs_tuning {
   int32_t gather_wgs_per_unit;  /* workgroups copying one unit's misses */
   int32_t attn_splits;          /* split-k factor of sparse attention */
-  int32_t reserved[6];
+  int32_t latent_heads_per_wg;  /* latent attention: query heads per workgroup
+                                   (16, 32 or 64, dividing n_q_heads) */
+  int32_t reserved[5];
 } hs_tuning;
 
 const char *hs_status_str(hs_status s);

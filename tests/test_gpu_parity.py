@@ -127,6 +127,7 @@ SMALL = [
     ("mha", I.F32, 16384, 4096, 40000, 4, 1000),
     ("latent", I.BF16, 97, 33, 500, 6, 10),
     ("latent", I.BF16, 2048, 2048, 9000, 4, 614),
+    ("latent", I.BF16, 4096, 4096, 9000, 3, 700),
 ]
 
 
@@ -141,6 +142,20 @@ def test_small_shapes(case):
         w = _small(kind, dt, B, k, ctx, steps, n_new, seed=case, Hq=32)
     say(f"small case {case}: {SMALL[case]}")
     compare_run(w, steps, fill="full")
+
+
+@pytest.mark.parametrize("hpw,splits,fused", [(16, 0, False), (32, 0, False), (64, 0, False),
+                                               (16, 3, False), (32, 1, False), (64, 5, False),
+                                               (32, 2, True), (64, 0, True)])
+def test_latent_heads_per_workgroup(hpw, splits, fused):
+    """Latent attention with every head split (16, 32 or 64 heads per
+    workgroup), several split-k factors, a ragged last step of 32 slots."""
+    w = _small("latent", I.BF16, 300, 197, 3000, 4, 40, R=2, seed=50 + hpw + splits, Hq=64)
+    H.hs_set_tuning(0, splits, hpw)
+    try:
+        compare_run(w, 4, fill="full", fused=fused)
+    finally:
+        H.hs_set_tuning(0, 0)
 
 
 def test_multi_request_multi_layer_small():

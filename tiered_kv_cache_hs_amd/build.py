@@ -35,13 +35,22 @@ def hipcc() -> str:
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs where they fit: no copies between
+    # accumulation and arithmetic registers around the softmax rescale
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE, "-I", CSRC,
 ]
 
 
+# Per-source additions. The latent attention kernel assumes no NaN operands
+# (its error outputs are written as NaN bit patterns), which lets max and its
+# DPP lane moves compile to single v_max_f32_dpp instructions.
+EXTRA = {"attn_latent.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # drop the host pass's notice about the device-only feature
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)

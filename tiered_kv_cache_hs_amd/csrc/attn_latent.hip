@@ -20,20 +20,24 @@
 // every row byte is loaded once per workgroup and each wave's latent slice is
 // exactly the value slice [128w, 128w+128) it needs for PV. Per 32 slots:
 //   1. each wave multiplies its row slices by the Q^T slices of every head
-//      group of 16 heads (MFMA A = rows, B = Q^T), reusing the loaded rows;
-//   2. the four waves' partial score tiles are summed through LDS in a fixed
-//      order (one barrier), so every wave holds the same scores;
-//   3. each wave runs the same online softmax (log2 units) per head group
-//      and rounds P to bf16;
-//   4. each wave writes its value slice transposed into its own LDS area
-//      once (two slots packed per 32-bit word) and accumulates
+//      group of 16 heads (MFMA A = rows, B = Q^T), reusing the loaded rows,
+//      and writes its value slice transposed into its own LDS area (two
+//      slots packed per 32-bit word);
+//   2. the partial score tiles go to LDS (barrier); wave g sums the four
+//      partials of head group g in a fixed order and runs that group's
+//      online softmax (log2 units), rounding P to bf16 (barrier);
+//   3. every wave reads P of every head group and accumulates
 //      O^T[v][head] += V^T[v][slot] P^T[slot][head] with MFMA, each value
 //      tile read once and used by every head group.
-// The P^T operand is the lane's own score accumulators: lane l of a 16x16
+// The running maximum is a lazy reference: it moves only when a score
+// exceeds it by more than 2^8 (log2 units), so P stays in [0, 256] and the
+// accumulators are rescaled only on those rare steps; the partial state
+// (reference max, sum, accumulators) combines exactly as with the true max.
+// The P^T operand is the softmax lane's own score layout: lane l of a 16x16
 // tile holds rows 4(l/16)+i, so the lane's 8 P values (2 tiles x 4 rows)
-// are used directly as the 8 k-elements of the PV operand, and the V^T
-// words are laid out in that same order. While one 32-slot step computes,
-// the rows of the next step and the slot ids of the one after are loading.
+// are the 8 k-elements of the PV operand, and the V^T words are laid out in
+// that same order. The chunk's slot ids are staged in LDS once; row slices
+// are loaded two steps ahead through three register buffers.
 //
 // Fetch mode (resolve + attention fused): a selected row that the resolve
 // just assigned to a victim slot has not been copied from the host pool yet;
@@ -55,7 +59,7 @@ constexpr int LAT_REC = LAT_DK * 2;                // 1152 bytes
 constexpr int LAT_VT_STRIDE = 20;                  // words per value row (16 used)
 constexpr int LAT_VT_WORDS = 128 * LAT_VT_STRIDE;  // per wave: 128 value rows
 constexpr float NEG_INF = -__builtin_huge_valf();
-constexpr int PAST_END = -0x7FFFFFFF - 1;          // row index beyond the chunk
+constexpr float LAT_LAZY_LOG2 = 8.f;               // reference-max slack, log2 units
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short short8 __attribute__((ext_vector_type(8)));
@@ -64,9 +68,41 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // round to nearest even (finite inputs)
+// Rotation of a value within each row of 16 lanes (DPP row_ror); every
+// lane reads a lane of its own row, so the move folds into the consuming
+// max or add as a DPP operand.
+template <int N>
+__device__ __forceinline__ float row_ror(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x120 + N, 0xF, 0xF, true));
+}
+// Maximum / sum over the 16 lanes of a row, left in every lane of the row.
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, row_ror<8>(x));
+  x = fmaxf(x, row_ror<4>(x));
+  x = fmaxf(x, row_ror<2>(x));
+  return fmaxf(x, row_ror<1>(x));
+}
+__device__ __forceinline__ float row_sum16(float x) {
+  x += row_ror<8>(x);
+  x += row_ror<4>(x);
+  x += row_ror<2>(x);
+  return x + row_ror<1>(x);
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to bf16 (nearest even, v_cvt_pk_bf16_f32): a in the
+// low half, b in the high half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{a, b}, bf16x2));
+}
+
+// The bits of x, or of a quiet NaN when c. Error outputs are stored as
+// integers: the file is compiled assuming no NaN operands, so a float select
+// of a NaN constant could be folded away.
+__device__ __forceinline__ uint32_t nan_bits_if(bool c, float x) {
+  return c ? 0x7FC00000u : __float_as_uint(x);
 }
 
 // Word address of value row v (0..127) of a wave's transposed-value area.
@@ -75,140 +111,165 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 // of the PV operand (one row per lane) are free of bank conflicts.
 __device__ __forceinline__ int vt_row(int v) { return LAT_VT_STRIDE * v; }
 
-// A tile row: its slot (or PAST_END), and in fetch mode its pool position
-// when it must come from the host (else -1).
+// A tile row: its slot, and in fetch mode its pool position when it must
+// come from the host (else -1).
 struct RowRef {
   int slot;
   int src;
 };
 
-template <int HG, bool FETCH>
+// HG head groups of 16 per workgroup; HS workgroups split a unit's Hq =
+// HS * HG * 16 heads; DEPTH steps of row loads in flight ahead of the one
+// computing (1 or 2; the register budget allows 2 up to HG = 2).
+//
+// Score layout: QK^T is computed transposed, S^T[head][slot] = Q x K^T
+// (MFMA A = Q slices, B = row slices), so a lane holds 4 heads x 1 slot per
+// 16-slot tile and the reductions over slots run within a row of 16 lanes
+// (DPP). Every wave issues the same loads in every step (rows past the
+// chunk repeat its last row and are masked), so the number of loads in
+// flight is the same on every path and each step waits only for its own.
+template <int HG, int DEPTH, bool FETCH>
 __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
     const UnitDesc *__restrict__ units, const uint16_t *__restrict__ q_all,
     const int32_t *__restrict__ slots_all, int n_units, int k, float scale_log2, int S,
-    int chunk, float *__restrict__ ws_o, float *__restrict__ ws_ml, float *__restrict__ out) {
-  constexpr int Hq = HG * 16;
+    int HS, int chunk, float *__restrict__ ws_o, float *__restrict__ ws_ml,
+    float *__restrict__ out) {
+  static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth 1 or 2");
   __shared__ uint32_t s_vt[4][LAT_VT_WORDS];
-  __shared__ floatx4 s_part[2][HG][4][2][64];
+  __shared__ floatx4 s_part[HG][4][2][64];
+  __shared__ v4u s_p[HG][64];          // PV operand P^T of every lane
+  __shared__ float s_alpha[HG][16];    // per head: rescale factor, then l
+  __shared__ int s_rescale[4];         // per wave: its reference maximum moved
+  __shared__ int s_ids[LAT_MAX_CHUNK];
+  __shared__ int s_src[FETCH ? LAT_MAX_CHUNK : 1];
 
-  // XCD-aware order: the S splits of a unit get block ids equal mod 8, i.e.
-  // run on one XCD and share its L2 for the unit's queries.
+  // XCD-aware order: the S x HS workgroups of a unit get block ids equal
+  // mod 8, i.e. run on one XCD and share its L2 for the unit's queries and,
+  // across head splits, its rows.
   const int b = blockIdx.x;
   const int xcd = b & 7;
   const int j8 = b >> 3;
   const int sp = j8 % S;
-  const int u = (j8 / S) * 8 + xcd;
+  const int hh = (j8 / S) % HS;
+  const int u = (j8 / (S * HS)) * 8 + xcd;
   if (u >= n_units) return;
+  const int Hq = HS * HG * 16;
+  const int h0 = hh * HG * 16;  // first head of this workgroup
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int r = lane & 15;
   const int q4 = lane >> 4;
 
-  const UnitDesc d = units[u];
+  const UnitG d = unit_g(units[u]);
   const int B = d.B;
   const int i_begin = sp * chunk;
   const int i_end = min(k, i_begin + chunk);
-  const int32_t *slots = slots_all + (size_t)u * k;
+  const int n_rows = i_end - i_begin;
+  const int n_steps = (n_rows + 31) >> 5;
+  const HS_GLOBAL int32_t *slots = glb(slots_all) + (size_t)u * k;
   const int64_t pool_len = FETCH ? *d.len : 0;
 
-  // the wave's d-steps: 4 latent ones, and one rope step for waves 0 and 1
+  // the chunk's slot ids (and fetch sources) into LDS; the ids past the
+  // chunk repeat its last row
+  for (int i = tid; i < n_steps * 32; i += LAT_THREADS) {
+    const int j = i_begin + min(i, n_rows - 1);
+    s_ids[i] = slots[j];
+    if (FETCH) s_src[i] = d.fsrc[j];
+  }
+
+  // the wave's d-steps: 4 latent ones, and one rope step for waves 0 and 1.
+  // Waves 2 and 3 load rope slices too and multiply them by a zero query
+  // slice, so every wave runs the same loads and MFMAs (no branch makes the
+  // number of loads in flight differ between paths).
   const int n_own = w < 2 ? 5 : 4;
   bf16x8 qb[HG][5];
 #pragma unroll
   for (int hg = 0; hg < HG; ++hg) {
 #pragma unroll
     for (int jj = 0; jj < 5; ++jj) {
-      const int ds = jj < 4 ? 4 * w + jj : 16 + w;
-      if (jj < n_own)
-        qb[hg][jj] = *(const bf16x8 *)(q_all + ((size_t)u * Hq + hg * 16 + r) * LAT_DK +
-                                       32 * ds + 8 * q4);
-      else
-        qb[hg][jj] = __builtin_bit_cast(bf16x8, short8{0, 0, 0, 0, 0, 0, 0, 0});
+      const int ds = jj < 4 ? 4 * w + jj : 16 + (w & 1);
+      qb[hg][jj] = *(const HS_GLOBAL bf16x8 *)(q_all + ((size_t)u * Hq + h0 + hg * 16 + r) *
+                                                           LAT_DK + 32 * ds + 8 * q4);
     }
+    if (w >= 2) qb[hg][4] = __builtin_bit_cast(bf16x8, short8{0, 0, 0, 0, 0, 0, 0, 0});
   }
 
   floatx4 o[HG][8];
-  float m_run[HG], l_run[HG];
 #pragma unroll
-  for (int hg = 0; hg < HG; ++hg) {
-    m_run[hg] = NEG_INF;
-    l_run[hg] = 0.f;
+  for (int hg = 0; hg < HG; ++hg)
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) o[hg][jj] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // softmax share of wave w: head group hg_w, heads my_h + i (i < HG) of it
+  // for lane (r, q4); they sit in score tile lanes r + 16 (my_h / 4),
+  // elements my_h % 4 + i
+  const int hg_w = w * HG / 4;
+  const int my_h = (w % (4 / HG)) * 4 * HG + HG * q4;
+  const float *part_src =
+      (const float *)&s_part[hg_w][0][0][r + 16 * (my_h >> 2)] + (my_h & 3);
+  float m_run[HG], l_run[HG];
+#pragma unroll
+  for (int i = 0; i < HG; ++i) {
+    m_run[i] = NEG_INF;
+    l_run[i] = 0.f;
   }
   bool bad = false;
   uint32_t *vt = s_vt[w];
+  lds_barrier();  // s_ids complete
 
-  auto fetch_ids = [&](int t0, RowRef &ra, RowRef &rb) {
-    const bool ina = t0 + r < i_end, inb = t0 + 16 + r < i_end;
-    ra.slot = ina ? slots[t0 + r] : PAST_END;
-    rb.slot = inb ? slots[t0 + 16 + r] : PAST_END;
-    if (FETCH) {
-      ra.src = ina ? d.fsrc[t0 + r] : -1;
-      rb.src = inb ? d.fsrc[t0 + 16 + r] : -1;
-    } else {
-      ra.src = rb.src = -1;
-    }
+  struct Rows {
+    v4u a[5], b[5];
+    RowRef ra, rb;
   };
-  // Loads the wave's slices of one tile row: from its slot in HBM, or (fetch
-  // mode, just-resolved miss) from the host pool. Invalid rows read 0.
+  // Loads the wave's slices of a tile row: from its slot in HBM, or (fetch
+  // mode, just-resolved miss) from the host pool. An invalid slot sets the
+  // error and reads row 0 (its output becomes NaN).
   auto load_row = [&](const RowRef &rf, v4u *dst) {
     const bool valid = (unsigned)rf.slot < (unsigned)B;
-    if (!valid && rf.slot != PAST_END) bad = true;
     const bool from_host = FETCH && valid && rf.src >= 0;
-    if (from_host && (int64_t)rf.src >= pool_len) bad = true;
     const bool host_ok = from_host && (int64_t)rf.src < pool_len;
-    const uint8_t *p = host_ok ? d.pool + (size_t)rf.src * LAT_REC + 16 * q4
-                               : d.rows + (size_t)(valid ? rf.slot : 0) * LAT_REC + 16 * q4;
+    if (!valid || from_host != host_ok) bad = true;
+    const HS_GLOBAL uint8_t *p =
+        (host_ok ? d.pool + (size_t)rf.src * LAT_REC
+                 : d.rows + (size_t)(valid && !from_host ? rf.slot : 0) * LAT_REC) +
+        16 * q4;
 #pragma unroll
     for (int jj = 0; jj < 5; ++jj) {
-      const int ds = jj < 4 ? 4 * w + jj : 16 + w;
-      dst[jj] = v4u{0, 0, 0, 0};
-      if (jj < n_own && valid && (host_ok || !from_host)) {
-        if (host_ok)
-          dst[jj] = __builtin_nontemporal_load((const v4u *)(p + 64 * ds));
-        else
-          dst[jj] = *(const v4u *)(p + 64 * ds);
-      }
+      const int ds = jj < 4 ? 4 * w + jj : 16 + (w & 1);
+      dst[jj] = *(const HS_GLOBAL v4u *)(p + 64 * ds);
     }
   };
   // fetch mode: the wave's slices of a host-loaded row go to the row's slot
   auto store_row = [&](const RowRef &rf, const v4u *src) {
     if (!FETCH) return;
     if ((unsigned)rf.slot >= (unsigned)B || rf.src < 0 || (int64_t)rf.src >= pool_len) return;
-    uint8_t *p = d.rows + (size_t)rf.slot * LAT_REC + 16 * q4;
+    HS_GLOBAL uint8_t *p = d.rows + (size_t)rf.slot * LAT_REC + 16 * q4;
 #pragma unroll
     for (int jj = 0; jj < 5; ++jj) {
       const int ds = jj < 4 ? 4 * w + jj : 16 + w;
-      if (jj < n_own) *(v4u *)(p + 64 * ds) = src[jj];
+      if (jj < n_own) *(HS_GLOBAL v4u *)(p + 64 * ds) = src[jj];
     }
   };
+  // loads of step st (clamped to the last step: the tail of the pipeline
+  // re-reads it, and nothing uses those values)
+  auto issue = [&](int st, Rows &R) {
+    const int i = 32 * min(st, n_steps - 1) + r;
+    R.ra.slot = s_ids[i];
+    R.rb.slot = s_ids[i + 16];
+    R.ra.src = FETCH ? s_src[i] : -1;
+    R.rb.src = FETCH ? s_src[i + 16] : -1;
+    load_row(R.ra, R.a);
+    load_row(R.rb, R.b);
+  };
 
-  RowRef ca, cb, na, nb;
-  v4u ka[5], kb[5];
-  na.slot = nb.slot = PAST_END;
-  na.src = nb.src = -1;
-  fetch_ids(i_begin, ca, cb);
-  if (i_begin + 32 < i_end) fetch_ids(i_begin + 32, na, nb);
-  load_row(ca, ka);
-  load_row(cb, kb);
+  // One 32-slot step on the rows in `cur`; first starts the loads of the
+  // step DEPTH ahead into `pre`.
+  auto step = [&](int st, Rows &cur, Rows &pre) {
+    issue(st + DEPTH, pre);
+    const int i0 = i_begin + 32 * st;
 
-  int it = 0;
-  for (int i0 = i_begin; i0 < i_end; i0 += 32, ++it) {
-    const bool has_next = i0 + 32 < i_end;
-    v4u xa[5], xb[5];
-    RowRef nna, nnb;
-    nna.slot = nnb.slot = PAST_END;
-    nna.src = nnb.src = -1;
-    if (has_next) {
-      load_row(na, xa);
-      load_row(nb, xb);
-      if (i0 + 64 < i_end) fetch_ids(i0 + 64, nna, nnb);
-    }
-
-    // partial scores of this wave's d-slices, every head group
+    // 1. partial S^T tiles of this wave's d-slices, every head group
     floatx4 acc[HG][2];
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg) {
@@ -216,23 +277,21 @@ __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
       acc[hg][1] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int jj = 0; jj < 5; ++jj) {
-        if (jj < n_own) {
-          acc[hg][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, ka[jj]), qb[hg][jj], acc[hg][0], 0, 0, 0);
-          acc[hg][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, kb[jj]), qb[hg][jj], acc[hg][1], 0, 0, 0);
-        }
+        acc[hg][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            qb[hg][jj], __builtin_bit_cast(bf16x8, cur.a[jj]), acc[hg][0], 0, 0, 0);
+        acc[hg][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            qb[hg][jj], __builtin_bit_cast(bf16x8, cur.b[jj]), acc[hg][1], 0, 0, 0);
       }
     }
-    store_row(ca, ka);
-    store_row(cb, kb);
+    store_row(cur.ra, cur.a);
+    store_row(cur.rb, cur.b);
     // transposed value slice: value row 32jj + 8q4 + e, column r, packed
     // (tile 0 low half, tile 1 high half) with one v_perm_b32 per word
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t a = ka[jj][e], c = kb[jj][e];
+        const uint32_t a = cur.a[jj][e], c = cur.b[jj][e];
         const int v = 32 * jj + 8 * q4 + 2 * e;
         vt[vt_row(v) + r] = __builtin_amdgcn_perm(c, a, 0x05040100u);
         vt[vt_row(v + 1) + r] = __builtin_amdgcn_perm(c, a, 0x07060302u);
@@ -240,56 +299,82 @@ __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
     }
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg) {
-      s_part[it & 1][hg][w][0][lane] = acc[hg][0];
-      s_part[it & 1][hg][w][1][lane] = acc[hg][1];
+      s_part[hg][w][0][lane] = acc[hg][0];
+      s_part[hg][w][1][lane] = acc[hg][1];
     }
     lds_barrier();
 
-    // per head group: full scores (fixed summation order), online softmax
+    // 2. online softmax, spread over the four waves: wave w takes heads
+    // hb + HG q4 + i (i < HG) of head group hg_w; lane (r, q4) holds them
+    // for slots i0 + 16t + r. Scores are the four waves' partials summed in
+    // a fixed order; the maximum is a lazy reference.
+    {
+      float sc[2][HG];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+#pragma unroll
+        for (int i = 0; i < HG; ++i) {
+          float x = 0.f;
+#pragma unroll
+          for (int ww = 0; ww < 4; ++ww) x += part_src[(ww * 2 + t) * 256 + i];
+          sc[t][i] = x;
+        }
+      }
+      if (i0 + 32 > i_end) {  // the last, partial step: slots past the chunk get -inf
+        const bool in0 = i0 + r < i_end, in1 = i0 + 16 + r < i_end;
+#pragma unroll
+        for (int i = 0; i < HG; ++i) {
+          sc[0][i] = in0 ? sc[0][i] : NEG_INF;
+          sc[1][i] = in1 ? sc[1][i] : NEG_INF;
+        }
+      }
+      bool moved = false;
+      float alpha[HG];
+      uint32_t pw[HG];
+#pragma unroll
+      for (int i = 0; i < HG; ++i) {
+        // raw scores; the reference maximum is kept in log2 units
+        const float mx = row_max16(fmaxf(sc[0][i], sc[1][i])) * scale_log2;  // finite
+        const float m_old = m_run[i];
+        if (mx > m_run[i] + LAT_LAZY_LOG2) m_run[i] = mx;
+        moved |= m_run[i] != m_old;
+        alpha[i] = exp2_fast(m_old - m_run[i]);  // 1 when unchanged, 0 at the start
+        pw[i] = pack_bf16(exp2_fast(__builtin_fmaf(sc[0][i], scale_log2, -m_run[i])),
+                          exp2_fast(__builtin_fmaf(sc[1][i], scale_log2, -m_run[i])));
+        const float ps =
+            row_sum16(__uint_as_float(pw[i] << 16) + __uint_as_float(pw[i] & 0xFFFF0000u));
+        l_run[i] = l_run[i] * alpha[i] + ps;
+      }
+      // P^T operand of PV lane (head h, k-group r / 4): word r % 4 holds
+      // slots 4(r / 4) + r % 4 of tiles 0 and 1
+      uint32_t *pdst = (uint32_t *)&s_p[hg_w][0];
+#pragma unroll
+      for (int i = 0; i < HG; ++i) pdst[((r >> 2) * 16 + my_h + i) * 4 + (r & 3)] = pw[i];
+      // alpha of every head every step (1 where unchanged): a group rescales
+      // all its heads when any of its waves moved
+      if (r == 0) {
+#pragma unroll
+        for (int i = 0; i < HG; ++i) s_alpha[hg_w][my_h + i] = alpha[i];
+      }
+      const bool any_moved = __any(moved);
+      if (lane == 0) s_rescale[w] = any_moved ? 1 : 0;
+    }
+    lds_barrier();
+
+    // 3. PV: each value tile is read once and used by every head group
     bf16x8 pB[HG];
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg) {
-      floatx4 sc0 = s_part[it & 1][hg][0][0][lane], sc1 = s_part[it & 1][hg][0][1][lane];
+      pB[hg] = __builtin_bit_cast(bf16x8, s_p[hg][lane]);
+      int moved = 0;  // any wave of the group moved its reference maximum
 #pragma unroll
-      for (int ww = 1; ww < 4; ++ww) {
-        sc0 += s_part[it & 1][hg][ww][0][lane];
-        sc1 += s_part[it & 1][hg][ww][1][lane];
-      }
-      // lane holds slots i0 + 16t + 4q4 + i for head 16hg + r; element e = 2i + t
-      float sv[8];
+      for (int ww = hg * (4 / HG); ww < (hg + 1) * (4 / HG); ++ww) moved |= s_rescale[ww];
+      if (__builtin_amdgcn_readfirstlane(moved)) {
+        const float a = s_alpha[hg][r];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int idx0 = i0 + 4 * q4 + i, idx1 = i0 + 16 + 4 * q4 + i;
-        sv[2 * i] = idx0 < i_end ? sc0[i] * scale_log2 : NEG_INF;
-        sv[2 * i + 1] = idx1 < i_end ? sc1[i] * scale_log2 : NEG_INF;
-      }
-      float mx = sv[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m_run[hg], mx);  // finite: slot i0 is always inside the chunk
-      const float alpha = exp2_fast(m_run[hg] - mn);
-      uint32_t pbits[8];
-      float psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pbits[e] = f32_to_bf16_bits(exp2_fast(sv[e] - mn));
-        psum += __uint_as_float(pbits[e] << 16);
-      }
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
-      l_run[hg] = l_run[hg] * alpha + psum;
-      m_run[hg] = mn;
-      const v4u pw = {pbits[0] | (pbits[1] << 16), pbits[2] | (pbits[3] << 16),
-                      pbits[4] | (pbits[5] << 16), pbits[6] | (pbits[7] << 16)};
-      pB[hg] = __builtin_bit_cast(bf16x8, pw);
-      if (__any(alpha != 1.f)) {  // the running max moved for some head
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) o[hg][jj] *= alpha;
+        for (int jj = 0; jj < 8; ++jj) o[hg][jj] *= a;
       }
     }
-    // PV: each value tile is read once and used by every head group
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
       const v4u a = *(const v4u *)(vt + vt_row(16 * jj + r) + 4 * q4);
@@ -298,62 +383,88 @@ __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
         o[hg][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pB[hg],
                                                              o[hg][jj], 0, 0, 0);
     }
-    if (has_next) {
-#pragma unroll
-      for (int jj = 0; jj < 5; ++jj) {
-        ka[jj] = xa[jj];
-        kb[jj] = xb[jj];
-      }
-      ca = na;
-      cb = nb;
-      na = nna;
-      nb = nnb;
+  };
+
+  if (DEPTH == 2) {
+    Rows R0, R1, R2;
+    issue(0, R0);
+    issue(1, R1);
+    for (int st = 0;;) {
+      if (st >= n_steps) break;
+      step(st++, R0, R2);
+      if (st >= n_steps) break;
+      step(st++, R1, R0);
+      if (st >= n_steps) break;
+      step(st++, R2, R1);
+    }
+  } else {
+    Rows R0, R1;
+    issue(0, R0);
+    for (int st = 0;;) {
+      if (st >= n_steps) break;
+      step(st++, R0, R1);
+      if (st >= n_steps) break;
+      step(st++, R1, R0);
     }
   }
 
   const int any_bad = __syncthreads_or(bad ? 1 : 0);
-  if (any_bad && tid == 0) atomicOr(&d.ctl[CTL_ERR], HS_ERR_SLOT);
+  if (any_bad && tid == 0) set_error(d.ctl, HS_ERR_SLOT);
+  // every wave needs l of every head of the workgroup
+  if (r == 0) {
+#pragma unroll
+    for (int i = 0; i < HG; ++i) s_alpha[hg_w][my_h + i] = l_run[i];
+  }
+  lds_barrier();
 
   // lane holds O^T[v = 128w + 16jj + 4q4 + i][head 16hg + r]
 #pragma unroll
   for (int hg = 0; hg < HG; ++hg) {
-    const size_t row = (size_t)u * Hq + hg * 16 + r;
+    const size_t row = (size_t)u * Hq + h0 + hg * 16 + r;
     if (S == 1) {
-      const float inv = any_bad ? __builtin_nanf("") : 1.f / l_run[hg];
+      const float inv = 1.f / s_alpha[hg][r];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const floatx4 v = o[hg][jj] * inv;
-        *(floatx4 *)(out + row * LAT_DL + 128 * w + 16 * jj + 4 * q4) = v;
+        const v4u bits = {nan_bits_if(any_bad, v[0]), nan_bits_if(any_bad, v[1]),
+                          nan_bits_if(any_bad, v[2]), nan_bits_if(any_bad, v[3])};
+        *(HS_GLOBAL v4u *)(out + row * LAT_DL + 128 * w + 16 * jj + 4 * q4) = bits;
       }
     } else {
-      float *dst = ws_o + (row * S + sp) * LAT_DL + 128 * w + 4 * q4;
+      HS_GLOBAL float *dst = glb(ws_o) + (row * S + sp) * LAT_DL + 128 * w + 4 * q4;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) *(floatx4 *)(dst + 16 * jj) = o[hg][jj];
-      if (w == 0 && q4 == 0) {
-        ws_ml[(row * S + sp) * 2] = any_bad ? __builtin_nanf("") : m_run[hg];
-        ws_ml[(row * S + sp) * 2 + 1] = l_run[hg];
-      }
+      for (int jj = 0; jj < 8; ++jj) *(HS_GLOBAL floatx4 *)(dst + 16 * jj) = o[hg][jj];
+    }
+  }
+  if (S > 1 && r == 0) {
+#pragma unroll
+    for (int i = 0; i < HG; ++i) {
+      const size_t row = (size_t)u * Hq + h0 + hg_w * 16 + my_h + i;
+      ((HS_GLOBAL uint32_t *)ws_ml)[(row * S + sp) * 2] = nan_bits_if(any_bad, m_run[i]);
+      ws_ml[(row * S + sp) * 2 + 1] = l_run[i];
     }
   }
 }
 
-template <int HG, bool FETCH>
+template <int HG, int DEPTH, bool FETCH>
 hipError_t launch_latent_t(const AttnLatentArgs &a, hipStream_t stream) {
-  const int grid = ((a.n_units + 7) / 8) * 8 * a.splits;
+  const int HS = a.Hq / (HG * 16);
+  if (a.chunk > LAT_MAX_CHUNK || a.chunk % 32) return hipErrorInvalidValue;
+  const int grid = ((a.n_units + 7) / 8) * 8 * a.splits * HS;
   trace_begin(HS_TRACE_ATTN, stream);
-  hipLaunchKernelGGL((hs_k_attn_latent<HG, FETCH>), dim3(grid), dim3(LAT_THREADS), 0, stream,
-                     a.units, a.q, a.slots, a.n_units, a.k, a.scale_log2, a.splits, a.chunk,
-                     a.ws_o, a.ws_ml, a.out);
+  hipLaunchKernelGGL((hs_k_attn_latent<HG, DEPTH, FETCH>), dim3(grid), dim3(LAT_THREADS), 0,
+                     stream, a.units, a.q, a.slots, a.n_units, a.k, a.scale_log2, a.splits, HS,
+                     a.chunk, a.ws_o, a.ws_ml, a.out);
   trace_end(stream);
   return hipGetLastError();
 }
 
 template <bool FETCH>
 hipError_t launch_latent_f(const AttnLatentArgs &a, hipStream_t stream) {
-  switch (a.Hq / 16) {
-    case 1: return launch_latent_t<1, FETCH>(a, stream);
-    case 2: return launch_latent_t<2, FETCH>(a, stream);
-    case 4: return launch_latent_t<4, FETCH>(a, stream);
+  switch (a.hpw / 16) {
+    case 1: return launch_latent_t<1, 1, FETCH>(a, stream);
+    case 2: return launch_latent_t<2, 2, FETCH>(a, stream);
+    case 4: return launch_latent_t<4, 1, FETCH>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

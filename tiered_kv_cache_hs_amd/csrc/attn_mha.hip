@@ -120,7 +120,7 @@ __global__ __launch_bounds__(MHA_THREADS) void hs_k_attn_mha(
   const int grp = wave * NG + lane / LPS;
   const int gl = lane % LPS;
 
-  const UnitDesc d = units[u];
+  const UnitG d = unit_g(units[u]);
   const int B = d.B;
   const int i_begin = s * chunk;
   const int i_end = min(k, i_begin + chunk);
@@ -168,14 +168,14 @@ __global__ __launch_bounds__(MHA_THREADS) void hs_k_attn_mha(
       }
       slot_of[uu] = slot;
       const bool host = FETCH && src[uu] >= 0;
-      const uint8_t *row = host ? d.pool + (size_t)src[uu] * rec_bytes
-                                : d.rows + (size_t)slot * rec_bytes;
+      const HS_GLOBAL uint8_t *row = host ? d.pool + (size_t)src[uu] * rec_bytes
+                                          : d.rows + (size_t)slot * rec_bytes;
       if (valid[uu] && host) {
-        kw[uu] = __builtin_nontemporal_load((const v4u *)(row + koff));
-        vw[uu] = __builtin_nontemporal_load((const v4u *)(row + voff));
+        kw[uu] = __builtin_nontemporal_load((const HS_GLOBAL v4u *)(row + koff));
+        vw[uu] = __builtin_nontemporal_load((const HS_GLOBAL v4u *)(row + voff));
       } else if (valid[uu]) {
-        kw[uu] = *(const v4u *)(row + koff);
-        vw[uu] = *(const v4u *)(row + voff);
+        kw[uu] = *(const HS_GLOBAL v4u *)(row + koff);
+        vw[uu] = *(const HS_GLOBAL v4u *)(row + voff);
       } else {
         kw[uu] = v4u{0, 0, 0, 0};
         vw[uu] = v4u{0, 0, 0, 0};
@@ -184,9 +184,9 @@ __global__ __launch_bounds__(MHA_THREADS) void hs_k_attn_mha(
 #pragma unroll
     for (int uu = 0; uu < MHA_UNROLL; ++uu) {
       if (FETCH && src[uu] >= 0) {  // the fetched slices go to the slot's row
-        uint8_t *row = d.rows + (size_t)slot_of[uu] * rec_bytes;
-        *(v4u *)(row + koff) = kw[uu];
-        *(v4u *)(row + voff) = vw[uu];
+        HS_GLOBAL uint8_t *row = d.rows + (size_t)slot_of[uu] * rec_bytes;
+        *(HS_GLOBAL v4u *)(row + koff) = kw[uu];
+        *(HS_GLOBAL v4u *)(row + voff) = vw[uu];
       }
       float kf[EPL], vf[EPL];
       Elem<T>::unpack(kw[uu], kf);
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(MHA_THREADS) void hs_k_attn_mha(
     }
   }
   const int any_bad = __syncthreads_or(bad ? 1 : 0);
-  if (any_bad && tid == 0) atomicOr(&d.ctl[CTL_ERR], HS_ERR_SLOT);
+  if (any_bad && tid == 0) set_error(d.ctl, HS_ERR_SLOT);
 
   // merge the waves; threads index (head, element)
   for (int t = tid; t < GQ * D; t += MHA_THREADS) {

@@ -23,10 +23,57 @@ struct __attribute__((aligned(128))) UnitDesc {
   int32_t pad[5];
 };
 
+#define HS_GLOBAL __attribute__((address_space(1)))
+
+// (slot, position) pair of a fetch list entry
+typedef int32_t int2v __attribute__((ext_vector_type(2)));
+
+// The same unit as seen by a kernel: every pointer in the global address
+// space, so accesses compile to global_* instructions. Generic (flat)
+// accesses are counted by the LDS wait counter as well as the vector-memory
+// one, so a flat load in flight makes every LDS wait, and every barrier
+// that orders LDS, wait for it too.
+struct UnitG {
+  HS_GLOBAL uint8_t *rows;
+  HS_GLOBAL int32_t *pos;
+  HS_GLOBAL uint32_t *stamp;
+  HS_GLOBAL int2v *work;
+  HS_GLOBAL int32_t *fsrc;
+  HS_GLOBAL uint32_t *ctl;
+  HS_GLOBAL const uint8_t *pool;
+  HS_GLOBAL const int64_t *len;
+  int32_t B;
+};
+
+__device__ __forceinline__ UnitG unit_g(const UnitDesc &d) {
+  UnitG g;
+  g.rows = (HS_GLOBAL uint8_t *)d.rows;
+  g.pos = (HS_GLOBAL int32_t *)d.pos;
+  g.stamp = (HS_GLOBAL uint32_t *)d.stamp;
+  g.work = (HS_GLOBAL int2v *)d.work;
+  g.fsrc = (HS_GLOBAL int32_t *)d.fsrc;
+  g.ctl = (HS_GLOBAL uint32_t *)d.ctl;
+  g.pool = (HS_GLOBAL const uint8_t *)d.pool;
+  g.len = (HS_GLOBAL const int64_t *)d.len;
+  g.B = d.B;
+  return g;
+}
+
+// A generic pointer taken as a global one (kernel arguments and workspace).
+template <class T>
+__device__ __forceinline__ HS_GLOBAL T *glb(T *p) {
+  return (HS_GLOBAL T *)p;
+}
+
 constexpr int CTL_CLOCK = 0;  // resolve steps done
 constexpr int CTL_ERR = 1;    // sticky HS_ERR_* bits
 constexpr int CTL_FETCH = 2;  // records the last resolve must fetch
 constexpr int CTL_WORDS = 64; // control block size in words (256 bytes)
+
+// Sticky error bits of a unit (device scope).
+__device__ __forceinline__ void set_error(HS_GLOBAL uint32_t *ctl, uint32_t bits) {
+  __hip_atomic_fetch_or(ctl + CTL_ERR, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Workgroup barrier that orders LDS accesses only. A plain __syncthreads()
 // also waits for every outstanding global load and store of the wave
@@ -89,11 +136,16 @@ struct AttnMhaArgs {
 };
 hipError_t launch_attn_mha(const AttnMhaArgs &a, hipStream_t stream);
 
+// Most selection entries one latent attention workgroup covers (its slot
+// ids are staged in LDS).
+constexpr int LAT_MAX_CHUNK = 2048;
+
 struct AttnLatentArgs {
   const UnitDesc *units;
   const uint16_t *q;
   const int32_t *slots;
   int n_units, k, Hq, splits, chunk;
+  int hpw;    // query heads per workgroup (16, 32 or 64; divides Hq)
   int fetch;  // fused resolve: read just-resolved misses from the host pool
   float scale_log2;
   float *ws_o, *ws_ml, *out;

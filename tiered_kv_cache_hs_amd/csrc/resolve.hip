@@ -145,7 +145,7 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   const int u = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const UnitDesc d = units[u];
+  const UnitG d = unit_g(units[u]);
   const int B = d.B;
   const int32_t *topk = topk_all + (size_t)u * k;
   int32_t *slots = slots_all + (size_t)u * k;
@@ -434,7 +434,7 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
     d.pos[s] = p;
     d.stamp[s] = 2u * c - 1u;
     slot_of[i] = s;
-    d.work[r] = make_int2(s, p);
+    d.work[r] = int2v{s, p};
   }
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
@@ -469,7 +469,7 @@ __global__ __launch_bounds__(GATHER_THREADS) void hs_k_gather(
     const UnitDesc *__restrict__ units, int G, int rec16) {
   const int u = blockIdx.x / G;
   const int g = blockIdx.x - u * G;
-  const UnitDesc d = units[u];
+  const UnitG d = unit_g(units[u]);
   const int m = (int)d.ctl[CTL_FETCH];
   if (m <= 0 || m > d.B) return;
   const int total = m * rec16;
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(GATHER_THREADS) void hs_k_gather(
   for (int c0 = g * GATHER_THREADS + (int)threadIdx.x; c0 < total;
        c0 += stride * GATHER_UNROLL) {
     v4u v[GATHER_UNROLL];
-    v4u *dst[GATHER_UNROLL];
+    HS_GLOBAL v4u *dst[GATHER_UNROLL];
 #pragma unroll
     for (int uu = 0; uu < GATHER_UNROLL; ++uu) {
       const int c = c0 + uu * stride;
@@ -486,10 +486,10 @@ __global__ __launch_bounds__(GATHER_THREADS) void hs_k_gather(
       if (c < total) {
         const int r = c / rec16;
         const int off = c - r * rec16;
-        const int2 w = d.work[r];
-        const v4u *src = (const v4u *)(d.pool + (size_t)w.y * rec) + off;
+        const int2v w = d.work[r];
+        const HS_GLOBAL v4u *src = (const HS_GLOBAL v4u *)(d.pool + (size_t)w.y * rec) + off;
         v[uu] = __builtin_nontemporal_load(src);
-        dst[uu] = (v4u *)(d.rows + (size_t)w.x * rec) + off;
+        dst[uu] = (HS_GLOBAL v4u *)(d.rows + (size_t)w.x * rec) + off;
       }
     }
 #pragma unroll
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(GATHER_THREADS) void hs_k_gather(
 // Re-gather every occupied row of one buffer (checkpoint restore).
 __global__ __launch_bounds__(256) void hs_k_regather(const UnitDesc *__restrict__ unit,
                                                      int B, int rec16) {
-  const UnitDesc d = *unit;
+  const UnitG d = unit_g(*unit);
   const size_t rec = (size_t)rec16 * 16;
   const int64_t total = (int64_t)B * rec16;
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < total;
@@ -510,8 +510,8 @@ __global__ __launch_bounds__(256) void hs_k_regather(const UnitDesc *__restrict_
     const int off = (int)(c - (int64_t)s * rec16);
     const int32_t p = d.pos[s];
     if (p < 0) continue;
-    const v4u *src = (const v4u *)(d.pool + (size_t)p * rec) + off;
-    ((v4u *)(d.rows + (size_t)s * rec))[off] = __builtin_nontemporal_load(src);
+    const HS_GLOBAL v4u *src = (const HS_GLOBAL v4u *)(d.pool + (size_t)p * rec) + off;
+    ((HS_GLOBAL v4u *)(d.rows + (size_t)s * rec))[off] = __builtin_nontemporal_load(src);
   }
 }
 

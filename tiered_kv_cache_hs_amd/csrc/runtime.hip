@@ -44,7 +44,7 @@ hs_status hip_fail(hipError_t e, const char *what) {
     if (e_ != hipSuccess) return hip_fail(e_, #call); \
   } while (0)
 
-hs_tuning g_tuning = {0, 0, {0, 0, 0, 0, 0, 0}};
+hs_tuning g_tuning = {0, 0, 0, {0, 0, 0, 0, 0}};
 
 inline hipStream_t S(void *s) { return (hipStream_t)s; }
 
@@ -136,6 +136,9 @@ hs_status hs_set_tuning(const hs_tuning *t) {
   if (t->gather_wgs_per_unit < 0 || t->gather_wgs_per_unit > 4096 || t->attn_splits < 0 ||
       t->attn_splits > 4096)
     return fail(HS_E_INVAL, "tuning value out of range");
+  const int hpw = t->latent_heads_per_wg;
+  if (hpw != 0 && hpw != 16 && hpw != 32 && hpw != 64)
+    return fail(HS_E_INVAL, "latent_heads_per_wg must be 0, 16, 32 or 64");
   g_tuning = *t;
   return HS_OK;
 }
@@ -520,6 +523,7 @@ hs_status hs_resolve(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_t *d_
 
 struct AttnPlan {
   int splits, chunk, dv;
+  int hpw;  // latent: query heads per workgroup
   size_t ws_o_floats, ws_ml_floats, ws_bytes;
 };
 
@@ -542,7 +546,11 @@ static hs_status plan_attn(hs_batch_t b, int32_t Hq, int32_t k, AttnPlan *pl) {
       return fail(HS_E_INVAL, "latent attention needs bf16, 512 + 64");
     if (Hq != 16 && Hq != 32 && Hq != 64)
       return fail(HS_E_INVAL, "latent attention supports 16, 32 or 64 query heads");
-    base = (b->n + 7) / 8 * 8;  // one workgroup covers all heads of a (unit, split)
+    // a workgroup covers hpw heads of a (unit, split)
+    int hpw = g_tuning.latent_heads_per_wg > 0 ? g_tuning.latent_heads_per_wg : Hq;
+    if (hpw > Hq || Hq % hpw) hpw = Hq;
+    pl->hpw = hpw;
+    base = (b->n + 7) / 8 * 8 * (Hq / hpw);
     min_chunk = 64;
     target = 256;
     pl->dv = p->Dl;
@@ -551,6 +559,7 @@ static hs_status plan_attn(hs_batch_t b, int32_t Hq, int32_t k, AttnPlan *pl) {
   const int max_splits = std::max(1, k / min_chunk);
   if (g_tuning.attn_splits <= 0) splits = std::min(splits, max_splits);
   splits = std::max(1, std::min(std::min(splits, k), 64));  // the combine merges <= 64
+  if (p->kind == HS_KV_LATENT) splits = std::max(splits, (k + hs::LAT_MAX_CHUNK - 1) / hs::LAT_MAX_CHUNK);
   int chunk = (k + splits - 1) / splits;
   if (p->kind == HS_KV_LATENT) chunk = (chunk + 31) / 32 * 32;
   splits = (k + chunk - 1) / chunk;  // every split has at least one slot
@@ -630,6 +639,7 @@ static hs_status enqueue_attn(hs_batch_t b, const void *d_q, int32_t Hq, const i
     a.Hq = Hq;
     a.splits = pl.splits;
     a.chunk = pl.chunk;
+    a.hpw = pl.hpw;
     a.fetch = fetch;
     a.scale_log2 = scale_log2;
     a.ws_o = ws_o;
