@@ -167,7 +167,9 @@ __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
   const int i_begin = sp * chunk;
   const int i_end = min(k, i_begin + chunk);
   const int n_rows = i_end - i_begin;
-  const int n_steps = (n_rows + 31) >> 5;
+  // uniform by construction; said so explicitly, or the step loop compiles
+  // as a divergent loop that drains every load at its back edge
+  const int n_steps = __builtin_amdgcn_readfirstlane((n_rows + 31) >> 5);
   const HS_GLOBAL int32_t *slots = glb(slots_all) + (size_t)u * k;
   const int64_t pool_len = FETCH ? *d.len : 0;
 
@@ -230,10 +232,11 @@ __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
     const bool from_host = FETCH && valid && rf.src >= 0;
     const bool host_ok = from_host && (int64_t)rf.src < pool_len;
     if (!valid || from_host != host_ok) bad = true;
-    const HS_GLOBAL uint8_t *p =
-        (host_ok ? d.pool + (size_t)rf.src * LAT_REC
-                 : d.rows + (size_t)(valid && !from_host ? rf.slot : 0) * LAT_REC) +
-        16 * q4;
+    // base and row index selected without branches, then one 32 x 32 -> 64
+    // multiply-add
+    const HS_GLOBAL uint8_t *base = host_ok ? d.pool : d.rows;
+    const uint32_t row = host_ok ? (uint32_t)rf.src : (valid && !from_host ? (uint32_t)rf.slot : 0u);
+    const HS_GLOBAL uint8_t *p = base + (uint64_t)row * LAT_REC + 16 * q4;
 #pragma unroll
     for (int jj = 0; jj < 5; ++jj) {
       const int ds = jj < 4 ? 4 * w + jj : 16 + (w & 1);
@@ -361,7 +364,11 @@ __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
     }
     lds_barrier();
 
-    // 3. PV: each value tile is read once and used by every head group
+    // 3. PV: each value tile is read once and used by every head group; all
+    // eight tiles are read before the MFMAs so the reads overlap
+    v4u vtile[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) vtile[jj] = *(const v4u *)(vt + vt_row(16 * jj + r) + 4 * q4);
     bf16x8 pB[HG];
 #pragma unroll
     for (int hg = 0; hg < HG; ++hg) {
@@ -377,11 +384,10 @@ __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
     }
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {
-      const v4u a = *(const v4u *)(vt + vt_row(16 * jj + r) + 4 * q4);
 #pragma unroll
       for (int hg = 0; hg < HG; ++hg)
-        o[hg][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pB[hg],
-                                                             o[hg][jj], 0, 0, 0);
+        o[hg][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vtile[jj]),
+                                                             pB[hg], o[hg][jj], 0, 0, 0);
     }
   };
 
