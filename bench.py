@@ -39,9 +39,11 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--path", choices=("fused", "split"), default="fused",
+    ap.add_argument("--path", choices=("auto", "fused", "split"), default="auto",
                     help="fused: hs_resolve_attn (misses fetched by the attention kernels); "
-                         "split: hs_resolve (with its gather kernel) then hs_sparse_attn")
+                         "split: hs_resolve (which also fetches the misses) then "
+                         "hs_sparse_attn; auto: fused for MHA records, split for latent "
+                         "records (the faster of the two for each on MI355X)")
     return ap.parse_args()
 
 
@@ -130,7 +132,7 @@ def main():
     total = W + K
     print(f"[bench] workload {w.name}: building session ({total} steps)", file=sys.stderr, flush=True)
     fill = "full" if w.n_units * max(w.ctx) * w.rec_bytes <= (8 << 30) else "touched"
-    fused = args.path == "fused"
+    fused = args.path == "fused" or (args.path == "auto" and w.kind == "mha")
     sess = Session(w, total, fill=fill, fused=fused)
     sess.capture()
     print("[bench] graphs captured", file=sys.stderr, flush=True)
@@ -173,9 +175,10 @@ def main():
     attn_us = per["attn"]
     attn_gbs = a_bytes / (attn_us * 1e-6) / 1e9 if attn_us else 0.0
     attn_kernel = "hs_k_attn_latent" if w.kind == "latent" else "hs_k_attn_mha"
-    # the kernel that moves the misses over the host link: the gather kernel,
-    # or in the fused path the attention kernel itself
-    fetch_class = "attn" if fused else "gather"
+    # the kernel that moves the misses over the host link: the attention
+    # kernel (fused path), the gather kernel (batches of fewer than 4 units),
+    # else the resolve kernel itself
+    fetch_class = "attn" if fused else ("gather" if tr["gather"][1] else "resolve")
     fetch_us = per[fetch_class]
     miss_bytes_launch = misses.sum() * w.rec_bytes / max(1, tr[fetch_class][1])
     host_gbs = miss_bytes_launch / (fetch_us * 1e-6) / 1e9 if fetch_us else 0.0
@@ -189,7 +192,8 @@ def main():
     roof_host = {"bound": "host_link", "achieved": round(host_gbs, 2),
                  "peak": HOST_LINK_PEAK_GBS, "unit": "GB/s",
                  "frac": round(host_gbs / HOST_LINK_PEAK_GBS, 4), "traffic": None,
-                 "kernel": attn_kernel if fused else "hs_k_gather", "avg_us": round(fetch_us, 2),
+                 "kernel": {"attn": attn_kernel, "gather": "hs_k_gather",
+                            "resolve": "hs_k_resolve"}[fetch_class], "avg_us": round(fetch_us, 2),
                  "bytes_per_launch": int(miss_bytes_launch)}
     if fused:
         # one kernel moves both; its bound is the resource whose peak-rate

@@ -103,11 +103,10 @@ typedef struct hs_pool_desc {
 
 /* Tuning knobs (library-wide; 0 = choose automatically). */
 typedef struct hs_tuning {
-  int32_t gather_wgs_per_unit;  /* workgroups copying one unit's misses */
   int32_t attn_splits;          /* split-k factor of sparse attention */
   int32_t latent_heads_per_wg;  /* latent attention: query heads per workgroup
                                    (16, 32 or 64, dividing n_q_heads) */
-  int32_t reserved[5];
+  int32_t reserved[6];
 } hs_tuning;
 
 const char *hs_status_str(hs_status s);
@@ -261,11 +260,14 @@ hs_status hs_resolve_attn(hs_batch_t batch, const int32_t *d_topk, int32_t k,
  * of HIP events recorded on the same stream (do not enable it around graph
  * capture). hs_trace_read synchronises the device, adds up the elapsed time
  * of every completed pair per kernel class and clears the record. Classes:
- * HS_TRACE_SELECT (hash, probe, victim select, update), HS_TRACE_GATHER
- * (host-to-device miss fetch), HS_TRACE_ATTN (sparse attention),
- * HS_TRACE_COMBINE (split-k merge). At most 4096 launches are recorded
- * between reads; later ones are counted in `dropped`. */
-#define HS_TRACE_SELECT 0
+ * HS_TRACE_RESOLVE (hash, probe, victim select, update; for hs_resolve on
+ * batches of 4 or more units also the host-to-device miss fetch),
+ * HS_TRACE_GATHER (the miss fetch of hs_resolve on smaller batches, a kernel
+ * of its own), HS_TRACE_ATTN (sparse attention; for hs_resolve_attn it
+ * includes the miss fetch), HS_TRACE_COMBINE (split-k merge). At most 4096
+ * launches are recorded between reads; later ones are counted in
+ * `dropped`. */
+#define HS_TRACE_RESOLVE 0
 #define HS_TRACE_GATHER 1
 #define HS_TRACE_ATTN 2
 #define HS_TRACE_COMBINE 3

@@ -39,14 +39,13 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_tuning_roundtrip():
     assert H.hs_status_str(H.HS_OK) == "ok"
     assert H.hs_status_str(H.HS_E_STATE) == "invalid buffer state"
-    H.hs_set_tuning(8, 4, 32)
-    assert H.hs_get_tuning() == {"gather_wgs_per_unit": 8, "attn_splits": 4,
-                                 "latent_heads_per_wg": 32}
+    H.hs_set_tuning(4, 32)
+    assert H.hs_get_tuning() == {"attn_splits": 4, "latent_heads_per_wg": 32}
     H.hs_set_tuning(0, 0)
     with pytest.raises(H.HsError):
         H.hs_set_tuning(-1, 0)
     with pytest.raises(H.HsError):
-        H.hs_set_tuning(0, 0, 48)
+        H.hs_set_tuning(0, 48)
 
 
 def test_null_and_shape_checks_without_device():

@@ -151,7 +151,7 @@ def test_latent_heads_per_workgroup(hpw, splits, fused):
     """Latent attention with every head split (16, 32 or 64 heads per
     workgroup), several split-k factors, a ragged last step of 32 slots."""
     w = _small("latent", I.BF16, 300, 197, 3000, 4, 40, R=2, seed=50 + hpw + splits, Hq=64)
-    H.hs_set_tuning(0, splits, hpw)
+    H.hs_set_tuning(splits, hpw)
     try:
         compare_run(w, 4, fill="full", fused=fused)
     finally:

@@ -28,6 +28,7 @@ struct __attribute__((aligned(128))) UnitDesc {
 // (slot, position) pair of a fetch list entry
 typedef int32_t int2v __attribute__((ext_vector_type(2)));
 
+
 // The same unit as seen by a kernel: every pointer in the global address
 // space, so accesses compile to global_* instructions. Generic (flat)
 // accesses are counted by the LDS wait counter as well as the vector-memory
@@ -67,7 +68,7 @@ __device__ __forceinline__ HS_GLOBAL T *glb(T *p) {
 
 constexpr int CTL_CLOCK = 0;  // resolve steps done
 constexpr int CTL_ERR = 1;    // sticky HS_ERR_* bits
-constexpr int CTL_FETCH = 2;  // records the last resolve must fetch
+constexpr int CTL_FETCH = 2;  // records the last resolve fetched (or left to fetch)
 constexpr int CTL_WORDS = 64; // control block size in words (256 bytes)
 
 // Sticky error bits of a unit (device scope).
@@ -115,9 +116,15 @@ void trace_end(hipStream_t stream);
 // return the hipError_t of the launch.
 hipError_t launch_buffer_init(int32_t *pos, uint32_t *stamp, int32_t *fsrc, uint32_t *ctl,
                               int B, hipStream_t stream);
+// How a resolve fetches its misses: not at all (the attention kernels read
+// them from the host pool), inside the resolve kernel (its first host reads
+// overlap the victim selection; one workgroup per unit), or with a second
+// kernel of many workgroups per unit (enough host reads in flight when the
+// batch has few units).
+constexpr int FETCH_NONE = 0, FETCH_INLINE = 1, FETCH_KERNEL = 2;
 hipError_t launch_resolve(const UnitDesc *d_units, int n_units, int max_B,
                           const int32_t *d_topk, int k, int32_t *d_slots,
-                          int32_t *d_miss, int gather_wgs, int rec_bytes,
+                          int32_t *d_miss, int fetch, int rec_bytes,
                           hipStream_t stream);
 size_t resolve_lds_bytes(int k);
 hipError_t launch_regather(const UnitDesc *d_unit, int B, int rec_bytes,

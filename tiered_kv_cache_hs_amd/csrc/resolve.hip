@@ -25,10 +25,14 @@
 //    digits (LDS histogram, one wave scans it) finds the exact threshold.
 //    Leading digits shared by every candidate are skipped, and the select
 //    stops at the first digit whose bucket is taken whole.
-//  * hs_k_gather: the fetch list is copied by many workgroups per unit with
-//    16-byte non-temporal loads from the device-mapped host pool, several
-//    loads in flight per lane, so the host link sees many outstanding reads
-//    even at small batch.
+//  * The fetch (batched gather): with 4 or more units per launch it runs in
+//    the same workgroup: each thread reads 16-byte chunks of the missed
+//    records with non-temporal loads from the device-mapped host pool, up to
+//    8 per thread in flight, the first batch issued as soon as the miss list
+//    is known, so host-link latency overlaps the victim selection. One
+//    compute unit keeps only so many host reads in flight, so smaller
+//    batches fetch with hs_k_gather instead: many workgroups per unit copy
+//    the fetch list the resolve wrote.
 #include <type_traits>
 
 #include "hs_device.h"
@@ -119,14 +123,21 @@ __device__ __forceinline__ uint32_t wave_minmax_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-template <int NT, int SPT, int KPT>
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+// GATHER: the kernel also copies the missed records from the host pool into
+// their victim rows (the batched gather of the fetch); the first batch of
+// host reads is issued as soon as the misses are known, so it overlaps the
+// victim selection. Without GATHER the fetch is left to the attention
+// kernels (fsrc says which rows they must read from the host).
+template <int NT, int SPT, int KPT, bool GATHER>
 __global__ __launch_bounds__(NT) void hs_k_resolve(
     const UnitDesc *__restrict__ units, const int32_t *__restrict__ topk_all,
-    int k, int hlog2, int32_t *__restrict__ slots_all,
+    int k, int hlog2, int rec16, int32_t *__restrict__ slots_all,
     int32_t *__restrict__ miss_all) {
   // LDS: region A holds the hash table (keys, values: 2H ints) during build
-  // and probe, then the miss and victim lists (2k ints); region B holds
-  // slot_of[k].
+  // and probe, then the miss, victim and miss-position lists (3k ints);
+  // region B holds slot_of[k].
   extern __shared__ int lds[];
   constexpr int NW = NT / 64;
   __shared__ int scan_buf[2][RES_MAX_WAVES];
@@ -139,7 +150,8 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   int *hval = lds + H;
   int *miss_list = lds;
   int *victim_list = lds + k;
-  const int regionA = (2 * H > 2 * k) ? 2 * H : 2 * k;
+  int *miss_pos = lds + 2 * k;
+  const int regionA = (2 * H > 3 * k) ? 2 * H : 3 * k;
   int *slot_of = lds + regionA;
 
   const int u = blockIdx.x;
@@ -321,9 +333,33 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   int m;
   int mrank = block_excl_scan<NW>(my_miss, &m, scan_buf, parity);
 #pragma unroll
-  for (int j = 0; j < KPT; ++j)
-    if (miss_here[j]) miss_list[mrank++] = k0 + j;
+  for (int j = 0; j < KPT; ++j) {
+    if (miss_here[j]) {
+      miss_pos[mrank] = tk[j];
+      miss_list[mrank++] = k0 + j;
+    }
+  }
   const int n_cand = B - (k - m);
+
+  // ---- gather, first batch: host reads of the first GB * NT record chunks
+  // (16 bytes each) of the misses, in flight during the victim selection
+  constexpr int GB = SPT >= 16 ? 4 : 8;
+  const size_t rec = (size_t)rec16 * 16;
+  const int g_total = m * rec16;
+  v4u gv[GB];
+  if (GATHER) {
+    lds_barrier();  // miss_pos complete
+#pragma unroll
+    for (int b = 0; b < GB; ++b) {
+      const int c = tid + NT * b;
+      if (c < g_total) {
+        const int j = c / rec16;
+        const int off = c - j * rec16;
+        gv[b] = __builtin_nontemporal_load(
+            (const HS_GLOBAL v4u *)(d.pool + (size_t)miss_pos[j] * rec) + off);
+      }
+    }
+  }
 
   // ---- 4. victims: the m smallest keys among non-hit slots, by an MSB-first
   // radix select over 8-bit digits; one barrier per digit (histograms rotate
@@ -434,12 +470,39 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
     d.pos[s] = p;
     d.stamp[s] = 2u * c - 1u;
     slot_of[i] = s;
-    d.work[r] = int2v{s, p};
+    if (!GATHER) d.work[r] = int2v{s, p};
   }
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
     if ((hitmask >> j) & 1u) d.stamp[s0 + j] = 2u * c;
   lds_barrier();
+
+  // ---- gather: the first batch into the victim rows, then the rest
+  if (GATHER) {
+    for (int base = 0; base < g_total; base += GB * NT) {
+      if (base > 0) {
+#pragma unroll
+        for (int b = 0; b < GB; ++b) {
+          const int c = base + tid + NT * b;
+          if (c < g_total) {
+            const int j = c / rec16;
+            const int off = c - j * rec16;
+            gv[b] = __builtin_nontemporal_load(
+                (const HS_GLOBAL v4u *)(d.pool + (size_t)miss_pos[j] * rec) + off);
+          }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < GB; ++b) {
+        const int c = base + tid + NT * b;
+        if (c < g_total) {
+          const int j = c / rec16;
+          const int off = c - j * rec16;
+          ((HS_GLOBAL v4u *)(d.rows + (size_t)victim_list[j] * rec))[off] = gv[b];
+        }
+      }
+    }
+  }
 
   // ---- 7. publish the slot vector, aligned with the selection
 #pragma unroll
@@ -462,8 +525,6 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
 // the unit's 16-byte chunks g*256 + tid, stepping by G*256.
 constexpr int GATHER_THREADS = 256;
 constexpr int GATHER_UNROLL = 4;
-
-typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(GATHER_THREADS) void hs_k_gather(
     const UnitDesc *__restrict__ units, int G, int rec16) {
@@ -538,11 +599,15 @@ __global__ __launch_bounds__(256) void hs_k_append(uint8_t *dst, const uint8_t *
 
 template <int NT, int SPT, int KPT>
 hipError_t launch_select(const UnitDesc *d_units, int n, const int32_t *d_topk, int k,
-                         int hlog2, size_t lds, int32_t *d_slots, int32_t *d_miss,
-                         hipStream_t stream) {
-  trace_begin(HS_TRACE_SELECT, stream);
-  hipLaunchKernelGGL((hs_k_resolve<NT, SPT, KPT>), dim3(n), dim3(NT), lds, stream, d_units,
-                     d_topk, k, hlog2, d_slots, d_miss);
+                         int hlog2, int rec16, bool gather, size_t lds, int32_t *d_slots,
+                         int32_t *d_miss, hipStream_t stream) {
+  trace_begin(HS_TRACE_RESOLVE, stream);
+  if (gather)
+    hipLaunchKernelGGL((hs_k_resolve<NT, SPT, KPT, true>), dim3(n), dim3(NT), lds, stream,
+                       d_units, d_topk, k, hlog2, rec16, d_slots, d_miss);
+  else
+    hipLaunchKernelGGL((hs_k_resolve<NT, SPT, KPT, false>), dim3(n), dim3(NT), lds, stream,
+                       d_units, d_topk, k, hlog2, rec16, d_slots, d_miss);
   trace_end(stream);
   return hipGetLastError();
 }
@@ -550,16 +615,17 @@ hipError_t launch_select(const UnitDesc *d_units, int n, const int32_t *d_topk, 
 // picks per thread: the power of two >= k / NT
 template <int NT, int SPT>
 hipError_t launch_select_k(const UnitDesc *d_units, int n, const int32_t *d_topk, int k,
-                           int hlog2, size_t lds, int32_t *d_slots, int32_t *d_miss,
-                           hipStream_t stream) {
-#define HS_SEL(KPT)                                                                        \
-  if (k <= NT * KPT)                                                                       \
-    return launch_select<NT, SPT, KPT>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, \
-                                       stream);
+                           int hlog2, int rec16, bool gather, size_t lds, int32_t *d_slots,
+                           int32_t *d_miss, hipStream_t stream) {
+#define HS_SEL(KPT)                                                                      \
+  if (k <= NT * KPT)                                                                     \
+    return launch_select<NT, SPT, KPT>(d_units, n, d_topk, k, hlog2, rec16, gather, lds, \
+                                       d_slots, d_miss, stream);
   HS_SEL(1)
   HS_SEL(2)
 #undef HS_SEL
-  return launch_select<NT, SPT, 4>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+  return launch_select<NT, SPT, 4>(d_units, n, d_topk, k, hlog2, rec16, gather, lds, d_slots,
+                                   d_miss, stream);
 }
 
 int hash_log2(int k) {
@@ -572,32 +638,40 @@ int hash_log2(int k) {
 
 size_t resolve_lds_bytes(int k) {
   const int H = 1 << hash_log2(k);
-  const int regionA = (2 * H > 2 * k) ? 2 * H : 2 * k;
+  const int regionA = (2 * H > 3 * k) ? 2 * H : 3 * k;
   return (size_t)(regionA + k) * sizeof(int);
 }
 
 hipError_t launch_resolve(const UnitDesc *d_units, int n, int max_B, const int32_t *d_topk,
-                          int k, int32_t *d_slots, int32_t *d_miss, int gather_wgs,
+                          int k, int32_t *d_slots, int32_t *d_miss, int fetch,
                           int rec_bytes, hipStream_t stream) {
-  // gather_wgs == 0: the fetch is left to the attention kernels
   const int hlog2 = hash_log2(k);
   const size_t lds = resolve_lds_bytes(k);
+  const int rec16 = rec_bytes / 16;
+  const bool inl = fetch == FETCH_INLINE;
   hipError_t e;
   // 16 waves per unit; each thread owns SPT = B / 1024 consecutive slots
   if (max_B <= 1024)
-    e = launch_select_k<1024, 1>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+    e = launch_select_k<1024, 1>(d_units, n, d_topk, k, hlog2, rec16, inl, lds, d_slots,
+                                 d_miss, stream);
   else if (max_B <= 2048)
-    e = launch_select_k<1024, 2>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+    e = launch_select_k<1024, 2>(d_units, n, d_topk, k, hlog2, rec16, inl, lds, d_slots,
+                                 d_miss, stream);
   else if (max_B <= 4096)
-    e = launch_select_k<1024, 4>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+    e = launch_select_k<1024, 4>(d_units, n, d_topk, k, hlog2, rec16, inl, lds, d_slots,
+                                 d_miss, stream);
   else if (max_B <= 8192)
-    e = launch_select_k<1024, 8>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
+    e = launch_select_k<1024, 8>(d_units, n, d_topk, k, hlog2, rec16, inl, lds, d_slots,
+                                 d_miss, stream);
   else
-    e = launch_select_k<1024, 16>(d_units, n, d_topk, k, hlog2, lds, d_slots, d_miss, stream);
-  if (e != hipSuccess || gather_wgs == 0) return e;
+    e = launch_select_k<1024, 16>(d_units, n, d_topk, k, hlog2, rec16, inl, lds, d_slots,
+                                  d_miss, stream);
+  if (e != hipSuccess || fetch != FETCH_KERNEL) return e;
+  // enough workgroups that about 512 copy the batch's misses
+  const int G = std::max(1, std::min(64, (512 + n - 1) / n));
   trace_begin(HS_TRACE_GATHER, stream);
-  hipLaunchKernelGGL(hs_k_gather, dim3(n * gather_wgs), dim3(GATHER_THREADS), 0, stream,
-                     d_units, gather_wgs, rec_bytes / 16);
+  hipLaunchKernelGGL(hs_k_gather, dim3(n * G), dim3(GATHER_THREADS), 0, stream, d_units, G,
+                     rec16);
   trace_end(stream);
   return hipGetLastError();
 }

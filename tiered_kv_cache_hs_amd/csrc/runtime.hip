@@ -44,7 +44,7 @@ hs_status hip_fail(hipError_t e, const char *what) {
     if (e_ != hipSuccess) return hip_fail(e_, #call); \
   } while (0)
 
-hs_tuning g_tuning = {0, 0, 0, {0, 0, 0, 0, 0}};
+hs_tuning g_tuning = {0, 0, {0, 0, 0, 0, 0, 0}};
 
 inline hipStream_t S(void *s) { return (hipStream_t)s; }
 
@@ -133,8 +133,7 @@ const char *hs_last_error(void) { return g_last_error.c_str(); }
 
 hs_status hs_set_tuning(const hs_tuning *t) {
   if (!t) return fail(HS_E_INVAL, "null tuning");
-  if (t->gather_wgs_per_unit < 0 || t->gather_wgs_per_unit > 4096 || t->attn_splits < 0 ||
-      t->attn_splits > 4096)
+  if (t->attn_splits < 0 || t->attn_splits > 4096)
     return fail(HS_E_INVAL, "tuning value out of range");
   const int hpw = t->latent_heads_per_wg;
   if (hpw != 0 && hpw != 16 && hpw != 32 && hpw != 64)
@@ -483,12 +482,6 @@ hs_status hs_batch_destroy(hs_batch_t b) {
 
 // ----------------------------------------------------------------- resolve
 
-static int gather_wgs_for(int n_units) {
-  if (g_tuning.gather_wgs_per_unit > 0) return g_tuning.gather_wgs_per_unit;
-  int g = (512 + n_units - 1) / n_units;
-  return std::max(1, std::min(64, g));
-}
-
 static hs_status check_resolve(hs_batch_t b, const int32_t *d_topk, int32_t k,
                                const int32_t *d_slots) {
   if (!b || !d_topk || !d_slots) return fail(HS_E_INVAL, "null argument");
@@ -513,8 +506,11 @@ hs_status hs_resolve(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_t *d_
                      int32_t *d_miss, void *stream) {
   hs_status s = check_resolve(b, d_topk, k, d_slots);
   if (s) return s;
+  // one workgroup per unit cannot keep enough host reads in flight for the
+  // link when the batch is small: fetch with a second, wider kernel there
+  const int fetch = b->n >= 4 ? hs::FETCH_INLINE : hs::FETCH_KERNEL;
   hipError_t e = hs::launch_resolve(b->d_units, b->n, b->max_B, d_topk, k, d_slots, d_miss,
-                                    gather_wgs_for(b->n), (int)b->pool->rec, S(stream));
+                                    fetch, (int)b->pool->rec, S(stream));
   if (e != hipSuccess) return hip_fail(e, "resolve launch");
   return HS_OK;
 }
@@ -668,9 +664,9 @@ hs_status hs_resolve_attn(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_
   AttnPlan pl;
   s = check_attn(b, d_q, Hq, d_slots, k, sm_scale, d_out, d_ws, ws_bytes, &pl);
   if (s) return s;
-  // resolve without the gather kernel: the attention kernels fetch the misses
-  hipError_t e = hs::launch_resolve(b->d_units, b->n, b->max_B, d_topk, k, d_slots, d_miss, 0,
-                                    (int)b->pool->rec, S(stream));
+  // resolve without the gather: the attention kernels fetch the misses
+  hipError_t e = hs::launch_resolve(b->d_units, b->n, b->max_B, d_topk, k, d_slots, d_miss,
+                                    hs::FETCH_NONE, (int)b->pool->rec, S(stream));
   if (e != hipSuccess) return hip_fail(e, "resolve launch");
   return enqueue_attn(b, d_q, Hq, d_slots, k, sm_scale, d_out, d_ws, pl, 1, stream);
 }

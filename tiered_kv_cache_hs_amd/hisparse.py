@@ -66,7 +66,7 @@ class PoolDesc(ctypes.Structure):
     ]
 
 
-TRACE_CLASSES = ("select", "gather", "attn", "combine")
+TRACE_CLASSES = ("resolve", "gather", "attn", "combine")
 
 
 class Trace(ctypes.Structure):
@@ -75,8 +75,8 @@ class Trace(ctypes.Structure):
 
 
 class Tuning(ctypes.Structure):
-    _fields_ = [("gather_wgs_per_unit", ctypes.c_int32), ("attn_splits", ctypes.c_int32),
-                ("latent_heads_per_wg", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
+    _fields_ = [("attn_splits", ctypes.c_int32), ("latent_heads_per_wg", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 6)]
 
 
 _lib = None
@@ -159,17 +159,15 @@ def hs_last_error() -> str:
     return lib().hs_last_error().decode()
 
 
-def hs_set_tuning(gather_wgs_per_unit: int = 0, attn_splits: int = 0,
-                  latent_heads_per_wg: int = 0) -> None:
-    t = Tuning(gather_wgs_per_unit, attn_splits, latent_heads_per_wg)
+def hs_set_tuning(attn_splits: int = 0, latent_heads_per_wg: int = 0) -> None:
+    t = Tuning(attn_splits, latent_heads_per_wg)
     _check(lib().hs_set_tuning(ctypes.byref(t)))
 
 
 def hs_get_tuning() -> dict:
     t = Tuning()
     _check(lib().hs_get_tuning(ctypes.byref(t)))
-    return {"gather_wgs_per_unit": t.gather_wgs_per_unit, "attn_splits": t.attn_splits,
-            "latent_heads_per_wg": t.latent_heads_per_wg}
+    return {"attn_splits": t.attn_splits, "latent_heads_per_wg": t.latent_heads_per_wg}
 
 
 # ------------------------------------------------------------------ pool
