@@ -39,12 +39,66 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 256 MiB device-to-device copy four times (the reference "
+                         "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE counters) and exit")
     ap.add_argument("--path", choices=("auto", "fused", "split"), default="auto",
                     help="fused: hs_resolve_attn (misses fetched by the attention kernels); "
                          "split: hs_resolve (which also fetches the misses) then "
                          "hs_sparse_attn; auto: fused for MHA records, split for latent "
                          "records (the faster of the two for each on MI355X)")
     return ap.parse_args()
+
+
+# sources whose hash keys the stored counter readings: a reading is used only
+# while the kernel it was taken from is unchanged
+KERNEL_SOURCES = {  # the kernel's file, the shared header, and the launch planner
+    "hs_k_resolve": ["resolve.hip", "hs_device.h", "runtime.hip"],
+    "hs_k_gather": ["resolve.hip", "hs_device.h", "runtime.hip"],
+    "hs_k_attn_latent": ["attn_latent.hip", "hs_device.h", "runtime.hip"],
+    "hs_k_attn_mha": ["attn_mha.hip", "hs_device.h", "runtime.hip"],
+}
+PMC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "pmc_traffic.json")
+
+
+def kernel_sources_sha1(kernel):
+    import hashlib
+    h = hashlib.sha1()
+    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tiered_kv_cache_hs_amd", "csrc")
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload, kernel):
+    """HBM bytes per dispatch of `kernel` on `workload` from the committed
+    rocprofv3 counter readings (FETCH_SIZE + WRITE_SIZE, each scaled by its
+    reading for a copy of known size), or None when there is no reading or
+    the kernel's sources changed since it was taken."""
+    try:
+        with open(PMC_FILE) as fh:
+            pmc = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    for e in pmc.get("entries", []):
+        if e.get("workload") == workload and e.get("kernel") == kernel:
+            if e.get("sources_sha1") != kernel_sources_sha1(kernel):
+                return None
+            return int(e["traffic_bytes"])
+    return None
+
+
+def copy_calibration():
+    import torch
+    n = 256 << 20
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(4):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "dispatches": 4}), flush=True)
 
 
 def attn_bytes(w, n_units):
@@ -120,6 +174,9 @@ def main():
               "single MI355X; multi-GPU sharding is described in the design notes only)",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
     import torch
 
     from tiered_kv_cache_hs_amd import hisparse as H
@@ -204,6 +261,8 @@ def main():
     else:
         dominant = roof_host if fetch_us >= attn_us else roof_attn
 
+    dominant["traffic"] = stored_traffic(w.name, dominant["kernel"])
+    roof_attn["traffic"] = stored_traffic(w.name, attn_kernel)
     result = {
         "metric": METRIC,
         "value": round(ms_step * 1000.0 / w.n_layers, 2),

@@ -542,8 +542,13 @@ static hs_status plan_attn(hs_batch_t b, int32_t Hq, int32_t k, AttnPlan *pl) {
       return fail(HS_E_INVAL, "latent attention needs bf16, 512 + 64");
     if (Hq != 16 && Hq != 32 && Hq != 64)
       return fail(HS_E_INVAL, "latent attention supports 16, 32 or 64 query heads");
-    // a workgroup covers hpw heads of a (unit, split)
-    int hpw = g_tuning.latent_heads_per_wg > 0 ? g_tuning.latent_heads_per_wg : Hq;
+    // a workgroup covers hpw heads of a (unit, split). Few units need many
+    // splits to fill the device, and every split writes a full (m, l, acc)
+    // partial per head: below 32 units, splitting the heads instead (16 per
+    // workgroup; the rows are then read once per head group, mostly from L2)
+    // keeps the partials four times smaller.
+    int hpw = g_tuning.latent_heads_per_wg > 0 ? g_tuning.latent_heads_per_wg
+                                               : (b->n >= 32 ? Hq : 16);
     if (hpw > Hq || Hq % hpw) hpw = Hq;
     pl->hpw = hpw;
     base = (b->n + 7) / 8 * 8 * (Hq / hpw);
@@ -555,7 +560,8 @@ static hs_status plan_attn(hs_batch_t b, int32_t Hq, int32_t k, AttnPlan *pl) {
   const int max_splits = std::max(1, k / min_chunk);
   if (g_tuning.attn_splits <= 0) splits = std::min(splits, max_splits);
   splits = std::max(1, std::min(std::min(splits, k), 64));  // the combine merges <= 64
-  if (p->kind == HS_KV_LATENT) splits = std::max(splits, (k + hs::LAT_MAX_CHUNK - 1) / hs::LAT_MAX_CHUNK);
+  if (p->kind == HS_KV_LATENT)
+    splits = std::max(splits, (k + hs::LAT_MAX_CHUNK - 1) / hs::LAT_MAX_CHUNK);
   int chunk = (k + splits - 1) / splits;
   if (p->kind == HS_KV_LATENT) chunk = (chunk + 31) / 32 * 32;
   splits = (k + chunk - 1) / chunk;  // every split has at least one slot
