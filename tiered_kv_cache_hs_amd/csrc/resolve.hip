@@ -18,7 +18,9 @@
 //    so ranks in slot order and in selection order are one exclusive block
 //    scan of per-thread counts (wave64 shuffles + one LDS pass over waves).
 //    The hash table is open addressing with linear probing in LDS,
-//    capacity the power of two >= 2k, keys inserted with atomicCAS.
+//    capacity the power of two >= 4k (>= 2k for the largest k), keys
+//    inserted with atomicCAS; inserts and lookups read 16-byte buckets of
+//    four entries, so a probe run costs one LDS read per four entries.
 //    Victims are the m smallest 64-bit keys (stamp << 32 | secondary) among
 //    non-hit slots, where secondary = slot for an empty slot and B + position
 //    otherwise; keys are distinct, so an MSB-first radix select with 8-bit
@@ -226,22 +228,44 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
     else
       pend |= 1u << j;
   }
+  // Linear probing, read 4 entries (one 16-byte aligned bucket) at a time:
+  // entries before the first empty one are taken for good (nothing is ever
+  // removed), so skipping them equals failed compare-and-swaps on them.
   while (pend) {
-    int old[KPT];
+    int4 kb[KPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j)
-      if ((pend >> j) & 1u) old[j] = atomicCAS(&hkey[hcur[j]], EMPTY_KEY, tk[j]);
+      if ((pend >> j) & 1u) kb[j] = *(const int4 *)&hkey[hcur[j] & ~3u];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) {
       if (!((pend >> j) & 1u)) continue;
-      if (old[j] == EMPTY_KEY) {
-        hval[hcur[j]] = k0 + j;
-        pend &= ~(1u << j);
-      } else if (old[j] == tk[j]) {
+      const int e0 = (int)(hcur[j] & 3u);
+      const int kv[4] = {kb[j].x, kb[j].y, kb[j].z, kb[j].w};
+      int target = -1;
+      bool dup = false;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (e < e0 || target >= 0 || dup) continue;
+        if (kv[e] == tk[j]) dup = true;
+        else if (kv[e] == EMPTY_KEY) target = e;
+      }
+      if (dup) {
         myflag |= HS_ERR_DUP;
         pend &= ~(1u << j);
+      } else if (target < 0) {
+        hcur[j] = ((hcur[j] | 3u) + 1u) & (uint32_t)(H - 1);  // next bucket
       } else {
-        hcur[j] = (hcur[j] + 1) & (uint32_t)(H - 1);
+        const uint32_t at = (hcur[j] & ~3u) + (uint32_t)target;
+        const int old = atomicCAS(&hkey[at], EMPTY_KEY, tk[j]);
+        if (old == EMPTY_KEY) {
+          hval[at] = k0 + j;
+          pend &= ~(1u << j);
+        } else if (old == tk[j]) {
+          myflag |= HS_ERR_DUP;
+          pend &= ~(1u << j);
+        } else {
+          hcur[j] = (at + 1u) & (uint32_t)(H - 1);  // taken meanwhile: probe on
+        }
       }
     }
   }
@@ -271,22 +295,34 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
       h[j] = hash_pos(sp[j], hlog2);
       if (s0 + j < B && sp[j] >= 0) pend |= 1u << j;
     }
+    // lookups read one 16-byte bucket (4 entries) per round, entries in
+    // probe order from the hashed one; a key is absent at the first empty
     while (pend) {
-      int kk[SPT];
+      int4 kb[SPT];
 #pragma unroll
       for (int j = 0; j < SPT; ++j)
-        if ((pend >> j) & 1u) kk[j] = hkey[h[j]];
+        if ((pend >> j) & 1u) kb[j] = *(const int4 *)&hkey[h[j] & ~3u];
 #pragma unroll
       for (int j = 0; j < SPT; ++j) {
         if (!((pend >> j) & 1u)) continue;
-        if (kk[j] == sp[j]) {
-          slot_of[hval[h[j]]] = s0 + j;
+        const int e0 = (int)(h[j] & 3u);
+        const int kv[4] = {kb[j].x, kb[j].y, kb[j].z, kb[j].w};
+        int found = -1;
+        bool empty = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (e < e0 || found >= 0 || empty) continue;
+          if (kv[e] == sp[j]) found = e;
+          else if (kv[e] == EMPTY_KEY) empty = true;
+        }
+        if (found >= 0) {
+          slot_of[hval[(h[j] & ~3u) + (uint32_t)found]] = s0 + j;
           hitmask |= 1u << j;
           pend &= ~(1u << j);
-        } else if (kk[j] == EMPTY_KEY) {
+        } else if (empty) {
           pend &= ~(1u << j);
         } else {
-          h[j] = (h[j] + 1) & (uint32_t)(H - 1);
+          h[j] = ((h[j] | 3u) + 1u) & (uint32_t)(H - 1);  // next bucket
         }
       }
     }
@@ -628,9 +664,13 @@ hipError_t launch_select_k(const UnitDesc *d_units, int n, const int32_t *d_topk
                                    d_miss, stream);
 }
 
+// Hash capacity: the power of two >= 4k (load factor <= 1/4, short probe
+// runs) while the resolve's LDS stays within 128 KB, else >= 2k.
 int hash_log2(int k) {
-  int h = 1;
-  while ((1 << h) < 2 * k) ++h;
+  int h = 2;
+  while ((1 << h) < 4 * k) ++h;
+  const size_t region_a = (size_t)(2 * (1 << h) > 3 * k ? 2 * (1 << h) : 3 * k);
+  if ((region_a + k) * sizeof(int) > (128u << 10)) --h;
   return h;
 }
 
