@@ -35,7 +35,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=120)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", type=int, default=3, help="workload 1..5 (3 = batch-8 MLA)")
+    ap.add_argument("--workload", type=int, default=3,
+                    help="workload 1..6 (3 = batch-8 MLA; 6 = batch-8 MLA over 8 layers in "
+                         "groups of 4 that reuse one selection)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate budget of the CPU oracle baseline")
     ap.add_argument("--no-cpu", action="store_true")
@@ -47,6 +49,11 @@ def parse():
                          "split: hs_resolve (which also fetches the misses) then "
                          "hs_sparse_attn; auto: fused for MHA records, split for latent "
                          "records (the faster of the two for each on MI355X)")
+    ap.add_argument("--share", choices=("prefetch", "serial", "none"), default="prefetch",
+                    help="layer groups that reuse one selection (workload 6): prefetch = one "
+                         "resolve per group, the later layers' fetches on a second stream "
+                         "overlapping attention; serial = the same on one stream; none = every "
+                         "layer resolves on its own")
     return ap.parse_args()
 
 
@@ -190,7 +197,8 @@ def main():
     print(f"[bench] workload {w.name}: building session ({total} steps)", file=sys.stderr, flush=True)
     fill = "full" if w.n_units * max(w.ctx) * w.rec_bytes <= (8 << 30) else "touched"
     fused = args.path == "fused" or (args.path == "auto" and w.kind == "mha")
-    sess = Session(w, total, fill=fill, fused=fused)
+    sess = Session(w, total, fill=fill, fused=fused, share_mode=args.share)
+    fused = fused and not sess.grouped  # a group's resolve is planned apart from attention
     sess.capture()
     print("[bench] graphs captured", file=sys.stderr, flush=True)
 
@@ -223,7 +231,10 @@ def main():
         miss_hist[t].copy_(sess.miss)
     tr = H.hs_trace_read()
     H.hs_trace_enable(False)
-    misses = miss_hist[W:].cpu().numpy().astype(np.int64)
+    # every layer fetches its own records of its resolve's misses (the misses
+    # of a layer in a group are those of the group's resolve)
+    src = [sess.resolved_layer(l) for l in range(w.n_layers)]
+    misses = miss_hist[W:, src, :].cpu().numpy().astype(np.int64)  # [K][L][R]
     per = {c: (tr[c][0] / tr[c][1] if tr[c][1] else 0.0) for c in H.TRACE_CLASSES}
 
     n_launch_units = w.n_requests  # one batch (one layer's requests) per launch
@@ -232,12 +243,22 @@ def main():
     attn_us = per["attn"]
     attn_gbs = a_bytes / (attn_us * 1e-6) / 1e9 if attn_us else 0.0
     attn_kernel = "hs_k_attn_latent" if w.kind == "latent" else "hs_k_attn_mha"
-    # the kernel that moves the misses over the host link: the attention
-    # kernel (fused path), the gather kernel (batches of fewer than 4 units),
-    # else the resolve kernel itself
-    fetch_class = "attn" if fused else ("gather" if tr["gather"][1] else "resolve")
+    # the kernels that move the misses over the host link: the attention
+    # kernel (fused path); else the resolve kernel itself on batches of 4 or
+    # more units, the gather kernel on smaller ones, and the gather kernel
+    # for the later layers of a group (hs_prefetch). The host-link roofline
+    # is that of the class moving the most bytes.
+    lead = np.array([src[l] == l for l in range(w.n_layers)])
+    lead_bytes = int(misses[:, lead, :].sum()) * w.rec_bytes
+    follow_bytes = int(misses[:, ~lead, :].sum()) * w.rec_bytes
+    if fused:
+        cls_bytes = {"attn": lead_bytes + follow_bytes}
+    else:
+        cls_bytes = {"resolve": 0, "gather": follow_bytes}
+        cls_bytes["resolve" if w.n_requests >= 4 else "gather"] += lead_bytes
+    fetch_class = max(cls_bytes, key=cls_bytes.get)
     fetch_us = per[fetch_class]
-    miss_bytes_launch = misses.sum() * w.rec_bytes / max(1, tr[fetch_class][1])
+    miss_bytes_launch = cls_bytes[fetch_class] / max(1, tr[fetch_class][1])
     host_gbs = miss_bytes_launch / (fetch_us * 1e-6) / 1e9 if fetch_us else 0.0
     miss_rate = float(misses.sum()) / (K * w.n_units * w.k)
 
@@ -281,12 +302,14 @@ def main():
                    "k": w.k, "B": w.B[0] if len(set(w.B)) == 1 else "per-request",
                    "q_heads": w.n_q_heads, "record_bytes": w.rec_bytes, "kind": w.kind,
                    "graph": "one hipGraph per step",
-                   "path": "hs_resolve_attn" if fused else "hs_resolve + hs_sparse_attn"},
+                   "path": ("hs_resolve_attn" if fused else "hs_resolve + hs_sparse_attn")
+                   + (f" (layer groups of {w.share}: {sess.share_mode})" if sess.grouped else "")},
         "roofline": dominant,
         "roofline_attn": roof_attn,
         "host_link": roof_host,
         "kernels_us": {c: round(per[c], 2) for c in H.TRACE_CLASSES},
         "miss_rate": round(miss_rate, 4),
+        "fetch_bytes_by_kernel": {c: int(v / K) for c, v in cls_bytes.items()},
         "miss_bytes_per_step": int(misses.sum() * w.rec_bytes / K),
     }
     sess.close()

@@ -21,6 +21,10 @@
  *     GPU threads loading the missing records straight from pinned host
  *     memory, and a published slot vector aligned with the selection; the
  *     whole step is capturable in a graph (no host synchronisation).
+ *   section 6 - exact cross-layer prefetch: when a group of layers reuses
+ *     one indexer selection (IndexShare), the group's fetch plan is known as
+ *     soon as that selection is resolved, so the records the later layers
+ *     miss can be fetched while earlier layers compute.
  *   section 8 - the knobs: top_k (k per call) and device_buffer_size (B).
  *
  * Conventions
@@ -106,7 +110,9 @@ typedef struct hs_tuning {
   int32_t attn_splits;          /* split-k factor of sparse attention */
   int32_t latent_heads_per_wg;  /* latent attention: query heads per workgroup
                                    (16, 32 or 64, dividing n_q_heads) */
-  int32_t reserved[6];
+  int32_t prefetch_workgroups;  /* hs_prefetch: workgroups per launch
+                                   (0 = 512; 1 to 65536) */
+  int32_t reserved[5];
 } hs_tuning;
 
 const char *hs_status_str(hs_status s);
@@ -185,6 +191,31 @@ hs_status hs_buffer_state_set(hs_buffer_t buf, const int32_t *pos,
                               const uint32_t *stamp, uint32_t clock,
                               int32_t err, void *stream);
 
+/* -------- buffers of layers sharing one selection (HiSparse summary, §6) ---
+ * When a group of layers of a request reuses one selection every step, their
+ * buffers see the same requests and would hold identical page tables, stamps
+ * and clocks; only the rows differ (each layer's own records). A shared
+ * buffer is the rows of one more layer attached to the state of an existing
+ * buffer `base` of the same request: page table, stamps, clock, error word
+ * and the last resolve's fetch list live in base's memory and are the
+ * group's; d_mem (caller-owned, 256-byte aligned, at least
+ * hs_buffer_shared_bytes(pool, B) bytes with B = base's) holds the rows.
+ * Resolving any one member (hs_resolve) advances the group's state and
+ * fetches that member's misses; hs_prefetch then fetches the same misses
+ * for the other members from their own layers' records. Attention works on
+ * every member as on any buffer, with the group's slot vector.
+ * Rules: resolve one member of a group per step (a batch holding two members
+ * of one group is refused by the resolve calls); hs_buffer_reset and
+ * hs_buffer_state_set on a member act on the group's state, and state_set
+ * re-gathers the rows of that member only (restore a group by calling it on
+ * every member with the same state); base's memory must outlive every
+ * member. No GPU work is enqueued; the rows start undefined, like those of
+ * empty slots. HS_E_INVAL for a null or misaligned argument, too few bytes,
+ * or base of another pool or request; HS_E_RANGE for a bad layer. */
+size_t hs_buffer_shared_bytes(hs_pool_t pool, int32_t B);
+hs_status hs_buffer_create_shared(hs_buffer_t base, int32_t layer, void *d_mem,
+                                  size_t bytes, hs_buffer_t *out);
+
 /* ------------------------------- batches -----------------------------------
  * An ordered list of n units (buffers of one pool; buffer sizes may
  * differ). Uploads a device descriptor table. Synchronous; create batches
@@ -212,7 +243,9 @@ hs_status hs_batch_destroy(hs_batch_t batch);
  * HS_MAX_B, null pointers. Device data errors (a position outside
  * [0, length), a repeated position, an exhausted clock) set the unit's
  * error bits, write slots = -1 and miss = -1 and leave its state unchanged;
- * other units proceed. Enqueue only; capture-safe. */
+ * other units proceed. The fetch list (slot and position of every miss) is
+ * kept in the unit's state for hs_prefetch. A batch holding two buffers of
+ * one shared state is refused (HS_E_INVAL). Enqueue only; capture-safe. */
 hs_status hs_resolve(hs_batch_t batch, const int32_t *d_topk, int32_t k,
                      int32_t *d_slots, int32_t *d_miss, void *stream);
 
@@ -254,6 +287,22 @@ hs_status hs_resolve_attn(hs_batch_t batch, const int32_t *d_topk, int32_t k,
                           int32_t n_q_heads, float sm_scale, float *d_out,
                           void *d_ws, size_t ws_bytes, void *stream);
 
+/* -------------- exact cross-layer prefetch (HiSparse summary, §6) ----------
+ * For every unit of the batch, copies into its rows the records its state's
+ * last resolve missed: slot s_j of the fetch list receives the record at
+ * position p_j of the unit's own (request, layer) pool. For a buffer that
+ * shares the state of another layer (hs_buffer_create_shared), this is that
+ * layer's share of the group's plan: after it, the buffer holds the record
+ * of its own layer at every position the group's page table names, so
+ * attention over it with the group's slot vector equals attention over a
+ * buffer resolved on its own. Must be ordered after the group's resolve
+ * (same stream, or an event) and before the next one; it may run on another
+ * stream concurrently with attention over other buffers. A fetch-list
+ * position at or past the unit's pool length is skipped and sets
+ * HS_ERR_RANGE. The number of workgroups is hs_tuning.prefetch_workgroups.
+ * Enqueue only; capture-safe. HS_E_INVAL for a null batch. */
+hs_status hs_prefetch(hs_batch_t batch, void *stream);
+
 /* ------------------------------- tracing -----------------------------------
  * Event timing of individual kernels, for measurement. While enabled, every
  * kernel that hs_resolve and hs_sparse_attn enqueue is bracketed by a pair
@@ -263,7 +312,7 @@ hs_status hs_resolve_attn(hs_batch_t batch, const int32_t *d_topk, int32_t k,
  * HS_TRACE_RESOLVE (hash, probe, victim select, update; for hs_resolve on
  * batches of 4 or more units also the host-to-device miss fetch),
  * HS_TRACE_GATHER (the miss fetch of hs_resolve on smaller batches, a kernel
- * of its own), HS_TRACE_ATTN (sparse attention; for hs_resolve_attn it
+ * of its own, and hs_prefetch), HS_TRACE_ATTN (sparse attention; for hs_resolve_attn it
  * includes the miss fetch), HS_TRACE_COMBINE (split-k merge). At most 4096
  * launches are recorded between reads; later ones are counted in
  * `dropped`. */

@@ -79,3 +79,67 @@ def check_attn(w: I.Workload, got: np.ndarray, want: np.ndarray, what: str = "")
         assert max_abs <= TOL_BF16_MAX_ABS, f"{what}: max abs {max_abs:.3e}"
         assert rel_l2 <= TOL_BF16_REL_L2, f"{what}: rel L2 {rel_l2:.3e}"
     return {"max_abs": max_abs, "rel_l2": rel_l2}
+
+
+def small_workload(kind, dtype, B, k, ctx, steps, n_new, R=1, L=1, seed=0, Hkv=1, D=64, Hq=1,
+                   share=1):
+    """A small synthetic workload (test shapes that span tiles and ragged tails)."""
+    if kind == "mha":
+        w = I.Workload(f"small_{seed}", R, L, "mha", dtype, dtype, Hkv, D, 0, 0, Hq, k, steps,
+                       n_new, (("uniform", 0.5), ("window", 0.5)), 1.0, 1000 + seed)
+    else:
+        w = I.Workload(f"small_{seed}", R, L, "latent", I.BF16, I.BF16, 1, 0, 512, 64, Hq, k,
+                       steps, n_new, (("uniform", 1.0),), 0.5, 1000 + seed)
+    w.ctx = [ctx] * R
+    w.B = [B] * R
+    w.share = share
+    return w
+
+
+def compare_run(w, steps, traces=None, attn_every=1, rows_every=1, attn_units=None,
+                graph=False, fill="touched", fused=False, share_mode="prefetch"):
+    """Run a GPU session step by step beside the oracle and compare slots,
+    miss counts, state, resident rows and attention outputs of every unit.
+    The oracle resolves every layer on its own, also where the session runs
+    a layer group on one shared state."""
+    from tiered_kv_cache_hs_amd.session import Session
+    import torch
+
+    sess = Session(w, steps, fill=fill, traces=traces, fused=fused, share_mode=share_mode)
+    orc = OracleRun(w, sess.traces, steps)
+    if graph:
+        sess.capture()
+    stats = []
+    try:
+        for t in range(steps):
+            if graph:
+                sess.replay(t)
+            else:
+                sess.step(t)
+            torch.cuda.synchronize()
+            slots_g = sess.slots.cpu().numpy()
+            miss_g = sess.miss.cpu().numpy()
+            out_g = sess.out.cpu().numpy()
+            for l in range(w.n_layers):
+                gl = sess.resolved_layer(l)
+                for r in range(w.n_requests):
+                    so, mo = orc.resolve(t, r, l)
+                    assert np.array_equal(slots_g[gl, r], so), f"slots t={t} r={r} l={l}"
+                    assert int(miss_g[gl, r]) == mo, f"miss t={t} r={r} l={l}"
+                    pos, stamp, clock, err = sess.state(l, r)
+                    ob = orc.bufs[(r, l)]
+                    assert np.array_equal(pos, ob.pos), f"pos t={t} r={r} l={l}"
+                    assert np.array_equal(stamp, ob.stamp), f"stamp t={t} r={r} l={l}"
+                    assert clock == int(ob.clock[0]) and err == int(ob.err[0])
+                    if rows_every and t % rows_every == 0:
+                        rows = sess.rows(l, r)
+                        occ = ob.pos >= 0
+                        assert np.array_equal(rows[occ], ob.rows[occ]), f"rows t={t} r={r} l={l}"
+                    if attn_every and t % attn_every == 0 and (attn_units is None or (r, l) in attn_units):
+                        want = orc.attend(t, r, l, so)
+                        stats.append(check_attn(w, out_g[l, r], want, f"attn t={t} r={r} l={l}"))
+                    if w.append:
+                        orc.append(t, r, l)
+    finally:
+        sess.close()
+    return stats

@@ -39,13 +39,17 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_tuning_roundtrip():
     assert H.hs_status_str(H.HS_OK) == "ok"
     assert H.hs_status_str(H.HS_E_STATE) == "invalid buffer state"
-    H.hs_set_tuning(4, 32)
-    assert H.hs_get_tuning() == {"attn_splits": 4, "latent_heads_per_wg": 32}
+    H.hs_set_tuning(4, 32, 96)
+    assert H.hs_get_tuning() == {"attn_splits": 4, "latent_heads_per_wg": 32,
+                                 "prefetch_workgroups": 96}
     H.hs_set_tuning(0, 0)
     with pytest.raises(H.HsError):
         H.hs_set_tuning(-1, 0)
     with pytest.raises(H.HsError):
         H.hs_set_tuning(0, 48)
+    with pytest.raises(H.HsError):
+        H.hs_set_tuning(0, 0, -3)
+    assert H.hs_get_tuning()["prefetch_workgroups"] == 0
 
 
 def test_null_and_shape_checks_without_device():
@@ -54,6 +58,9 @@ def test_null_and_shape_checks_without_device():
     assert L.hs_batch_create(None, 0, None) == H.HS_E_INVAL
     assert L.hs_resolve(None, None, 1, None, None, None) == H.HS_E_INVAL
     assert L.hs_buffer_bytes(None, 4) == 0
+    assert L.hs_buffer_shared_bytes(None, 4) == 0
+    assert L.hs_buffer_create_shared(None, 0, None, 0, None) == H.HS_E_INVAL
+    assert L.hs_prefetch(None, None) == H.HS_E_INVAL
     d = H.PoolDesc(1, 1, 7, H.HS_BF16, 1, 64, 0, 0, (ctypes.c_int64 * 1)(100))
     out = ctypes.c_void_p()
     assert L.hs_pool_create(ctypes.byref(d), ctypes.byref(out)) == H.HS_E_INVAL

@@ -13,7 +13,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
-from tests.parity import OracleRun, check_attn  # noqa: E402
+from tests.parity import OracleRun, check_attn, compare_run, small_workload as _small  # noqa: E402,F401
 from tiered_kv_cache_hs_amd import hisparse as H  # noqa: E402
 from tiered_kv_cache_hs_amd import inputs as I  # noqa: E402
 from tiered_kv_cache_hs_amd.session import Session  # noqa: E402
@@ -34,47 +34,6 @@ def _gpu():
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
-
-
-def compare_run(w, steps, traces=None, attn_every=1, rows_every=1, attn_units=None,
-                graph=False, fill="touched", fused=False):
-    sess = Session(w, steps, fill=fill, traces=traces, fused=fused)
-    orc = OracleRun(w, sess.traces, steps)
-    if graph:
-        sess.capture()
-    stats = []
-    try:
-        for t in range(steps):
-            if graph:
-                sess.replay(t)
-            else:
-                sess.step(t)
-            torch.cuda.synchronize()
-            slots_g = sess.slots.cpu().numpy()
-            miss_g = sess.miss.cpu().numpy()
-            out_g = sess.out.cpu().numpy()
-            for l in range(w.n_layers):
-                for r in range(w.n_requests):
-                    so, mo = orc.resolve(t, r, l)
-                    assert np.array_equal(slots_g[l, r], so), f"slots t={t} r={r} l={l}"
-                    assert int(miss_g[l, r]) == mo, f"miss t={t} r={r} l={l}"
-                    pos, stamp, clock, err = sess.state(l, r)
-                    ob = orc.bufs[(r, l)]
-                    assert np.array_equal(pos, ob.pos), f"pos t={t} r={r} l={l}"
-                    assert np.array_equal(stamp, ob.stamp), f"stamp t={t} r={r} l={l}"
-                    assert clock == int(ob.clock[0]) and err == int(ob.err[0])
-                    if rows_every and t % rows_every == 0:
-                        rows = sess.rows(l, r)
-                        occ = ob.pos >= 0
-                        assert np.array_equal(rows[occ], ob.rows[occ]), f"rows t={t} r={r} l={l}"
-                    if attn_every and t % attn_every == 0 and (attn_units is None or (r, l) in attn_units):
-                        want = orc.attend(t, r, l, so)
-                        stats.append(check_attn(w, out_g[l, r], want, f"attn t={t} r={r} l={l}"))
-                    if w.append:
-                        orc.append(t, r, l)
-    finally:
-        sess.close()
-    return stats
 
 
 def test_tiny_fp32_every_step():
@@ -101,18 +60,6 @@ def test_mla_b8_prefix():
     say("workload 3 (MLA batch 8), 12 steps")
     st = compare_run(w, 12, attn_every=4, rows_every=6, attn_units=[(0, 0), (5, 0)])
     say("worst", max(s["max_abs"] for s in st), max(s["rel_l2"] for s in st))
-
-
-def _small(kind, dtype, B, k, ctx, steps, n_new, R=1, L=1, seed=0, Hkv=1, D=64, Hq=1):
-    if kind == "mha":
-        w = I.Workload(f"small_{seed}", R, L, "mha", dtype, dtype, Hkv, D, 0, 0, Hq, k, steps,
-                       n_new, (("uniform", 0.5), ("window", 0.5)), 1.0, 1000 + seed)
-    else:
-        w = I.Workload(f"small_{seed}", R, L, "latent", I.BF16, I.BF16, 1, 0, 512, 64, Hq, k,
-                       steps, n_new, (("uniform", 1.0),), 0.5, 1000 + seed)
-    w.ctx = [ctx] * R
-    w.B = [B] * R
-    return w
 
 
 SMALL = [

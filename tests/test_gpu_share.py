@@ -1,0 +1,224 @@
+"""GPU parity of layer groups that reuse one selection (HiSparse summary,
+section 6: cross-layer index sharing and exact prefetch).
+
+A group's later layers hold buffers that share the first layer's state
+(hs_buffer_create_shared); one hs_resolve per group plans the fetch and
+hs_prefetch copies each later layer's own records from that plan. The
+oracle resolves every layer on its own, so these tests check that sharing
+the plan changes nothing: slots, miss counts, state and every layer's rows
+bit for bit, attention within tolerance, and bit-identical outputs against
+the same layers run without sharing.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from tests.parity import compare_run, small_workload  # noqa: E402
+from tiered_kv_cache_hs_amd import hisparse as H  # noqa: E402
+from tiered_kv_cache_hs_amd import inputs as I  # noqa: E402
+from tiered_kv_cache_hs_amd.session import Session  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    H.lib()
+    H.hs_set_tuning(0, 0, 0)
+    yield
+    H.hs_set_tuning(0, 0, 0)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# kind, dtype, B, k, ctx, steps, n_new, R, L, share, Hkv, D, Hq
+GROUPS = [
+    ("mha", I.F32, 40, 17, 300, 8, 5, 2, 4, 2, 1, 64, 1),
+    ("mha", I.BF16, 600, 200, 3000, 6, 50, 3, 4, 4, 2, 128, 8),
+    ("mha", I.F32, 64, 64, 500, 5, 20, 1, 3, 3, 1, 64, 1),      # B = k: every step swaps
+    ("latent", I.BF16, 300, 197, 3000, 5, 40, 2, 4, 2, 1, 0, 32),
+    ("latent", I.BF16, 2048, 2048, 9000, 4, 614, 2, 4, 4, 1, 0, 64),
+]
+
+
+@pytest.mark.parametrize("mode", ["prefetch", "serial"])
+@pytest.mark.parametrize("case", range(len(GROUPS)))
+def test_groups_match_independent_layers(case, mode):
+    kind, dt, B, k, ctx, steps, n_new, R, L, share, Hkv, D, Hq = GROUPS[case]
+    w = small_workload(kind, dt, B, k, ctx, steps, n_new, R=R, L=L, seed=300 + case, Hkv=Hkv,
+                       D=D, Hq=Hq, share=share)
+    say(f"group case {case} ({mode}): {GROUPS[case]}")
+    compare_run(w, steps, fill="full", share_mode=mode)
+
+
+@pytest.mark.parametrize("mode", ["prefetch", "serial"])
+def test_groups_graph_replay(mode):
+    w = small_workload("mha", I.BF16, 600, 200, 3000, 6, 50, R=2, L=4, seed=320, Hkv=2, D=128,
+                       Hq=8, share=2)
+    compare_run(w, 6, fill="full", graph=True, share_mode=mode)
+
+
+def test_groups_with_write_through_appends():
+    w = small_workload("mha", I.F32, 48, 24, 200, 8, 6, R=2, L=4, seed=330, share=4)
+    w.append = True
+    compare_run(w, 8, fill="full", share_mode="prefetch")
+
+
+def test_prefetch_workgroup_counts():
+    w = small_workload("latent", I.BF16, 300, 197, 3000, 4, 40, R=2, L=4, seed=340, Hq=16,
+                       share=4)
+    for wg in (1, 7, 96, 4096):
+        H.hs_set_tuning(0, 0, wg)
+        try:
+            say(f"prefetch_workgroups={wg}")
+            compare_run(w, 4, fill="full", attn_every=2, share_mode="prefetch")
+        finally:
+            H.hs_set_tuning(0, 0, 0)
+
+
+def _bitwise_same(a, b, steps, graph):
+    if graph:
+        a.capture()
+        b.capture()
+    for t in range(steps):
+        if graph:
+            a.replay(t)
+            b.replay(t)
+        else:
+            a.step(t)
+            b.step(t)
+        torch.cuda.synchronize()
+        assert np.array_equal(a.out.cpu().numpy().view(np.uint32),
+                              b.out.cpu().numpy().view(np.uint32)), f"step {t}"
+        for l in range(a.L):
+            ga, gb = a.resolved_layer(l), b.resolved_layer(l)
+            assert np.array_equal(a.slots[ga].cpu().numpy(), b.slots[gb].cpu().numpy()), (t, l)
+            assert np.array_equal(a.miss[ga].cpu().numpy(), b.miss[gb].cpu().numpy()), (t, l)
+            for r in range(a.R):
+                pa = a.state(l, r)[0]
+                assert np.array_equal(a.rows(l, r)[pa >= 0], b.rows(l, r)[pa >= 0]), (t, l, r)
+
+
+@pytest.mark.parametrize("graph", [False, True])
+def test_grouped_workload_bitwise_equals_ungrouped(graph):
+    """The 8-layer batch-8 MLA workload with groups of 4 (first steps): the
+    prefetch path gives the outputs, slots and rows of every layer resolving
+    on its own, bit for bit."""
+    w = I.workload(6)
+    steps = 4
+    say(f"workload {w.name}: prefetch vs ungrouped, {steps} steps, graph={graph}")
+    a = Session(w, steps, fill="touched", share_mode="prefetch")
+    try:
+        b = Session(w, steps, fill="touched", share_mode="none", traces=a.traces)
+        try:
+            _bitwise_same(a, b, steps, graph)
+        finally:
+            b.close()
+    finally:
+        a.close()
+
+
+def _tiny_pool(L=2, ctx=64):
+    """Two requests, L layers of fp32 MHA records of 64 bytes."""
+    return H.hs_pool_create(2, L, H.HS_KV_MHA, H.HS_F32, [ctx, ctx], n_kv_heads=1, head_dim=8)
+
+
+def test_shared_buffer_argument_checks_and_resolve_refusal():
+    pool = _tiny_pool()
+    mems, bufs, batches = [], [], []
+    try:
+        B = 16
+        m0 = torch.empty(H.hs_buffer_bytes(pool, B), dtype=torch.uint8, device="cuda")
+        mems.append(m0)
+        base = H.hs_buffer_create(pool, 0, 0, B, m0)
+        bufs.append(base)
+        need = H.hs_buffer_shared_bytes(pool, B)
+        assert need == B * H.hs_pool_record_bytes(pool)
+        small = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+        with pytest.raises(H.HsError):
+            H.hs_buffer_create_shared(base, 1, small)
+        m1 = torch.empty(need + 256, dtype=torch.uint8, device="cuda")
+        mems.append(m1)
+        with pytest.raises(H.HsError):  # misaligned
+            H.hs_buffer_create_shared(base, 1, m1[16:])
+        with pytest.raises(H.HsError):  # no such layer
+            H.hs_buffer_create_shared(base, 2, m1)
+        sh = H.hs_buffer_create_shared(base, 1, m1)
+        bufs.append(sh)
+        both = H.hs_batch_create([base, sh])
+        batches.append(both)
+        topk = torch.arange(8, dtype=torch.int32, device="cuda").repeat(2, 1)
+        slots = torch.empty((2, 8), dtype=torch.int32, device="cuda")
+        H.hs_pool_set_length(pool, 0, 0, 64)
+        H.hs_pool_set_length(pool, 0, 1, 64)
+        with pytest.raises(H.HsError):  # two members of one state in one resolve
+            H.hs_resolve(both, topk, 8, slots)
+        single = H.hs_batch_create([sh])
+        batches.append(single)
+        H.hs_resolve(single, topk[:1], 8, slots[:1])  # resolving any one member is allowed
+        H.hs_prefetch(both)
+        torch.cuda.synchronize()
+        pos, stamp, clock, err = H.hs_buffer_state_get(base, B)
+        assert clock == 1 and err == 0 and sorted(pos[pos >= 0].tolist()) == list(range(8))
+        assert H.hs_buffer_state_get(sh, B)[2] == 1
+    finally:
+        torch.cuda.synchronize()
+        for b in batches:
+            H.hs_batch_destroy(b)
+        for b in bufs:
+            H.hs_buffer_destroy(b)
+        H.hs_pool_destroy(pool)
+
+
+def test_prefetch_past_a_members_length_sets_range_error():
+    """A member whose own pool is shorter than the plan's positions: those
+    records are skipped and HS_ERR_RANGE is set; the others arrive."""
+    ctx, B = 64, 16
+    pool = _tiny_pool(ctx=ctx)
+    bufs, batches = [], []
+    try:
+        rec = H.hs_pool_record_bytes(pool)
+        for l in range(2):
+            arr = H.hs_pool_unit_array(pool, 0, l)
+            arr[:] = (np.arange(ctx * rec, dtype=np.int64).reshape(ctx, rec) * (l + 3) % 251).astype(np.uint8)
+        H.hs_pool_set_length(pool, 0, 0, 64)
+        H.hs_pool_set_length(pool, 0, 1, 20)
+        m0 = torch.empty(H.hs_buffer_bytes(pool, B), dtype=torch.uint8, device="cuda")
+        m1 = torch.empty(H.hs_buffer_shared_bytes(pool, B), dtype=torch.uint8, device="cuda")
+        base = H.hs_buffer_create(pool, 0, 0, B, m0)
+        sh = H.hs_buffer_create_shared(base, 1, m1)
+        bufs += [base, sh]
+        b0, b1 = H.hs_batch_create([base]), H.hs_batch_create([sh])
+        batches += [b0, b1]
+        sel = np.array([3, 40, 11, 19, 25, 0], dtype=np.int32)
+        topk = torch.from_numpy(sel[None]).to("cuda")
+        slots = torch.empty((1, 6), dtype=torch.int32, device="cuda")
+        m1.fill_(0)
+        H.hs_resolve(b0, topk, 6, slots)
+        H.hs_prefetch(b1)
+        torch.cuda.synchronize()
+        pos, _, _, err = H.hs_buffer_state_get(sh, B)
+        assert err & H.HS_ERR_RANGE
+        rows = m1[: B * rec].cpu().numpy().reshape(B, rec)
+        src = H.hs_pool_unit_array(pool, 0, 1)
+        s = slots.cpu().numpy()[0]
+        for i, p in enumerate(sel):
+            if p < 20:
+                assert np.array_equal(rows[s[i]], src[p]), p
+            else:
+                assert not rows[s[i]].any(), p  # skipped: the row was left as it was
+    finally:
+        torch.cuda.synchronize()
+        for b in batches:
+            H.hs_batch_destroy(b)
+        for b in bufs:
+            H.hs_buffer_destroy(b)
+        H.hs_pool_destroy(pool)

@@ -1,4 +1,6 @@
 """Properties of the seeded input generators (traces, records, queries)."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -67,4 +69,20 @@ def test_queries_shape_and_steps_differ():
     w = I.workload(3)
     a, b = I.gen_queries(w, 0), I.gen_queries(w, 1)
     assert a.shape == (8, 64, 576) and a.dtype == np.uint16
+    assert not np.array_equal(a, b)
+
+
+def test_layer_groups_reuse_one_selection():
+    w = I.workload(6)
+    assert (w.n_requests, w.n_layers, w.share, w.k, w.rec_bytes) == (8, 8, 4, 2048, 1152)
+    assert [w.group_base(l) for l in range(8)] == [0, 0, 0, 0, 4, 4, 4, 4]
+    tr = I.gen_traces(dataclasses.replace(w, n_requests=2, ctx=w.ctx[:2], B=w.B[:2]), 6)
+    for r in range(2):
+        for l in range(8):
+            g = w.group_base(l)
+            assert np.array_equal(tr[:, r * 8 + l], tr[:, r * 8 + g])
+        assert not np.array_equal(tr[:, r * 8], tr[:, r * 8 + 4])  # groups differ
+    assert np.array_equal(tr[:, 4], I.gen_trace(w, 0, 4, 6))  # a group's trace is its first layer's
+    # records still differ per layer
+    a, b = I.record_array(w, 0, 0, [5]), I.record_array(w, 0, 1, [5])
     assert not np.array_equal(a, b)

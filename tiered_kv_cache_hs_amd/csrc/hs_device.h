@@ -127,6 +127,10 @@ hipError_t launch_resolve(const UnitDesc *d_units, int n_units, int max_B,
                           int32_t *d_miss, int fetch, int rec_bytes,
                           hipStream_t stream);
 size_t resolve_lds_bytes(int k);
+// Fetch every unit's share of its state's last fetch list (about `workgroups`
+// workgroups in total; 0 = 512).
+hipError_t launch_prefetch(const UnitDesc *d_units, int n, int rec_bytes, int workgroups,
+                           hipStream_t stream);
 hipError_t launch_regather(const UnitDesc *d_unit, int B, int rec_bytes,
                            hipStream_t stream);
 hipError_t launch_append(uint8_t *dst_dev, const uint8_t *src, int64_t bytes,

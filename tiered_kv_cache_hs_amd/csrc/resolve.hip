@@ -506,7 +506,9 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
     d.pos[s] = p;
     d.stamp[s] = 2u * c - 1u;
     slot_of[i] = s;
-    if (!GATHER) d.work[r] = int2v{s, p};
+    // the fetch list is written even when this kernel fetches: buffers of
+    // other layers that share this state fetch their own records from it
+    d.work[r] = int2v{s, p};
   }
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
@@ -556,7 +558,13 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   }
 }
 
-// Copy each unit's fetch list from host records into device rows.
+// Copy each unit's fetch list from host records into device rows: the list
+// of the last resolve of the unit's state. A buffer that shares the state of
+// another layer's buffer (layers reusing one selection) reads the list that
+// the group's resolve wrote and copies its own layer's records, which is why
+// positions are checked against this unit's pool length here (the resolve
+// checked them against the resolving unit's); a position past it is skipped
+// and sets HS_ERR_RANGE.
 // Grid: n_units * G workgroups of 256 threads; workgroup g of unit u walks
 // the unit's 16-byte chunks g*256 + tid, stepping by G*256.
 constexpr int GATHER_THREADS = 256;
@@ -569,9 +577,11 @@ __global__ __launch_bounds__(GATHER_THREADS) void hs_k_gather(
   const UnitG d = unit_g(units[u]);
   const int m = (int)d.ctl[CTL_FETCH];
   if (m <= 0 || m > d.B) return;
+  const int64_t len = *d.len;
   const int total = m * rec16;
   const int stride = G * GATHER_THREADS;
   const size_t rec = (size_t)rec16 * 16;
+  bool bad = false;
   for (int c0 = g * GATHER_THREADS + (int)threadIdx.x; c0 < total;
        c0 += stride * GATHER_UNROLL) {
     v4u v[GATHER_UNROLL];
@@ -584,15 +594,21 @@ __global__ __launch_bounds__(GATHER_THREADS) void hs_k_gather(
         const int r = c / rec16;
         const int off = c - r * rec16;
         const int2v w = d.work[r];
-        const HS_GLOBAL v4u *src = (const HS_GLOBAL v4u *)(d.pool + (size_t)w.y * rec) + off;
-        v[uu] = __builtin_nontemporal_load(src);
-        dst[uu] = (HS_GLOBAL v4u *)(d.rows + (size_t)w.x * rec) + off;
+        if (w.y >= 0 && (int64_t)w.y < len) {
+          const HS_GLOBAL v4u *src =
+              (const HS_GLOBAL v4u *)(d.pool + (size_t)w.y * rec) + off;
+          v[uu] = __builtin_nontemporal_load(src);
+          dst[uu] = (HS_GLOBAL v4u *)(d.rows + (size_t)w.x * rec) + off;
+        } else {
+          bad = true;
+        }
       }
     }
 #pragma unroll
     for (int uu = 0; uu < GATHER_UNROLL; ++uu)
       if (dst[uu]) *dst[uu] = v[uu];
   }
+  if (bad) set_error(d.ctl, HS_ERR_RANGE);
 }
 
 // Re-gather every occupied row of one buffer (checkpoint restore).
@@ -712,6 +728,17 @@ hipError_t launch_resolve(const UnitDesc *d_units, int n, int max_B, const int32
   trace_begin(HS_TRACE_GATHER, stream);
   hipLaunchKernelGGL(hs_k_gather, dim3(n * G), dim3(GATHER_THREADS), 0, stream, d_units, G,
                      rec16);
+  trace_end(stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefetch(const UnitDesc *d_units, int n, int rec_bytes, int workgroups,
+                           hipStream_t stream) {
+  const int wg = workgroups > 0 ? workgroups : 512;
+  const int G = std::max(1, std::min(64, (wg + n - 1) / n));
+  trace_begin(HS_TRACE_GATHER, stream);
+  hipLaunchKernelGGL(hs_k_gather, dim3(n * G), dim3(GATHER_THREADS), 0, stream, d_units, G,
+                     rec_bytes / 16);
   trace_end(stream);
   return hipGetLastError();
 }

@@ -44,7 +44,7 @@ hs_status hip_fail(hipError_t e, const char *what) {
     if (e_ != hipSuccess) return hip_fail(e_, #call); \
   } while (0)
 
-hs_tuning g_tuning = {0, 0, {0, 0, 0, 0, 0, 0}};
+hs_tuning g_tuning = {0, 0, 0, {0, 0, 0, 0, 0}};
 
 inline hipStream_t S(void *s) { return (hipStream_t)s; }
 
@@ -112,6 +112,7 @@ struct hs_buffer_s {
 struct hs_batch_s {
   hs_pool_t pool = nullptr;
   int32_t n = 0, min_B = 0, max_B = 0;
+  bool shared_twice = false;  // two units share one state (not resolvable)
   UnitDesc *d_units = nullptr;
 };
 
@@ -138,6 +139,8 @@ hs_status hs_set_tuning(const hs_tuning *t) {
   const int hpw = t->latent_heads_per_wg;
   if (hpw != 0 && hpw != 16 && hpw != 32 && hpw != 64)
     return fail(HS_E_INVAL, "latent_heads_per_wg must be 0, 16, 32 or 64");
+  if (t->prefetch_workgroups < 0 || t->prefetch_workgroups > 65536)
+    return fail(HS_E_INVAL, "prefetch_workgroups outside [0, 65536]");
   g_tuning = *t;
   return HS_OK;
 }
@@ -365,6 +368,47 @@ hs_status hs_buffer_create(hs_pool_t p, int32_t req, int32_t layer, int32_t B, v
   return HS_OK;
 }
 
+size_t hs_buffer_shared_bytes(hs_pool_t p, int32_t B) {
+  if (!p || B < 1) return 0;
+  return hs::align_up((size_t)B * p->rec, 256);
+}
+
+hs_status hs_buffer_create_shared(hs_buffer_t base, int32_t layer, void *d_mem, size_t bytes,
+                                  hs_buffer_t *out) {
+  if (!base || !out || !d_mem) return fail(HS_E_INVAL, "null argument");
+  *out = nullptr;
+  hs_pool_t p = base->pool;
+  hs_status s = check_unit(p, base->req, layer);
+  if (s) return s;
+  if ((uintptr_t)d_mem % 256) return fail(HS_E_INVAL, "buffer memory must be 256-byte aligned");
+  const size_t need = hs_buffer_shared_bytes(p, base->B);
+  if (bytes < need) return fail(HS_E_INVAL, "shared buffer needs %zu bytes, got %zu", need, bytes);
+  hs_buffer_s *b = new (std::nothrow) hs_buffer_s;
+  if (!b) return fail(HS_E_NOMEM, "buffer handle");
+  b->pool = p;
+  b->req = base->req;
+  b->layer = layer;
+  b->B = base->B;
+  b->mem = (uint8_t *)d_mem;
+  b->lay = base->lay;
+  // the group's state (page table, stamps, fetch list, control words) is
+  // base's; rows, pool records and length are this layer's
+  b->desc = base->desc;
+  b->desc.rows = b->mem;
+  b->desc.pool = p->dev[b->req] + unit_offset(p, b->req, layer);
+  b->desc.len = p->d_len + (size_t)b->req * p->L + layer;
+  hipError_t e = hipMalloc(&b->d_desc, sizeof(UnitDesc));
+  if (e == hipSuccess)
+    e = hipMemcpy(b->d_desc, &b->desc, sizeof(UnitDesc), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    if (b->d_desc) (void)hipFree(b->d_desc);
+    delete b;
+    return hip_fail(e, "shared buffer create");
+  }
+  *out = b;
+  return HS_OK;
+}
+
 hs_status hs_buffer_destroy(hs_buffer_t b) {
   if (!b) return fail(HS_E_INVAL, "null buffer");
   if (b->d_desc) (void)hipFree(b->d_desc);
@@ -455,12 +499,18 @@ hs_status hs_batch_create(const hs_buffer_t *bufs, int32_t n, hs_batch_t *out) {
     min_B = std::min(min_B, bufs[i]->B);
     max_B = std::max(max_B, bufs[i]->B);
   }
+  // a state (page table) named twice cannot be resolved by one launch
+  std::vector<uintptr_t> states(n);
+  for (int i = 0; i < n; ++i) states[i] = (uintptr_t)h[i].pos;
+  std::sort(states.begin(), states.end());
+  const bool shared_twice = std::adjacent_find(states.begin(), states.end()) != states.end();
   hs_batch_s *bt = new (std::nothrow) hs_batch_s;
   if (!bt) return fail(HS_E_NOMEM, "batch handle");
   bt->pool = pool;
   bt->n = n;
   bt->min_B = min_B;
   bt->max_B = max_B;
+  bt->shared_twice = shared_twice;
   hipError_t e = hipMalloc(&bt->d_units, sizeof(UnitDesc) * n);
   if (e == hipSuccess)
     e = hipMemcpy(bt->d_units, h.data(), sizeof(UnitDesc) * n, hipMemcpyHostToDevice);
@@ -485,6 +535,8 @@ hs_status hs_batch_destroy(hs_batch_t b) {
 static hs_status check_resolve(hs_batch_t b, const int32_t *d_topk, int32_t k,
                                const int32_t *d_slots) {
   if (!b || !d_topk || !d_slots) return fail(HS_E_INVAL, "null argument");
+  if (b->shared_twice)
+    return fail(HS_E_INVAL, "the batch holds two buffers of one shared state");
   if (k < 1 || k > HS_MAX_K || k > b->min_B)
     return fail(HS_E_INVAL, "k = %d outside [1, min(%d, smallest B = %d)]", k, HS_MAX_K,
                 b->min_B);
@@ -675,6 +727,16 @@ hs_status hs_resolve_attn(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_
                                     hs::FETCH_NONE, (int)b->pool->rec, S(stream));
   if (e != hipSuccess) return hip_fail(e, "resolve launch");
   return enqueue_attn(b, d_q, Hq, d_slots, k, sm_scale, d_out, d_ws, pl, 1, stream);
+}
+
+// ---------------------------------------------------------------- prefetch
+
+hs_status hs_prefetch(hs_batch_t b, void *stream) {
+  if (!b) return fail(HS_E_INVAL, "null batch");
+  hipError_t e = hs::launch_prefetch(b->d_units, b->n, (int)b->pool->rec,
+                                     g_tuning.prefetch_workgroups, S(stream));
+  if (e != hipSuccess) return hip_fail(e, "prefetch launch");
+  return HS_OK;
 }
 
 // ------------------------------------------------------------------ tracing

@@ -44,8 +44,9 @@ EXPORTS = (
     "hs_pool_length", "hs_pool_set_length", "hs_pool_append",
     "hs_buffer_bytes", "hs_buffer_create", "hs_buffer_destroy", "hs_buffer_reset",
     "hs_buffer_rows", "hs_buffer_state_get", "hs_buffer_state_set",
+    "hs_buffer_shared_bytes", "hs_buffer_create_shared",
     "hs_batch_create", "hs_batch_destroy", "hs_resolve",
-    "hs_sparse_attn_workspace", "hs_sparse_attn", "hs_resolve_attn",
+    "hs_sparse_attn_workspace", "hs_sparse_attn", "hs_resolve_attn", "hs_prefetch",
     "hs_trace_enable", "hs_trace_read",
 )
 
@@ -76,7 +77,7 @@ class Trace(ctypes.Structure):
 
 class Tuning(ctypes.Structure):
     _fields_ = [("attn_splits", ctypes.c_int32), ("latent_heads_per_wg", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 6)]
+                ("prefetch_workgroups", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
 
 
 _lib = None
@@ -111,12 +112,15 @@ def lib():
         "hs_buffer_rows": ([vp, P(vp), P(sz)], i32),
         "hs_buffer_state_get": ([vp, vp, vp, P(u32), P(i32), vp], i32),
         "hs_buffer_state_set": ([vp, vp, vp, u32, i32, vp], i32),
+        "hs_buffer_shared_bytes": ([vp, i32], sz),
+        "hs_buffer_create_shared": ([vp, i32, vp, sz, P(vp)], i32),
         "hs_batch_create": ([P(vp), i32, P(vp)], i32),
         "hs_batch_destroy": ([vp], i32),
         "hs_resolve": ([vp, vp, i32, vp, vp, vp], i32),
         "hs_sparse_attn_workspace": ([vp, i32, i32], sz),
         "hs_sparse_attn": ([vp, vp, i32, vp, i32, ctypes.c_float, vp, vp, sz, vp], i32),
         "hs_resolve_attn": ([vp, vp, i32, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz, vp], i32),
+        "hs_prefetch": ([vp, vp], i32),
         "hs_trace_enable": ([i32], i32),
         "hs_trace_read": ([P(Trace)], i32),
     }
@@ -159,15 +163,17 @@ def hs_last_error() -> str:
     return lib().hs_last_error().decode()
 
 
-def hs_set_tuning(attn_splits: int = 0, latent_heads_per_wg: int = 0) -> None:
-    t = Tuning(attn_splits, latent_heads_per_wg)
+def hs_set_tuning(attn_splits: int = 0, latent_heads_per_wg: int = 0,
+                  prefetch_workgroups: int = 0) -> None:
+    t = Tuning(attn_splits, latent_heads_per_wg, prefetch_workgroups)
     _check(lib().hs_set_tuning(ctypes.byref(t)))
 
 
 def hs_get_tuning() -> dict:
     t = Tuning()
     _check(lib().hs_get_tuning(ctypes.byref(t)))
-    return {"attn_splits": t.attn_splits, "latent_heads_per_wg": t.latent_heads_per_wg}
+    return {"attn_splits": t.attn_splits, "latent_heads_per_wg": t.latent_heads_per_wg,
+            "prefetch_workgroups": t.prefetch_workgroups}
 
 
 # ------------------------------------------------------------------ pool
@@ -250,6 +256,20 @@ def hs_buffer_create(pool: int, req: int, layer: int, B: int, mem, stream=None) 
     return out.value
 
 
+def hs_buffer_shared_bytes(pool: int, B: int) -> int:
+    return int(lib().hs_buffer_shared_bytes(pool, B))
+
+
+def hs_buffer_create_shared(base: int, layer: int, mem) -> int:
+    """Rows of `layer` attached to the state of buffer `base` (same request):
+    layers that reuse one selection. mem: a device tensor of at least
+    hs_buffer_shared_bytes(pool, B) bytes."""
+    out = ctypes.c_void_p()
+    nbytes = mem.numel() * mem.element_size()
+    _check(lib().hs_buffer_create_shared(base, layer, _ptr(mem), nbytes, ctypes.byref(out)))
+    return out.value
+
+
 def hs_buffer_destroy(buf: int) -> None:
     _check(lib().hs_buffer_destroy(buf))
 
@@ -320,6 +340,12 @@ def hs_resolve_attn(batch: int, topk, k: int, slots, miss, q, n_q_heads: int, sm
     _check(lib().hs_resolve_attn(batch, _ptr(topk), int(k), _ptr(slots), _ptr(miss), _ptr(q),
                                  int(n_q_heads), float(sm_scale), _ptr(out), _ptr(ws), ws_bytes,
                                  _stream(stream)))
+
+
+def hs_prefetch(batch: int, stream=None) -> None:
+    """Fetch every unit's records of its state's last fetch list (the other
+    layers of a group sharing one selection)."""
+    _check(lib().hs_prefetch(batch, _stream(stream)))
 
 
 # ------------------------------------------------------------------ tracing

@@ -96,6 +96,7 @@ class Workload:
     B: List[int] = field(default_factory=list)  # per request buffer slots
     window: int = 512  # width of the "window" source
     zipf_s: float = 1.1  # exponent of the "zipf" source
+    share: int = 1  # consecutive layers that reuse one selection (a layer group)
 
     @property
     def n_units(self) -> int:
@@ -135,6 +136,10 @@ class Workload:
         """(request, layer) of unit u; units are request-major."""
         return u // self.n_layers, u % self.n_layers
 
+    def group_base(self, l: int) -> int:
+        """First layer of the group of layers whose selections layer l reuses."""
+        return l - l % self.share
+
 
 def _n_new(frac: float, k: int) -> int:
     return int(round(frac * k))
@@ -145,7 +150,9 @@ def workload(idx: int) -> Workload:
 
     1 tiny fp32 MHA; 2 GQA 32K bf16 with write-through appends; 3 batch-8 MLA
     latent (the headline); 4 batch 32 x 2 layers, 256K context; 5 miss-heavy
-    stress with per-request context and buffer sizes.
+    stress with per-request context and buffer sizes; 6 the batch-8 MLA
+    setting over 8 layers in two groups of 4 that each reuse one selection
+    (cross-layer index sharing).
     """
     if idx == 1:
         w = Workload("tiny_mha_f32", 1, 1, "mha", F32, F32, 1, 64, 0, 0, 1, 256, 32,
@@ -170,8 +177,14 @@ def workload(idx: int) -> Workload:
         lo, hi = math.log(16384), math.log(1048576)
         w.ctx = [int(math.floor(math.exp(rng.uniform(lo, hi)))) for _ in range(64)]
         w.B = [int(b) for b in rng.choice(np.array([2048, 4096, 8192]), size=64)]
+    elif idx == 6:
+        w = Workload("mla_b8_128k_share4", 8, 8, "latent", BF16, BF16, 1, 0, 512, 64, 64, 2048,
+                     64, _n_new(0.13, 2048), (("zipf", 1.0),), 0.5, 6, share=4)
+        w.ctx, w.B = [131072] * 8, [4096] * 8
     else:
         raise ValueError(f"no workload {idx}")
+    if w.n_layers % w.share:
+        raise ValueError("layer groups must divide the layers")
     return w
 
 
@@ -265,12 +278,17 @@ def gen_trace(w: Workload, r: int, l: int, steps: Optional[int] = None) -> np.nd
 
 
 def gen_traces(w: Workload, steps: Optional[int] = None) -> np.ndarray:
-    """All units' traces: int32 [steps][n_units][k] (units request-major)."""
+    """All units' traces: int32 [steps][n_units][k] (units request-major).
+    Every layer of a group takes its first layer's trace."""
     steps = w.steps if steps is None else steps
     out = np.empty((steps, w.n_units, w.k), dtype=np.int32)
     for u in range(w.n_units):
         r, l = w.unit(u)
-        out[:, u, :] = gen_trace(w, r, l, steps)
+        g = w.group_base(l)
+        if g != l:
+            out[:, u, :] = out[:, r * w.n_layers + g, :]
+        else:
+            out[:, u, :] = gen_trace(w, r, l, steps)
     return out
 
 

@@ -10,6 +10,17 @@ hs_resolve_attn) -> (write-through) hs_pool_append of that layer's new token. St
 captured once each into a hipGraph (torch.cuda.CUDAGraph) and replayed with
 no host synchronisation.
 
+Layer groups that reuse one selection (Workload.share > 1; HiSparse summary,
+section 6) run in one of three ways:
+  "prefetch" - the group's later layers get buffers sharing the first
+      layer's state (hs_buffer_create_shared); per group, hs_resolve of the
+      first layer (the plan, and that layer's fetch), then on a second stream
+      hs_prefetch of each later layer in order, each layer's attention
+      waiting only for its own fetch, so the host-link transfer of layer
+      l + 1 overlaps the attention of layer l;
+  "serial"   - the same shared buffers, every call on one stream;
+  "none"     - every layer has its own state and resolves on its own.
+
 Only the library's entry points do work here; this module allocates and
 orders. Unit order inside the session is layer-major: index l * R + r.
 """
@@ -27,9 +38,13 @@ from . import inputs as I
 class Session:
     def __init__(self, w: I.Workload, steps: Optional[int] = None, device: str = "cuda",
                  fill: str = "touched", traces: Optional[np.ndarray] = None,
-                 fused: bool = False):
+                 fused: bool = False, share_mode: str = "prefetch"):
         self.w = w
         self.fused = fused  # hs_resolve_attn instead of hs_resolve + hs_sparse_attn
+        if share_mode not in ("prefetch", "serial", "none"):
+            raise ValueError(share_mode)
+        self.share_mode = share_mode if w.share > 1 else "none"
+        self.grouped = self.share_mode != "none"
         self.steps = w.steps if steps is None else steps
         self.device = torch.device(device)
         R, L, k = w.n_requests, w.n_layers, w.k
@@ -57,16 +72,25 @@ class Session:
                     I.fill_records(w, addr, r, l, positions=pos)
                 H.hs_pool_set_length(self.pool, r, l, w.ctx[r])
 
-        # device buffers, one allocation per unit
+        # device buffers, one allocation per unit; in a grouped session the
+        # later layers of a group hold rows only and share the first's state
         self.mem: List[torch.Tensor] = []
         self.bufs: List[List[int]] = [[0] * R for _ in range(L)]
         for l in range(L):
+            g = w.group_base(l)
             for r in range(R):
-                nbytes = H.hs_buffer_bytes(self.pool, w.B[r])
-                t = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+                if self.grouped and g != l:
+                    nbytes = H.hs_buffer_shared_bytes(self.pool, w.B[r])
+                    t = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+                    self.bufs[l][r] = H.hs_buffer_create_shared(self.bufs[g][r], l, t)
+                else:
+                    nbytes = H.hs_buffer_bytes(self.pool, w.B[r])
+                    t = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+                    self.bufs[l][r] = H.hs_buffer_create(self.pool, r, l, w.B[r], t)
                 self.mem.append(t)
-                self.bufs[l][r] = H.hs_buffer_create(self.pool, r, l, w.B[r], t)
         self.batches = [H.hs_batch_create(self.bufs[l]) for l in range(L)]
+        self.side = torch.cuda.Stream(device=self.device) if self.share_mode == "prefetch" else None
+        self.fetched = [torch.cuda.Event() for _ in range(w.share)]
 
         # queries [T][L][R][Hq][qdim] (bf16 bits as int16, or fp32)
         qdt = torch.float32 if w.q_dtype == I.F32 else torch.int16
@@ -96,6 +120,47 @@ class Session:
         torch.cuda.synchronize()
 
     # -------------------------------------------------------------- steps
+    def resolved_layer(self, l: int) -> int:
+        """The layer whose resolve produced layer l's slots and misses."""
+        return self.w.group_base(l) if self.grouped else l
+
+    def _append(self, t: int, l: int) -> None:
+        if self.app is not None:
+            for r in range(self.R):
+                H.hs_pool_append(self.pool, r, l, self.w.ctx[r] + t, self.app[t, l, r], n=1)
+
+    def _attn(self, t: int, l: int) -> None:
+        g = self.resolved_layer(l)
+        H.hs_sparse_attn(self.batches[l], self.q[t, l], self.w.n_q_heads, self.slots[g], self.k,
+                         self.scale, self.out[l], self.ws)
+
+    def group(self, t: int, g: int) -> None:
+        """Enqueue step t of the layer group starting at layer g (grouped
+        sessions): one resolve for the group, the later layers' fetches
+        from its plan, every layer's attention."""
+        w = self.w
+        H.hs_resolve(self.batches[g], self.topk[t, g], self.k, self.slots[g], self.miss[g])
+        if self.share_mode == "serial":
+            self._attn(t, g)
+            self._append(t, g)
+            for l in range(g + 1, g + w.share):
+                H.hs_prefetch(self.batches[l])
+                self._attn(t, l)
+                self._append(t, l)
+            return
+        cur = torch.cuda.current_stream()
+        self.side.wait_stream(cur)
+        with torch.cuda.stream(self.side):
+            for j in range(1, w.share):
+                H.hs_prefetch(self.batches[g + j])
+                self.fetched[j].record(self.side)
+        self._attn(t, g)
+        self._append(t, g)
+        for j in range(1, w.share):
+            cur.wait_event(self.fetched[j])
+            self._attn(t, g + j)
+            self._append(t, g + j)
+
     def layer(self, t: int, l: int) -> None:
         """Enqueue step t of layer l on the current stream."""
         w = self.w
@@ -112,6 +177,10 @@ class Session:
                 H.hs_pool_append(self.pool, r, l, w.ctx[r] + t, self.app[t, l, r], n=1)
 
     def step(self, t: int) -> None:
+        if self.grouped:
+            for g in range(0, self.L, self.w.share):
+                self.group(t, g)
+            return
         for l in range(self.L):
             self.layer(t, l)
 
@@ -136,6 +205,8 @@ class Session:
         """Every buffer back to empty; pool lengths back to the prefill."""
         torch.cuda.synchronize()
         for l in range(self.L):
+            if self.resolved_layer(l) != l:
+                continue  # a shared state is reset through its group's first layer
             for r in range(self.R):
                 H.hs_buffer_reset(self.bufs[l][r])
         for r in range(self.R):
