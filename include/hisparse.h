@@ -111,7 +111,7 @@ typedef struct hs_tuning {
   int32_t latent_heads_per_wg;  /* latent attention: query heads per workgroup
                                    (16, 32 or 64, dividing n_q_heads) */
   int32_t prefetch_workgroups;  /* hs_prefetch: workgroups per launch
-                                   (0 = 512; 1 to 65536) */
+                                   (0 = 64; 1 to 65536) */
   int32_t reserved[5];
 } hs_tuning;
 

@@ -1,6 +1,8 @@
-"""GPU parity at the five workloads' full sizes, in the benchmark's launch
-configuration (one captured hipGraph per decode step, replayed in order, each
-layer one fused hs_resolve_attn).
+"""GPU parity at the workloads' full sizes, in the benchmark's launch
+configuration: one captured hipGraph per decode step, replayed in order; MHA
+layers through the fused hs_resolve_attn, latent layers through hs_resolve
+then hs_sparse_attn; layer groups that reuse one selection with one resolve
+per group and the later layers' fetches on a second stream.
 
 Every step: slot vectors, miss counts, page tables, LRU stamps, clocks and
 error words of every unit are compared bit for bit with the oracle. Sampled
@@ -45,15 +47,17 @@ PLAN = {
     3: (range(0, 128, 32), [(0, 0), (7, 0)], 64),
     4: (range(0, 64, 32), [(0, 0), (31, 1)], 32),
     5: (range(0, 64, 32), [(0, 0), (63, 0)], 32),
+    6: (range(0, 64, 32), [(0, 0), (0, 3), (7, 5)], 32),
+    7: (range(0, 64, 16), [(0, 0), (31, 0)], 16),
 }
 
 
-@pytest.mark.parametrize("wl", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("wl", [1, 2, 3, 4, 5, 6, 7])
 def test_full_size_workload(wl):
     w = I.workload(wl)
     attn_steps, attn_units, rows_every = PLAN[wl]
     t0 = time.time()
-    sess = Session(w, w.steps, fill="touched", fused=True)
+    sess = Session(w, w.steps, fill="touched", fused=w.kind == "mha", share_mode="prefetch")
     orc = OracleRun(w, sess.traces, w.steps)
     sess.capture()
     say(f"workload {wl} {w.name}: setup {time.time() - t0:.1f}s")
@@ -66,10 +70,11 @@ def test_full_size_workload(wl):
             miss_g = sess.miss.cpu().numpy()
             out_g = sess.out.cpu().numpy() if t in attn_steps else None
             for l in range(w.n_layers):
+                gl = sess.resolved_layer(l)
                 for r in range(w.n_requests):
                     so, mo = orc.resolve(t, r, l)
-                    assert np.array_equal(slots_g[l, r], so), f"slots t={t} r={r} l={l}"
-                    assert int(miss_g[l, r]) == mo, f"miss t={t} r={r} l={l}"
+                    assert np.array_equal(slots_g[gl, r], so), f"slots t={t} r={r} l={l}"
+                    assert int(miss_g[gl, r]) == mo, f"miss t={t} r={r} l={l}"
                     pos, stamp, clock, err = sess.state(l, r)
                     ob = orc.bufs[(r, l)]
                     assert np.array_equal(pos, ob.pos), f"pos t={t} r={r} l={l}"

@@ -7,7 +7,7 @@ import pytest
 from tiered_kv_cache_hs_amd import inputs as I
 
 
-@pytest.mark.parametrize("wl", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("wl", [1, 2, 3, 4, 5, 6, 7])
 def test_trace_properties(wl):
     w = I.workload(wl)
     steps = min(w.steps, 24)
@@ -32,8 +32,11 @@ def test_trace_streams_differ_per_unit_and_prefix_stable():
 
 
 def test_workload_shapes():
-    assert [I.workload(i).n_new for i in (1, 2, 3, 4, 5)] == [26, 266, 266, 143, 614]
-    assert [I.workload(i).rec_bytes for i in (1, 2, 3, 4, 5)] == [512, 4096, 1152, 4096, 1152]
+    assert [I.workload(i).n_new for i in (1, 2, 3, 4, 5, 6, 7)] == [26, 266, 266, 143, 614, 266, 67]
+    assert [I.workload(i).rec_bytes for i in range(1, 8)] == [512, 4096, 1152, 4096, 1152, 1152,
+                                                              1152]
+    w7 = I.workload(7)  # compressed entries: 512 of 32768 / 4 per step
+    assert (w7.k, w7.ctx[0], w7.B[0], w7.n_requests) == (512, 8192, 1024, 32)
     w5 = I.workload(5)
     assert all(16384 <= c < 1048576 for c in w5.ctx) and set(w5.B) <= {2048, 4096, 8192}
     assert len(set(w5.B)) == 3

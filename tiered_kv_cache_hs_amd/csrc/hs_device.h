@@ -128,7 +128,7 @@ hipError_t launch_resolve(const UnitDesc *d_units, int n_units, int max_B,
                           hipStream_t stream);
 size_t resolve_lds_bytes(int k);
 // Fetch every unit's share of its state's last fetch list (about `workgroups`
-// workgroups in total; 0 = 512).
+// workgroups in total; 0 = 64).
 hipError_t launch_prefetch(const UnitDesc *d_units, int n, int rec_bytes, int workgroups,
                            hipStream_t stream);
 hipError_t launch_regather(const UnitDesc *d_unit, int B, int rec_bytes,

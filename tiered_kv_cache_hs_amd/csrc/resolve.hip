@@ -732,9 +732,13 @@ hipError_t launch_resolve(const UnitDesc *d_units, int n, int max_B, const int32
   return hipGetLastError();
 }
 
+// A prefetch runs beside attention kernels: 64 workgroups keep enough host
+// reads in flight for the link (about 1 MB) while leaving most compute units
+// free of long-latency host loads; 512 slowed the attention beside them and,
+// on a batch of 8 latent units, was slower even alone.
 hipError_t launch_prefetch(const UnitDesc *d_units, int n, int rec_bytes, int workgroups,
                            hipStream_t stream) {
-  const int wg = workgroups > 0 ? workgroups : 512;
+  const int wg = workgroups > 0 ? workgroups : 64;
   const int G = std::max(1, std::min(64, (wg + n - 1) / n));
   trace_begin(HS_TRACE_GATHER, stream);
   hipLaunchKernelGGL(hs_k_gather, dim3(n * G), dim3(GATHER_THREADS), 0, stream, d_units, G,

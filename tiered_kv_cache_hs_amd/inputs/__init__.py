@@ -152,7 +152,9 @@ def workload(idx: int) -> Workload:
     latent (the headline); 4 batch 32 x 2 layers, 256K context; 5 miss-heavy
     stress with per-request context and buffer sizes; 6 the batch-8 MLA
     setting over 8 layers in two groups of 4 that each reuse one selection
-    (cross-layer index sharing).
+    (cross-layer index sharing); 7 compressed entries: each record is one
+    entry standing for 4 tokens, 512 of the 8192 entries of a 32K context
+    selected per step, 32 requests.
     """
     if idx == 1:
         w = Workload("tiny_mha_f32", 1, 1, "mha", F32, F32, 1, 64, 0, 0, 1, 256, 32,
@@ -181,6 +183,10 @@ def workload(idx: int) -> Workload:
         w = Workload("mla_b8_128k_share4", 8, 8, "latent", BF16, BF16, 1, 0, 512, 64, 64, 2048,
                      64, _n_new(0.13, 2048), (("zipf", 1.0),), 0.5, 6, share=4)
         w.ctx, w.B = [131072] * 8, [4096] * 8
+    elif idx == 7:
+        w = Workload("csa_b32_32k_top512", 32, 1, "latent", BF16, BF16, 1, 0, 512, 64, 64, 512,
+                     64, _n_new(0.13, 512), (("zipf", 1.0),), 0.5, 7)
+        w.ctx, w.B = [32768 // 4] * 32, [1024] * 32
     else:
         raise ValueError(f"no workload {idx}")
     if w.n_layers % w.share:
