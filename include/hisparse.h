@@ -171,8 +171,22 @@ size_t hs_buffer_bytes(hs_pool_t pool, int32_t B);
 hs_status hs_buffer_create(hs_pool_t pool, int32_t req, int32_t layer,
                            int32_t B, void *d_mem, size_t bytes, void *stream,
                            hs_buffer_t *out);
-/* Frees the handle only (not d_mem). */
+/* Frees the handle only (not d_mem). HS_E_INVAL while shared buffers made
+ * from it (hs_buffer_create_shared) still exist: destroy those first. */
 hs_status hs_buffer_destroy(hs_buffer_t buf);
+/* On-demand growth (HiSparse summary, section 8: the per-request, per-layer
+ * device cache is allocated and grown as needed). Moves the buffer into new
+ * caller-owned memory of at least hs_buffer_bytes(pool, new_B) bytes
+ * (256-byte aligned, not overlapping the current memory), with
+ * B <= new_B <= HS_MAX_B: slots [0, B) keep their positions, stamps and
+ * rows, slots [B, new_B) are empty; clock, error word and the last fetch list
+ * carry over. From then on the handle uses the new memory and the old memory
+ * is no longer read (the caller may free it). Batches made before hold the
+ * old layout: create them again. Refused (HS_E_INVAL) for a buffer whose
+ * state is shared with others (either side of hs_buffer_create_shared).
+ * Synchronous (waits for stream). */
+hs_status hs_buffer_grow(hs_buffer_t buf, int32_t new_B, void *d_mem, size_t bytes,
+                         void *stream);
 /* Enqueues the empty state again (also clears the error word). */
 hs_status hs_buffer_reset(hs_buffer_t buf, void *stream);
 /* Device pointer and size of the rows region: row s (the record held by

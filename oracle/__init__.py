@@ -109,6 +109,23 @@ class OracleBuffer:
         return o
 
 
+def grow(buf: OracleBuffer, new_B: int) -> OracleBuffer:
+    """The buffer with new_B - B slots added (HiSparse summary, section 8: the
+    per-request, per-layer device cache is allocated and grown on demand).
+    Reading: growth only adds empty slots after the existing ones; positions,
+    stamps, rows, clock and error word of slots [0, B) are unchanged."""
+    if new_B < buf.B:
+        raise ValueError("a buffer does not shrink")
+    g = OracleBuffer(new_B, buf.rec_bytes, with_rows=buf.rows is not None)
+    g.pos[: buf.B] = buf.pos
+    g.stamp[: buf.B] = buf.stamp
+    g.clock[:] = buf.clock
+    g.err[:] = buf.err
+    if buf.rows is not None:
+        g.rows[: buf.B] = buf.rows
+    return g
+
+
 def resolve(buf: OracleBuffer, topk: np.ndarray, pool: Optional[np.ndarray], pool_len: int):
     """Resolve one selection against buf in place.
 

@@ -26,6 +26,13 @@ class BruteLRU:
     def resident(self) -> Set[int]:
         return set(self.order)
 
+    def grow(self, new_B: int) -> None:
+        """More capacity: the added slots are free (never used), after the
+        existing ones."""
+        assert new_B >= self.B
+        self.free.extend(range(self.B, new_B))
+        self.B = new_B
+
     def step(self, sel: Sequence[int]) -> Tuple[List[int], int, List[int]]:
         """Returns (slots aligned with sel, miss count, evicted positions)."""
         S = set(sel)

@@ -97,11 +97,13 @@ def small_workload(kind, dtype, B, k, ctx, steps, n_new, R=1, L=1, seed=0, Hkv=1
 
 
 def compare_run(w, steps, traces=None, attn_every=1, rows_every=1, attn_units=None,
-                graph=False, fill="touched", fused=False, share_mode="prefetch"):
+                graph=False, fill="touched", fused=False, share_mode="prefetch", grow=None):
     """Run a GPU session step by step beside the oracle and compare slots,
     miss counts, state, resident rows and attention outputs of every unit.
     The oracle resolves every layer on its own, also where the session runs
-    a layer group on one shared state."""
+    a layer group on one shared state. grow = (step, [new B per request]):
+    before that step every buffer grows (hs_buffer_grow on the GPU side,
+    oracle.grow on the oracle's)."""
     from tiered_kv_cache_hs_amd.session import Session
     import torch
 
@@ -112,6 +114,12 @@ def compare_run(w, steps, traces=None, attn_every=1, rows_every=1, attn_units=No
     stats = []
     try:
         for t in range(steps):
+            if grow is not None and t == grow[0]:
+                sess.grow(grow[1])
+                for (r, l), b in list(orc.bufs.items()):
+                    orc.bufs[(r, l)] = oracle.grow(b, grow[1][r])
+                if graph:
+                    sess.capture(range(t, steps))
             if graph:
                 sess.replay(t)
             else:

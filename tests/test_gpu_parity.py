@@ -325,3 +325,18 @@ def test_fused_equals_resolve_then_attention_bitwise(wl, steps, hq):
     finally:
         a.close()
         b.close()
+
+
+@pytest.mark.parametrize("kind,graph", [("mha", False), ("latent", False), ("mha", True)])
+def test_buffer_growth_mid_run(kind, graph):
+    """Every buffer grows (B 40 -> 96, and 300 -> 300 + 211 for latent) after
+    a few steps; slots, state, rows and outputs keep matching the oracle
+    grown the same way, the new empty slots being used first."""
+    if kind == "mha":
+        w = _small("mha", I.F32, 40, 17, 300, 9, 6, R=2, L=2, seed=400)
+        new_B = [96, 60]
+    else:
+        w = _small("latent", I.BF16, 300, 197, 3000, 6, 40, R=2, seed=401, Hq=32)
+        new_B = [511, 300]
+    compare_run(w, w.steps, fill="full", graph=graph, grow=(3, new_B))
+

@@ -169,11 +169,19 @@ def test_shared_buffer_argument_checks_and_resolve_refusal():
         pos, stamp, clock, err = H.hs_buffer_state_get(base, B)
         assert clock == 1 and err == 0 and sorted(pos[pos >= 0].tolist()) == list(range(8))
         assert H.hs_buffer_state_get(sh, B)[2] == 1
+        with pytest.raises(H.HsError):  # its state is still in use by sh
+            H.hs_buffer_destroy(base)
+        grown = torch.empty(H.hs_buffer_bytes(pool, 2 * B), dtype=torch.uint8, device="cuda")
+        mems.append(grown)
+        with pytest.raises(H.HsError):  # a shared state cannot grow
+            H.hs_buffer_grow(base, 2 * B, grown)
+        with pytest.raises(H.HsError):
+            H.hs_buffer_grow(sh, 2 * B, grown)
     finally:
         torch.cuda.synchronize()
         for b in batches:
             H.hs_batch_destroy(b)
-        for b in bufs:
+        for b in reversed(bufs):
             H.hs_buffer_destroy(b)
         H.hs_pool_destroy(pool)
 
@@ -219,6 +227,6 @@ def test_prefetch_past_a_members_length_sets_range_error():
         torch.cuda.synchronize()
         for b in batches:
             H.hs_batch_destroy(b)
-        for b in bufs:
+        for b in reversed(bufs):
             H.hs_buffer_destroy(b)
         H.hs_pool_destroy(pool)

@@ -239,3 +239,57 @@ def test_snapshot_restore_is_deterministic():
         sb = oracle.resolve(b, tr[t], None, w.ctx[0])
         assert np.array_equal(sa[0], sb[0]) and sa[1] == sb[1]
     assert np.array_equal(a.pos, b.pos) and np.array_equal(a.stamp, b.stamp)
+
+
+def test_growth_matches_brute_force():
+    """Growing a buffer mid-trace (oracle.grow) against the recency-list
+    model given more free slots at the same step: slots, miss counts,
+    resident sets and evictions agree at every step; rows carry over."""
+    rng = np.random.default_rng(777)
+    for case in range(3000):
+        ctx = int(rng.integers(3, 49))
+        k = int(rng.integers(1, min(6, ctx) + 1))
+        B = int(rng.integers(k, 13))
+        T = int(rng.integers(2, 9))
+        grow_at = int(rng.integers(1, T))
+        new_B = B + int(rng.integers(0, 9))
+        buf = oracle.OracleBuffer(B, 4, with_rows=False)
+        br = BruteLRU(B)
+        prev = None
+        for t in range(T):
+            if t == grow_at:
+                buf = oracle.grow(buf, new_B)
+                br.grow(new_B)
+                assert buf.B == new_B and (buf.pos[B:] == -1).all() and (buf.stamp[B:] == 0).all()
+            if prev is not None and rng.random() < 0.7:
+                keep = list(rng.permutation(prev)[: int(rng.integers(0, k + 1))])
+                pool = [p for p in range(ctx) if p not in keep]
+                new = list(rng.choice(pool, size=k - len(keep), replace=False))
+                sel = [int(x) for x in rng.permutation(keep + new)]
+            else:
+                sel = [int(x) for x in rng.choice(ctx, size=k, replace=False)]
+            prev = sel
+            before = set(int(p) for p in buf.pos if p >= 0)
+            slots, miss = oracle.resolve(buf, np.asarray(sel, dtype=np.int32), None, ctx)
+            bslots, bmiss, bev = br.step(sel)
+            after = set(int(p) for p in buf.pos if p >= 0)
+            assert miss == bmiss and after == br.resident(), (case, t)
+            assert sorted(before - after) == sorted(bev) and slots.tolist() == bslots, (case, t)
+
+
+def test_growth_keeps_rows_and_fills_new_slots_first():
+    ctx, rec = 40, 8
+    pool = (np.arange(ctx)[:, None] * 7 + np.arange(rec)[None, :]).astype(np.uint8)
+    buf = oracle.OracleBuffer(4, rec, with_rows=True)
+    for sel in ([1, 2, 3, 4], [5, 6, 1, 2]):
+        oracle.resolve(buf, np.array(sel), pool, ctx)
+    g = oracle.grow(buf, 7)
+    assert np.array_equal(g.rows[:4], buf.rows) and np.array_equal(g.pos[:4], buf.pos)
+    assert int(g.clock[0]) == 2
+    # three new positions: the three new (empty) slots take them, nothing evicted
+    slots, miss = oracle.resolve(g, np.array([10, 11, 12]), pool, ctx)
+    assert miss == 3 and sorted(slots.tolist()) == [4, 5, 6]
+    assert set(g.pos.tolist()) == {5, 6, 1, 2, 10, 11, 12}
+    assert np.array_equal(g.rows[4], pool[10])
+    with pytest.raises(ValueError):
+        oracle.grow(g, 6)

@@ -114,6 +114,7 @@ void trace_end(hipStream_t stream);
 // ---------------------------------------------------------------- launches
 // Declared here, defined in the .hip files; all enqueue on `stream` and
 // return the hipError_t of the launch.
+// Slots [0, B) empty; the control words cleared too unless ctl is null.
 hipError_t launch_buffer_init(int32_t *pos, uint32_t *stamp, int32_t *fsrc, uint32_t *ctl,
                               int B, hipStream_t stream);
 // How a resolve fetches its misses: not at all (the attention kernels read

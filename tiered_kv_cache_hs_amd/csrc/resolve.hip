@@ -635,7 +635,7 @@ __global__ void hs_k_buffer_init(int32_t *pos, uint32_t *stamp, int32_t *fsrc, u
     stamp[s] = 0u;
     fsrc[s] = -1;
   }
-  if (blockIdx.x == 0 && threadIdx.x < CTL_WORDS) ctl[threadIdx.x] = 0u;
+  if (ctl && blockIdx.x == 0 && threadIdx.x < CTL_WORDS) ctl[threadIdx.x] = 0u;
 }
 
 // Write-through append from device memory into the mapped host pool, then

@@ -103,6 +103,8 @@ struct hs_pool_s {
 struct hs_buffer_s {
   hs_pool_t pool = nullptr;
   int32_t req = 0, layer = 0, B = 0;
+  hs_buffer_s *base = nullptr;  // owner of the shared state, if not this one
+  int32_t n_members = 0;        // live buffers sharing this one's state
   uint8_t *mem = nullptr;
   hs::BufferLayout lay{};
   UnitDesc desc{};
@@ -393,6 +395,7 @@ hs_status hs_buffer_create_shared(hs_buffer_t base, int32_t layer, void *d_mem, 
   b->lay = base->lay;
   // the group's state (page table, stamps, fetch list, control words) is
   // base's; rows, pool records and length are this layer's
+  b->base = base->base ? base->base : base;
   b->desc = base->desc;
   b->desc.rows = b->mem;
   b->desc.pool = p->dev[b->req] + unit_offset(p, b->req, layer);
@@ -405,14 +408,67 @@ hs_status hs_buffer_create_shared(hs_buffer_t base, int32_t layer, void *d_mem, 
     delete b;
     return hip_fail(e, "shared buffer create");
   }
+  ++b->base->n_members;
   *out = b;
   return HS_OK;
 }
 
 hs_status hs_buffer_destroy(hs_buffer_t b) {
   if (!b) return fail(HS_E_INVAL, "null buffer");
+  if (b->n_members > 0)
+    return fail(HS_E_INVAL, "%d shared buffers still use this buffer's state", b->n_members);
+  if (b->base) --b->base->n_members;
   if (b->d_desc) (void)hipFree(b->d_desc);
   delete b;
+  return HS_OK;
+}
+
+hs_status hs_buffer_grow(hs_buffer_t b, int32_t new_B, void *d_mem, size_t bytes,
+                         void *stream) {
+  if (!b || !d_mem) return fail(HS_E_INVAL, "null argument");
+  if (b->base || b->n_members > 0)
+    return fail(HS_E_INVAL, "a buffer whose state is shared cannot grow");
+  if (new_B < b->B || new_B > HS_MAX_B)
+    return fail(HS_E_INVAL, "new B = %d outside [%d, %d]", new_B, b->B, HS_MAX_B);
+  if ((uintptr_t)d_mem % 256) return fail(HS_E_INVAL, "buffer memory must be 256-byte aligned");
+  const size_t rec = b->pool->rec;
+  const hs::BufferLayout lay = hs::buffer_layout(rec, new_B);
+  if (bytes < lay.total)
+    return fail(HS_E_INVAL, "buffer needs %zu bytes, got %zu", lay.total, bytes);
+  const uint8_t *o0 = b->mem, *o1 = b->mem + b->lay.total;
+  const uint8_t *n0 = (const uint8_t *)d_mem, *n1 = n0 + lay.total;
+  if (n0 < o1 && o0 < n1) return fail(HS_E_INVAL, "new memory overlaps the buffer's");
+  uint8_t *nm = (uint8_t *)d_mem;
+  const size_t B = (size_t)b->B;
+  hipStream_t st = S(stream);
+  // slots [0, B) keep their rows and metadata; [B, new_B) start empty
+  HS_HIP(hipMemcpyAsync(nm + lay.rows, b->mem + b->lay.rows, B * rec, hipMemcpyDeviceToDevice, st));
+  HS_HIP(hipMemcpyAsync(nm + lay.pos, b->mem + b->lay.pos, B * 4, hipMemcpyDeviceToDevice, st));
+  HS_HIP(hipMemcpyAsync(nm + lay.stamp, b->mem + b->lay.stamp, B * 4, hipMemcpyDeviceToDevice, st));
+  HS_HIP(hipMemcpyAsync(nm + lay.work, b->mem + b->lay.work, B * 8, hipMemcpyDeviceToDevice, st));
+  HS_HIP(hipMemcpyAsync(nm + lay.fsrc, b->mem + b->lay.fsrc, B * 4, hipMemcpyDeviceToDevice, st));
+  HS_HIP(hipMemcpyAsync(nm + lay.ctl, b->mem + b->lay.ctl, hs::CTL_WORDS * 4,
+                        hipMemcpyDeviceToDevice, st));
+  if (new_B > b->B) {
+    hipError_t e = hs::launch_buffer_init((int32_t *)(nm + lay.pos) + B,
+                                          (uint32_t *)(nm + lay.stamp) + B,
+                                          (int32_t *)(nm + lay.fsrc) + B, nullptr, new_B - b->B, st);
+    if (e != hipSuccess) return hip_fail(e, "grow init");
+  }
+  HS_HIP(hipStreamSynchronize(st));
+  UnitDesc d = b->desc;
+  d.rows = nm + lay.rows;
+  d.pos = (int32_t *)(nm + lay.pos);
+  d.stamp = (uint32_t *)(nm + lay.stamp);
+  d.work = (int2 *)(nm + lay.work);
+  d.fsrc = (int32_t *)(nm + lay.fsrc);
+  d.ctl = (uint32_t *)(nm + lay.ctl);
+  d.B = new_B;
+  HS_HIP(hipMemcpy(b->d_desc, &d, sizeof(UnitDesc), hipMemcpyHostToDevice));
+  b->desc = d;
+  b->mem = nm;
+  b->lay = lay;
+  b->B = new_B;
   return HS_OK;
 }
 

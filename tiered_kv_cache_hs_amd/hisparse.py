@@ -42,7 +42,8 @@ EXPORTS = (
     "hs_status_str", "hs_last_error", "hs_set_tuning", "hs_get_tuning",
     "hs_pool_create", "hs_pool_destroy", "hs_pool_record_bytes", "hs_pool_unit_ptr",
     "hs_pool_length", "hs_pool_set_length", "hs_pool_append",
-    "hs_buffer_bytes", "hs_buffer_create", "hs_buffer_destroy", "hs_buffer_reset",
+    "hs_buffer_bytes", "hs_buffer_create", "hs_buffer_destroy", "hs_buffer_grow",
+    "hs_buffer_reset",
     "hs_buffer_rows", "hs_buffer_state_get", "hs_buffer_state_set",
     "hs_buffer_shared_bytes", "hs_buffer_create_shared",
     "hs_batch_create", "hs_batch_destroy", "hs_resolve",
@@ -108,6 +109,7 @@ def lib():
         "hs_buffer_bytes": ([vp, i32], sz),
         "hs_buffer_create": ([vp, i32, i32, i32, vp, sz, vp, P(vp)], i32),
         "hs_buffer_destroy": ([vp], i32),
+        "hs_buffer_grow": ([vp, i32, vp, sz, vp], i32),
         "hs_buffer_reset": ([vp, vp], i32),
         "hs_buffer_rows": ([vp, P(vp), P(sz)], i32),
         "hs_buffer_state_get": ([vp, vp, vp, P(u32), P(i32), vp], i32),
@@ -272,6 +274,13 @@ def hs_buffer_create_shared(base: int, layer: int, mem) -> int:
 
 def hs_buffer_destroy(buf: int) -> None:
     _check(lib().hs_buffer_destroy(buf))
+
+
+def hs_buffer_grow(buf: int, new_B: int, mem, stream=None) -> None:
+    """Move the buffer into `mem` (a device tensor of at least
+    hs_buffer_bytes(pool, new_B) bytes) with new_B - B empty slots added."""
+    nbytes = mem.numel() * mem.element_size()
+    _check(lib().hs_buffer_grow(buf, int(new_B), _ptr(mem), nbytes, _stream(stream)))
 
 
 def hs_buffer_reset(buf: int, stream=None) -> None:

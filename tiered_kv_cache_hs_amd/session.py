@@ -89,6 +89,7 @@ class Session:
                     self.bufs[l][r] = H.hs_buffer_create(self.pool, r, l, w.B[r], t)
                 self.mem.append(t)
         self.batches = [H.hs_batch_create(self.bufs[l]) for l in range(L)]
+        self.Bs = [list(w.B) for _ in range(L)]  # slots of each buffer [l][r]
         self.side = torch.cuda.Stream(device=self.device) if self.share_mode == "prefetch" else None
         self.fetched = [torch.cuda.Event() for _ in range(w.share)]
 
@@ -198,6 +199,28 @@ class Session:
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
 
+    def grow(self, new_B: List[int]) -> None:
+        """Grow every buffer of request r to new_B[r] slots (hs_buffer_grow)
+        and rebuild the batches; graphs captured before must be captured again."""
+        if self.grouped:
+            raise ValueError("buffers of layer groups share their state and do not grow")
+        torch.cuda.synchronize()
+        self.graphs = []
+        for l in range(self.L):
+            for r in range(self.R):
+                t = torch.empty(H.hs_buffer_bytes(self.pool, new_B[r]), dtype=torch.uint8,
+                                device=self.device)
+                H.hs_buffer_grow(self.bufs[l][r], new_B[r], t)
+                self.mem[l * self.R + r] = t
+                self.Bs[l][r] = new_B[r]
+            H.hs_batch_destroy(self.batches[l])
+            self.batches[l] = H.hs_batch_create(self.bufs[l])
+        wsb = max(H.hs_sparse_attn_workspace(self.batches[l], self.w.n_q_heads, self.k)
+                  for l in range(self.L))
+        if wsb > self.ws.numel():
+            self.ws = torch.empty(wsb, dtype=torch.uint8, device=self.device)
+        torch.cuda.synchronize()
+
     def replay(self, t: int) -> None:
         self.graphs[t].replay()
 
@@ -216,11 +239,11 @@ class Session:
 
     # -------------------------------------------------------------- state
     def state(self, l: int, r: int):
-        return H.hs_buffer_state_get(self.bufs[l][r], self.w.B[r])
+        return H.hs_buffer_state_get(self.bufs[l][r], self.Bs[l][r])
 
     def rows(self, l: int, r: int) -> np.ndarray:
         addr, rec = H.hs_buffer_rows(self.bufs[l][r])
-        B = self.w.B[r]
+        B = self.Bs[l][r]
         t = self.mem[l * self.R + r][: B * rec]
         return t.cpu().numpy().reshape(B, rec)
 
@@ -229,7 +252,7 @@ class Session:
         self.graphs = []
         for b in self.batches:
             H.hs_batch_destroy(b)
-        for l in range(self.L):
+        for l in reversed(range(self.L)):  # shared buffers before the state they use
             for r in range(self.R):
                 H.hs_buffer_destroy(self.bufs[l][r])
         H.hs_pool_destroy(self.pool)
