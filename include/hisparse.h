@@ -102,7 +102,14 @@ typedef struct hs_pool_desc {
   int32_t head_dim;               /* HS_KV_MHA */
   int32_t latent_dim;             /* HS_KV_LATENT: value part */
   int32_t rope_dim;               /* HS_KV_LATENT: key-only part */
-  const int64_t *capacity_tokens; /* [n_requests] records per layer, host */
+  const int64_t *capacity_tokens; /* [n_requests] records per layer allocated
+                                     at creation, host */
+  const int64_t *max_tokens;      /* [n_requests] the most records per layer a
+                                     request may reserve later (hs_pool_reserve),
+                                     host; NULL = capacity_tokens */
+  int32_t page_tokens;            /* records per pool page, a power of two;
+                                     0 = 65536, or less when every request's
+                                     maximum fits in a smaller power of two */
 } hs_pool_desc;
 
 /* Tuning knobs (library-wide; 0 = choose automatically). */
@@ -121,28 +128,51 @@ const char *hs_last_error(void);
 hs_status hs_set_tuning(const hs_tuning *t);
 hs_status hs_get_tuning(hs_tuning *t);
 
-/* ---------------- host KV pool (HiSparse summary, section 3) ---------------
- * hs_pool_create: allocates, for every request, n_layers x capacity records
- * of pinned host memory mapped into the current device's address space
- * (hipHostMalloc), plus a small device table of per-unit lengths (all 0).
- * The library owns that memory until hs_pool_destroy. Synchronous.
+/* ---------------- host KV pool (HiSparse summary, sections 3, 8) -----------
+ * The pool is the authoritative copy of every record (section 3), kept in
+ * pinned host memory mapped into the current device's address space
+ * (hipHostMalloc) and allocated in pages as requests grow (section 8: the
+ * host pool is allocated in pages). A page holds page_tokens consecutive
+ * records of every layer of one request; each (request, layer) unit has a
+ * device page table (entry i: the device-visible address of its records
+ * [i * page_tokens, (i + 1) * page_tokens)) through which the kernels reach
+ * host records, so records of one unit need not be contiguous and adding
+ * pages never moves existing records or invalidates buffers or batches.
+ * hs_pool_create allocates each request's pages up to capacity_tokens and
+ * page tables sized for max_tokens, plus a device table of per-unit lengths
+ * (all 0). The library owns that memory until hs_pool_destroy. Synchronous.
  * Errors: HS_E_INVAL (bad descriptor), HS_E_NOMEM (allocation failed). */
 hs_status hs_pool_create(const hs_pool_desc *desc, hs_pool_t *out);
 /* The caller must have synchronised every stream that used the pool. */
 hs_status hs_pool_destroy(hs_pool_t pool);
 /* Bytes of one record. */
 hs_status hs_pool_record_bytes(hs_pool_t pool, size_t *rec_bytes);
-/* Host pointer of unit (req, layer)'s record array: record p is at
- * host_ptr + p * rec_bytes for 0 <= p < capacity. Used to write prefill
- * records directly. HS_E_RANGE for a bad req/layer. */
-hs_status hs_pool_unit_ptr(hs_pool_t pool, int32_t req, int32_t layer,
-                           void **host_ptr, int64_t *capacity);
+/* Records allocated for request req (whole pages), its maximum and the page
+ * size (any pointer may be NULL). HS_E_RANGE for a bad req. */
+hs_status hs_pool_capacity(hs_pool_t pool, int32_t req, int64_t *capacity,
+                           int64_t *max_tokens, int64_t *page_tokens);
+/* Allocates request req's pages so that at least `records` records per
+ * layer exist (no-op if they do); existing records stay where they are.
+ * Synchronous; not while a stream is being captured. HS_E_RANGE above the
+ * request's max_tokens, HS_E_NOMEM if an allocation fails. */
+hs_status hs_pool_reserve(hs_pool_t pool, int32_t req, int64_t records);
+/* Host pointer of record pos of unit (req, layer), for writing prefill
+ * records directly and for reading them back. HS_E_RANGE for a bad
+ * req/layer or pos outside [0, capacity). */
+hs_status hs_pool_record_ptr(hs_pool_t pool, int32_t req, int32_t layer,
+                             int64_t pos, void **host_ptr, size_t *rec_bytes);
+/* Host pointer of page `page` of unit (req, layer): records
+ * [page * page_tokens, (page + 1) * page_tokens) lie contiguously from it.
+ * HS_E_RANGE for a bad req/layer or a page not allocated. */
+hs_status hs_pool_page_ptr(hs_pool_t pool, int32_t req, int32_t layer,
+                           int64_t page, void **host_ptr);
 /* Current length (records valid for selection) of unit (req, layer).
  * Synchronous (reads the device table). */
 hs_status hs_pool_length(hs_pool_t pool, int32_t req, int32_t layer,
                          int64_t *len);
 /* Declare that records [0, len) of the unit were written through
- * hs_pool_unit_ptr (prefill). Synchronous. HS_E_RANGE if len > capacity. */
+ * hs_pool_record_ptr / hs_pool_page_ptr (prefill). Synchronous. HS_E_RANGE if
+ * len > the allocated capacity. */
 hs_status hs_pool_set_length(hs_pool_t pool, int32_t req, int32_t layer,
                              int64_t len);
 /* Write-through append (HiSparse summary, section 3, arrow 5): write n
@@ -153,7 +183,8 @@ hs_status hs_pool_set_length(hs_pool_t pool, int32_t req, int32_t layer,
  * records only through later misses.
  * src_on_device = 0: src is host memory; copied synchronously.
  * src_on_device = 1: src is device memory; enqueued on stream (capture-safe).
- * Errors: HS_E_RANGE (pos > length or pos + n > capacity), HS_E_INVAL. */
+ * Errors: HS_E_RANGE (pos > length or pos + n > the allocated capacity:
+ * reserve first), HS_E_INVAL. */
 hs_status hs_pool_append(hs_pool_t pool, int32_t req, int32_t layer,
                          int64_t pos, int64_t n, const void *src,
                          int32_t src_on_device, void *stream);

@@ -97,7 +97,8 @@ def small_workload(kind, dtype, B, k, ctx, steps, n_new, R=1, L=1, seed=0, Hkv=1
 
 
 def compare_run(w, steps, traces=None, attn_every=1, rows_every=1, attn_units=None,
-                graph=False, fill="touched", fused=False, share_mode="prefetch", grow=None):
+                graph=False, fill="touched", fused=False, share_mode="prefetch", grow=None,
+                **session_kw):
     """Run a GPU session step by step beside the oracle and compare slots,
     miss counts, state, resident rows and attention outputs of every unit.
     The oracle resolves every layer on its own, also where the session runs
@@ -107,7 +108,8 @@ def compare_run(w, steps, traces=None, attn_every=1, rows_every=1, attn_units=No
     from tiered_kv_cache_hs_amd.session import Session
     import torch
 
-    sess = Session(w, steps, fill=fill, traces=traces, fused=fused, share_mode=share_mode)
+    sess = Session(w, steps, fill=fill, traces=traces, fused=fused, share_mode=share_mode,
+                   **session_kw)
     orc = OracleRun(w, sess.traces, steps)
     if graph:
         sess.capture()

@@ -57,6 +57,14 @@ def test_null_and_shape_checks_without_device():
     assert L.hs_pool_create(None, None) == H.HS_E_INVAL
     assert L.hs_batch_create(None, 0, None) == H.HS_E_INVAL
     assert L.hs_resolve(None, None, 1, None, None, None) == H.HS_E_INVAL
+    # descriptor checks that come before any allocation
+    d = H.PoolDesc(1, 1, H.HS_KV_MHA, H.HS_F32, 1, 8, 0, 0, (ctypes.c_int64 * 1)(100), None, 48)
+    assert L.hs_pool_create(ctypes.byref(d), ctypes.byref(ctypes.c_void_p())) == H.HS_E_INVAL
+    d = H.PoolDesc(1, 1, H.HS_KV_MHA, H.HS_F32, 1, 8, 0, 0, (ctypes.c_int64 * 1)(100),
+                   (ctypes.c_int64 * 1)(99), 0)  # maximum below the capacity
+    assert L.hs_pool_create(ctypes.byref(d), ctypes.byref(ctypes.c_void_p())) == H.HS_E_INVAL
+    assert L.hs_pool_reserve(None, 0, 10) == H.HS_E_INVAL
+    assert L.hs_pool_record_ptr(None, 0, 0, 0, None, None) == H.HS_E_INVAL
     assert L.hs_buffer_bytes(None, 4) == 0
     assert L.hs_buffer_shared_bytes(None, 4) == 0
     assert L.hs_buffer_create_shared(None, 0, None, 0, None) == H.HS_E_INVAL

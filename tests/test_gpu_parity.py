@@ -340,3 +340,69 @@ def test_buffer_growth_mid_run(kind, graph):
         new_B = [511, 300]
     compare_run(w, w.steps, fill="full", graph=graph, grow=(3, new_B))
 
+
+
+@pytest.mark.parametrize("kind,fused,page", [("mha", False, 64), ("mha", True, 16),
+                                             ("latent", False, 128), ("latent", True, 32)])
+def test_paged_pool_small_pages(kind, fused, page):
+    """Pool pages much smaller than the context: every host read (resolve's
+    fetch, the gather, the attention kernels' fetch) goes through the page
+    table across many pages."""
+    if kind == "mha":
+        w = _small("mha", I.BF16, 600, 200, 3000, 5, 50, R=2, L=2, seed=410, Hkv=2, D=128, Hq=8)
+    else:
+        w = _small("latent", I.BF16, 300, 197, 3000, 5, 40, R=2, seed=411, Hq=32)
+    compare_run(w, 5, fill="full", fused=fused, page_tokens=page)
+
+
+@pytest.mark.parametrize("graph", [False, True])
+def test_paged_pool_grows_with_appends(graph):
+    """Write-through appends past the prefill's pages: pages are reserved on
+    demand (eagerly step by step, or all before capture), appends cross page
+    boundaries, and new tokens come back as misses through the page table."""
+    w = _small("mha", I.F32, 48, 24, 200, 40, 6, R=2, L=2, seed=420)
+    w.append = True
+    compare_run(w, 40, fill="full", graph=graph, page_tokens=16, reserve="prefill")
+
+
+def test_pool_pages_and_reserve():
+    pool = H.hs_pool_create(2, 3, H.HS_KV_MHA, H.HS_F32, [40, 10], n_kv_heads=1, head_dim=8,
+                            max_tokens=[100, 10], page_tokens=16)
+    try:
+        assert H.hs_pool_capacity(pool, 0) == (48, 100, 16)
+        assert H.hs_pool_capacity(pool, 1) == (16, 10, 16)  # whole pages
+        rec = H.hs_pool_record_bytes(pool)
+        a = H.hs_pool_record_ptr(pool, 0, 2, 17)
+        b = H.hs_pool_record_ptr(pool, 0, 2, 18)
+        assert b - a == rec
+        assert H.hs_pool_page_ptr(pool, 0, 2, 1) == H.hs_pool_record_ptr(pool, 0, 2, 16)
+        with pytest.raises(H.HsError):
+            H.hs_pool_record_ptr(pool, 0, 0, 48)
+        with pytest.raises(H.HsError):
+            H.hs_pool_page_ptr(pool, 0, 0, 3)
+        with pytest.raises(H.HsError):
+            H.hs_pool_reserve(pool, 0, 101)
+        with pytest.raises(H.HsError):  # append past the allocated pages
+            H.hs_pool_append(pool, 0, 0, 0, np.zeros((49, rec), np.uint8))
+        # existing records stay where they are when pages are added
+        arr = np.arange(40 * rec, dtype=np.uint32).astype(np.uint8).reshape(40, rec)
+        H.hs_pool_append(pool, 0, 1, 0, arr)
+        H.hs_pool_reserve(pool, 0, 90)
+        assert H.hs_pool_capacity(pool, 0)[0] == 96
+        assert H.hs_pool_record_ptr(pool, 0, 2, 17) == a
+        more = (np.arange(50 * rec, dtype=np.uint32) * 3).astype(np.uint8).reshape(50, rec)
+        H.hs_pool_append(pool, 0, 1, 40, more)  # crosses pages 2 -> 5
+        assert H.hs_pool_length(pool, 0, 1) == 90
+        got = H.pool_read(pool, 0, 1, np.arange(90))
+        assert np.array_equal(got[:40], arr) and np.array_equal(got[40:], more)
+        # device-side append across a page boundary
+        src = torch.from_numpy((np.arange(5 * rec) % 199).astype(np.uint8)).to("cuda")
+        H.hs_pool_append(pool, 0, 0, 0, np.zeros((14, rec), np.uint8))
+        H.hs_pool_append(pool, 0, 0, 14, src, n=5)
+        torch.cuda.synchronize()
+        assert np.array_equal(H.pool_read(pool, 0, 0, np.arange(14, 19)).reshape(-1),
+                              src.cpu().numpy())
+        assert H.hs_pool_length(pool, 0, 0) == 19
+    finally:
+        torch.cuda.synchronize()
+        H.hs_pool_destroy(pool)

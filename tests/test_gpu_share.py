@@ -195,7 +195,7 @@ def test_prefetch_past_a_members_length_sets_range_error():
     try:
         rec = H.hs_pool_record_bytes(pool)
         for l in range(2):
-            arr = H.hs_pool_unit_array(pool, 0, l)
+            (first, arr), = H.pool_pages(pool, 0, l)
             arr[:] = (np.arange(ctx * rec, dtype=np.int64).reshape(ctx, rec) * (l + 3) % 251).astype(np.uint8)
         H.hs_pool_set_length(pool, 0, 0, 64)
         H.hs_pool_set_length(pool, 0, 1, 20)
@@ -216,7 +216,7 @@ def test_prefetch_past_a_members_length_sets_range_error():
         pos, _, _, err = H.hs_buffer_state_get(sh, B)
         assert err & H.HS_ERR_RANGE
         rows = m1[: B * rec].cpu().numpy().reshape(B, rec)
-        src = H.hs_pool_unit_array(pool, 0, 1)
+        src = H.pool_read(pool, 0, 1, np.arange(ctx))
         s = slots.cpu().numpy()[0]
         for i, p in enumerate(sel):
             if p < 20:

@@ -234,8 +234,10 @@ __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
     if (!valid || from_host != host_ok) bad = true;
     // base and row index selected without branches, then one 32 x 32 -> 64
     // multiply-add
-    const HS_GLOBAL uint8_t *base = host_ok ? d.pool : d.rows;
-    const uint32_t row = host_ok ? (uint32_t)rf.src : (valid && !from_host ? (uint32_t)rf.slot : 0u);
+    const HS_GLOBAL uint8_t *base =
+        host_ok ? (const HS_GLOBAL uint8_t *)d.pages[(uint32_t)rf.src >> d.page_shift] : d.rows;
+    const uint32_t row = host_ok ? ((uint32_t)rf.src & ((1u << d.page_shift) - 1u))
+                                 : (valid && !from_host ? (uint32_t)rf.slot : 0u);
     const HS_GLOBAL uint8_t *p = base + (uint64_t)row * LAT_REC + 16 * q4;
 #pragma unroll
     for (int jj = 0; jj < 5; ++jj) {

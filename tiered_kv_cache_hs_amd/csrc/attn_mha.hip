@@ -168,7 +168,7 @@ __global__ __launch_bounds__(MHA_THREADS) void hs_k_attn_mha(
       }
       slot_of[uu] = slot;
       const bool host = FETCH && src[uu] >= 0;
-      const HS_GLOBAL uint8_t *row = host ? d.pool + (size_t)src[uu] * rec_bytes
+      const HS_GLOBAL uint8_t *row = host ? pool_record(d, (uint32_t)src[uu], rec_bytes)
                                           : d.rows + (size_t)slot * rec_bytes;
       if (valid[uu] && host) {
         kw[uu] = __builtin_nontemporal_load((const HS_GLOBAL v4u *)(row + koff));

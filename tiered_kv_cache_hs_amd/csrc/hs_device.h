@@ -17,10 +17,14 @@ struct __attribute__((aligned(128))) UnitDesc {
   int32_t *fsrc;        // last resolve, per selection index: its position if it
                         // was a miss (fetched from the pool), else -1; B entries
   uint32_t *ctl;        // [CTL_CLOCK], [CTL_ERR], [CTL_FETCH]
-  const uint8_t *pool;  // device-visible address of the unit's host records
+  const uint64_t *pages;  // the unit's pool page table (device memory): entry i
+                          // is the device-visible address of records
+                          // [i << page_shift, (i + 1) << page_shift) in host memory
   const int64_t *len;   // the unit's pool length (device memory)
   int32_t B;
-  int32_t pad[5];
+  int32_t page_shift;   // log2 of the records per pool page
+  int32_t n_pages;      // entries of the page table
+  int32_t pad[3];
 };
 
 #define HS_GLOBAL __attribute__((address_space(1)))
@@ -41,9 +45,11 @@ struct UnitG {
   HS_GLOBAL int2v *work;
   HS_GLOBAL int32_t *fsrc;
   HS_GLOBAL uint32_t *ctl;
-  HS_GLOBAL const uint8_t *pool;
+  HS_GLOBAL const uint64_t *pages;
   HS_GLOBAL const int64_t *len;
   int32_t B;
+  int32_t page_shift;
+  int32_t n_pages;
 };
 
 __device__ __forceinline__ UnitG unit_g(const UnitDesc &d) {
@@ -54,10 +60,20 @@ __device__ __forceinline__ UnitG unit_g(const UnitDesc &d) {
   g.work = (HS_GLOBAL int2v *)d.work;
   g.fsrc = (HS_GLOBAL int32_t *)d.fsrc;
   g.ctl = (HS_GLOBAL uint32_t *)d.ctl;
-  g.pool = (HS_GLOBAL const uint8_t *)d.pool;
+  g.pages = (HS_GLOBAL const uint64_t *)d.pages;
   g.len = (HS_GLOBAL const int64_t *)d.len;
   g.B = d.B;
+  g.page_shift = d.page_shift;
+  g.n_pages = d.n_pages;
   return g;
+}
+
+// Host record p of a unit, through its pool page table (global address space).
+__device__ __forceinline__ const HS_GLOBAL uint8_t *pool_record(const UnitG &d, uint32_t p,
+                                                               size_t rec_bytes) {
+  const uint64_t page = d.pages[p >> d.page_shift];
+  const uint32_t in_page = p & ((1u << d.page_shift) - 1u);
+  return (const HS_GLOBAL uint8_t *)page + (size_t)in_page * rec_bytes;
 }
 
 // A generic pointer taken as a global one (kernel arguments and workspace).
@@ -134,8 +150,11 @@ hipError_t launch_prefetch(const UnitDesc *d_units, int n, int rec_bytes, int wo
                            hipStream_t stream);
 hipError_t launch_regather(const UnitDesc *d_unit, int B, int rec_bytes,
                            hipStream_t stream);
-hipError_t launch_append(uint8_t *dst_dev, const uint8_t *src, int64_t bytes,
-                         int64_t *d_len, int64_t new_len, hipStream_t stream);
+// Records [pos, pos + n) of a unit's pool (page table d_pages) from device
+// memory, then its length raised to new_len.
+hipError_t launch_append(const uint64_t *d_pages, int page_shift, int64_t pos, int64_t n,
+                         int rec_bytes, const uint8_t *src, int64_t *d_len, int64_t new_len,
+                         hipStream_t stream);
 
 struct AttnMhaArgs {
   const UnitDesc *units;

@@ -138,9 +138,9 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
     int k, int hlog2, int rec16, int32_t *__restrict__ slots_all,
     int32_t *__restrict__ miss_all) {
   // LDS: region A holds the hash table (keys, values: 2H ints) during build
-  // and probe, then the miss, victim and miss-position lists (3k ints);
-  // region B holds slot_of[k].
-  extern __shared__ int lds[];
+  // and probe, then the miss and victim lists (k ints each) and the missed
+  // records' host addresses (k 64-bit words); region B holds slot_of[k].
+  extern __shared__ __attribute__((aligned(16))) int lds[];
   constexpr int NW = NT / 64;
   __shared__ int scan_buf[2][RES_MAX_WAVES];
   __shared__ uint32_t hist[3][256];
@@ -152,8 +152,8 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   int *hval = lds + H;
   int *miss_list = lds;
   int *victim_list = lds + k;
-  int *miss_pos = lds + 2 * k;
-  const int regionA = (2 * H > 3 * k) ? 2 * H : 3 * k;
+  uint64_t *miss_addr = (uint64_t *)(lds + 2 * k);
+  const int regionA = (2 * H > 4 * k) ? 2 * H : 4 * k;
   int *slot_of = lds + regionA;
 
   const int u = blockIdx.x;
@@ -178,6 +178,14 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   }
   int32_t sp[SPT];
   uint32_t st[SPT];
+  // the pool page of each selected position (clamped into the page table: an
+  // invalid position is a data error found below, its entry never used)
+  uint64_t tpage[KPT];
+  if (GATHER) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j)
+      tpage[j] = d.pages[min((uint32_t)tk[j] >> d.page_shift, (uint32_t)d.n_pages - 1u)];
+  }
   if (s0 + SPT <= B && (SPT % 4) == 0) {
     // the whole run is in range: 16-byte loads, no per-slot branches
 #pragma unroll
@@ -371,7 +379,9 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     if (miss_here[j]) {
-      miss_pos[mrank] = tk[j];
+      if (GATHER)
+        miss_addr[mrank] = tpage[j] + (uint64_t)((uint32_t)tk[j] & ((1u << d.page_shift) - 1u)) *
+                                          (uint64_t)(rec16 * 16);
       miss_list[mrank++] = k0 + j;
     }
   }
@@ -384,15 +394,14 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   const int g_total = m * rec16;
   v4u gv[GB];
   if (GATHER) {
-    lds_barrier();  // miss_pos complete
+    lds_barrier();  // miss_addr complete
 #pragma unroll
     for (int b = 0; b < GB; ++b) {
       const int c = tid + NT * b;
       if (c < g_total) {
         const int j = c / rec16;
         const int off = c - j * rec16;
-        gv[b] = __builtin_nontemporal_load(
-            (const HS_GLOBAL v4u *)(d.pool + (size_t)miss_pos[j] * rec) + off);
+        gv[b] = __builtin_nontemporal_load((const HS_GLOBAL v4u *)miss_addr[j] + off);
       }
     }
   }
@@ -525,8 +534,7 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
           if (c < g_total) {
             const int j = c / rec16;
             const int off = c - j * rec16;
-            gv[b] = __builtin_nontemporal_load(
-                (const HS_GLOBAL v4u *)(d.pool + (size_t)miss_pos[j] * rec) + off);
+            gv[b] = __builtin_nontemporal_load((const HS_GLOBAL v4u *)miss_addr[j] + off);
           }
         }
       }
@@ -596,7 +604,7 @@ __global__ __launch_bounds__(GATHER_THREADS) void hs_k_gather(
         const int2v w = d.work[r];
         if (w.y >= 0 && (int64_t)w.y < len) {
           const HS_GLOBAL v4u *src =
-              (const HS_GLOBAL v4u *)(d.pool + (size_t)w.y * rec) + off;
+              (const HS_GLOBAL v4u *)pool_record(d, (uint32_t)w.y, rec) + off;
           v[uu] = __builtin_nontemporal_load(src);
           dst[uu] = (HS_GLOBAL v4u *)(d.rows + (size_t)w.x * rec) + off;
         } else {
@@ -623,7 +631,7 @@ __global__ __launch_bounds__(256) void hs_k_regather(const UnitDesc *__restrict_
     const int off = (int)(c - (int64_t)s * rec16);
     const int32_t p = d.pos[s];
     if (p < 0) continue;
-    const HS_GLOBAL v4u *src = (const HS_GLOBAL v4u *)(d.pool + (size_t)p * rec) + off;
+    const HS_GLOBAL v4u *src = (const HS_GLOBAL v4u *)pool_record(d, (uint32_t)p, rec) + off;
     ((HS_GLOBAL v4u *)(d.rows + (size_t)s * rec))[off] = __builtin_nontemporal_load(src);
   }
 }
@@ -638,14 +646,22 @@ __global__ void hs_k_buffer_init(int32_t *pos, uint32_t *stamp, int32_t *fsrc, u
   if (ctl && blockIdx.x == 0 && threadIdx.x < CTL_WORDS) ctl[threadIdx.x] = 0u;
 }
 
-// Write-through append from device memory into the mapped host pool, then
-// extend the unit's length.
-__global__ __launch_bounds__(256) void hs_k_append(uint8_t *dst, const uint8_t *src,
-                                                   int64_t n16, int64_t *len,
+// Write-through append from device memory into the mapped host pool (records
+// [pos, pos + n), each through the unit's page table), then extend the unit's
+// length.
+__global__ __launch_bounds__(256) void hs_k_append(const uint64_t *pages, int page_shift,
+                                                   int64_t pos, int64_t n16, int rec16,
+                                                   const uint8_t *src, int64_t *len,
                                                    int64_t new_len) {
+  const uint64_t mask = (1ull << page_shift) - 1ull;
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n16;
-       c += (int64_t)gridDim.x * blockDim.x)
-    ((v4u *)dst)[c] = ((const v4u *)src)[c];
+       c += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = c / rec16;
+    const int64_t off = c - r * rec16;
+    const uint64_t p = (uint64_t)(pos + r);
+    v4u *dst = (v4u *)(pages[p >> page_shift] + (p & mask) * (uint64_t)rec16 * 16u) + off;
+    *dst = ((const v4u *)src)[c];
+  }
   if (blockIdx.x == 0 && threadIdx.x == 0 && *len < new_len) *len = new_len;
 }
 
@@ -685,7 +701,7 @@ hipError_t launch_select_k(const UnitDesc *d_units, int n, const int32_t *d_topk
 int hash_log2(int k) {
   int h = 2;
   while ((1 << h) < 4 * k) ++h;
-  const size_t region_a = (size_t)(2 * (1 << h) > 3 * k ? 2 * (1 << h) : 3 * k);
+  const size_t region_a = (size_t)(2 * (1 << h) > 4 * k ? 2 * (1 << h) : 4 * k);
   if ((region_a + k) * sizeof(int) > (128u << 10)) --h;
   return h;
 }
@@ -694,7 +710,7 @@ int hash_log2(int k) {
 
 size_t resolve_lds_bytes(int k) {
   const int H = 1 << hash_log2(k);
-  const int regionA = (2 * H > 3 * k) ? 2 * H : 3 * k;
+  const int regionA = (2 * H > 4 * k) ? 2 * H : 4 * k;
   return (size_t)(regionA + k) * sizeof(int);
 }
 
@@ -767,14 +783,15 @@ hipError_t launch_buffer_init(int32_t *pos, uint32_t *stamp, int32_t *fsrc, uint
   return hipGetLastError();
 }
 
-hipError_t launch_append(uint8_t *dst_dev, const uint8_t *src, int64_t bytes, int64_t *d_len,
-                         int64_t new_len, hipStream_t stream) {
-  const int64_t n16 = bytes / 16;
+hipError_t launch_append(const uint64_t *d_pages, int page_shift, int64_t pos, int64_t n,
+                         int rec_bytes, const uint8_t *src, int64_t *d_len, int64_t new_len,
+                         hipStream_t stream) {
+  const int64_t n16 = n * (rec_bytes / 16);
   int64_t blocks = (n16 + 255) / 256;
   if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(hs_k_append, dim3((unsigned)blocks), dim3(256), 0, stream, dst_dev, src,
-                     n16, d_len, new_len);
+  hipLaunchKernelGGL(hs_k_append, dim3((unsigned)blocks), dim3(256), 0, stream, d_pages,
+                     page_shift, pos, n16, rec_bytes / 16, src, d_len, new_len);
   return hipGetLastError();
 }
 

@@ -92,12 +92,19 @@ void trace_end(hipStream_t stream) {
 struct hs_pool_s {
   int32_t R = 0, L = 0, kind = 0, dtype = 0, Hkv = 0, D = 0, Dl = 0, Dr = 0;
   size_t rec = 0;
-  std::vector<int64_t> cap;
-  std::vector<uint8_t *> host;  // per request: L * cap[r] records
-  std::vector<uint8_t *> dev;   // device-visible address of host[r]
-  int64_t *d_len = nullptr;     // [R * L]
-  std::vector<int64_t> shadow;  // lengths as of the calls made so far
+  int32_t page_shift = 0;      // records per page: 1 << page_shift
+  std::vector<int64_t> cap;    // records allocated per request (whole pages)
+  std::vector<int64_t> max_cap;
+  // per request, per page: one pinned allocation holding that page of every
+  // layer, layer-major (layer l's records at l * page_records * rec)
+  std::vector<std::vector<uint8_t *>> host, dev;
+  std::vector<int64_t> max_pages;   // page-table entries per unit of request r
+  std::vector<size_t> table_off;    // entry offset of request r's tables
+  uint64_t *d_pages = nullptr;      // device page tables of every unit
+  int64_t *d_len = nullptr;         // [R * L]
+  std::vector<int64_t> shadow;      // lengths as of the calls made so far
   int device = 0;
+  int64_t page_records() const { return (int64_t)1 << page_shift; }
 };
 
 struct hs_buffer_s {
@@ -155,6 +162,70 @@ hs_status hs_get_tuning(hs_tuning *t) {
 
 // ------------------------------------------------------------------- pool
 
+static hs_status check_unit(hs_pool_t p, int32_t req, int32_t layer) {
+  if (!p) return fail(HS_E_INVAL, "null pool");
+  if (req < 0 || req >= p->R || layer < 0 || layer >= p->L)
+    return fail(HS_E_RANGE, "unit (%d, %d) outside %d x %d", req, layer, p->R, p->L);
+  return HS_OK;
+}
+
+// Page table of unit (req, layer) in device memory.
+static uint64_t *unit_table(hs_pool_t p, int32_t req, int32_t layer) {
+  return p->d_pages + p->table_off[req] + (size_t)layer * p->max_pages[req];
+}
+
+static size_t page_bytes(hs_pool_t p) { return (size_t)p->page_records() * p->rec; }
+
+// Host address of record pos of unit (req, layer); pos < cap[req].
+static uint8_t *record_host(hs_pool_t p, int32_t req, int32_t layer, int64_t pos) {
+  const int64_t pg = pos >> p->page_shift, in = pos & (p->page_records() - 1);
+  return p->host[req][pg] + ((size_t)layer * p->page_records() + (size_t)in) * p->rec;
+}
+
+// Allocates request req's pages up to `records` (whole pages) and enters
+// them in its units' device page tables. Synchronous.
+static hs_status reserve_pages(hs_pool_t p, int32_t req, int64_t records) {
+  const int64_t need = (records + p->page_records() - 1) >> p->page_shift;
+  const int64_t have = (int64_t)p->host[req].size();
+  if (need <= have) return HS_OK;
+  const size_t pb = page_bytes(p);
+  std::vector<uint64_t> entries((size_t)(need - have) * p->L);
+  for (int64_t g = have; g < need; ++g) {
+    void *h = nullptr;
+    hipError_t e = hipHostMalloc(&h, pb * p->L, hipHostMallocMapped | hipHostMallocCoherent);
+    if (e != hipSuccess || !h)
+      return fail(HS_E_NOMEM, "hipHostMalloc(%zu bytes) for request %d: %s", pb * p->L, req,
+                  hipGetErrorString(e));
+    void *dp = nullptr;
+    e = hipHostGetDevicePointer(&dp, h, 0);
+    if (e != hipSuccess) {
+      (void)hipHostFree(h);
+      return hip_fail(e, "hipHostGetDevicePointer");
+    }
+    p->host[req].push_back((uint8_t *)h);
+    p->dev[req].push_back((uint8_t *)dp);
+  }
+  // entries of each layer's new pages (pages not yet allocated stay 0 and are
+  // never read: positions are checked against lengths <= the capacity)
+  for (int l = 0; l < p->L; ++l) {
+    for (int64_t g = have; g < need; ++g)
+      entries[(size_t)(g - have)] = (uint64_t)(uintptr_t)(p->dev[req][g] + (size_t)l * pb);
+    HS_HIP(hipMemcpy(unit_table(p, req, l) + have, entries.data(),
+                     sizeof(uint64_t) * (size_t)(need - have), hipMemcpyHostToDevice));
+  }
+  p->cap[req] = need << p->page_shift;
+  return HS_OK;
+}
+
+static void pool_free(hs_pool_t p) {
+  for (auto &v : p->host)
+    for (auto h : v)
+      if (h) (void)hipHostFree(h);
+  if (p->d_pages) (void)hipFree(p->d_pages);
+  if (p->d_len) (void)hipFree(p->d_len);
+  delete p;
+}
+
 hs_status hs_pool_create(const hs_pool_desc *d, hs_pool_t *out) {
   if (!d || !out) return fail(HS_E_INVAL, "null argument");
   *out = nullptr;
@@ -173,9 +244,24 @@ hs_status hs_pool_create(const hs_pool_desc *d, hs_pool_t *out) {
     return fail(HS_E_INVAL, "bad kind");
   }
   if (rec % 16) return fail(HS_E_INVAL, "record bytes %zu not a multiple of 16", rec);
-  for (int r = 0; r < d->n_requests; ++r)
-    if (d->capacity_tokens[r] < 1 || d->capacity_tokens[r] > 0x7FFFFFFF)
-      return fail(HS_E_INVAL, "capacity of request %d outside [1, 2^31)", r);
+  int64_t largest = 1;
+  for (int r = 0; r < d->n_requests; ++r) {
+    const int64_t c = d->capacity_tokens[r];
+    const int64_t m = d->max_tokens ? d->max_tokens[r] : c;
+    if (c < 1 || m < c || m > 0x7FFFFFFF)
+      return fail(HS_E_INVAL, "request %d: need 1 <= capacity <= max < 2^31", r);
+    largest = std::max(largest, m);
+  }
+  int shift = 0;
+  if (d->page_tokens > 0) {
+    if (d->page_tokens & (d->page_tokens - 1))
+      return fail(HS_E_INVAL, "page_tokens %d is not a power of two", d->page_tokens);
+    while ((1 << shift) < d->page_tokens) ++shift;
+  } else {  // 65536 records, or the largest request rounded up to a power of two
+    while (shift < 16 && ((int64_t)1 << shift) < largest) ++shift;
+  }
+  if ((size_t)1 << shift > ((size_t)1 << 40) / rec)
+    return fail(HS_E_INVAL, "page of %lld records too large", (long long)1 << shift);
 
   hs_pool_s *p = new (std::nothrow) hs_pool_s;
   if (!p) return fail(HS_E_NOMEM, "pool handle");
@@ -188,45 +274,37 @@ hs_status hs_pool_create(const hs_pool_desc *d, hs_pool_t *out) {
   p->Dl = d->latent_dim;
   p->Dr = d->rope_dim;
   p->rec = rec;
-  p->cap.assign(d->capacity_tokens, d->capacity_tokens + d->n_requests);
-  p->host.assign(p->R, nullptr);
-  p->dev.assign(p->R, nullptr);
+  p->page_shift = shift;
+  p->cap.assign(p->R, 0);
+  p->max_cap.resize(p->R);
+  p->host.resize(p->R);
+  p->dev.resize(p->R);
+  p->max_pages.resize(p->R);
+  p->table_off.resize(p->R);
   p->shadow.assign((size_t)p->R * p->L, 0);
   (void)hipGetDevice(&p->device);
-  auto cleanup = [p]() {
-    for (auto h : p->host)
-      if (h) (void)hipHostFree(h);
-    if (p->d_len) (void)hipFree(p->d_len);
-    delete p;
-  };
+  size_t entries = 0;
   for (int r = 0; r < p->R; ++r) {
-    const size_t bytes = (size_t)p->L * (size_t)p->cap[r] * rec;
-    void *h = nullptr;
-    hipError_t e = hipHostMalloc(&h, bytes, hipHostMallocMapped | hipHostMallocCoherent);
-    if (e != hipSuccess || !h) {
-      cleanup();
-      return fail(HS_E_NOMEM, "hipHostMalloc(%zu bytes) for request %d: %s", bytes, r,
-                  hipGetErrorString(e));
-    }
-    p->host[r] = (uint8_t *)h;
-    void *dp = nullptr;
-    e = hipHostGetDevicePointer(&dp, h, 0);
-    if (e != hipSuccess) {
-      cleanup();
-      return hip_fail(e, "hipHostGetDevicePointer");
-    }
-    p->dev[r] = (uint8_t *)dp;
+    p->max_cap[r] = d->max_tokens ? d->max_tokens[r] : d->capacity_tokens[r];
+    p->max_pages[r] = (p->max_cap[r] + p->page_records() - 1) >> shift;
+    p->table_off[r] = entries;
+    entries += (size_t)p->L * p->max_pages[r];
   }
-  hipError_t e = hipMalloc(&p->d_len, sizeof(int64_t) * p->R * p->L);
-  if (e != hipSuccess) {
-    cleanup();
-    return fail(HS_E_NOMEM, "hipMalloc lengths: %s", hipGetErrorString(e));
-  }
-  e = hipMemset(p->d_len, 0, sizeof(int64_t) * p->R * p->L);
+  hipError_t e = hipMalloc(&p->d_pages, sizeof(uint64_t) * entries);
+  if (e == hipSuccess) e = hipMemset(p->d_pages, 0, sizeof(uint64_t) * entries);
+  if (e == hipSuccess) e = hipMalloc(&p->d_len, sizeof(int64_t) * p->R * p->L);
+  if (e == hipSuccess) e = hipMemset(p->d_len, 0, sizeof(int64_t) * p->R * p->L);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
-    cleanup();
-    return hip_fail(e, "hipMemset lengths");
+    pool_free(p);
+    return fail(HS_E_NOMEM, "pool tables: %s", hipGetErrorString(e));
+  }
+  for (int r = 0; r < p->R; ++r) {
+    hs_status s = reserve_pages(p, r, d->capacity_tokens[r]);
+    if (s) {
+      pool_free(p);
+      return s;
+    }
   }
   *out = p;
   return HS_OK;
@@ -234,10 +312,7 @@ hs_status hs_pool_create(const hs_pool_desc *d, hs_pool_t *out) {
 
 hs_status hs_pool_destroy(hs_pool_t p) {
   if (!p) return fail(HS_E_INVAL, "null pool");
-  for (auto h : p->host)
-    if (h) (void)hipHostFree(h);
-  if (p->d_len) (void)hipFree(p->d_len);
-  delete p;
+  pool_free(p);
   return HS_OK;
 }
 
@@ -247,23 +322,44 @@ hs_status hs_pool_record_bytes(hs_pool_t p, size_t *rec) {
   return HS_OK;
 }
 
-static hs_status check_unit(hs_pool_t p, int32_t req, int32_t layer) {
-  if (!p) return fail(HS_E_INVAL, "null pool");
-  if (req < 0 || req >= p->R || layer < 0 || layer >= p->L)
-    return fail(HS_E_RANGE, "unit (%d, %d) outside %d x %d", req, layer, p->R, p->L);
+hs_status hs_pool_capacity(hs_pool_t p, int32_t req, int64_t *capacity, int64_t *max_tokens,
+                           int64_t *page_tokens) {
+  hs_status s = check_unit(p, req, 0);
+  if (s) return s;
+  if (capacity) *capacity = p->cap[req];
+  if (max_tokens) *max_tokens = p->max_cap[req];
+  if (page_tokens) *page_tokens = p->page_records();
   return HS_OK;
 }
 
-static size_t unit_offset(hs_pool_t p, int32_t req, int32_t layer) {
-  return (size_t)layer * (size_t)p->cap[req] * p->rec;
+hs_status hs_pool_reserve(hs_pool_t p, int32_t req, int64_t records) {
+  hs_status s = check_unit(p, req, 0);
+  if (s) return s;
+  if (records < 0 || records > p->max_cap[req])
+    return fail(HS_E_RANGE, "request %d: %lld records above its maximum %lld", req,
+                (long long)records, (long long)p->max_cap[req]);
+  return reserve_pages(p, req, records);
 }
 
-hs_status hs_pool_unit_ptr(hs_pool_t p, int32_t req, int32_t layer, void **host_ptr,
-                           int64_t *capacity) {
+hs_status hs_pool_record_ptr(hs_pool_t p, int32_t req, int32_t layer, int64_t pos,
+                             void **host_ptr, size_t *rec_bytes) {
   hs_status s = check_unit(p, req, layer);
   if (s) return s;
-  if (host_ptr) *host_ptr = p->host[req] + unit_offset(p, req, layer);
-  if (capacity) *capacity = p->cap[req];
+  if (pos < 0 || pos >= p->cap[req])
+    return fail(HS_E_RANGE, "position %lld outside the capacity %lld", (long long)pos,
+                (long long)p->cap[req]);
+  if (host_ptr) *host_ptr = record_host(p, req, layer, pos);
+  if (rec_bytes) *rec_bytes = p->rec;
+  return HS_OK;
+}
+
+hs_status hs_pool_page_ptr(hs_pool_t p, int32_t req, int32_t layer, int64_t page,
+                           void **host_ptr) {
+  hs_status s = check_unit(p, req, layer);
+  if (s) return s;
+  if (page < 0 || page >= (int64_t)p->host[req].size())
+    return fail(HS_E_RANGE, "page %lld of request %d not allocated", (long long)page, req);
+  if (host_ptr) *host_ptr = record_host(p, req, layer, page << p->page_shift);
   return HS_OK;
 }
 
@@ -302,17 +398,22 @@ hs_status hs_pool_append(hs_pool_t p, int32_t req, int32_t layer, int64_t pos, i
                 (long long)pos, (long long)(pos + n), (long long)p->shadow[ui],
                 (long long)p->cap[req]);
   if (n == 0) return HS_OK;
-  const size_t off = unit_offset(p, req, layer) + (size_t)pos * p->rec;
   const int64_t new_len = std::max(p->shadow[ui], pos + n);
   if (src_on_device) {
     if ((uintptr_t)src % 16) return fail(HS_E_INVAL, "device source must be 16-byte aligned");
-    hipError_t e = hs::launch_append(p->dev[req] + off, (const uint8_t *)src,
-                                     (int64_t)n * (int64_t)p->rec, p->d_len + ui, new_len,
+    hipError_t e = hs::launch_append(unit_table(p, req, layer), p->page_shift, pos, n,
+                                     (int)p->rec, (const uint8_t *)src, p->d_len + ui, new_len,
                                      S(stream));
     if (e != hipSuccess) return hip_fail(e, "append launch");
   } else {
     HS_HIP(hipStreamSynchronize(S(stream)));
-    memcpy(p->host[req] + off, src, (size_t)n * p->rec);
+    const uint8_t *in = (const uint8_t *)src;
+    for (int64_t q = pos; q < pos + n;) {  // one run per page
+      const int64_t end = std::min(pos + n, ((q >> p->page_shift) + 1) << p->page_shift);
+      memcpy(record_host(p, req, layer, q), in, (size_t)(end - q) * p->rec);
+      in += (size_t)(end - q) * p->rec;
+      q = end;
+    }
     HS_HIP(hipMemcpyAsync(p->d_len + ui, &new_len, sizeof(int64_t), hipMemcpyHostToDevice,
                           S(stream)));
     HS_HIP(hipStreamSynchronize(S(stream)));
@@ -354,9 +455,11 @@ hs_status hs_buffer_create(hs_pool_t p, int32_t req, int32_t layer, int32_t B, v
   d.work = (int2 *)(b->mem + lay.work);
   d.fsrc = (int32_t *)(b->mem + lay.fsrc);
   d.ctl = (uint32_t *)(b->mem + lay.ctl);
-  d.pool = p->dev[req] + unit_offset(p, req, layer);
+  d.pages = unit_table(p, req, layer);
   d.len = p->d_len + (size_t)req * p->L + layer;
   d.B = B;
+  d.page_shift = p->page_shift;
+  d.n_pages = (int32_t)p->max_pages[req];
   hipError_t e = hipMalloc(&b->d_desc, sizeof(UnitDesc));
   if (e == hipSuccess)
     e = hipMemcpy(b->d_desc, &b->desc, sizeof(UnitDesc), hipMemcpyHostToDevice);
@@ -398,7 +501,7 @@ hs_status hs_buffer_create_shared(hs_buffer_t base, int32_t layer, void *d_mem, 
   b->base = base->base ? base->base : base;
   b->desc = base->desc;
   b->desc.rows = b->mem;
-  b->desc.pool = p->dev[b->req] + unit_offset(p, b->req, layer);
+  b->desc.pages = unit_table(p, b->req, layer);
   b->desc.len = p->d_len + (size_t)b->req * p->L + layer;
   hipError_t e = hipMalloc(&b->d_desc, sizeof(UnitDesc));
   if (e == hipSuccess)

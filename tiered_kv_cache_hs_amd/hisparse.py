@@ -40,7 +40,8 @@ HS_MAX_B = 16384
 # every symbol include/hisparse.h declares
 EXPORTS = (
     "hs_status_str", "hs_last_error", "hs_set_tuning", "hs_get_tuning",
-    "hs_pool_create", "hs_pool_destroy", "hs_pool_record_bytes", "hs_pool_unit_ptr",
+    "hs_pool_create", "hs_pool_destroy", "hs_pool_record_bytes", "hs_pool_capacity",
+    "hs_pool_reserve", "hs_pool_record_ptr", "hs_pool_page_ptr",
     "hs_pool_length", "hs_pool_set_length", "hs_pool_append",
     "hs_buffer_bytes", "hs_buffer_create", "hs_buffer_destroy", "hs_buffer_grow",
     "hs_buffer_reset",
@@ -65,6 +66,8 @@ class PoolDesc(ctypes.Structure):
         ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
         ("latent_dim", ctypes.c_int32), ("rope_dim", ctypes.c_int32),
         ("capacity_tokens", ctypes.POINTER(ctypes.c_int64)),
+        ("max_tokens", ctypes.POINTER(ctypes.c_int64)),
+        ("page_tokens", ctypes.c_int32),
     ]
 
 
@@ -102,7 +105,10 @@ def lib():
         "hs_pool_create": ([P(PoolDesc), P(vp)], i32),
         "hs_pool_destroy": ([vp], i32),
         "hs_pool_record_bytes": ([vp, P(sz)], i32),
-        "hs_pool_unit_ptr": ([vp, i32, i32, P(vp), P(i64)], i32),
+        "hs_pool_capacity": ([vp, i32, P(i64), P(i64), P(i64)], i32),
+        "hs_pool_reserve": ([vp, i32, i64], i32),
+        "hs_pool_record_ptr": ([vp, i32, i32, i64, P(vp), P(sz)], i32),
+        "hs_pool_page_ptr": ([vp, i32, i32, i64, P(vp)], i32),
         "hs_pool_length": ([vp, i32, i32, P(i64)], i32),
         "hs_pool_set_length": ([vp, i32, i32, i64], i32),
         "hs_pool_append": ([vp, i32, i32, i64, i64, vp, i32, vp], i32),
@@ -182,10 +188,12 @@ def hs_get_tuning() -> dict:
 
 def hs_pool_create(n_requests: int, n_layers: int, kind: int, dtype: int,
                    capacity_tokens: Sequence[int], n_kv_heads: int = 0, head_dim: int = 0,
-                   latent_dim: int = 0, rope_dim: int = 0) -> int:
+                   latent_dim: int = 0, rope_dim: int = 0,
+                   max_tokens: Optional[Sequence[int]] = None, page_tokens: int = 0) -> int:
     cap = (ctypes.c_int64 * len(capacity_tokens))(*[int(c) for c in capacity_tokens])
+    mx = None if max_tokens is None else (ctypes.c_int64 * len(max_tokens))(*[int(c) for c in max_tokens])
     d = PoolDesc(n_requests, n_layers, kind, dtype, n_kv_heads, head_dim, latent_dim, rope_dim,
-                 cap)
+                 cap, mx, int(page_tokens))
     out = ctypes.c_void_p()
     _check(lib().hs_pool_create(ctypes.byref(d), ctypes.byref(out)))
     return out.value
@@ -201,19 +209,54 @@ def hs_pool_record_bytes(pool: int) -> int:
     return v.value
 
 
-def hs_pool_unit_ptr(pool: int, req: int, layer: int):
-    """(host address, capacity) of unit (req, layer)'s record array."""
-    p, cap = ctypes.c_void_p(), ctypes.c_int64()
-    _check(lib().hs_pool_unit_ptr(pool, req, layer, ctypes.byref(p), ctypes.byref(cap)))
-    return p.value, cap.value
+def hs_pool_capacity(pool: int, req: int):
+    """(records allocated, maximum, records per page) of request req."""
+    c, m, pg = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().hs_pool_capacity(pool, req, ctypes.byref(c), ctypes.byref(m), ctypes.byref(pg)))
+    return c.value, m.value, pg.value
 
 
-def hs_pool_unit_array(pool: int, req: int, layer: int) -> np.ndarray:
-    """numpy view (uint8 [capacity][rec_bytes]) of a unit's host records."""
-    addr, cap = hs_pool_unit_ptr(pool, req, layer)
+def hs_pool_reserve(pool: int, req: int, records: int) -> None:
+    _check(lib().hs_pool_reserve(pool, req, int(records)))
+
+
+def hs_pool_record_ptr(pool: int, req: int, layer: int, pos: int) -> int:
+    """Host address of record pos of unit (req, layer)."""
+    p, rec = ctypes.c_void_p(), ctypes.c_size_t()
+    _check(lib().hs_pool_record_ptr(pool, req, layer, int(pos), ctypes.byref(p), ctypes.byref(rec)))
+    return p.value
+
+
+def hs_pool_page_ptr(pool: int, req: int, layer: int, page: int) -> int:
+    """Host address of page `page` of unit (req, layer)."""
+    p = ctypes.c_void_p()
+    _check(lib().hs_pool_page_ptr(pool, req, layer, int(page), ctypes.byref(p)))
+    return p.value
+
+
+def pool_pages(pool: int, req: int, layer: int):
+    """[(first position, numpy uint8 view [page_tokens][rec_bytes])] of the
+    unit's allocated pages (host memory, writable)."""
+    cap, _, pg = hs_pool_capacity(pool, req)
     rec = hs_pool_record_bytes(pool)
-    buf = (ctypes.c_uint8 * (cap * rec)).from_address(addr)
-    return np.frombuffer(buf, dtype=np.uint8).reshape(cap, rec)
+    out = []
+    for i in range(cap // pg):
+        addr = hs_pool_page_ptr(pool, req, layer, i)
+        buf = (ctypes.c_uint8 * (pg * rec)).from_address(addr)
+        out.append((i * pg, np.frombuffer(buf, dtype=np.uint8).reshape(pg, rec)))
+    return out
+
+
+def pool_read(pool: int, req: int, layer: int, positions: Sequence[int]) -> np.ndarray:
+    """Copies of the unit's host records at `positions`: uint8 [n][rec_bytes]."""
+    _, _, pg = hs_pool_capacity(pool, req)
+    pages = dict(pool_pages(pool, req, layer))
+    pos = np.asarray(positions, dtype=np.int64)
+    out = np.empty((pos.size, hs_pool_record_bytes(pool)), dtype=np.uint8)
+    for j, p in enumerate(pos):
+        first = int(p) // pg * pg
+        out[j] = pages[first][int(p) - first]
+    return out
 
 
 def hs_pool_length(pool: int, req: int, layer: int) -> int:

@@ -38,7 +38,8 @@ from . import inputs as I
 class Session:
     def __init__(self, w: I.Workload, steps: Optional[int] = None, device: str = "cuda",
                  fill: str = "touched", traces: Optional[np.ndarray] = None,
-                 fused: bool = False, share_mode: str = "prefetch"):
+                 fused: bool = False, share_mode: str = "prefetch", page_tokens: int = 0,
+                 reserve: str = "all"):
         self.w = w
         self.fused = fused  # hs_resolve_attn instead of hs_resolve + hs_sparse_attn
         if share_mode not in ("prefetch", "serial", "none"):
@@ -54,22 +55,31 @@ class Session:
         lm = self.traces.reshape(self.steps, R, L, k).transpose(0, 2, 1, 3)
         self.topk = torch.from_numpy(np.ascontiguousarray(lm)).to(self.device)  # [T][L][R][k]
 
+        # reserve "all": every record the steps will append is allocated up
+        # front; "prefill": only the prefill, the rest with hs_pool_reserve
         kind = H.HS_KV_MHA if w.kind == "mha" else H.HS_KV_LATENT
+        cap_all = [w.capacity(r, self.steps) for r in range(R)]
         self.pool = H.hs_pool_create(R, L, kind, w.dtype,
-                                     [w.capacity(r, self.steps) for r in range(R)],
+                                     cap_all if reserve == "all" else list(w.ctx),
                                      n_kv_heads=w.n_kv_heads, head_dim=w.head_dim,
-                                     latent_dim=w.latent_dim, rope_dim=w.rope_dim)
+                                     latent_dim=w.latent_dim, rope_dim=w.rope_dim,
+                                     max_tokens=cap_all, page_tokens=page_tokens)
         self.rec = H.hs_pool_record_bytes(self.pool)
+        self.reserve = reserve
         for r in range(R):
             for l in range(L):
-                addr, _ = H.hs_pool_unit_ptr(self.pool, r, l)
+                u = r * L + l
                 if fill == "full":
-                    I.fill_records(w, addr, r, l, p0=0, p1=w.ctx[r])
+                    want = np.arange(w.ctx[r], dtype=np.int64)
                 else:  # only the positions the trace ever selects are written
-                    u = r * L + l
-                    pos = np.unique(self.traces[:, u, :].astype(np.int64))
-                    pos = pos[(pos >= 0) & (pos < w.ctx[r])]
-                    I.fill_records(w, addr, r, l, positions=pos)
+                    want = np.unique(self.traces[:, u, :].astype(np.int64))
+                    want = want[(want >= 0) & (want < w.ctx[r])]
+                for first, page in H.pool_pages(self.pool, r, l):
+                    sel = want[(want >= first) & (want < first + page.shape[0])]
+                    if sel.size:  # record p of this page lies at base + p * rec
+                        base = page.ctypes.data - first * self.rec
+                        assert base > 0
+                        I.fill_records(w, base, r, l, positions=sel)
                 H.hs_pool_set_length(self.pool, r, l, w.ctx[r])
 
         # device buffers, one allocation per unit; in a grouped session the
@@ -178,6 +188,10 @@ class Session:
                 H.hs_pool_append(self.pool, r, l, w.ctx[r] + t, self.app[t, l, r], n=1)
 
     def step(self, t: int) -> None:
+        if self.reserve == "prefill" and self.app is not None:
+            # pool pages on demand: room for this step's appended records
+            for r in range(self.R):
+                H.hs_pool_reserve(self.pool, r, self.w.ctx[r] + t + 1)
         if self.grouped:
             for g in range(0, self.L, self.w.share):
                 self.group(t, g)
@@ -188,6 +202,9 @@ class Session:
     def capture(self, steps: Optional[range] = None) -> None:
         """Capture one graph per step (arguments of step t baked in)."""
         steps = range(self.steps) if steps is None else steps
+        if self.reserve == "prefill" and self.app is not None:
+            for r in range(self.R):  # pages cannot be allocated inside a graph
+                H.hs_pool_reserve(self.pool, r, self.w.capacity(r, self.steps))
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         self.graphs = [None] * self.steps
