@@ -18,7 +18,6 @@ from __future__ import annotations
 
 import argparse
 import json
-import os
 import sys
 import time
 
@@ -55,45 +54,6 @@ def parse():
                          "overlapping attention; serial = the same on one stream; none = every "
                          "layer resolves on its own")
     return ap.parse_args()
-
-
-# sources whose hash keys the stored counter readings: a reading is used only
-# while the kernel it was taken from is unchanged
-KERNEL_SOURCES = {  # the kernel's file, the shared header, and the launch planner
-    "hs_k_resolve": ["resolve.hip", "hs_device.h", "runtime.hip"],
-    "hs_k_gather": ["resolve.hip", "hs_device.h", "runtime.hip"],
-    "hs_k_attn_latent": ["attn_latent.hip", "hs_device.h", "runtime.hip"],
-    "hs_k_attn_mha": ["attn_mha.hip", "hs_device.h", "runtime.hip"],
-}
-PMC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "pmc_traffic.json")
-
-
-def kernel_sources_sha1(kernel):
-    import hashlib
-    h = hashlib.sha1()
-    csrc = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tiered_kv_cache_hs_amd", "csrc")
-    for f in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
-
-
-def stored_traffic(workload, kernel):
-    """HBM bytes per dispatch of `kernel` on `workload` from the committed
-    rocprofv3 counter readings (FETCH_SIZE + WRITE_SIZE, each scaled by its
-    reading for a copy of known size), or None when there is no reading or
-    the kernel's sources changed since it was taken."""
-    try:
-        with open(PMC_FILE) as fh:
-            pmc = json.load(fh)
-    except (OSError, ValueError):
-        return None
-    for e in pmc.get("entries", []):
-        if e.get("workload") == workload and e.get("kernel") == kernel:
-            if e.get("sources_sha1") != kernel_sources_sha1(kernel):
-                return None
-            return int(e["traffic_bytes"])
-    return None
 
 
 def copy_calibration():
@@ -282,6 +242,7 @@ def main():
     else:
         dominant = roof_host if fetch_us >= attn_us else roof_attn
 
+    from tiered_kv_cache_hs_amd.profiling import stored_traffic
     dominant["traffic"] = stored_traffic(w.name, dominant["kernel"])
     roof_attn["traffic"] = stored_traffic(w.name, attn_kernel)
     result = {

@@ -1,0 +1,56 @@
+"""The profiler report (CPU): counter scaling and the stored-traffic lookup,
+on hand-made rocprofv3 CSV files."""
+import csv
+import json
+import os
+
+from tiered_kv_cache_hs_amd import inputs as I
+from tiered_kv_cache_hs_amd import profiling as P
+
+
+def _write(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_report_scales_counters_by_the_copy_reading(tmp_path):
+    out = str(tmp_path)
+    # the 256 MiB copy reads as 128 MiB of FETCH_SIZE and 256 MiB of WRITE_SIZE
+    _write(f"{out}/pmc_copy_FETCH_SIZE/h/run_counter_collection.csv", ["Kernel_Name", "Counter_Value"],
+           [["__amd_rocclr_copyBuffer", 131072.0]])
+    _write(f"{out}/pmc_copy_WRITE_SIZE/h/run_counter_collection.csv", ["Kernel_Name", "Counter_Value"],
+           [["__amd_rocclr_copyBuffer", 262144.0]])
+    for c, vals in (("FETCH_SIZE", [100.0, 300.0, 200.0]), ("WRITE_SIZE", [10.0, 10.0, 40.0])):
+        _write(f"{out}/pmc_wl1_{c}/h/run_counter_collection.csv", ["Kernel_Name", "Counter_Value"],
+               [["hs_k_attn_mha<float, 64, 1, true>(...)", v] for v in vals])
+    _write(f"{out}/trace_wl1/h/bench_kernel_stats.csv",
+           ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"],
+           [["hs_k_attn_mha<float, 64, 1, true>", 64, 11000, 10000, 12000, 50.0]])
+    _write(f"{out}/trace_wl1/h/bench_kernel_trace.csv",
+           ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+           [["hs_k_attn_mha<float, 64, 1, true>", 1000 * i, 1000 * i + 5000 + (9000 if i % 32 == 0 else 0)]
+            for i in range(64)])
+    P.report([1], out)
+    doc = json.load(open(f"{out}/report/pmc_traffic.json"))
+    assert doc["scale"]["FETCH_SIZE"] == 2.0 and doc["scale"]["WRITE_SIZE"] == 1.0
+    (e,) = doc["entries"]
+    assert e["kernel"] == "hs_k_attn_mha" and e["workload"] == I.workload(1).name
+    assert e["traffic_bytes"] == int((200.0 * 2.0 + 10.0) * 1024)
+    assert e["sources_sha1"] == P.kernel_sources_sha1("hs_k_attn_mha")
+    md = open(f"{out}/report/hs_kernels_{I.workload(1).name}.md").read()
+    assert "| hs_k_attn_mha<float, 64, 1, true> | 62 | 5.00 | 5.00 |" in md  # cold steps dropped
+
+
+def test_stored_traffic_only_while_sources_match(tmp_path, monkeypatch):
+    f = tmp_path / "pmc.json"
+    good = P.kernel_sources_sha1("hs_k_resolve")
+    f.write_text(json.dumps({"entries": [
+        {"workload": "w", "kernel": "hs_k_resolve", "sources_sha1": good, "traffic_bytes": 123},
+        {"workload": "w", "kernel": "hs_k_gather", "sources_sha1": "0" * 40, "traffic_bytes": 9}]}))
+    monkeypatch.setattr(P, "PMC_FILE", str(f))
+    assert P.stored_traffic("w", "hs_k_resolve") == 123
+    assert P.stored_traffic("w", "hs_k_gather") is None
+    assert P.stored_traffic("other", "hs_k_resolve") is None

@@ -1,0 +1,297 @@
+"""Kernel-time and HBM-traffic measurement of the benchmark with rocprofv3.
+
+    python -m tiered_kv_cache_hs_amd.profiling run --workloads 3 4 5 6 7 --out DIR
+
+runs, for each workload, from the repository root:
+
+  * one kernel-trace pass:
+      rocprofv3 --kernel-trace --stats --output-format csv -d DIR/trace_wlN -o bench --
+          python3 -u bench.py --workload N --steps 24 --warmup 8 --no-cpu
+  * two counter passes (one counter each, as the profiler collects in one pass):
+      rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR/pmc_wlN_FETCH_SIZE -o run --
+          python3 -u bench.py --workload N --steps 3 --warmup 1 --no-cpu
+      (then WRITE_SIZE)
+  * once, the same two counters over a 256 MiB device-to-device copy
+    (bench.py --copy-calibration), which scale the counters to bytes;
+
+each as a child process under a time limit (this process never touches the
+GPU), and writes into DIR/report: one summary per workload
+(hs_kernels_<workload>.md: the profiler's per-kernel statistics, warm
+averages, the benchmark's own event-timed kernel durations from the same run
+and the HBM bytes per dispatch) and pmc_traffic.json, the per-dispatch HBM
+bytes that bench.py reports as `traffic`, keyed by the SHA-1 of each kernel's
+sources so a reading is used only while the kernel is unchanged.
+
+    python -m tiered_kv_cache_hs_amd.profiling report --workloads ... --out DIR
+
+rebuilds the report from existing run directories.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import statistics
+import subprocess
+import sys
+import time
+from typing import Dict, List, Optional
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "tiered_kv_cache_hs_amd", "csrc")
+PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
+COUNTERS = ("FETCH_SIZE", "WRITE_SIZE")
+COPY_BYTES = 256 << 20
+
+# the kernel's file, the shared header and the launch planner: a stored
+# reading is used only while all three are unchanged
+KERNEL_SOURCES = {
+    "hs_k_resolve": ["resolve.hip", "hs_device.h", "runtime.hip"],
+    "hs_k_gather": ["resolve.hip", "hs_device.h", "runtime.hip"],
+    "hs_k_attn_latent": ["attn_latent.hip", "hs_device.h", "runtime.hip"],
+    "hs_k_attn_mha": ["attn_mha.hip", "hs_device.h", "runtime.hip"],
+    "hs_k_combine": ["attn_mha.hip", "hs_device.h", "runtime.hip"],
+}
+
+
+def kernel_sources_sha1(kernel: str) -> str:
+    h = hashlib.sha1()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str, kernel: str) -> Optional[int]:
+    """HBM bytes per dispatch of `kernel` on `workload` from the committed
+    counter readings, or None when there is none or the kernel's sources
+    changed since it was taken."""
+    try:
+        with open(PMC_FILE) as fh:
+            pmc = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    for e in pmc.get("entries", []):
+        if e.get("workload") == workload and e.get("kernel") == kernel:
+            if e.get("sources_sha1") != kernel_sources_sha1(kernel):
+                return None
+            return int(e["traffic_bytes"])
+    return None
+
+
+def short_name(name: str) -> str:
+    m = re.search(r"(hs_k_\w+)", name)
+    return m.group(1) if m else name.split("(")[0][:48]
+
+
+def _one(pattern: str) -> Optional[str]:
+    f = sorted(glob.glob(pattern, recursive=True))
+    return f[0] if f else None
+
+
+# ------------------------------------------------------------------ runs
+
+def _child(cmd: List[str], log: str, limit: int) -> int:
+    """Run cmd from the repository root under a time limit (killed with
+    SIGKILL when it runs over); output to log."""
+    print(f"[profiling] {' '.join(cmd)}", flush=True)
+    t0 = time.time()
+    with open(log, "w") as fh:
+        try:
+            p = subprocess.run(["timeout", "-s", "KILL", str(limit)] + cmd, cwd=ROOT, stdout=fh,
+                               stderr=subprocess.STDOUT, timeout=limit + 30)
+            rc = p.returncode
+        except subprocess.TimeoutExpired:
+            rc = 124
+    print(f"[profiling]   rc={rc} in {time.time() - t0:.1f}s", flush=True)
+    return rc
+
+
+def bench_cmd(wl: Optional[int], steps: int, warmup: int) -> List[str]:
+    if wl is None:
+        return ["python3", "-u", "bench.py", "--copy-calibration"]
+    return ["python3", "-u", "bench.py", "--workload", str(wl), "--steps", str(steps),
+            "--warmup", str(warmup), "--no-cpu"]
+
+
+def trace_cmd(out: str, wl: int) -> List[str]:
+    return ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
+            os.path.join(out, f"trace_wl{wl}"), "-o", "bench", "--"] + bench_cmd(wl, 24, 8)
+
+
+def pmc_cmd(out: str, tag: str, counter: str, wl: Optional[int]) -> List[str]:
+    return ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d",
+            os.path.join(out, f"pmc_{tag}_{counter}"), "-o", "run", "--"] + bench_cmd(wl, 3, 1)
+
+
+def run_all(workloads: List[int], out: str, limit: int) -> None:
+    os.makedirs(out, exist_ok=True)
+    env_ok = os.environ.get("TMPDIR")
+    if not env_ok:
+        os.environ["TMPDIR"] = "/tmp"
+    for c in COUNTERS:
+        if _child(pmc_cmd(out, "copy", c, None), os.path.join(out, f"pmc_copy_{c}.log"), limit):
+            raise SystemExit("copy calibration pass failed")
+    for wl in workloads:
+        if _child(trace_cmd(out, wl), os.path.join(out, f"trace_wl{wl}.log"), limit):
+            raise SystemExit(f"trace pass of workload {wl} failed")
+        for c in COUNTERS:
+            if _child(pmc_cmd(out, f"wl{wl}", c, wl), os.path.join(out, f"pmc_wl{wl}_{c}.log"),
+                      limit):
+                raise SystemExit(f"{c} pass of workload {wl} failed")
+
+
+# ---------------------------------------------------------------- report
+
+def read_counter(d: str) -> Dict[str, List[float]]:
+    f = _one(os.path.join(d, "**", "*counter_collection.csv"))
+    per: Dict[str, List[float]] = {}
+    if f:
+        for r in csv.DictReader(open(f)):
+            per.setdefault(short_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return per
+
+
+def read_stats(d: str):
+    f = _one(os.path.join(d, "**", "*kernel_stats.csv"))
+    rows = []
+    if f:
+        for r in csv.DictReader(open(f)):
+            rows.append(r)
+    return rows
+
+
+def read_trace(d: str) -> Dict[str, List[float]]:
+    f = _one(os.path.join(d, "**", "*kernel_trace.csv"))
+    per: Dict[str, List[float]] = {}
+    if f:
+        for r in csv.DictReader(open(f)):
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+            per.setdefault(r["Kernel_Name"], []).append(dur)
+    return per
+
+
+def bench_line(log: str) -> Optional[dict]:
+    try:
+        for line in open(log):
+            line = line.strip()
+            if line.startswith("{") and '"metric"' in line:
+                return json.loads(line)
+    except OSError:
+        pass
+    return None
+
+
+def report(workloads: List[int], out: str) -> None:
+    from . import inputs as I
+
+    rep = os.path.join(out, "report")
+    os.makedirs(rep, exist_ok=True)
+    copy = {c: read_counter(os.path.join(out, f"pmc_copy_{c}")) for c in COUNTERS}
+    copy_kib = {}
+    for c in COUNTERS:
+        vals = [v for k, vs in copy[c].items() if "copy" in k.lower() for v in vs]
+        if not vals:
+            raise SystemExit(f"no copy-kernel reading of {c}")
+        copy_kib[c] = statistics.median(vals)
+    scale = {c: COPY_BYTES / (copy_kib[c] * 1024.0) for c in COUNTERS}
+    entries = []
+    for wl in workloads:
+        w = I.workload(wl)
+        pmc = {c: read_counter(os.path.join(out, f"pmc_wl{wl}_{c}")) for c in COUNTERS}
+        stats = read_stats(os.path.join(out, f"trace_wl{wl}"))
+        trace = read_trace(os.path.join(out, f"trace_wl{wl}"))
+        bl = bench_line(os.path.join(out, f"trace_wl{wl}.log"))
+        lines = [f"# Kernel time and HBM traffic: workload {w.name}", "",
+                 f"{w.n_requests} requests x {w.n_layers} layers, context "
+                 f"{w.ctx[0] if len(set(w.ctx)) == 1 else 'per request'}, {w.kind} records of "
+                 f"{w.rec_bytes} bytes, {w.n_q_heads} query heads, k = {w.k}, B = "
+                 f"{w.B[0] if len(set(w.B)) == 1 else 'per request'}"
+                 + (f", layer groups of {w.share}" if w.share > 1 else "") + ".",
+                 "", "Commands (repository root, one MI355X; written by "
+                 "`python -m tiered_kv_cache_hs_amd.profiling run`):", "",
+                 "    " + " ".join(trace_cmd("DIR", wl)),
+                 "    " + " ".join(pmc_cmd("DIR", f"wl{wl}", "FETCH_SIZE", wl)),
+                 "    " + " ".join(pmc_cmd("DIR", f"wl{wl}", "WRITE_SIZE", wl)),
+                 "    " + " ".join(pmc_cmd("DIR", "copy", "FETCH_SIZE", None)) + "   (and WRITE_SIZE)",
+                 "", "The trace run replays 32 decode steps from their hipGraphs (8 warm-up + 24 "
+                 "timed), then runs them again eagerly with HIP events around every kernel, so "
+                 "each kernel has two dispatches per layer and step.", "",
+                 "## rocprofv3 --stats (all dispatches)", "",
+                 "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
+        for r in stats:
+            if not r["Name"].startswith("hs_k"):
+                continue
+            lines.append(f"| {r['Name'][:60]} | {r['Calls']} | {float(r['AverageNs']) / 1000:.2f} | "
+                         f"{float(r['MinNs']) / 1000:.2f} | {float(r['MaxNs']) / 1000:.2f} | "
+                         f"{float(r['Percentage']):.2f} |")
+        lines += ["", "## Warm averages (kernel trace, End - Start; each pass's cold first step dropped)",
+                  "", "| kernel | dispatches | avg us (warm) | median us (warm) |", "|---|---|---|---|"]
+        steps_per_pass = 32
+        for name, durs in trace.items():
+            if not name.startswith("hs_k") or "buffer_init" in name:
+                continue
+            per_step = max(1, len(durs) // (2 * steps_per_pass))
+            half = len(durs) // 2
+            warm = durs[per_step:half] + durs[half + per_step:]
+            if warm:
+                lines.append(f"| {name[:60]} | {len(warm)} | {statistics.mean(warm):.2f} | "
+                             f"{statistics.median(warm):.2f} |")
+        if bl:
+            lines += ["", "## The benchmark's own timing in the same run", "",
+                      f"Event-timed kernel durations per launch (us): {json.dumps(bl.get('kernels_us'))}; "
+                      f"value {bl.get('value')} us/layer under the profiler; path "
+                      f"{bl.get('config', {}).get('path')}. The event pair adds 2-4 us to a "
+                      "launch, and in a layer group the prefetch runs beside attention, so "
+                      "event times there include the overlap."]
+        lines += ["", "## HBM bytes per dispatch (FETCH_SIZE, WRITE_SIZE; separate passes)", "",
+                  f"Scale from the 256 MiB copy: FETCH_SIZE reads {copy_kib['FETCH_SIZE']:.1f} KiB "
+                  f"(x{scale['FETCH_SIZE']:.4f}), WRITE_SIZE {copy_kib['WRITE_SIZE']:.1f} KiB "
+                  f"(x{scale['WRITE_SIZE']:.4f}).", "",
+                  "| kernel | dispatches | FETCH_SIZE KiB (median) | WRITE_SIZE KiB (median) | "
+                  "HBM bytes per dispatch |", "|---|---|---|---|---|"]
+        for k in sorted(set(pmc["FETCH_SIZE"]) & set(pmc["WRITE_SIZE"])):
+            if k not in KERNEL_SOURCES:
+                continue
+            f = statistics.median(pmc["FETCH_SIZE"][k])
+            wv = statistics.median(pmc["WRITE_SIZE"][k])
+            b = int(round((f * scale["FETCH_SIZE"] + wv * scale["WRITE_SIZE"]) * 1024))
+            lines.append(f"| {k} | {len(pmc['FETCH_SIZE'][k])} | {f:.1f} | {wv:.1f} | {b:,} |")
+            entries.append({"workload": w.name, "kernel": k, "sources_sha1": kernel_sources_sha1(k),
+                            "dispatches": len(pmc["FETCH_SIZE"][k]), "fetch_kib_median": round(f, 1),
+                            "write_kib_median": round(wv, 1), "traffic_bytes": b})
+        with open(os.path.join(rep, f"hs_kernels_{w.name}.md"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+    doc = {"about": "HBM bytes per dispatch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
+                    "(separate passes), median over the dispatches of `python3 -u bench.py "
+                    "--workload N --steps 3 --warmup 1 --no-cpu`; each counter scaled by its "
+                    "reading for a 256 MiB device-to-device copy (`python3 -u bench.py "
+                    "--copy-calibration`). Written by `python -m tiered_kv_cache_hs_amd.profiling`.",
+           "scale": {"FETCH_SIZE": round(scale["FETCH_SIZE"], 4),
+                     "WRITE_SIZE": round(scale["WRITE_SIZE"], 4),
+                     "copy_fetch_kib": round(copy_kib["FETCH_SIZE"], 1),
+                     "copy_write_kib": round(copy_kib["WRITE_SIZE"], 1), "copy_bytes": COPY_BYTES},
+           "entries": entries}
+    with open(os.path.join(rep, "pmc_traffic.json"), "w") as fh:
+        json.dump(doc, fh, indent=1)
+    print(f"[profiling] report in {rep}", flush=True)
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("action", choices=("run", "report"))
+    ap.add_argument("--workloads", type=int, nargs="+", default=[3, 4, 5, 6, 7])
+    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    ap.add_argument("--limit", type=int, default=240, help="seconds per profiler pass")
+    a = ap.parse_args()
+    if a.action == "run":
+        run_all(a.workloads, a.out, a.limit)
+    report(a.workloads, a.out)
+
+
+if __name__ == "__main__":
+    main()
