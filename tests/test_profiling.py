@@ -26,12 +26,13 @@ def test_report_scales_counters_by_the_copy_reading(tmp_path):
     for c, vals in (("FETCH_SIZE", [100.0, 300.0, 200.0]), ("WRITE_SIZE", [10.0, 10.0, 40.0])):
         _write(f"{out}/pmc_wl1_{c}/h/run_counter_collection.csv", ["Kernel_Name", "Counter_Value"],
                [["hs_k_attn_mha<float, 64, 1, true>(...)", v] for v in vals])
+    kname = "void hs::(anonymous namespace)::hs_k_attn_mha<float, 64, 1, true>(hs::UnitDesc const*)"
     _write(f"{out}/trace_wl1/h/bench_kernel_stats.csv",
            ["Name", "Calls", "AverageNs", "MinNs", "MaxNs", "Percentage"],
-           [["hs_k_attn_mha<float, 64, 1, true>", 64, 11000, 10000, 12000, 50.0]])
+           [[kname, 64, 11000, 10000, 12000, 50.0]])
     _write(f"{out}/trace_wl1/h/bench_kernel_trace.csv",
-           ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
-           [["hs_k_attn_mha<float, 64, 1, true>", 1000 * i, 1000 * i + 5000 + (9000 if i % 32 == 0 else 0)]
+           ["Kernel_Name", "Start_Timestamp", "End_Timestamp", "VGPR_Count"],
+           [[kname, 1000 * i, 1000 * i + 5000 + (9000 if i % 32 == 0 else 0), 96]
             for i in range(64)])
     P.report([1], out)
     doc = json.load(open(f"{out}/report/pmc_traffic.json"))
@@ -42,6 +43,8 @@ def test_report_scales_counters_by_the_copy_reading(tmp_path):
     assert e["sources_sha1"] == P.kernel_sources_sha1("hs_k_attn_mha")
     md = open(f"{out}/report/hs_kernels_{I.workload(1).name}.md").read()
     assert "| hs_k_attn_mha<float, 64, 1, true> | 62 | 5.00 | 5.00 |" in md  # cold steps dropped
+    assert "| hs_k_attn_mha<float, 64, 1, true> | 64 | 11.00 | 10.00 | 12.00 | 50.00 |" in md
+    assert "| hs_k_attn_mha<float, 64, 1, true> | 96 |" in md
 
 
 def test_stored_traffic_only_while_sources_match(tmp_path, monkeypatch):

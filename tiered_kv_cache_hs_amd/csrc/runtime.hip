@@ -753,17 +753,32 @@ static hs_status plan_attn(hs_batch_t b, int32_t Hq, int32_t k, AttnPlan *pl) {
       return fail(HS_E_INVAL, "latent attention needs bf16, 512 + 64");
     if (Hq != 16 && Hq != 32 && Hq != 64)
       return fail(HS_E_INVAL, "latent attention supports 16, 32 or 64 query heads");
-    // a workgroup covers hpw heads of a (unit, split). Few units need many
-    // splits to fill the device, and every split writes a full (m, l, acc)
-    // partial per head: below 32 units, splitting the heads instead (16 per
-    // workgroup; the rows are then read once per head group, mostly from L2)
-    // keeps the partials four times smaller.
-    int hpw = g_tuning.latent_heads_per_wg > 0 ? g_tuning.latent_heads_per_wg
-                                               : (b->n >= 32 ? Hq : 16);
+    // A workgroup covers hpw heads of a (unit, split). Every split writes a
+    // full fp32 (m, l, acc[512]) partial per head, about 2 KB, as much as
+    // two 1152-byte rows: splits shorter than 256 rows write more partial
+    // bytes than they read. So splits stay at 256 rows or more, and the
+    // heads are split instead when that leaves the device short of
+    // workgroups: the largest hpw of 64, 32, 16 (dividing Hq) whose grid
+    // reaches 256 workgroups, else 16 (the rows are then read once per head
+    // group, mostly from L2).
+    const int n8 = (b->n + 7) / 8 * 8;
+    const int split_cap = std::max(1, k / 256);
+    int hpw = g_tuning.latent_heads_per_wg;
+    if (hpw <= 0) {
+      hpw = 16;
+      for (int h : {64, 32}) {
+        if (h > Hq || Hq % h) continue;
+        const int bw = n8 * (Hq / h);
+        if (bw * std::min(split_cap, (256 + bw - 1) / bw) >= 256) {
+          hpw = h;
+          break;
+        }
+      }
+    }
     if (hpw > Hq || Hq % hpw) hpw = Hq;
     pl->hpw = hpw;
-    base = (b->n + 7) / 8 * 8 * (Hq / hpw);
-    min_chunk = 64;
+    base = n8 * (Hq / hpw);
+    min_chunk = 256;
     target = 256;
     pl->dv = p->Dl;
   }

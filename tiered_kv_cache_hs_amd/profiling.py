@@ -88,6 +88,12 @@ def short_name(name: str) -> str:
     return m.group(1) if m else name.split("(")[0][:48]
 
 
+def display_name(name: str) -> str:
+    """hs_k_name<template arguments> out of a demangled kernel name."""
+    m = re.search(r"(hs_k_\w+(<[^>]*>)?)", name)
+    return m.group(1) if m else name.split("(")[0][:60]
+
+
 def _one(pattern: str) -> Optional[str]:
     f = sorted(glob.glob(pattern, recursive=True))
     return f[0] if f else None
@@ -165,14 +171,21 @@ def read_stats(d: str):
     return rows
 
 
-def read_trace(d: str) -> Dict[str, List[float]]:
+def read_trace(d: str):
+    """({kernel: [durations us]}, {kernel: resource columns of its dispatches})."""
     f = _one(os.path.join(d, "**", "*kernel_trace.csv"))
     per: Dict[str, List[float]] = {}
+    res: Dict[str, dict] = {}
     if f:
         for r in csv.DictReader(open(f)):
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
-            per.setdefault(r["Kernel_Name"], []).append(dur)
-    return per
+            n = display_name(r["Kernel_Name"])
+            per.setdefault(n, []).append(dur)
+            res.setdefault(n, {k: r.get(k) for k in ("VGPR_Count", "Accum_VGPR_Count",
+                                                      "SGPR_Count", "LDS_Block_Size",
+                                                      "Scratch_Size", "Workgroup_Size_X",
+                                                      "Grid_Size_X")})
+    return per, res
 
 
 def bench_line(log: str) -> Optional[dict]:
@@ -191,6 +204,7 @@ def report(workloads: List[int], out: str) -> None:
 
     rep = os.path.join(out, "report")
     os.makedirs(rep, exist_ok=True)
+    rel = os.path.relpath(out, ROOT)
     copy = {c: read_counter(os.path.join(out, f"pmc_copy_{c}")) for c in COUNTERS}
     copy_kib = {}
     for c in COUNTERS:
@@ -204,7 +218,7 @@ def report(workloads: List[int], out: str) -> None:
         w = I.workload(wl)
         pmc = {c: read_counter(os.path.join(out, f"pmc_wl{wl}_{c}")) for c in COUNTERS}
         stats = read_stats(os.path.join(out, f"trace_wl{wl}"))
-        trace = read_trace(os.path.join(out, f"trace_wl{wl}"))
+        trace, res = read_trace(os.path.join(out, f"trace_wl{wl}"))
         bl = bench_line(os.path.join(out, f"trace_wl{wl}.log"))
         lines = [f"# Kernel time and HBM traffic: workload {w.name}", "",
                  f"{w.n_requests} requests x {w.n_layers} layers, context "
@@ -212,21 +226,23 @@ def report(workloads: List[int], out: str) -> None:
                  f"{w.rec_bytes} bytes, {w.n_q_heads} query heads, k = {w.k}, B = "
                  f"{w.B[0] if len(set(w.B)) == 1 else 'per request'}"
                  + (f", layer groups of {w.share}" if w.share > 1 else "") + ".",
-                 "", "Commands (repository root, one MI355X; written by "
-                 "`python -m tiered_kv_cache_hs_amd.profiling run`):", "",
-                 "    " + " ".join(trace_cmd("DIR", wl)),
-                 "    " + " ".join(pmc_cmd("DIR", f"wl{wl}", "FETCH_SIZE", wl)),
-                 "    " + " ".join(pmc_cmd("DIR", f"wl{wl}", "WRITE_SIZE", wl)),
-                 "    " + " ".join(pmc_cmd("DIR", "copy", "FETCH_SIZE", None)) + "   (and WRITE_SIZE)",
+                 "", "Made on one MI355X from the repository root by", "",
+                 f"    python3 -u -m tiered_kv_cache_hs_amd.profiling run --workloads "
+                 f"{' '.join(str(x) for x in workloads)} --out {rel}", "",
+                 "which runs these passes for this workload, each under `timeout -s KILL`:", "",
+                 "    " + " ".join(trace_cmd(rel, wl)),
+                 "    " + " ".join(pmc_cmd(rel, f"wl{wl}", "FETCH_SIZE", wl)),
+                 "    " + " ".join(pmc_cmd(rel, f"wl{wl}", "WRITE_SIZE", wl)),
+                 "    " + " ".join(pmc_cmd(rel, "copy", "FETCH_SIZE", None)) + "   (and WRITE_SIZE)",
                  "", "The trace run replays 32 decode steps from their hipGraphs (8 warm-up + 24 "
                  "timed), then runs them again eagerly with HIP events around every kernel, so "
                  "each kernel has two dispatches per layer and step.", "",
                  "## rocprofv3 --stats (all dispatches)", "",
                  "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
         for r in stats:
-            if not r["Name"].startswith("hs_k"):
+            if "hs_k_" not in r["Name"]:
                 continue
-            lines.append(f"| {r['Name'][:60]} | {r['Calls']} | {float(r['AverageNs']) / 1000:.2f} | "
+            lines.append(f"| {display_name(r['Name'])} | {r['Calls']} | {float(r['AverageNs']) / 1000:.2f} | "
                          f"{float(r['MinNs']) / 1000:.2f} | {float(r['MaxNs']) / 1000:.2f} | "
                          f"{float(r['Percentage']):.2f} |")
         lines += ["", "## Warm averages (kernel trace, End - Start; each pass's cold first step dropped)",
@@ -241,6 +257,17 @@ def report(workloads: List[int], out: str) -> None:
             if warm:
                 lines.append(f"| {name[:60]} | {len(warm)} | {statistics.mean(warm):.2f} | "
                              f"{statistics.median(warm):.2f} |")
+        lines += ["", "## Resources (first dispatch of each kernel)", "",
+                  "LDS bytes as the profiler reports them: the static allocation (the "
+                  "resolve kernel's dynamic LDS, (max(2H, 4k) + k) * 4 bytes for a hash "
+                  "of H entries, is not included).", "",
+                  "| kernel | VGPR | AGPR | SGPR | LDS bytes | scratch | workgroup | grid (threads) |",
+                  "|---|---|---|---|---|---|---|---|"]
+        for name, r in res.items():
+            if name.startswith("hs_k") and "buffer_init" not in name:
+                lines.append(f"| {name} | {r['VGPR_Count']} | {r['Accum_VGPR_Count']} | "
+                             f"{r['SGPR_Count']} | {r['LDS_Block_Size']} | {r['Scratch_Size']} | "
+                             f"{r['Workgroup_Size_X']} | {r['Grid_Size_X']} |")
         if bl:
             lines += ["", "## The benchmark's own timing in the same run", "",
                       f"Event-timed kernel durations per launch (us): {json.dumps(bl.get('kernels_us'))}; "
