@@ -138,8 +138,9 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
     int k, int hlog2, int rec16, int32_t *__restrict__ slots_all,
     int32_t *__restrict__ miss_all) {
   // LDS: region A holds the hash table (keys, values: 2H ints) during build
-  // and probe, then the miss and victim lists (k ints each) and the missed
-  // records' host addresses (k 64-bit words); region B holds slot_of[k].
+  // and probe, then the miss and victim lists (k ints each), the missed
+  // records' host addresses (k 64-bit words) and positions (k ints); region B
+  // holds slot_of[k].
   extern __shared__ __attribute__((aligned(16))) int lds[];
   constexpr int NW = NT / 64;
   __shared__ int scan_buf[2][RES_MAX_WAVES];
@@ -153,7 +154,8 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   int *miss_list = lds;
   int *victim_list = lds + k;
   uint64_t *miss_addr = (uint64_t *)(lds + 2 * k);
-  const int regionA = (2 * H > 4 * k) ? 2 * H : 4 * k;
+  int *miss_pos = lds + 4 * k;
+  const int regionA = (2 * H > 5 * k) ? 2 * H : 5 * k;
   int *slot_of = lds + regionA;
 
   const int u = blockIdx.x;
@@ -379,6 +381,7 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
 #pragma unroll
   for (int j = 0; j < KPT; ++j) {
     if (miss_here[j]) {
+      miss_pos[mrank] = tk[j];
       if (GATHER)
         miss_addr[mrank] = tpage[j] + (uint64_t)((uint32_t)tk[j] & ((1u << d.page_shift) - 1u)) *
                                           (uint64_t)(rec16 * 16);
@@ -388,21 +391,31 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   const int n_cand = B - (k - m);
 
   // ---- gather, first batch: host reads of the first GB * NT record chunks
-  // (16 bytes each) of the misses, in flight during the victim selection
+  // (16 bytes each) of the misses, in flight during the victim selection.
+  // Every lane issues the same loads and stores: a lane past the last chunk
+  // takes the last chunk again (the same bytes to the same place), so no
+  // load or store sits on a lane-dependent path and the waits before each
+  // store count exactly the loads it needs (a guarded load made the
+  // compiler wait for every earlier load before the next one).
   constexpr int GB = SPT >= 16 ? 4 : 8;
   const size_t rec = (size_t)rec16 * 16;
   const int g_total = m * rec16;
   v4u gv[GB];
+  auto chunk_src = [&](int c) {
+    c = min(c, g_total - 1);
+    const int j = c / rec16;
+    return (const HS_GLOBAL v4u *)miss_addr[j] + (c - j * rec16);
+  };
+  auto chunk_dst = [&](int c) {
+    c = min(c, g_total - 1);
+    const int j = c / rec16;
+    return (HS_GLOBAL v4u *)(d.rows + (size_t)victim_list[j] * rec) + (c - j * rec16);
+  };
   if (GATHER) {
     lds_barrier();  // miss_addr complete
+    if (g_total > 0) {
 #pragma unroll
-    for (int b = 0; b < GB; ++b) {
-      const int c = tid + NT * b;
-      if (c < g_total) {
-        const int j = c / rec16;
-        const int off = c - j * rec16;
-        gv[b] = __builtin_nontemporal_load((const HS_GLOBAL v4u *)miss_addr[j] + off);
-      }
+      for (int b = 0; b < GB; ++b) gv[b] = __builtin_nontemporal_load(chunk_src(tid + NT * b));
     }
   }
 
@@ -509,9 +522,11 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   // ---- 6. in-place update: fills get 2c - 1, hits get 2c
   const uint32_t c = clock + 1u;
   for (int r = tid; r < m; r += NT) {
+    // the position from LDS, not from the selection in global memory: a
+    // global load here would wait behind every host read in flight
     const int s = victim_list[r];
     const int i = miss_list[r];
-    const int32_t p = topk[i];
+    const int32_t p = miss_pos[r];
     d.pos[s] = p;
     d.stamp[s] = 2u * c - 1u;
     slot_of[i] = s;
@@ -529,24 +544,11 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
     for (int base = 0; base < g_total; base += GB * NT) {
       if (base > 0) {
 #pragma unroll
-        for (int b = 0; b < GB; ++b) {
-          const int c = base + tid + NT * b;
-          if (c < g_total) {
-            const int j = c / rec16;
-            const int off = c - j * rec16;
-            gv[b] = __builtin_nontemporal_load((const HS_GLOBAL v4u *)miss_addr[j] + off);
-          }
-        }
+        for (int b = 0; b < GB; ++b)
+          gv[b] = __builtin_nontemporal_load(chunk_src(base + tid + NT * b));
       }
 #pragma unroll
-      for (int b = 0; b < GB; ++b) {
-        const int c = base + tid + NT * b;
-        if (c < g_total) {
-          const int j = c / rec16;
-          const int off = c - j * rec16;
-          ((HS_GLOBAL v4u *)(d.rows + (size_t)victim_list[j] * rec))[off] = gv[b];
-        }
-      }
+      for (int b = 0; b < GB; ++b) *chunk_dst(base + tid + NT * b) = gv[b];
     }
   }
 
@@ -701,7 +703,7 @@ hipError_t launch_select_k(const UnitDesc *d_units, int n, const int32_t *d_topk
 int hash_log2(int k) {
   int h = 2;
   while ((1 << h) < 4 * k) ++h;
-  const size_t region_a = (size_t)(2 * (1 << h) > 4 * k ? 2 * (1 << h) : 4 * k);
+  const size_t region_a = (size_t)(2 * (1 << h) > 5 * k ? 2 * (1 << h) : 5 * k);
   if ((region_a + k) * sizeof(int) > (128u << 10)) --h;
   return h;
 }
@@ -710,7 +712,7 @@ int hash_log2(int k) {
 
 size_t resolve_lds_bytes(int k) {
   const int H = 1 << hash_log2(k);
-  const int regionA = (2 * H > 4 * k) ? 2 * H : 4 * k;
+  const int regionA = (2 * H > 5 * k) ? 2 * H : 5 * k;
   return (size_t)(regionA + k) * sizeof(int);
 }
 
