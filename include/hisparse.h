@@ -119,7 +119,9 @@ typedef struct hs_tuning {
                                    (16, 32 or 64, dividing n_q_heads) */
   int32_t prefetch_workgroups;  /* hs_prefetch: workgroups per launch
                                    (0 = 64; 1 to 65536) */
-  int32_t reserved[5];
+  int32_t prefetch_batch;       /* hs_prefetch: host reads in flight per lane
+                                   (0 = 1; 1, 2, 4 or 8) */
+  int32_t reserved[4];
 } hs_tuning;
 
 const char *hs_status_str(hs_status s);

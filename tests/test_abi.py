@@ -39,9 +39,9 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_tuning_roundtrip():
     assert H.hs_status_str(H.HS_OK) == "ok"
     assert H.hs_status_str(H.HS_E_STATE) == "invalid buffer state"
-    H.hs_set_tuning(4, 32, 96)
+    H.hs_set_tuning(4, 32, 96, 2)
     assert H.hs_get_tuning() == {"attn_splits": 4, "latent_heads_per_wg": 32,
-                                 "prefetch_workgroups": 96}
+                                 "prefetch_workgroups": 96, "prefetch_batch": 2}
     H.hs_set_tuning(0, 0)
     with pytest.raises(H.HsError):
         H.hs_set_tuning(-1, 0)
@@ -49,6 +49,8 @@ def test_status_strings_and_tuning_roundtrip():
         H.hs_set_tuning(0, 48)
     with pytest.raises(H.HsError):
         H.hs_set_tuning(0, 0, -3)
+    with pytest.raises(H.HsError):
+        H.hs_set_tuning(0, 0, 0, 3)
     assert H.hs_get_tuning()["prefetch_workgroups"] == 0
 
 

@@ -75,13 +75,13 @@ def test_groups_with_write_through_appends():
 def test_prefetch_workgroup_counts():
     w = small_workload("latent", I.BF16, 300, 197, 3000, 4, 40, R=2, L=4, seed=340, Hq=16,
                        share=4)
-    for wg in (1, 7, 96, 4096):
-        H.hs_set_tuning(0, 0, wg)
+    for wg, batch in ((1, 1), (7, 2), (96, 4), (4096, 8), (5, 8)):
+        H.hs_set_tuning(0, 0, wg, batch)
         try:
-            say(f"prefetch_workgroups={wg}")
+            say(f"prefetch_workgroups={wg} prefetch_batch={batch}")
             compare_run(w, 4, fill="full", attn_every=2, share_mode="prefetch")
         finally:
-            H.hs_set_tuning(0, 0, 0)
+            H.hs_set_tuning(0, 0, 0, 0)
 
 
 def _bitwise_same(a, b, steps, graph):

@@ -145,9 +145,9 @@ hipError_t launch_resolve(const UnitDesc *d_units, int n_units, int max_B,
                           hipStream_t stream);
 size_t resolve_lds_bytes(int k);
 // Fetch every unit's share of its state's last fetch list (about `workgroups`
-// workgroups in total; 0 = 64).
+// workgroups in total, 0 = 64; `batch` host reads in flight per lane, 1-8).
 hipError_t launch_prefetch(const UnitDesc *d_units, int n, int rec_bytes, int workgroups,
-                           hipStream_t stream);
+                           int batch, hipStream_t stream);
 hipError_t launch_regather(const UnitDesc *d_unit, int B, int rec_bytes,
                            hipStream_t stream);
 // Records [pos, pos + n) of a unit's pool (page table d_pages) from device

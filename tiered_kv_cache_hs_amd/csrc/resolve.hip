@@ -573,13 +573,22 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
 // another layer's buffer (layers reusing one selection) reads the list that
 // the group's resolve wrote and copies its own layer's records, which is why
 // positions are checked against this unit's pool length here (the resolve
-// checked them against the resolving unit's); a position past it is skipped
-// and sets HS_ERR_RANGE.
-// Grid: n_units * G workgroups of 256 threads; workgroup g of unit u walks
-// the unit's 16-byte chunks g*256 + tid, stepping by G*256.
+// checked them against the resolving unit's); a position past it is not read
+// (its row is rewritten with its own bytes) and sets HS_ERR_RANGE.
+// Grid: n_units * G workgroups of 256 threads; lane t of workgroup g of a
+// unit copies the unit's 16-byte chunks g*256 + t + j*G*256. Per batch of
+// BATCH chunks a lane first loads their fetch-list and page-table entries
+// (device memory), then issues all its host loads back to back, then
+// stores: the vector-memory counter retires in issue order, so a device load
+// issued after a host load would wait for it. Lanes past the last chunk
+// repeat it (the same bytes to the same place), so every lane issues the
+// same instructions and the waits count exactly. BATCH sets the host reads
+// in flight per lane: a copy running alone takes 8; one running beside
+// attention takes 1 (enough workgroups keep the link busy, and fewer
+// long-latency reads per compute unit slow the attention less).
 constexpr int GATHER_THREADS = 256;
-constexpr int GATHER_UNROLL = 4;
 
+template <int BATCH>
 __global__ __launch_bounds__(GATHER_THREADS) void hs_k_gather(
     const UnitDesc *__restrict__ units, int G, int rec16) {
   const int u = blockIdx.x / G;
@@ -591,32 +600,37 @@ __global__ __launch_bounds__(GATHER_THREADS) void hs_k_gather(
   const int total = m * rec16;
   const int stride = G * GATHER_THREADS;
   const size_t rec = (size_t)rec16 * 16;
+  const uint32_t in_mask = (1u << d.page_shift) - 1u;
   bool bad = false;
-  for (int c0 = g * GATHER_THREADS + (int)threadIdx.x; c0 < total;
-       c0 += stride * GATHER_UNROLL) {
-    v4u v[GATHER_UNROLL];
-    HS_GLOBAL v4u *dst[GATHER_UNROLL];
+  for (int b0 = g * GATHER_THREADS; b0 < total; b0 += stride * BATCH) {
+    int2v w[BATCH];
+    int off[BATCH];
 #pragma unroll
-    for (int uu = 0; uu < GATHER_UNROLL; ++uu) {
-      const int c = c0 + uu * stride;
-      dst[uu] = nullptr;
-      if (c < total) {
-        const int r = c / rec16;
-        const int off = c - r * rec16;
-        const int2v w = d.work[r];
-        if (w.y >= 0 && (int64_t)w.y < len) {
-          const HS_GLOBAL v4u *src =
-              (const HS_GLOBAL v4u *)pool_record(d, (uint32_t)w.y, rec) + off;
-          v[uu] = __builtin_nontemporal_load(src);
-          dst[uu] = (HS_GLOBAL v4u *)(d.rows + (size_t)w.x * rec) + off;
-        } else {
-          bad = true;
-        }
-      }
+    for (int j = 0; j < BATCH; ++j) {
+      const int c = min(b0 + (int)threadIdx.x + j * stride, total - 1);
+      const int r = c / rec16;
+      off[j] = c - r * rec16;
+      w[j] = d.work[r];
+    }
+    uint64_t page[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j)
+      page[j] = d.pages[min((uint32_t)w[j].y >> d.page_shift, (uint32_t)d.n_pages - 1u)];
+    v4u v[BATCH];
+    HS_GLOBAL v4u *dst[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      dst[j] = (HS_GLOBAL v4u *)(d.rows + (size_t)w[j].x * rec) + off[j];
+      const bool ok = w[j].y >= 0 && (int64_t)w[j].y < len;
+      bad |= !ok;
+      const HS_GLOBAL v4u *src =
+          ok ? (const HS_GLOBAL v4u *)((const HS_GLOBAL uint8_t *)page[j] +
+                                        (size_t)((uint32_t)w[j].y & in_mask) * rec) + off[j]
+             : dst[j];
+      v[j] = __builtin_nontemporal_load(src);
     }
 #pragma unroll
-    for (int uu = 0; uu < GATHER_UNROLL; ++uu)
-      if (dst[uu]) *dst[uu] = v[uu];
+    for (int j = 0; j < BATCH; ++j) *dst[j] = v[j];
   }
   if (bad) set_error(d.ctl, HS_ERR_RANGE);
 }
@@ -744,7 +758,7 @@ hipError_t launch_resolve(const UnitDesc *d_units, int n, int max_B, const int32
   // enough workgroups that about 512 copy the batch's misses
   const int G = std::max(1, std::min(64, (512 + n - 1) / n));
   trace_begin(HS_TRACE_GATHER, stream);
-  hipLaunchKernelGGL(hs_k_gather, dim3(n * G), dim3(GATHER_THREADS), 0, stream, d_units, G,
+  hipLaunchKernelGGL(hs_k_gather<8>, dim3(n * G), dim3(GATHER_THREADS), 0, stream, d_units, G,
                      rec16);
   trace_end(stream);
   return hipGetLastError();
@@ -755,12 +769,19 @@ hipError_t launch_resolve(const UnitDesc *d_units, int n, int max_B, const int32
 // free of long-latency host loads; 512 slowed the attention beside them and,
 // on a batch of 8 latent units, was slower even alone.
 hipError_t launch_prefetch(const UnitDesc *d_units, int n, int rec_bytes, int workgroups,
-                           hipStream_t stream) {
+                           int batch, hipStream_t stream) {
   const int wg = workgroups > 0 ? workgroups : 64;
   const int G = std::max(1, std::min(64, (wg + n - 1) / n));
   trace_begin(HS_TRACE_GATHER, stream);
-  hipLaunchKernelGGL(hs_k_gather, dim3(n * G), dim3(GATHER_THREADS), 0, stream, d_units, G,
-                     rec_bytes / 16);
+  const dim3 grid(n * G), block(GATHER_THREADS);
+  if (batch >= 8)
+    hipLaunchKernelGGL(hs_k_gather<8>, grid, block, 0, stream, d_units, G, rec_bytes / 16);
+  else if (batch >= 4)
+    hipLaunchKernelGGL(hs_k_gather<4>, grid, block, 0, stream, d_units, G, rec_bytes / 16);
+  else if (batch >= 2)
+    hipLaunchKernelGGL(hs_k_gather<2>, grid, block, 0, stream, d_units, G, rec_bytes / 16);
+  else
+    hipLaunchKernelGGL(hs_k_gather<1>, grid, block, 0, stream, d_units, G, rec_bytes / 16);
   trace_end(stream);
   return hipGetLastError();
 }

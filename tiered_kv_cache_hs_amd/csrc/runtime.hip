@@ -44,7 +44,7 @@ hs_status hip_fail(hipError_t e, const char *what) {
     if (e_ != hipSuccess) return hip_fail(e_, #call); \
   } while (0)
 
-hs_tuning g_tuning = {0, 0, 0, {0, 0, 0, 0, 0}};
+hs_tuning g_tuning = {0, 0, 0, 0, {0, 0, 0, 0}};
 
 inline hipStream_t S(void *s) { return (hipStream_t)s; }
 
@@ -150,6 +150,9 @@ hs_status hs_set_tuning(const hs_tuning *t) {
     return fail(HS_E_INVAL, "latent_heads_per_wg must be 0, 16, 32 or 64");
   if (t->prefetch_workgroups < 0 || t->prefetch_workgroups > 65536)
     return fail(HS_E_INVAL, "prefetch_workgroups outside [0, 65536]");
+  const int pb = t->prefetch_batch;
+  if (pb != 0 && pb != 1 && pb != 2 && pb != 4 && pb != 8)
+    return fail(HS_E_INVAL, "prefetch_batch must be 0, 1, 2, 4 or 8");
   g_tuning = *t;
   return HS_OK;
 }
@@ -908,7 +911,9 @@ hs_status hs_resolve_attn(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_
 hs_status hs_prefetch(hs_batch_t b, void *stream) {
   if (!b) return fail(HS_E_INVAL, "null batch");
   hipError_t e = hs::launch_prefetch(b->d_units, b->n, (int)b->pool->rec,
-                                     g_tuning.prefetch_workgroups, S(stream));
+                                     g_tuning.prefetch_workgroups,
+                                     g_tuning.prefetch_batch > 0 ? g_tuning.prefetch_batch : 1,
+                                     S(stream));
   if (e != hipSuccess) return hip_fail(e, "prefetch launch");
   return HS_OK;
 }

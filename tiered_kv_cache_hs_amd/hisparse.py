@@ -81,7 +81,8 @@ class Trace(ctypes.Structure):
 
 class Tuning(ctypes.Structure):
     _fields_ = [("attn_splits", ctypes.c_int32), ("latent_heads_per_wg", ctypes.c_int32),
-                ("prefetch_workgroups", ctypes.c_int32), ("reserved", ctypes.c_int32 * 5)]
+                ("prefetch_workgroups", ctypes.c_int32), ("prefetch_batch", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 4)]
 
 
 _lib = None
@@ -172,8 +173,8 @@ def hs_last_error() -> str:
 
 
 def hs_set_tuning(attn_splits: int = 0, latent_heads_per_wg: int = 0,
-                  prefetch_workgroups: int = 0) -> None:
-    t = Tuning(attn_splits, latent_heads_per_wg, prefetch_workgroups)
+                  prefetch_workgroups: int = 0, prefetch_batch: int = 0) -> None:
+    t = Tuning(attn_splits, latent_heads_per_wg, prefetch_workgroups, prefetch_batch)
     _check(lib().hs_set_tuning(ctypes.byref(t)))
 
 
@@ -181,7 +182,7 @@ def hs_get_tuning() -> dict:
     t = Tuning()
     _check(lib().hs_get_tuning(ctypes.byref(t)))
     return {"attn_splits": t.attn_splits, "latent_heads_per_wg": t.latent_heads_per_wg,
-            "prefetch_workgroups": t.prefetch_workgroups}
+            "prefetch_workgroups": t.prefetch_workgroups, "prefetch_batch": t.prefetch_batch}
 
 
 # ------------------------------------------------------------------ pool
