@@ -68,6 +68,39 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "dispatches": 4}), flush=True)
 
 
+def host_dma_rate():
+    """Pinned host-to-device copy rate (GB/s) of the DMA engines for 2 MB and
+    256 MB copies: the practical ceiling of the host link on this machine."""
+    import torch
+    out = {}
+    for mb in (2, 256):
+        n = mb << 20
+        h = torch.empty(n, dtype=torch.uint8, pin_memory=True)
+        d = torch.empty(n, dtype=torch.uint8, device="cuda")
+        d.copy_(h, non_blocking=True)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 8 if mb == 2 else 3
+        e0.record()
+        for _ in range(reps):
+            d.copy_(h, non_blocking=True)
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"{mb}MB"] = round(n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+        del h, d
+    return out
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def attn_bytes(w, n_units):
     """Algorithmic HBM bytes of one attention launch over n_units units:
     the k selected rows read once, the queries read, the outputs written."""
@@ -179,6 +212,26 @@ def main():
     print(f"[bench] timed {K} steps: {ms_step * 1000:.1f} us/step (wall {wall * 1e3 / K:.3f} ms/step)",
           file=sys.stderr, flush=True)
 
+    # ---- outside the timed region: every step replayed again from a reset
+    # state with an event pair around each replay (per-step spread; step 0,
+    # the cold all-miss step, reported on its own)
+    sess.reset()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(total)]
+    for t in range(total):
+        evs[t][0].record()
+        sess.replay(t)
+        evs[t][1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([a.elapsed_time(b) * 1000.0 / w.n_layers for a, b in evs])
+    warm = per_step[1:]
+    step_spread = {"cold_step0": round(float(per_step[0]), 2),
+                   "p10": round(float(np.percentile(warm, 10)), 2),
+                   "median": round(float(np.median(warm)), 2),
+                   "p90": round(float(np.percentile(warm, 90)), 2),
+                   "unit": "us/layer, one event pair per replayed step"}
+    dma = host_dma_rate()
+
     # ---- the same steps again, eagerly, with each kernel bracketed by events
     sess.reset()
     miss_hist = torch.zeros((total, w.n_layers, w.n_requests), dtype=torch.int32, device="cuda")
@@ -272,6 +325,8 @@ def main():
         "miss_rate": round(miss_rate, 4),
         "fetch_bytes_by_kernel": {c: int(v / K) for c, v in cls_bytes.items()},
         "miss_bytes_per_step": int(misses.sum() * w.rec_bytes / K),
+        "step_spread": step_spread,
+        "host_dma_h2d_gbs": dma,
     }
     sess.close()
 
@@ -280,7 +335,7 @@ def main():
         traces = I.gen_traces(w, total)
         us, n_steps, threads = cpu_baseline(w, traces, args.cpu_seconds)
         result["cpu_baseline"] = {
-            "value": round(us, 1), "unit": "us/layer", "cores": int(threads), "kind": "oracle",
+            "value": round(us, 1), "unit": "us/layer", "cores": int(threads), "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"first {n_steps} steps of the same trace (step 0 cold, median of the rest), "
                       f"all {w.n_units} units per step, resolve + fp64 attention"}
     print(json.dumps(result), flush=True)
