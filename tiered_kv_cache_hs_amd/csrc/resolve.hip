@@ -397,7 +397,10 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   // load or store sits on a lane-dependent path and the waits before each
   // store count exactly the loads it needs (a guarded load made the
   // compiler wait for every earlier load before the next one).
-  constexpr int GB = SPT >= 16 ? 4 : 8;
+  // 8 chunks per thread; 4 where registers are short (B > 8192) or where few
+  // misses per buffer are the rule (B <= 1024: the repeated last chunk of
+  // lanes past the end would cost host reads of its own)
+  constexpr int GB = (SPT >= 16 || SPT == 1) ? 4 : 8;
   const size_t rec = (size_t)rec16 * 16;
   const int g_total = m * rec16;
   v4u gv[GB];
