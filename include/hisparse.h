@@ -214,8 +214,10 @@ hs_status hs_buffer_destroy(hs_buffer_t buf);
  * B <= new_B <= HS_MAX_B: slots [0, B) keep their positions, stamps and
  * rows, slots [B, new_B) are empty; clock, error word and the last fetch list
  * carry over. From then on the handle uses the new memory and the old memory
- * is no longer read (the caller may free it). Batches made before hold the
- * old layout: create them again. Refused (HS_E_INVAL) for a buffer whose
+ * is no longer read (the caller may free it). Batches of the pool made
+ * before describe the old memory: the resolve, attention and prefetch calls
+ * refuse them (HS_E_INVAL) until they are created again, and graphs captured
+ * before must be captured again. Refused (HS_E_INVAL) for a buffer whose
  * state is shared with others (either side of hs_buffer_create_shared).
  * Synchronous (waits for stream). */
 hs_status hs_buffer_grow(hs_buffer_t buf, int32_t new_B, void *d_mem, size_t bytes,

@@ -406,3 +406,30 @@ def test_pool_pages_and_reserve():
     finally:
         torch.cuda.synchronize()
         H.hs_pool_destroy(pool)
+
+
+def test_batches_made_before_growth_are_refused():
+    w = _small("mha", I.F32, 16, 8, 64, 2, 2, R=2, seed=430)
+    sess = Session(w, 2, fill="full")
+    try:
+        sess.step(0)
+        old = H.hs_batch_create(sess.bufs[0])
+        t = torch.empty(H.hs_buffer_bytes(sess.pool, 32), dtype=torch.uint8, device="cuda")
+        H.hs_buffer_grow(sess.bufs[0][0], 32, t)
+        sess.mem[0] = t
+        with pytest.raises(H.HsError):
+            H.hs_resolve(old, sess.topk[1, 0], 8, sess.slots[0], sess.miss[0])
+        with pytest.raises(H.HsError):
+            H.hs_sparse_attn(old, sess.q[1, 0], 1, sess.slots[0], 8, 0.1, sess.out[0], sess.ws)
+        with pytest.raises(H.HsError):
+            H.hs_prefetch(old)
+        H.hs_batch_destroy(old)
+        fresh = H.hs_batch_create(sess.bufs[0])
+        H.hs_resolve(fresh, sess.topk[1, 0], 8, sess.slots[0], sess.miss[0])
+        torch.cuda.synchronize()
+        H.hs_batch_destroy(fresh)
+        H.hs_batch_destroy(sess.batches[0])
+        sess.batches[0] = H.hs_batch_create(sess.bufs[0])
+    finally:
+        sess.close()
+

@@ -103,6 +103,7 @@ struct hs_pool_s {
   uint64_t *d_pages = nullptr;      // device page tables of every unit
   int64_t *d_len = nullptr;         // [R * L]
   std::vector<int64_t> shadow;      // lengths as of the calls made so far
+  uint64_t epoch = 0;               // bumped when a buffer of the pool moves (grows)
   int device = 0;
   int64_t page_records() const { return (int64_t)1 << page_shift; }
 };
@@ -122,6 +123,7 @@ struct hs_batch_s {
   hs_pool_t pool = nullptr;
   int32_t n = 0, min_B = 0, max_B = 0;
   bool shared_twice = false;  // two units share one state (not resolvable)
+  uint64_t epoch = 0;         // the pool's epoch when the table was made
   UnitDesc *d_units = nullptr;
 };
 
@@ -186,36 +188,49 @@ static uint8_t *record_host(hs_pool_t p, int32_t req, int32_t layer, int64_t pos
 }
 
 // Allocates request req's pages up to `records` (whole pages) and enters
-// them in its units' device page tables. Synchronous.
+// them in its units' device page tables. Synchronous. All or nothing: on a
+// failure the pages of this call are freed and the pool is as before (the
+// table entries past the capacity are never read: positions are checked
+// against lengths <= the capacity).
 static hs_status reserve_pages(hs_pool_t p, int32_t req, int64_t records) {
   const int64_t need = (records + p->page_records() - 1) >> p->page_shift;
   const int64_t have = (int64_t)p->host[req].size();
   if (need <= have) return HS_OK;
   const size_t pb = page_bytes(p);
-  std::vector<uint64_t> entries((size_t)(need - have) * p->L);
+  std::vector<uint8_t *> nh, nd;  // this call's pages: host and device addresses
+  auto undo = [&nh]() {
+    for (auto h : nh) (void)hipHostFree(h);
+  };
   for (int64_t g = have; g < need; ++g) {
     void *h = nullptr;
     hipError_t e = hipHostMalloc(&h, pb * p->L, hipHostMallocMapped | hipHostMallocCoherent);
-    if (e != hipSuccess || !h)
+    if (e != hipSuccess || !h) {
+      undo();
       return fail(HS_E_NOMEM, "hipHostMalloc(%zu bytes) for request %d: %s", pb * p->L, req,
                   hipGetErrorString(e));
+    }
+    nh.push_back((uint8_t *)h);
     void *dp = nullptr;
     e = hipHostGetDevicePointer(&dp, h, 0);
     if (e != hipSuccess) {
-      (void)hipHostFree(h);
+      undo();
       return hip_fail(e, "hipHostGetDevicePointer");
     }
-    p->host[req].push_back((uint8_t *)h);
-    p->dev[req].push_back((uint8_t *)dp);
+    nd.push_back((uint8_t *)dp);
   }
-  // entries of each layer's new pages (pages not yet allocated stay 0 and are
-  // never read: positions are checked against lengths <= the capacity)
+  std::vector<uint64_t> entries((size_t)(need - have));
   for (int l = 0; l < p->L; ++l) {
-    for (int64_t g = have; g < need; ++g)
-      entries[(size_t)(g - have)] = (uint64_t)(uintptr_t)(p->dev[req][g] + (size_t)l * pb);
-    HS_HIP(hipMemcpy(unit_table(p, req, l) + have, entries.data(),
-                     sizeof(uint64_t) * (size_t)(need - have), hipMemcpyHostToDevice));
+    for (int64_t g = 0; g < need - have; ++g)
+      entries[(size_t)g] = (uint64_t)(uintptr_t)(nd[(size_t)g] + (size_t)l * pb);
+    hipError_t e = hipMemcpy(unit_table(p, req, l) + have, entries.data(),
+                             sizeof(uint64_t) * entries.size(), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      undo();
+      return hip_fail(e, "page table upload");
+    }
   }
+  p->host[req].insert(p->host[req].end(), nh.begin(), nh.end());
+  p->dev[req].insert(p->dev[req].end(), nd.begin(), nd.end());
   p->cap[req] = need << p->page_shift;
   return HS_OK;
 }
@@ -396,7 +411,7 @@ hs_status hs_pool_append(hs_pool_t p, int32_t req, int32_t layer, int64_t pos, i
   if (s) return s;
   if (n < 0 || (n > 0 && !src)) return fail(HS_E_INVAL, "bad source");
   const size_t ui = (size_t)req * p->L + layer;
-  if (pos < 0 || pos > p->shadow[ui] || pos + n > p->cap[req])
+  if (pos < 0 || pos > p->shadow[ui] || n > p->cap[req] || pos + n > p->cap[req])
     return fail(HS_E_RANGE, "append [%lld, %lld) with length %lld, capacity %lld",
                 (long long)pos, (long long)(pos + n), (long long)p->shadow[ui],
                 (long long)p->cap[req]);
@@ -575,6 +590,7 @@ hs_status hs_buffer_grow(hs_buffer_t b, int32_t new_B, void *d_mem, size_t bytes
   b->mem = nm;
   b->lay = lay;
   b->B = new_B;
+  ++b->pool->epoch;  // batch tables made before describe the old memory
   return HS_OK;
 }
 
@@ -673,6 +689,7 @@ hs_status hs_batch_create(const hs_buffer_t *bufs, int32_t n, hs_batch_t *out) {
   bt->min_B = min_B;
   bt->max_B = max_B;
   bt->shared_twice = shared_twice;
+  bt->epoch = pool->epoch;
   hipError_t e = hipMalloc(&bt->d_units, sizeof(UnitDesc) * n);
   if (e == hipSuccess)
     e = hipMemcpy(bt->d_units, h.data(), sizeof(UnitDesc) * n, hipMemcpyHostToDevice);
@@ -692,11 +709,20 @@ hs_status hs_batch_destroy(hs_batch_t b) {
   return HS_OK;
 }
 
+// A batch made before a buffer of its pool moved describes freed memory.
+static hs_status check_epoch(hs_batch_t b) {
+  if (b->epoch != b->pool->epoch)
+    return fail(HS_E_INVAL, "a buffer of the pool grew after this batch was made: create the "
+                            "batch again");
+  return HS_OK;
+}
+
 // ----------------------------------------------------------------- resolve
 
 static hs_status check_resolve(hs_batch_t b, const int32_t *d_topk, int32_t k,
                                const int32_t *d_slots) {
   if (!b || !d_topk || !d_slots) return fail(HS_E_INVAL, "null argument");
+  if (check_epoch(b)) return HS_E_INVAL;
   if (b->shared_twice)
     return fail(HS_E_INVAL, "the batch holds two buffers of one shared state");
   if (k < 1 || k > HS_MAX_K || k > b->min_B)
@@ -818,6 +844,7 @@ static hs_status check_attn(hs_batch_t b, const void *d_q, int32_t Hq, const int
                             int32_t k, float sm_scale, float *d_out, void *d_ws, size_t ws_bytes,
                             AttnPlan *pl) {
   if (!b || !d_q || !d_slots || !d_out) return fail(HS_E_INVAL, "null argument");
+  if (check_epoch(b)) return HS_E_INVAL;
   if (k > b->min_B) return fail(HS_E_INVAL, "k = %d above smallest B = %d", k, b->min_B);
   if (!(sm_scale > 0.f) || sm_scale == __builtin_huge_valf())
     return fail(HS_E_INVAL, "sm_scale must be positive and finite");
@@ -910,6 +937,7 @@ hs_status hs_resolve_attn(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_
 
 hs_status hs_prefetch(hs_batch_t b, void *stream) {
   if (!b) return fail(HS_E_INVAL, "null batch");
+  if (check_epoch(b)) return HS_E_INVAL;
   hipError_t e = hs::launch_prefetch(b->d_units, b->n, (int)b->pool->rec,
                                      g_tuning.prefetch_workgroups,
                                      g_tuning.prefetch_batch > 0 ? g_tuning.prefetch_batch : 1,

@@ -230,6 +230,8 @@ class Session:
                 H.hs_buffer_grow(self.bufs[l][r], new_B[r], t)
                 self.mem[l * self.R + r] = t
                 self.Bs[l][r] = new_B[r]
+        # every batch of the pool is made again once all buffers have moved
+        for l in range(self.L):
             H.hs_batch_destroy(self.batches[l])
             self.batches[l] = H.hs_batch_create(self.bufs[l])
         wsb = max(H.hs_sparse_attn_workspace(self.batches[l], self.w.n_q_heads, self.k)
