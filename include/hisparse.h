@@ -348,8 +348,11 @@ hs_status hs_resolve_attn(hs_batch_t batch, const int32_t *d_topk, int32_t k,
  * (same stream, or an event) and before the next one; it may run on another
  * stream concurrently with attention over other buffers. A fetch-list
  * position at or past the unit's pool length is skipped and sets
- * HS_ERR_RANGE. The number of workgroups is hs_tuning.prefetch_workgroups.
- * Enqueue only; capture-safe. HS_E_INVAL for a null batch. */
+ * HS_ERR_RANGE. The number of workgroups and the host reads each lane keeps
+ * in flight are hs_tuning.prefetch_workgroups and prefetch_batch (defaults
+ * 64 and 1: few long-latency reads per compute unit, so that attention
+ * running beside the prefetch is slowed little). Enqueue only; capture-safe.
+ * HS_E_INVAL for a null batch or one made before a buffer of its pool grew. */
 hs_status hs_prefetch(hs_batch_t batch, void *stream);
 
 /* ------------------------------- tracing -----------------------------------
