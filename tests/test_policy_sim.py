@@ -132,3 +132,19 @@ def test_study_on_a_workload_trace():
     assert rate[("belady", 2)] <= min(rate[("lru", 2)], rate[("fifo", 2)], rate[("random", 2)])
     assert rate[("lru", 4)] <= rate[("lru", 2)] + 1e-12
     assert all(0.0 <= v <= 1.0 for v in rate.values())
+
+
+def test_B_sweep_is_monotone_for_belady_and_starts_at_swap():
+    """Belady never misses more with a larger buffer (an optimal policy with
+    more room can always mimic the smaller one); at B = k every policy is
+    Swap-vanilla."""
+    w = I.workload(1)
+    tr = I.gen_traces(w, 16)
+    rows = P.sweep_B(tr, policies=("lru", "belady", "fifo"), mults=(1.0, 1.5, 2.0, 4.0))
+    bel = [r["mean_miss_rate"] for r in rows if r["policy"] == "belady"]
+    assert all(b1 >= b2 - 1e-12 for b1, b2 in zip(bel, bel[1:]))
+    swap = np.mean([P.misses_swap(tr[:, u, :])[1:] / w.k for u in range(tr.shape[1])])
+    for r in rows:
+        if r["B"] == w.k:
+            assert abs(r["mean_miss_rate"] - swap) < 1e-12, r
+

@@ -203,6 +203,24 @@ def study(traces: np.ndarray, configs: Sequence = STUDY, skip_cold: bool = True,
     return rows
 
 
+def sweep_B(traces: np.ndarray, policies: Sequence[str] = ("lru", "belady"),
+            mults: Sequence[float] = (1.0, 1.25, 1.5, 2.0, 3.0, 4.0), skip_cold: bool = True,
+            seed: int = 0) -> List[dict]:
+    """Mean per-step miss rate of each policy at B = mult * k (at least k) over
+    every unit's trace: the page weighs a larger buffer (fewer misses)
+    against its HBM and probe cost."""
+    T, n, k = traces.shape
+    lo = 1 if skip_cold and T > 1 else 0
+    rows = []
+    for mult in mults:
+        B = max(k, int(round(mult * k)))
+        for pol in policies:
+            per_unit = np.stack([simulate(traces[:, u, :], pol, B, seed + u) for u in range(n)])
+            rate = per_unit / float(k)
+            rows.append({"policy": pol, "B": B, "mean_miss_rate": float(rate[:, lo:].mean())})
+    return rows
+
+
 def main() -> None:
     from . import inputs as I
 
@@ -210,6 +228,8 @@ def main() -> None:
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--steps", type=int, default=None, help="decode steps (default: the workload's)")
     ap.add_argument("--units", type=int, default=None, help="first N (request, layer) units only")
+    ap.add_argument("--sweep", action="store_true",
+                    help="LRU and Belady at B = 1, 1.25, 1.5, 2, 3, 4 times k instead of the study")
     args = ap.parse_args()
     w = I.workload(args.workload)
     steps = args.steps or w.steps
@@ -218,6 +238,11 @@ def main() -> None:
         traces = traces[:, : args.units, :]
     print(f"workload {w.name}: {traces.shape[1]} units x {steps} steps, k = {w.k}; "
           "mean per-step miss rate over steps 1.. (step 0 misses all)")
+    if args.sweep:
+        print(f"{'policy':8s} {'B':>6s} {'miss rate':>10s}")
+        for r in sweep_B(traces):
+            print(f"{r['policy']:8s} {r['B']:6d} {r['mean_miss_rate']:10.4f}")
+        return
     print(f"{'policy':8s} {'B':>6s} {'miss rate':>10s} {'seconds':>8s}")
     for r in study(traces):
         print(f"{r['policy']:8s} {r['B']:6d} {r['mean_miss_rate']:10.4f} {r['seconds']:8.2f}")
