@@ -250,9 +250,12 @@ def main():
     misses = miss_hist[W:, src, :].cpu().numpy().astype(np.int64)  # [K][L][R]
     per = {c: (tr[c][0] / tr[c][1] if tr[c][1] else 0.0) for c in H.TRACE_CLASSES}
 
-    n_launch_units = w.n_requests  # one batch (one layer's requests) per launch
-    a_bytes = attn_bytes(w, n_launch_units)
-    a_flops = attn_flops(w, n_launch_units)
+    # units attended per launch, on average (each launch covers one layer's
+    # requests)
+    attn_launches_per_step = tr["attn"][1] / K if tr["attn"][1] else 1.0
+    units_per_launch = w.n_units / attn_launches_per_step
+    a_bytes = attn_bytes(w, 1) * units_per_launch
+    a_flops = attn_flops(w, 1) * units_per_launch
     attn_us = per["attn"]
     attn_gbs = a_bytes / (attn_us * 1e-6) / 1e9 if attn_us else 0.0
     attn_kernel = "hs_k_attn_latent" if w.kind == "latent" else "hs_k_attn_mha"
