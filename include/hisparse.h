@@ -158,6 +158,14 @@ hs_status hs_pool_capacity(hs_pool_t pool, int32_t req, int64_t *capacity,
  * Synchronous; not while a stream is being captured. HS_E_RANGE above the
  * request's max_tokens, HS_E_NOMEM if an allocation fails. */
 hs_status hs_pool_reserve(hs_pool_t pool, int32_t req, int64_t records);
+/* Returns all of request req's pages (the request finished): its units'
+ * lengths become 0 and its capacity 0; hs_pool_reserve gives the request
+ * index pages again (for a new request, up to the same maximum). Buffers of
+ * the request keep positions that no longer exist: reset them
+ * (hs_buffer_reset) before resolving for the new request (until then a
+ * resolve reports HS_ERR_RANGE and reads nothing). Synchronous (waits for
+ * the device). HS_E_RANGE for a bad req. */
+hs_status hs_pool_release(hs_pool_t pool, int32_t req);
 /* Host pointer of record pos of unit (req, layer), for writing prefill
  * records directly and for reading them back. HS_E_RANGE for a bad
  * req/layer or pos outside [0, capacity). */

@@ -433,3 +433,49 @@ def test_batches_made_before_growth_are_refused():
     finally:
         sess.close()
 
+
+def test_pool_release_and_reuse_of_a_request_index():
+    """A finished request returns its pages; its buffer then reports range
+    errors and reads nothing; after a new reservation, prefill and a buffer
+    reset the request index serves a new request like a fresh one."""
+    w = _small("mha", I.F32, 40, 17, 300, 6, 5, R=2, seed=440)
+    sess = Session(w, 6, fill="full", page_tokens=64)
+    try:
+        for t in range(3):
+            sess.step(t)
+        torch.cuda.synchronize()
+        H.hs_pool_release(sess.pool, 0)
+        assert H.hs_pool_capacity(sess.pool, 0)[0] == 0
+        assert H.hs_pool_length(sess.pool, 0, 0) == 0
+        assert H.hs_pool_capacity(sess.pool, 1)[0] >= 300  # the other request keeps its pages
+        with pytest.raises(H.HsError):
+            H.hs_pool_record_ptr(sess.pool, 0, 0, 0)
+        sess.step(3)  # request 0's resolve: every position is out of range now
+        torch.cuda.synchronize()
+        assert sess.state(0, 0)[3] & H.HS_ERR_RANGE
+        assert sess.state(0, 1)[3] == 0  # request 1 unaffected
+        # a new request in index 0: pages, prefill, empty buffer
+        H.hs_pool_reserve(sess.pool, 0, 300)
+        for first, page in H.pool_pages(sess.pool, 0, 0):
+            n = min(page.shape[0], 300 - first)
+            if n > 0:
+                I.fill_records(w, page.ctypes.data - first * w.rec_bytes, 0, 0,
+                               positions=np.arange(first, first + n))
+        H.hs_pool_set_length(sess.pool, 0, 0, 300)
+        H.hs_buffer_reset(sess.bufs[0][0])
+        torch.cuda.synchronize()
+        sel = sess.topk[4, 0, 0].cpu().numpy()
+        ob = oracle.OracleBuffer(40, w.rec_bytes, with_rows=True)
+        pool = np.zeros((300, w.rec_bytes), np.uint8)
+        I.fill_records(w, pool.ctypes.data, 0, 0, p0=0, p1=300)
+        so, mo = oracle.resolve(ob, sel, pool, 300)
+        H.hs_resolve(sess.batches[0], sess.topk[4, 0], w.k, sess.slots[0], sess.miss[0])
+        torch.cuda.synchronize()
+        assert np.array_equal(sess.slots[0, 0].cpu().numpy(), so) and int(sess.miss[0, 0]) == mo
+        pos, stamp, clock, err = sess.state(0, 0)
+        assert np.array_equal(pos, ob.pos) and err == 0
+        rows = sess.rows(0, 0)
+        assert np.array_equal(rows[pos >= 0], ob.rows[ob.pos >= 0])
+    finally:
+        sess.close()
+

@@ -359,6 +359,27 @@ hs_status hs_pool_reserve(hs_pool_t p, int32_t req, int64_t records) {
   return reserve_pages(p, req, records);
 }
 
+hs_status hs_pool_release(hs_pool_t p, int32_t req) {
+  hs_status s = check_unit(p, req, 0);
+  if (s) return s;
+  HS_HIP(hipDeviceSynchronize());  // no kernel may still read these pages
+  // lengths first (every later access is checked against them), then the
+  // page-table entries, then the memory
+  for (int l = 0; l < p->L; ++l) {
+    const size_t ui = (size_t)req * p->L + l;
+    HS_HIP(hipMemset(p->d_len + ui, 0, sizeof(int64_t)));
+    p->shadow[ui] = 0;
+  }
+  HS_HIP(hipMemset(unit_table(p, req, 0), 0,
+                   sizeof(uint64_t) * (size_t)p->L * (size_t)p->max_pages[req]));
+  HS_HIP(hipDeviceSynchronize());
+  for (auto h : p->host[req]) (void)hipHostFree(h);
+  p->host[req].clear();
+  p->dev[req].clear();
+  p->cap[req] = 0;
+  return HS_OK;
+}
+
 hs_status hs_pool_record_ptr(hs_pool_t p, int32_t req, int32_t layer, int64_t pos,
                              void **host_ptr, size_t *rec_bytes) {
   hs_status s = check_unit(p, req, layer);

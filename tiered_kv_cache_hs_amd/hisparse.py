@@ -41,7 +41,7 @@ HS_MAX_B = 16384
 EXPORTS = (
     "hs_status_str", "hs_last_error", "hs_set_tuning", "hs_get_tuning",
     "hs_pool_create", "hs_pool_destroy", "hs_pool_record_bytes", "hs_pool_capacity",
-    "hs_pool_reserve", "hs_pool_record_ptr", "hs_pool_page_ptr",
+    "hs_pool_reserve", "hs_pool_release", "hs_pool_record_ptr", "hs_pool_page_ptr",
     "hs_pool_length", "hs_pool_set_length", "hs_pool_append",
     "hs_buffer_bytes", "hs_buffer_create", "hs_buffer_destroy", "hs_buffer_grow",
     "hs_buffer_reset",
@@ -108,6 +108,7 @@ def lib():
         "hs_pool_record_bytes": ([vp, P(sz)], i32),
         "hs_pool_capacity": ([vp, i32, P(i64), P(i64), P(i64)], i32),
         "hs_pool_reserve": ([vp, i32, i64], i32),
+        "hs_pool_release": ([vp, i32], i32),
         "hs_pool_record_ptr": ([vp, i32, i32, i64, P(vp), P(sz)], i32),
         "hs_pool_page_ptr": ([vp, i32, i32, i64, P(vp)], i32),
         "hs_pool_length": ([vp, i32, i32, P(i64)], i32),
@@ -219,6 +220,11 @@ def hs_pool_capacity(pool: int, req: int):
 
 def hs_pool_reserve(pool: int, req: int, records: int) -> None:
     _check(lib().hs_pool_reserve(pool, req, int(records)))
+
+
+def hs_pool_release(pool: int, req: int) -> None:
+    """Return all of a finished request's pages (lengths and capacity 0)."""
+    _check(lib().hs_pool_release(pool, req))
 
 
 def hs_pool_record_ptr(pool: int, req: int, layer: int, pos: int) -> int:
