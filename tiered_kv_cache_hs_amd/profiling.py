@@ -45,6 +45,11 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "tiered_kv_cache_hs_amd", "csrc")
 PMC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic.json")
 COUNTERS = ("FETCH_SIZE", "WRITE_SIZE")
+# one pass of shader-sequencer counters (at most 8 SQ counters per pass):
+# where a kernel's cycles go
+SQ_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
+               "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM", "SQ_VALU_MFMA_BUSY_CYCLES",
+               "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE")
 COPY_BYTES = 256 << 20
 
 # the kernel's file, the shared header and the launch planner: a stored
@@ -132,6 +137,77 @@ def trace_cmd(out: str, wl: int) -> List[str]:
 def pmc_cmd(out: str, tag: str, counter: str, wl: Optional[int]) -> List[str]:
     return ["rocprofv3", "--pmc", counter, "--output-format", "csv", "-d",
             os.path.join(out, f"pmc_{tag}_{counter}"), "-o", "run", "--"] + bench_cmd(wl, 3, 1)
+
+
+def sq_cmd(out: str, wl: int) -> List[str]:
+    return ["rocprofv3", "--pmc", *SQ_COUNTERS, "--output-format", "csv", "-d",
+            os.path.join(out, f"sq_wl{wl}"), "-o", "run", "--"] + bench_cmd(wl, 3, 1)
+
+
+def run_sq(workloads: List[int], out: str, limit: int) -> None:
+    os.makedirs(out, exist_ok=True)
+    os.environ.setdefault("TMPDIR", "/tmp")
+    for wl in workloads:
+        if _child(sq_cmd(out, wl), os.path.join(out, f"sq_wl{wl}.log"), limit):
+            raise SystemExit(f"counter pass of workload {wl} failed")
+
+
+def read_counters_by_name(d: str) -> Dict[str, Dict[str, List[float]]]:
+    """{kernel: {counter: [value per dispatch]}} from a counter-collection CSV."""
+    f = _one(os.path.join(d, "**", "*counter_collection.csv"))
+    per: Dict[str, Dict[str, List[float]]] = {}
+    if f:
+        for r in csv.DictReader(open(f)):
+            k = display_name(r["Kernel_Name"])
+            per.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def sq_report(workloads: List[int], out: str) -> None:
+    """hs_sq_<workload>.md: per kernel, the median of each SQ counter over
+    its dispatches and the derived shares of busy cycles."""
+    from . import inputs as I
+
+    rep_dir = os.path.join(out, "report")
+    os.makedirs(rep_dir, exist_ok=True)
+    rel = os.path.relpath(out, ROOT)
+    for wl in workloads:
+        w = I.workload(wl)
+        per = read_counters_by_name(os.path.join(out, f"sq_wl{wl}"))
+        lines = [f"# Shader-sequencer counters: workload {w.name}", "",
+                 "Made on one MI355X from the repository root by", "",
+                 f"    python3 -u -m tiered_kv_cache_hs_amd.profiling sq --workloads "
+                 f"{' '.join(str(x) for x in workloads)} --out {rel}", "",
+                 "which runs", "", "    " + " ".join(sq_cmd(rel, wl)), "",
+                 "Medians over each kernel's dispatches (counts summed over the device).", "",
+                 "| kernel | dispatches | " + " | ".join(SQ_COUNTERS) + " |",
+                 "|---|---|" + "---|" * len(SQ_COUNTERS)]
+        derived = []
+        for k, cs in sorted(per.items()):
+            if not k.startswith("hs_k") or "buffer_init" in k:
+                continue
+            med = {c: statistics.median(cs[c]) if c in cs else float("nan") for c in SQ_COUNTERS}
+            n = len(next(iter(cs.values())))
+            lines.append(f"| {k} | {n} | " + " | ".join(f"{med[c]:.3g}" for c in SQ_COUNTERS) + " |")
+            wave = med["SQ_WAVE_CYCLES"]
+            # GRBM_GUI_ACTIVE is summed over the 8 XCDs (divided by 8 it
+            # matches the traced kernel duration); 256 CUs x 4 SIMDs
+            cycles = med["GRBM_GUI_ACTIVE"] / 8.0
+            if wave > 0 and cycles > 0:
+                derived.append(f"| {k} | {cycles:.0f} | {med['SQ_WAIT_INST_ANY'] / wave:.2f} | "
+                               f"{med['SQ_ACTIVE_INST_VALU'] / wave:.2f} | "
+                               f"{med['SQ_ACTIVE_INST_LDS'] / wave:.2f} | "
+                               f"{med['SQ_ACTIVE_INST_VMEM'] / wave:.2f} | "
+                               f"{100.0 * med['SQ_VALU_MFMA_BUSY_CYCLES'] / (cycles * 1024):.1f} |")
+        lines += ["", "Derived: kernel cycles = GRBM_GUI_ACTIVE / 8 (the counter is summed over "
+                  "the 8 XCDs; so divided it matches the traced duration); the wait and "
+                  "active-instruction counters as shares of wave cycles; MFMA busy = "
+                  "SQ_VALU_MFMA_BUSY_CYCLES over kernel cycles x 1024 SIMDs.", "",
+                  "| kernel | kernel cycles | waiting | VALU issue | LDS issue | VMEM issue | "
+                  "MFMA busy % |", "|---|---|---|---|---|---|---|"] + derived
+        with open(os.path.join(rep_dir, f"hs_sq_{w.name}.md"), "w") as fh:
+            fh.write("\n".join(lines) + "\n")
+    print(f"[profiling] counter report in {rep_dir}", flush=True)
 
 
 def run_all(workloads: List[int], out: str, limit: int) -> None:
@@ -310,11 +386,16 @@ def report(workloads: List[int], out: str) -> None:
 
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("action", choices=("run", "report"))
+    ap.add_argument("action", choices=("run", "report", "sq", "sq-report"))
     ap.add_argument("--workloads", type=int, nargs="+", default=[3, 4, 5, 6, 7])
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "prof"))
     ap.add_argument("--limit", type=int, default=240, help="seconds per profiler pass")
     a = ap.parse_args()
+    if a.action in ("sq", "sq-report"):
+        if a.action == "sq":
+            run_sq(a.workloads, a.out, a.limit)
+        sq_report(a.workloads, a.out)
+        return
     if a.action == "run":
         run_all(a.workloads, a.out, a.limit)
     report(a.workloads, a.out)
