@@ -116,10 +116,12 @@ def attn_flops(w, n_units):
     return n_units * 2.0 * w.n_q_heads * w.k * (w.q_dim + w.out_dim)
 
 
-def cpu_baseline(w, traces, budget_s):
+def cpu_baseline(w, traces, budget_s, one_thread_steps=0):
     """The oracle (resolve + fp64 attention) on the first steps of the same
     trace, all units of each step in parallel over the host cores, until
-    the time budget is spent. Returns (us per layer-step, steps, threads)."""
+    the time budget is spent; then, if asked, the next few steps on one
+    thread. Returns (us per layer-step, steps, threads, us per layer-step on
+    one thread or None)."""
     import oracle
     from tiered_kv_cache_hs_amd import inputs as I
 
@@ -139,6 +141,7 @@ def cpu_baseline(w, traces, budget_s):
     miss = np.empty(R * L, np.int32)
     out = np.empty((R * L, w.n_q_heads, w.out_dim), np.float32)
     step_times, threads = [], 1
+    one_times = []
     t_start = time.perf_counter()
     for t in range(max_steps):
         q = I.gen_queries(w, t)
@@ -158,13 +161,19 @@ def cpu_baseline(w, traces, budget_s):
             x.q, x.out = q[u].ctypes.data, out[u].ctypes.data
             units.append(x)
         t0 = time.perf_counter()
+        over = len(step_times) >= 2 and time.perf_counter() - t_start > budget_s
+        if over or (one_thread_steps and t >= max_steps - one_thread_steps):
+            if len(one_times) >= one_thread_steps:
+                break
+            oracle.step_batch(units, 1)  # the same oracle on one host thread
+            one_times.append(time.perf_counter() - t0)
+            continue
         threads = oracle.step_batch(units, 0)
         step_times.append(time.perf_counter() - t0)
-        if time.perf_counter() - t_start > budget_s and len(step_times) >= 2:
-            break
     # step 0 is the cold all-miss step; report the warm steps when there are any
     warm = step_times[1:] if len(step_times) > 1 else step_times
-    return 1e6 * float(np.median(warm)) / L, len(step_times), threads
+    one = 1e6 * float(np.median(one_times)) / L if one_times else None
+    return 1e6 * float(np.median(warm)) / L, len(step_times), threads, one
 
 
 def main():
@@ -336,11 +345,16 @@ def main():
     if not args.no_cpu:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
         traces = I.gen_traces(w, total)
-        us, n_steps, threads = cpu_baseline(w, traces, args.cpu_seconds)
+        us, n_steps, threads, us1 = cpu_baseline(w, traces, args.cpu_seconds,
+                                                 one_thread_steps=3 if w.n_units <= 8 else 0)
         result["cpu_baseline"] = {
-            "value": round(us, 1), "unit": "us/layer", "cores": int(threads), "kind": "oracle", "cpu_model": cpu_model(),
-            "sample": f"first {n_steps} steps of the same trace (step 0 cold, median of the rest), "
-                      f"all {w.n_units} units per step, resolve + fp64 attention"}
+            "value": round(us, 1), "unit": "us/layer", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"first {n_steps} steps of the same trace (step 0 cold, median of the "
+                      f"rest), all {w.n_units} units per step, resolve + fp64 attention",
+            "single_thread": None if us1 is None else round(us1, 1),
+            "single_thread_sample": "the next 3 steps on one host thread (median)"
+                                    if us1 is not None else None}
     print(json.dumps(result), flush=True)
 
 
