@@ -226,7 +226,8 @@ hs_status hs_buffer_destroy(hs_buffer_t buf);
  * before describe the old memory: the resolve, attention and prefetch calls
  * refuse them (HS_E_INVAL) until they are created again, and graphs captured
  * before must be captured again. Refused (HS_E_INVAL) for a buffer whose
- * state is shared with others (either side of hs_buffer_create_shared).
+ * state is shared with others (either side of hs_buffer_create_shared):
+ * such a group grows as a whole with hs_buffer_grow_group.
  * Synchronous (waits for stream). */
 hs_status hs_buffer_grow(hs_buffer_t buf, int32_t new_B, void *d_mem, size_t bytes,
                          void *stream);
@@ -272,6 +273,25 @@ hs_status hs_buffer_state_set(hs_buffer_t buf, const int32_t *pos,
 size_t hs_buffer_shared_bytes(hs_pool_t pool, int32_t B);
 hs_status hs_buffer_create_shared(hs_buffer_t base, int32_t layer, void *d_mem,
                                   size_t bytes, hs_buffer_t *out);
+/* Growth of a layer group (HiSparse summary, sections 6 and 8): the group's
+ * state moves with base into d_mem (as hs_buffer_grow, at least
+ * hs_buffer_bytes(pool, new_B) bytes) and the rows of members[i] into
+ * member_mem[i] (at least hs_buffer_shared_bytes(pool, new_B) bytes,
+ * member_bytes[i] given), all 256-byte aligned, with B <= new_B <= HS_MAX_B.
+ * members lists every live buffer made from base or its members by
+ * hs_buffer_create_shared, each once, in any order (n_members of them; 0 when
+ * base has none). Slots [0, B) keep position, stamp and each layer's rows;
+ * slots [B, new_B) are empty; clock, error word and fetch list carry over.
+ * No new region may overlap another or any current region of the group; the
+ * old memory is no longer read afterwards. Batches and graphs made before
+ * must be made again, as after hs_buffer_grow. HS_E_INVAL for a null or
+ * misaligned argument, too few bytes, overlapping memory, a base that is a
+ * member, or a member list that is not exactly the group; nothing changes
+ * then. Synchronous (waits for stream). */
+hs_status hs_buffer_grow_group(hs_buffer_t base, const hs_buffer_t *members,
+                               int32_t n_members, int32_t new_B, void *d_mem,
+                               size_t bytes, void *const *member_mem,
+                               const size_t *member_bytes, void *stream);
 
 /* ------------------------------- batches -----------------------------------
  * An ordered list of n units (buffers of one pool; buffer sizes may

@@ -70,6 +70,7 @@ def test_null_and_shape_checks_without_device():
     assert L.hs_buffer_bytes(None, 4) == 0
     assert L.hs_buffer_shared_bytes(None, 4) == 0
     assert L.hs_buffer_create_shared(None, 0, None, 0, None) == H.HS_E_INVAL
+    assert L.hs_buffer_grow_group(None, None, 0, 4, None, 0, None, None, None) == H.HS_E_INVAL
     assert L.hs_prefetch(None, None) == H.HS_E_INVAL
     d = H.PoolDesc(1, 1, 7, H.HS_BF16, 1, 64, 0, 0, (ctypes.c_int64 * 1)(100))
     out = ctypes.c_void_p()

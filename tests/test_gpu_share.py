@@ -66,6 +66,24 @@ def test_groups_graph_replay(mode):
     compare_run(w, 6, fill="full", graph=True, share_mode=mode)
 
 
+@pytest.mark.parametrize("kind,mode,graph", [("mha", "prefetch", False), ("mha", "serial", True),
+                                             ("latent", "prefetch", True)])
+def test_group_growth_mid_run(kind, mode, graph):
+    """Every layer group grows as a whole (hs_buffer_grow_group) after a few
+    steps: the shared state and each member's rows move, the new empty slots
+    are used first, and slots, state, rows and outputs of every layer keep
+    matching the oracle, which grows each layer's buffer on its own."""
+    if kind == "mha":
+        w = small_workload("mha", I.F32, 40, 17, 300, 7, 6, R=2, L=4, seed=350, share=2)
+        new_B = [96, 60]
+    else:
+        w = small_workload("latent", I.BF16, 300, 197, 3000, 6, 40, R=2, L=4, seed=351, Hq=16,
+                           share=4)
+        new_B = [511, 300]
+    say(f"group growth {kind} {mode} graph={graph}")
+    compare_run(w, w.steps, fill="full", graph=graph, share_mode=mode, grow=(3, new_B))
+
+
 def test_groups_with_write_through_appends():
     w = small_workload("mha", I.F32, 48, 24, 200, 8, 6, R=2, L=4, seed=330, share=4)
     w.append = True
@@ -181,6 +199,92 @@ def test_shared_buffer_argument_checks_and_resolve_refusal():
         torch.cuda.synchronize()
         for b in batches:
             H.hs_batch_destroy(b)
+        for b in reversed(bufs):
+            H.hs_buffer_destroy(b)
+        H.hs_pool_destroy(pool)
+
+
+def test_group_growth_argument_checks():
+    """hs_buffer_grow_group takes exactly the group, fresh memory of the
+    right sizes, and changes nothing when it refuses."""
+    pool = _tiny_pool(L=4)
+    mems, bufs = [], []
+    dev = "cuda"
+
+    def mem(n):
+        t = torch.empty(n, dtype=torch.uint8, device=dev)
+        mems.append(t)
+        return t
+
+    try:
+        B, nB = 16, 40
+        base = H.hs_buffer_create(pool, 0, 0, B, mem(H.hs_buffer_bytes(pool, B)))
+        bufs.append(base)
+        sh1 = H.hs_buffer_create_shared(base, 1, mem(H.hs_buffer_shared_bytes(pool, B)))
+        bufs.append(sh1)
+        sh2 = H.hs_buffer_create_shared(sh1, 2, mem(H.hs_buffer_shared_bytes(pool, B)))
+        bufs.append(sh2)  # made from a member: still base's group
+        other = H.hs_buffer_create(pool, 1, 0, B, mem(H.hs_buffer_bytes(pool, B)))
+        bufs.append(other)
+        for l in range(3):
+            H.hs_pool_set_length(pool, 0, l, 64)
+        single = H.hs_batch_create([base])
+        topk = torch.arange(8, dtype=torch.int32, device=dev)[None]
+        H.hs_resolve(single, topk, 8, torch.empty((1, 8), dtype=torch.int32, device=dev))
+        members3 = H.hs_batch_create([sh1, sh2])
+        H.hs_prefetch(members3)
+        torch.cuda.synchronize()
+        H.hs_batch_destroy(single)
+        H.hs_batch_destroy(members3)
+        rec = H.hs_pool_record_bytes(pool)
+        before = {b: H.hs_buffer_rows(b)[0] for b in (base, sh1, sh2)}
+        state0 = H.hs_buffer_state_get(base, B)
+
+        full = H.hs_buffer_bytes(pool, nB)
+        rows = H.hs_buffer_shared_bytes(pool, nB)
+        g, m1, m2 = mem(full), mem(rows), mem(rows)
+        bad = [
+            ([sh1], [m1]),                  # a member missing
+            ([sh1, sh1], [m1, m2]),         # listed twice
+            ([sh1, other], [m1, m2]),       # not in the group
+            ([sh1, sh2], [m1, m1]),         # members' new memory overlaps
+            ([sh1, sh2], [m1, m2[:rows - 16]]),  # too small
+            ([sh1, sh2], [m1, mem(rows + 256)[16:]]),  # misaligned
+            ([sh1, sh2], [m1, g]),          # overlaps the state's new memory
+        ]
+        for members, mm in bad:
+            with pytest.raises(H.HsError):
+                H.hs_buffer_grow_group(base, members, nB, g, mm)
+        with pytest.raises(H.HsError):  # a member is not a group's base
+            H.hs_buffer_grow_group(sh1, [sh2], nB, g, [m2])
+        with pytest.raises(H.HsError):  # shrinking
+            H.hs_buffer_grow_group(base, [sh1, sh2], B - 1, g, [m1, m2])
+        # nothing changed
+        assert {b: H.hs_buffer_rows(b)[0] for b in (base, sh1, sh2)} == before
+        s1 = H.hs_buffer_state_get(base, B)
+        assert all(np.array_equal(a, b) for a, b in zip(s1[:2], state0[:2]))
+
+        old_rows = {}
+        for b in (base, sh1, sh2):
+            addr, _ = H.hs_buffer_rows(b)
+            t = next(t for t in mems if t.data_ptr() == addr)
+            old_rows[b] = t[: B * rec].clone()
+        H.hs_buffer_grow_group(base, [sh2, sh1], nB, g, [m2, m1])  # any order
+        torch.cuda.synchronize()
+        assert H.hs_buffer_rows(base)[0] == g.data_ptr()
+        assert H.hs_buffer_rows(sh1)[0] == m1.data_ptr()
+        assert H.hs_buffer_rows(sh2)[0] == m2.data_ptr()
+        pos, stamp, clock, err = H.hs_buffer_state_get(sh2, nB)
+        assert np.array_equal(pos[:B], state0[0]) and (pos[B:] == -1).all()
+        assert np.array_equal(stamp[:B], state0[1]) and (stamp[B:] == 0).all()
+        assert clock == state0[2] and err == state0[3]
+        occ = torch.from_numpy(np.repeat(state0[0] >= 0, rec)).to(dev)
+        for b, t in ((base, g), (sh1, m1), (sh2, m2)):
+            assert torch.equal(t[: B * rec][occ], old_rows[b][occ])
+        with pytest.raises(H.HsError):  # still a group: plain growth refused
+            H.hs_buffer_grow(base, nB + 8, mem(H.hs_buffer_bytes(pool, nB + 8)))
+    finally:
+        torch.cuda.synchronize()
         for b in reversed(bufs):
             H.hs_buffer_destroy(b)
         H.hs_pool_destroy(pool)

@@ -565,40 +565,56 @@ hs_status hs_buffer_destroy(hs_buffer_t b) {
   return HS_OK;
 }
 
-hs_status hs_buffer_grow(hs_buffer_t b, int32_t new_B, void *d_mem, size_t bytes,
-                         void *stream) {
-  if (!b || !d_mem) return fail(HS_E_INVAL, "null argument");
-  if (b->base || b->n_members > 0)
-    return fail(HS_E_INVAL, "a buffer whose state is shared cannot grow");
-  if (new_B < b->B || new_B > HS_MAX_B)
-    return fail(HS_E_INVAL, "new B = %d outside [%d, %d]", new_B, b->B, HS_MAX_B);
+static bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uint8_t *a0 = (const uint8_t *)a, *b0 = (const uint8_t *)b;
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// Checks new memory for a buffer that grows to new_B (full state when rows_only
+// is false, rows only for a member of a layer group).
+static hs_status check_grow_mem(const hs_buffer_s *b, int32_t new_B, const void *d_mem,
+                                size_t bytes, bool rows_only) {
+  if (!d_mem) return fail(HS_E_INVAL, "null memory");
   if ((uintptr_t)d_mem % 256) return fail(HS_E_INVAL, "buffer memory must be 256-byte aligned");
-  const size_t rec = b->pool->rec;
+  const size_t need = rows_only ? hs_buffer_shared_bytes(b->pool, new_B)
+                                : hs::buffer_layout(b->pool->rec, new_B).total;
+  if (bytes < need) return fail(HS_E_INVAL, "buffer needs %zu bytes, got %zu", need, bytes);
+  const size_t old = rows_only ? hs_buffer_shared_bytes(b->pool, b->B) : b->lay.total;
+  if (overlaps(d_mem, need, b->mem, old))
+    return fail(HS_E_INVAL, "new memory overlaps the buffer's");
+  return HS_OK;
+}
+
+// Enqueues the move of b's rows [0, B) to nm, and unless rows_only, of its
+// metadata into the layout for new_B, with slots [B, new_B) made empty.
+static hs_status enqueue_move(const hs_buffer_s *b, int32_t new_B, uint8_t *nm, bool rows_only,
+                              hipStream_t st) {
+  const size_t rec = b->pool->rec, B = (size_t)b->B;
+  HS_HIP(hipMemcpyAsync(nm, b->desc.rows, B * rec, hipMemcpyDeviceToDevice, st));
+  if (rows_only) return HS_OK;
   const hs::BufferLayout lay = hs::buffer_layout(rec, new_B);
-  if (bytes < lay.total)
-    return fail(HS_E_INVAL, "buffer needs %zu bytes, got %zu", lay.total, bytes);
-  const uint8_t *o0 = b->mem, *o1 = b->mem + b->lay.total;
-  const uint8_t *n0 = (const uint8_t *)d_mem, *n1 = n0 + lay.total;
-  if (n0 < o1 && o0 < n1) return fail(HS_E_INVAL, "new memory overlaps the buffer's");
-  uint8_t *nm = (uint8_t *)d_mem;
-  const size_t B = (size_t)b->B;
-  hipStream_t st = S(stream);
-  // slots [0, B) keep their rows and metadata; [B, new_B) start empty
-  HS_HIP(hipMemcpyAsync(nm + lay.rows, b->mem + b->lay.rows, B * rec, hipMemcpyDeviceToDevice, st));
   HS_HIP(hipMemcpyAsync(nm + lay.pos, b->mem + b->lay.pos, B * 4, hipMemcpyDeviceToDevice, st));
   HS_HIP(hipMemcpyAsync(nm + lay.stamp, b->mem + b->lay.stamp, B * 4, hipMemcpyDeviceToDevice, st));
   HS_HIP(hipMemcpyAsync(nm + lay.work, b->mem + b->lay.work, B * 8, hipMemcpyDeviceToDevice, st));
   HS_HIP(hipMemcpyAsync(nm + lay.fsrc, b->mem + b->lay.fsrc, B * 4, hipMemcpyDeviceToDevice, st));
   HS_HIP(hipMemcpyAsync(nm + lay.ctl, b->mem + b->lay.ctl, hs::CTL_WORDS * 4,
                         hipMemcpyDeviceToDevice, st));
-  if (new_B > b->B) {
+  if ((size_t)new_B > B) {
     hipError_t e = hs::launch_buffer_init((int32_t *)(nm + lay.pos) + B,
                                           (uint32_t *)(nm + lay.stamp) + B,
-                                          (int32_t *)(nm + lay.fsrc) + B, nullptr, new_B - b->B, st);
+                                          (int32_t *)(nm + lay.fsrc) + B, nullptr,
+                                          new_B - (int32_t)B, st);
     if (e != hipSuccess) return hip_fail(e, "grow init");
   }
-  HS_HIP(hipStreamSynchronize(st));
-  UnitDesc d = b->desc;
+  return HS_OK;
+}
+
+// Points base (full state in nm) and its members (rows in member_mem[i]) at
+// their new memory and uploads their descriptors.
+static hs_status commit_move(hs_buffer_s *base, int32_t new_B, uint8_t *nm,
+                             hs_buffer_s *const *members, void *const *member_mem, int32_t n) {
+  const hs::BufferLayout lay = hs::buffer_layout(base->pool->rec, new_B);
+  UnitDesc d = base->desc;
   d.rows = nm + lay.rows;
   d.pos = (int32_t *)(nm + lay.pos);
   d.stamp = (uint32_t *)(nm + lay.stamp);
@@ -606,13 +622,88 @@ hs_status hs_buffer_grow(hs_buffer_t b, int32_t new_B, void *d_mem, size_t bytes
   d.fsrc = (int32_t *)(nm + lay.fsrc);
   d.ctl = (uint32_t *)(nm + lay.ctl);
   d.B = new_B;
-  HS_HIP(hipMemcpy(b->d_desc, &d, sizeof(UnitDesc), hipMemcpyHostToDevice));
-  b->desc = d;
-  b->mem = nm;
-  b->lay = lay;
-  b->B = new_B;
-  ++b->pool->epoch;  // batch tables made before describe the old memory
+  HS_HIP(hipMemcpy(base->d_desc, &d, sizeof(UnitDesc), hipMemcpyHostToDevice));
+  base->desc = d;
+  base->mem = nm;
+  base->lay = lay;
+  base->B = new_B;
+  for (int32_t i = 0; i < n; ++i) {
+    hs_buffer_s *m = members[i];
+    UnitDesc md = d;  // the group's state, this member's rows and pool records
+    md.rows = (uint8_t *)member_mem[i];
+    md.pages = m->desc.pages;
+    md.len = m->desc.len;
+    HS_HIP(hipMemcpy(m->d_desc, &md, sizeof(UnitDesc), hipMemcpyHostToDevice));
+    m->desc = md;
+    m->mem = (uint8_t *)member_mem[i];
+    m->lay = lay;
+    m->B = new_B;
+  }
+  ++base->pool->epoch;  // batch tables made before describe the old memory
   return HS_OK;
+}
+
+hs_status hs_buffer_grow(hs_buffer_t b, int32_t new_B, void *d_mem, size_t bytes,
+                         void *stream) {
+  if (!b || !d_mem) return fail(HS_E_INVAL, "null argument");
+  if (b->base || b->n_members > 0)
+    return fail(HS_E_INVAL, "a buffer whose state is shared grows with hs_buffer_grow_group");
+  if (new_B < b->B || new_B > HS_MAX_B)
+    return fail(HS_E_INVAL, "new B = %d outside [%d, %d]", new_B, b->B, HS_MAX_B);
+  hs_status s = check_grow_mem(b, new_B, d_mem, bytes, false);
+  if (s) return s;
+  hipStream_t st = S(stream);
+  s = enqueue_move(b, new_B, (uint8_t *)d_mem, false, st);
+  if (s) return s;
+  HS_HIP(hipStreamSynchronize(st));
+  return commit_move(b, new_B, (uint8_t *)d_mem, nullptr, nullptr, 0);
+}
+
+hs_status hs_buffer_grow_group(hs_buffer_t base, const hs_buffer_t *members,
+                               int32_t n_members, int32_t new_B, void *d_mem, size_t bytes,
+                               void *const *member_mem, const size_t *member_bytes,
+                               void *stream) {
+  if (!base || !d_mem || (n_members > 0 && (!members || !member_mem || !member_bytes)))
+    return fail(HS_E_INVAL, "null argument");
+  if (base->base) return fail(HS_E_INVAL, "base is itself a member of a group");
+  if (n_members != base->n_members)
+    return fail(HS_E_INVAL, "the group has %d members, %d given", base->n_members, n_members);
+  if (new_B < base->B || new_B > HS_MAX_B)
+    return fail(HS_E_INVAL, "new B = %d outside [%d, %d]", new_B, base->B, HS_MAX_B);
+  hs_status s = check_grow_mem(base, new_B, d_mem, bytes, false);
+  if (s) return s;
+  const size_t full = hs::buffer_layout(base->pool->rec, new_B).total;
+  const size_t rows = hs_buffer_shared_bytes(base->pool, new_B);
+  for (int32_t i = 0; i < n_members; ++i) {
+    const hs_buffer_s *m = members[i];
+    if (!m || m->base != base) return fail(HS_E_INVAL, "member %d is not in base's group", i);
+    for (int32_t j = 0; j < i; ++j)
+      if (members[j] == m) return fail(HS_E_INVAL, "member %d is listed twice", i);
+    s = check_grow_mem(m, new_B, member_mem[i], member_bytes[i], true);
+    if (s) return s;
+    // new regions must not overlap one another or any memory the move reads
+    if (overlaps(member_mem[i], rows, d_mem, full) ||
+        overlaps(member_mem[i], rows, base->mem, base->lay.total))
+      return fail(HS_E_INVAL, "member %d's new memory overlaps the group's", i);
+    for (int32_t j = 0; j < n_members; ++j) {
+      const size_t old_j = hs_buffer_shared_bytes(base->pool, members[j]->B);
+      if ((j != i && overlaps(member_mem[i], rows, members[j]->mem, old_j)) ||
+          (j < i && overlaps(member_mem[i], rows, member_mem[j], rows)))
+        return fail(HS_E_INVAL, "member %d's new memory overlaps another member's", i);
+    }
+  }
+  for (int32_t i = 0; i < n_members; ++i) {
+    const size_t old_i = hs_buffer_shared_bytes(base->pool, members[i]->B);
+    if (overlaps(d_mem, full, members[i]->mem, old_i))
+      return fail(HS_E_INVAL, "new memory overlaps member %d's rows", i);
+  }
+  hipStream_t st = S(stream);
+  s = enqueue_move(base, new_B, (uint8_t *)d_mem, false, st);
+  for (int32_t i = 0; !s && i < n_members; ++i)
+    s = enqueue_move(members[i], new_B, (uint8_t *)member_mem[i], true, st);
+  HS_HIP(hipStreamSynchronize(st));
+  if (s) return s;
+  return commit_move(base, new_B, (uint8_t *)d_mem, members, member_mem, n_members);
 }
 
 hs_status hs_buffer_reset(hs_buffer_t b, void *stream) {

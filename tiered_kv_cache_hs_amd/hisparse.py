@@ -46,7 +46,7 @@ EXPORTS = (
     "hs_buffer_bytes", "hs_buffer_create", "hs_buffer_destroy", "hs_buffer_grow",
     "hs_buffer_reset",
     "hs_buffer_rows", "hs_buffer_state_get", "hs_buffer_state_set",
-    "hs_buffer_shared_bytes", "hs_buffer_create_shared",
+    "hs_buffer_shared_bytes", "hs_buffer_create_shared", "hs_buffer_grow_group",
     "hs_batch_create", "hs_batch_destroy", "hs_resolve",
     "hs_sparse_attn_workspace", "hs_sparse_attn", "hs_resolve_attn", "hs_prefetch",
     "hs_trace_enable", "hs_trace_read",
@@ -124,6 +124,7 @@ def lib():
         "hs_buffer_state_set": ([vp, vp, vp, u32, i32, vp], i32),
         "hs_buffer_shared_bytes": ([vp, i32], sz),
         "hs_buffer_create_shared": ([vp, i32, vp, sz, P(vp)], i32),
+        "hs_buffer_grow_group": ([vp, P(vp), i32, i32, vp, sz, P(vp), P(sz), vp], i32),
         "hs_batch_create": ([P(vp), i32, P(vp)], i32),
         "hs_batch_destroy": ([vp], i32),
         "hs_resolve": ([vp, vp, i32, vp, vp, vp], i32),
@@ -331,6 +332,22 @@ def hs_buffer_grow(buf: int, new_B: int, mem, stream=None) -> None:
     hs_buffer_bytes(pool, new_B) bytes) with new_B - B empty slots added."""
     nbytes = mem.numel() * mem.element_size()
     _check(lib().hs_buffer_grow(buf, int(new_B), _ptr(mem), nbytes, _stream(stream)))
+
+
+def hs_buffer_grow_group(base: int, members, new_B: int, mem, member_mems, stream=None) -> None:
+    """Grow a layer group: base's state and rows move into `mem` (at least
+    hs_buffer_bytes(pool, new_B) bytes), the rows of members[i] into
+    member_mems[i] (at least hs_buffer_shared_bytes(pool, new_B) bytes).
+    members must be every buffer sharing base's state."""
+    n = len(members)
+    if len(member_mems) != n:
+        raise ValueError("one memory block per member")
+    arr = (ctypes.c_void_p * max(n, 1))(*members)
+    ptrs = (ctypes.c_void_p * max(n, 1))(*[_ptr(m) for m in member_mems])
+    sizes = (ctypes.c_size_t * max(n, 1))(*[m.numel() * m.element_size() for m in member_mems])
+    nbytes = mem.numel() * mem.element_size()
+    _check(lib().hs_buffer_grow_group(base, arr, n, int(new_B), _ptr(mem), nbytes, ptrs, sizes,
+                                      _stream(stream)))
 
 
 def hs_buffer_reset(buf: int, stream=None) -> None:

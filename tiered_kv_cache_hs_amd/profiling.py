@@ -335,7 +335,7 @@ def report(workloads: List[int], out: str) -> None:
                              f"{statistics.median(warm):.2f} |")
         lines += ["", "## Resources (first dispatch of each kernel)", "",
                   "LDS bytes as the profiler reports them: the static allocation (the "
-                  "resolve kernel's dynamic LDS, (max(2H, 4k) + k) * 4 bytes for a hash "
+                  "resolve kernel's dynamic LDS, (max(2H, 5k) + k) * 4 bytes for a hash "
                   "of H entries, is not included).", "",
                   "| kernel | VGPR | AGPR | SGPR | LDS bytes | scratch | workgroup | grid (threads) |",
                   "|---|---|---|---|---|---|---|---|"]

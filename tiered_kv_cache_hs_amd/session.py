@@ -217,17 +217,29 @@ class Session:
         torch.cuda.synchronize()
 
     def grow(self, new_B: List[int]) -> None:
-        """Grow every buffer of request r to new_B[r] slots (hs_buffer_grow)
-        and rebuild the batches; graphs captured before must be captured again."""
-        if self.grouped:
-            raise ValueError("buffers of layer groups share their state and do not grow")
+        """Grow every buffer of request r to new_B[r] slots (hs_buffer_grow, or
+        hs_buffer_grow_group for a layer group) and rebuild the batches;
+        graphs captured before must be captured again."""
         torch.cuda.synchronize()
         self.graphs = []
+        dev = self.device
         for l in range(self.L):
+            if self.resolved_layer(l) != l:
+                continue  # grown with its group's first layer
+            members = [m for m in range(l + 1, self.L) if self.resolved_layer(m) == l]
             for r in range(self.R):
                 t = torch.empty(H.hs_buffer_bytes(self.pool, new_B[r]), dtype=torch.uint8,
-                                device=self.device)
-                H.hs_buffer_grow(self.bufs[l][r], new_B[r], t)
+                                device=dev)
+                if members:
+                    nb = H.hs_buffer_shared_bytes(self.pool, new_B[r])
+                    mts = [torch.empty(nb, dtype=torch.uint8, device=dev) for _ in members]
+                    H.hs_buffer_grow_group(self.bufs[l][r], [self.bufs[m][r] for m in members],
+                                           new_B[r], t, mts)
+                    for m, mt in zip(members, mts):
+                        self.mem[m * self.R + r] = mt
+                        self.Bs[m][r] = new_B[r]
+                else:
+                    H.hs_buffer_grow(self.bufs[l][r], new_B[r], t)
                 self.mem[l * self.R + r] = t
                 self.Bs[l][r] = new_B[r]
         # every batch of the pool is made again once all buffers have moved
