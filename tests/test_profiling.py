@@ -57,3 +57,25 @@ def test_stored_traffic_only_while_sources_match(tmp_path, monkeypatch):
     assert P.stored_traffic("w", "hs_k_resolve") == 123
     assert P.stored_traffic("w", "hs_k_gather") is None
     assert P.stored_traffic("other", "hs_k_resolve") is None
+
+
+def test_bench_report_takes_the_launches_the_benchmark_times(tmp_path):
+    """The default-benchmark summary averages, per kernel, the dispatches of
+    the benchmark's last (eager, event-timed) pass: the last K of 3 (W + K)."""
+    out = str(tmp_path)
+    W, K = 2, 4
+    kname = "void hs::(anonymous namespace)::hs_k_resolve<1024, 4, 2, true>(hs::UnitDesc const*)"
+    # three passes of W + K steps; durations 10 us in the first two passes,
+    # 20 us in the eager pass's warm-up steps and 30 us in its K timed ones
+    durs = [10.0] * (2 * (W + K)) + [20.0] * W + [30.0] * K
+    _write(f"{out}/trace_bench/h/bench_kernel_trace.csv",
+           ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
+           [[kname, 100000 * i, 100000 * i + int(d * 1000)] for i, d in enumerate(durs)])
+    line = {"metric": "m", "value": 1.0, "warmup": W, "steps": K,
+            "config": {"workload": I.workload(3).name, "path": "p"},
+            "kernels_us": {"resolve": 33.0}, "roofline": {}}
+    os.makedirs(out, exist_ok=True)
+    with open(f"{out}/trace_bench.log", "w") as fh:
+        fh.write("noise\n" + json.dumps(line) + "\n")
+    md = open(P.bench_report(out)).read()
+    assert "| hs_k_resolve<1024, 4, 2, true> | 18 | 30.00 | 30.00 | 33.00 | 10.00 |" in md

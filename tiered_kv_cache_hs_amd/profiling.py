@@ -384,13 +384,94 @@ def report(workloads: List[int], out: str) -> None:
     print(f"[profiling] report in {rep}", flush=True)
 
 
+# --------------------------------------------- the default benchmark command
+
+BENCH_DEFAULT = ["python3", "-u", "bench.py"]
+
+
+def bench_trace_cmd(out: str) -> List[str]:
+    return ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
+            os.path.join(out, "trace_bench"), "-o", "bench", "--"] + BENCH_DEFAULT
+
+
+def run_bench_trace(out: str, limit: int) -> None:
+    """Kernel trace of exactly the default benchmark command."""
+    os.makedirs(out, exist_ok=True)
+    os.environ.setdefault("TMPDIR", "/tmp")
+    if _child(bench_trace_cmd(out), os.path.join(out, "trace_bench.log"), limit):
+        raise SystemExit("trace pass of the default benchmark failed")
+
+
+def bench_report(out: str) -> str:
+    """Summary of the default benchmark's kernel trace: for every kernel, the
+    rocprofv3 durations of the launches the benchmark itself times with HIP
+    events (its last, eager pass: the K steps after the W warm-up steps),
+    beside the benchmark's own event-timed averages from the same run, and
+    the launches of the timed graph replays."""
+    from . import inputs as I
+
+    bl = bench_line(os.path.join(out, "trace_bench.log"))
+    if bl is None:
+        raise SystemExit("no benchmark line in the trace log")
+    trace, res = read_trace(os.path.join(out, "trace_bench"))
+    W, K = int(bl["warmup"]), int(bl["steps"])
+    w = next(I.workload(i) for i in range(1, 8) if I.workload(i).name == bl["config"]["workload"])
+    rel = os.path.relpath(out, ROOT)
+    cls_of = {"hs_k_resolve": "resolve", "hs_k_gather": "gather", "hs_k_attn_latent": "attn",
+              "hs_k_attn_mha": "attn", "hs_k_combine": "combine"}
+    lines = [f"# Kernel time of the default benchmark: workload {w.name}", "",
+             f"{w.n_requests} requests x {w.n_layers} layers, {w.kind} records of "
+             f"{w.rec_bytes} bytes, {w.n_q_heads} query heads, k = {w.k}; path "
+             f"{bl['config'].get('path')}.", "",
+             "Made on one MI355X from the repository root by", "",
+             f"    python3 -u -m tiered_kv_cache_hs_amd.profiling bench --out {rel}", "",
+             "which runs the benchmark's default command under the kernel tracer:", "",
+             "    " + " ".join(bench_trace_cmd(rel)), "",
+             f"The benchmark replays W + K = {W} + {K} steps from their hipGraphs (the timed "
+             "region: the last K), replays them all again with an event pair around each "
+             "step, then runs them eagerly with an event pair around every kernel launch "
+             "(the launches whose average is its `kernels_us` and its roofline `avg_us`). "
+             "Each kernel below has its dispatches in that order; the columns take the "
+             "same launches the benchmark averages.", "",
+             "| kernel | dispatches | rocprofv3 avg us (the benchmark's K eager launches) | "
+             "median us | benchmark event-timed avg us | rocprofv3 avg us (timed graph "
+             "replays) |", "|---|---|---|---|---|---|"]
+    ev = bl.get("kernels_us", {})
+    for name, durs in trace.items():
+        base = short_name(name)
+        if base not in cls_of:
+            continue
+        per_step = max(1, len(durs) // (3 * (W + K)))
+        eager = durs[-K * per_step:]
+        timed = durs[W * per_step:(W + K) * per_step]
+        lines.append(f"| {name[:60]} | {len(durs)} | {statistics.mean(eager):.2f} | "
+                     f"{statistics.median(eager):.2f} | {ev.get(cls_of[base], 0.0):.2f} | "
+                     f"{statistics.mean(timed):.2f} |")
+    lines += ["", f"Benchmark line of this run: value {bl['value']} us/layer; roofline "
+              f"{json.dumps(bl.get('roofline'))}.", "",
+              "The event pair around an eager launch also holds the launch's own dispatch "
+              "latency, so event-timed averages read a few us above the kernel's duration."]
+    os.makedirs(os.path.join(out, "report"), exist_ok=True)
+    path = os.path.join(out, "report", f"hs_kernels_bench_default_{w.name}.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"[profiling] {path}", flush=True)
+    return path
+
+
 def main() -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("action", choices=("run", "report", "sq", "sq-report"))
+    ap.add_argument("action", choices=("run", "report", "sq", "sq-report", "bench",
+                                       "bench-report"))
     ap.add_argument("--workloads", type=int, nargs="+", default=[3, 4, 5, 6, 7])
     ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "prof"))
     ap.add_argument("--limit", type=int, default=240, help="seconds per profiler pass")
     a = ap.parse_args()
+    if a.action in ("bench", "bench-report"):
+        if a.action == "bench":
+            run_bench_trace(a.out, a.limit)
+        bench_report(a.out)
+        return
     if a.action in ("sq", "sq-report"):
         if a.action == "sq":
             run_sq(a.workloads, a.out, a.limit)
