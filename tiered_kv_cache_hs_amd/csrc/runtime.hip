@@ -885,9 +885,13 @@ static hs_status plan_attn(hs_batch_t b, int32_t Hq, int32_t k, AttnPlan *pl) {
     const int gq = Hq / p->Hkv;
     if (gq != 1 && gq != 2 && gq != 4 && gq != 8)
       return fail(HS_E_INVAL, "GQA group %d unsupported", gq);
+    // splits until the grid reaches 512 workgroups (two per compute unit)
+    // or a split would hold fewer than 64 slots; on the 32-request GQA
+    // workload (256 (unit, KV head) pairs) 2 splits of 1024 slots measured
+    // 2.4% faster per layer than 4 of 512
     base = b->n * p->Hkv;
     min_chunk = 64;
-    target = 1024;
+    target = 512;
     pl->dv = p->D;
   } else {
     if (p->dtype != HS_BF16 || p->Dl != 512 || p->Dr != 64)
