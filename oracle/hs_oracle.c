@@ -405,7 +405,8 @@ typedef struct {
 
 /* Resolve then attend for every unit; units are independent, so they are
  * spread over n_threads OpenMP threads (<= 0: the runtime default). Returns
- * the number of threads used. */
+ * the number of threads that get work: the team size, at most one thread per
+ * unit. */
 int oracle_step_batch(int32_t n, const oracle_unit *u, int32_t n_threads) {
   int used = 1;
 #ifdef _OPENMP
@@ -415,6 +416,7 @@ int oracle_step_batch(int32_t n, const oracle_unit *u, int32_t n_threads) {
 #pragma omp single
     used = omp_get_num_threads();
   }
+  if (used > n) used = n > 0 ? n : 1;
 #pragma omp parallel for schedule(dynamic, 1)
 #endif
   for (int32_t i = 0; i < n; ++i) {
