@@ -204,11 +204,15 @@ hs_status hs_pool_append(hs_pool_t pool, int32_t req, int32_t layer,
  * (slot -> logical position, -1 when empty), LRU stamps, clock and error
  * word. The memory is caller-owned device memory of at least
  * hs_buffer_bytes(pool, B) bytes, 256-byte aligned; the library only writes
- * into it and never frees it. */
+ * into it and never frees it. Beside it the library keeps the inverse page
+ * table (position -> slot, -1 when not resident; 4 bytes per position the
+ * request can reach, max_tokens), allocated by hs_buffer_create and freed by
+ * hs_buffer_destroy, which lets the resolve classify a selected position
+ * with one read. */
 size_t hs_buffer_bytes(hs_pool_t pool, int32_t B);
 /* Enqueues the empty state (every slot empty, clock 0, error 0) on stream.
  * HS_E_INVAL for B < 1, too few bytes or misaligned memory; HS_E_RANGE for
- * a bad req/layer. */
+ * a bad req/layer; HS_E_HIP if the inverse page table cannot be allocated. */
 hs_status hs_buffer_create(hs_pool_t pool, int32_t req, int32_t layer,
                            int32_t B, void *d_mem, size_t bytes, void *stream,
                            hs_buffer_t *out);

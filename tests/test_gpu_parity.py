@@ -166,6 +166,72 @@ def test_data_errors_leave_state_unchanged():
         sess.close()
 
 
+@pytest.mark.parametrize("B", [16, 2048])
+def test_restored_state_then_resolves_and_repeats(B):
+    """A state restored by hs_buffer_state_set, then resolves checked against
+    the oracle step by step (for B > 1024 the resolve classifies positions
+    through the inverse page table, which the restore rebuilds), then a
+    position repeated among the hits and one repeated among the misses: each
+    is refused with the state unchanged, and a valid selection resolves
+    after them."""
+    k = 4 if B == 16 else 600
+    ctx = 64 if B == 16 else 4000
+    rng = np.random.default_rng(B)
+    held = rng.choice(ctx, size=B // 2, replace=False).astype(np.int32)
+    pos = np.full(B, -1, dtype=np.int32)
+    at = rng.choice(B, size=B // 2, replace=False)
+    pos[at] = held
+    clock = 9
+    stamp = np.where(pos >= 0, rng.integers(1, 2 * clock + 1, size=B), 0).astype(np.uint32)
+    # steps: half from the restored positions (hits), half new (misses)
+    def sel(t):
+        h = rng.choice(held, size=k // 2, replace=False)
+        fresh = np.setdiff1d(np.arange(ctx, dtype=np.int32), held)
+        m = rng.choice(fresh, size=k - k // 2, replace=False)
+        return rng.permutation(np.concatenate([h, m])).astype(np.int32)
+    tr = np.stack([sel(t)[None, :] for t in range(3)])
+    hit_dup = tr[2, 0].copy()
+    hit_dup[1] = hit_dup[0] = held[0]
+    miss_dup = tr[2, 0].copy()
+    fresh0 = int(np.setdiff1d(np.arange(ctx), np.concatenate([held, tr[:, 0].ravel()]))[0])
+    miss_dup[1] = miss_dup[0] = fresh0
+    tr = np.concatenate([tr, hit_dup[None, None], miss_dup[None, None], tr[2:3]])
+    w = _small("mha", I.F32, B, k, ctx, tr.shape[0], 1, seed=B + 3)
+    sess = Session(w, tr.shape[0], fill="full", traces=tr)
+    try:
+        H.hs_buffer_state_set(sess.bufs[0][0], pos, stamp, clock)
+        ob = oracle.OracleBuffer(B, w.rec_bytes, with_rows=False)
+        ob.pos[:] = pos
+        ob.stamp[:] = stamp
+        ob.clock[0] = clock
+        for t in range(3):
+            sess.step(t)
+            torch.cuda.synchronize()
+            so, mo = oracle.resolve(ob, tr[t, 0], None, ctx)
+            g_pos, g_stamp, g_clock, g_err = sess.state(0, 0)
+            assert g_err == 0 and g_clock == int(ob.clock[0])
+            assert np.array_equal(sess.slots[0, 0].cpu().numpy(), so)
+            assert int(sess.miss[0, 0]) == mo
+            assert np.array_equal(g_pos, ob.pos) and np.array_equal(g_stamp, ob.stamp)
+        p0, s0, c0, _ = sess.state(0, 0)
+        for t in (3, 4):
+            sess.step(t)
+            torch.cuda.synchronize()
+            p, s, c, e = sess.state(0, 0)
+            assert e & H.HS_ERR_DUP
+            assert np.array_equal(p, p0) and np.array_equal(s, s0) and c == c0
+            assert int(sess.miss[0, 0]) == -1
+        sess.step(5)  # the selection of step 2 again: all hits
+        torch.cuda.synchronize()
+        so, mo = oracle.resolve(ob, tr[5, 0], None, ctx)
+        g_pos, g_stamp, g_clock, _ = sess.state(0, 0)
+        assert mo == 0 and int(sess.miss[0, 0]) == 0
+        assert np.array_equal(sess.slots[0, 0].cpu().numpy(), so)
+        assert np.array_equal(g_pos, ob.pos) and np.array_equal(g_stamp, ob.stamp)
+    finally:
+        sess.close()
+
+
 def test_clock_exhaustion_and_state_validation():
     w = _small("mha", I.F32, 4, 1, 16, 2, 1, seed=11)
     sess = Session(w, 2, fill="full", traces=np.array([[[1]], [[1]]], dtype=np.int32))

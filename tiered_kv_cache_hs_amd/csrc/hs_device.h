@@ -21,10 +21,12 @@ struct __attribute__((aligned(128))) UnitDesc {
                           // is the device-visible address of records
                           // [i << page_shift, (i + 1) << page_shift) in host memory
   const int64_t *len;   // the unit's pool length (device memory)
+  int32_t *inv;         // inverse page table: position -> slot, -1 when the
+                        // position is not resident; inv_len entries
   int32_t B;
   int32_t page_shift;   // log2 of the records per pool page
   int32_t n_pages;      // entries of the page table
-  int32_t pad[3];
+  int32_t inv_len;      // the request's most positions
 };
 
 #define HS_GLOBAL __attribute__((address_space(1)))
@@ -47,9 +49,11 @@ struct UnitG {
   HS_GLOBAL uint32_t *ctl;
   HS_GLOBAL const uint64_t *pages;
   HS_GLOBAL const int64_t *len;
+  HS_GLOBAL int32_t *inv;
   int32_t B;
   int32_t page_shift;
   int32_t n_pages;
+  int32_t inv_len;
 };
 
 __device__ __forceinline__ UnitG unit_g(const UnitDesc &d) {
@@ -62,9 +66,11 @@ __device__ __forceinline__ UnitG unit_g(const UnitDesc &d) {
   g.ctl = (HS_GLOBAL uint32_t *)d.ctl;
   g.pages = (HS_GLOBAL const uint64_t *)d.pages;
   g.len = (HS_GLOBAL const int64_t *)d.len;
+  g.inv = (HS_GLOBAL int32_t *)d.inv;
   g.B = d.B;
   g.page_shift = d.page_shift;
   g.n_pages = d.n_pages;
+  g.inv_len = d.inv_len;
   return g;
 }
 
@@ -150,6 +156,11 @@ hipError_t launch_prefetch(const UnitDesc *d_units, int n, int rec_bytes, int wo
                            int batch, hipStream_t stream);
 hipError_t launch_regather(const UnitDesc *d_unit, int B, int rec_bytes,
                            hipStream_t stream);
+// Inverse page table upkeep: every entry -1; then (rebuild) entry pos[s] = s
+// for every occupied slot s < B.
+hipError_t launch_inv_clear(int32_t *inv, int64_t n, hipStream_t stream);
+hipError_t launch_inv_rebuild(int32_t *inv, int64_t n, const int32_t *pos, int B,
+                              hipStream_t stream);
 // Records [pos, pos + n) of a unit's pool (page table d_pages) from device
 // memory, then its length raised to new_len.
 hipError_t launch_append(const uint64_t *d_pages, int page_shift, int64_t pos, int64_t n,

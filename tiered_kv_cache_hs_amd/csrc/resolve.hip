@@ -17,6 +17,15 @@
 //    Thread t owns a contiguous run of SPT slots and KPT selection entries,
 //    so ranks in slot order and in selection order are one exclusive block
 //    scan of per-thread counts (wave64 shuffles + one LDS pass over waves).
+//    Hits, for buffers of more than 1024 slots: each unit keeps an inverse
+//    page table (position -> slot, -1 when not resident) in device memory,
+//    updated with every eviction and fill, so one dependent read per
+//    selected position tells hit from miss and the host reads of the misses
+//    start without probing every slot; a hit claims its slot in an LDS
+//    bitmap (a slot claimed twice is a repeated position) and only the
+//    misses go into the hash table, which catches repeats among them. For
+//    1024 slots or fewer, the probe is cheaper than that dependent read:
+//    the whole selection goes into the hash table and every slot probes it.
 //    The hash table is open addressing with linear probing in LDS,
 //    capacity the power of two >= 4k (>= 2k for the largest k), keys
 //    inserted with atomicCAS; inserts and lookups read 16-byte buckets of
@@ -132,19 +141,22 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 // host reads is issued as soon as the misses are known, so it overlaps the
 // victim selection. Without GATHER the fetch is left to the attention
 // kernels (fsrc says which rows they must read from the host).
-template <int NT, int SPT, int KPT, bool GATHER>
+template <int NT, int SPT, int KPT, bool GATHER, bool INV>
 __global__ __launch_bounds__(NT) void hs_k_resolve(
     const UnitDesc *__restrict__ units, const int32_t *__restrict__ topk_all,
     int k, int hlog2, int rec16, int32_t *__restrict__ slots_all,
     int32_t *__restrict__ miss_all) {
-  // LDS: region A holds the hash table (keys, values: 2H ints) during build
-  // and probe, then the miss and victim lists (k ints each), the missed
-  // records' host addresses (k 64-bit words) and positions (k ints); region B
-  // holds slot_of[k].
+  // LDS: region A holds the hash table (keys, and without INV the
+  // selection index of each: 2H ints) during the hit search, then the miss
+  // and victim lists (k ints each), the missed records' host addresses (k
+  // 64-bit words), their positions and the victims' previous positions (k
+  // ints each); region B holds slot_of[k]. s_claim (INV): one bit per slot,
+  // set by the hit that claims it.
   extern __shared__ __attribute__((aligned(16))) int lds[];
   constexpr int NW = NT / 64;
   __shared__ int scan_buf[2][RES_MAX_WAVES];
   __shared__ uint32_t hist[3][256];
+  __shared__ uint32_t s_claim[INV ? HS_MAX_B / 32 : 1];
   __shared__ uint32_t s_flag;
   __shared__ uint32_t s_smin, s_smax, s_cmin, s_cmax;  // stamp / secondary bounds
 
@@ -155,7 +167,8 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   int *victim_list = lds + k;
   uint64_t *miss_addr = (uint64_t *)(lds + 2 * k);
   int *miss_pos = lds + 4 * k;
-  const int regionA = (2 * H > 5 * k) ? 2 * H : 5 * k;
+  int *victim_old = lds + 5 * k;
+  const int regionA = (2 * H > 6 * k) ? 2 * H : 6 * k;
   int *slot_of = lds + regionA;
 
   const int u = blockIdx.x;
@@ -180,13 +193,16 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   }
   int32_t sp[SPT];
   uint32_t st[SPT];
-  // the pool page of each selected position (clamped into the page table: an
-  // invalid position is a data error found below, its entry never used)
+  // the pool page (and with INV the inverse page-table entry) of each
+  // selected position, clamped into the table: an invalid position is a
+  // data error found below, its entries never used
   uint64_t tpage[KPT];
-  if (GATHER) {
+  int32_t tinv[KPT];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j)
+  for (int j = 0; j < KPT; ++j) {
+    if (GATHER)
       tpage[j] = d.pages[min((uint32_t)tk[j] >> d.page_shift, (uint32_t)d.n_pages - 1u)];
+    if (INV) tinv[j] = d.inv[min((uint32_t)tk[j], (uint32_t)d.inv_len - 1u)];
   }
   if (s0 + SPT <= B && (SPT % 4) == 0) {
     // the whole run is in range: 16-byte loads, no per-slot branches
@@ -210,6 +226,8 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
 
   for (int i = tid; i < H; i += NT) hkey[i] = EMPTY_KEY;
   for (int i = tid; i < k; i += NT) slot_of[i] = -1;
+  if (INV)
+    for (int i = tid; i < (B + 31) / 32; i += NT) s_claim[i] = 0u;
   if (tid < 256) {
     hist[0][tid] = 0;
     hist[1][tid] = 0;
@@ -224,9 +242,31 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   int parity = 0;
   lds_barrier();
 
-  // ---- 1. hash build of the selection (and range / duplicate checks); the
-  // KPT inserts of a thread advance together, one probe step per round
+  // ---- 1. hits. INV: through the inverse page table, a selected position
+  // whose entry names a slot is resident there; each hit claims its slot in
+  // an LDS bitmap, and a slot claimed twice means a repeated position.
+  // Otherwise the hits are found by the probe of step 2.
   uint32_t myflag = 0;
+  if (INV) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (k0 + j >= k || tk[j] < 0 || (int64_t)tk[j] >= len) continue;
+      const int c = tinv[j];
+      if ((unsigned)c < (unsigned)B) {
+        const uint32_t bit = 1u << (c & 31);
+        if (atomicOr(&s_claim[c >> 5], bit) & bit) myflag |= HS_ERR_DUP;
+        slot_of[k0 + j] = c;
+      }
+    }
+    if (myflag) atomicOr(&s_flag, myflag);
+    lds_barrier();
+    myflag = 0;
+  }
+
+  // hash build (with range and repeat checks): INV, of the missed positions
+  // only (repeats among them); otherwise of the whole selection, each entry
+  // keeping its selection index for the probe. The KPT inserts of a thread
+  // advance together, one probe step per round.
   uint32_t hcur[KPT];
   uint32_t pend = 0;  // inserts still probing
 #pragma unroll
@@ -235,7 +275,7 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
     if (k0 + j >= k) continue;
     if (tk[j] < 0 || (int64_t)tk[j] >= len)
       myflag |= HS_ERR_RANGE;
-    else
+    else if (!INV || slot_of[k0 + j] < 0)
       pend |= 1u << j;
   }
   // Linear probing, read 4 entries (one 16-byte aligned bucket) at a time:
@@ -268,7 +308,7 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
         const uint32_t at = (hcur[j] & ~3u) + (uint32_t)target;
         const int old = atomicCAS(&hkey[at], EMPTY_KEY, tk[j]);
         if (old == EMPTY_KEY) {
-          hval[at] = k0 + j;
+          if (!INV) hval[at] = k0 + j;
           pend &= ~(1u << j);
         } else if (old == tk[j]) {
           myflag |= HS_ERR_DUP;
@@ -295,9 +335,41 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
     return;
   }
 
-  // ---- 2. probe every slot of the buffer (SPT lookups advance together)
+  // candidate keys: (stamp << 32) | secondary, secondary = slot when empty,
+  // B + position otherwise; bounds of both halves over the candidates (non-
+  // hit slots), met in LDS
   uint32_t hitmask = 0;
-  {
+  uint64_t key[SPT];
+  uint32_t candmask = 0;
+  auto candidate_keys = [&]() {
+    uint32_t smin = 0xFFFFFFFFu, smax = 0u, cmin = 0xFFFFFFFFu, cmax = 0u;
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int s = s0 + j;
+      const uint32_t second = sp[j] < 0 ? (uint32_t)s : (uint32_t)(B + sp[j]);
+      key[j] = ((uint64_t)st[j] << 32) | second;
+      if (s < B && !((hitmask >> j) & 1u)) {
+        candmask |= 1u << j;
+        smin = st[j] < smin ? st[j] : smin;
+        smax = st[j] > smax ? st[j] : smax;
+        cmin = second < cmin ? second : cmin;
+        cmax = second > cmax ? second : cmax;
+      }
+    }
+    smin = wave_minmax_u32<false>(smin);
+    smax = wave_minmax_u32<true>(smax);
+    cmin = wave_minmax_u32<false>(cmin);
+    cmax = wave_minmax_u32<true>(cmax);
+    if (lane == 0) {
+      atomicMin(&s_smin, smin);
+      atomicMax(&s_smax, smax);
+      atomicMin(&s_cmin, cmin);
+      atomicMax(&s_cmax, cmax);
+    }
+  };
+
+  if (!INV) {
+    // ---- 2. probe every slot of the buffer (SPT lookups advance together)
     uint32_t h[SPT];
     uint32_t pend = 0;
 #pragma unroll
@@ -336,38 +408,11 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
         }
       }
     }
+    candidate_keys();
+    lds_barrier();  // slot_of complete
   }
-  // candidate keys: (stamp << 32) | secondary, secondary = slot when empty,
-  // B + position otherwise; bounds of both halves over the candidates
-  uint64_t key[SPT];
-  uint32_t candmask = 0;
-  uint32_t smin = 0xFFFFFFFFu, smax = 0u, cmin = 0xFFFFFFFFu, cmax = 0u;
-#pragma unroll
-  for (int j = 0; j < SPT; ++j) {
-    const int s = s0 + j;
-    const uint32_t second = sp[j] < 0 ? (uint32_t)s : (uint32_t)(B + sp[j]);
-    key[j] = ((uint64_t)st[j] << 32) | second;
-    if (s < B && !((hitmask >> j) & 1u)) {
-      candmask |= 1u << j;
-      smin = st[j] < smin ? st[j] : smin;
-      smax = st[j] > smax ? st[j] : smax;
-      cmin = second < cmin ? second : cmin;
-      cmax = second > cmax ? second : cmax;
-    }
-  }
-  smin = wave_minmax_u32<false>(smin);
-  smax = wave_minmax_u32<true>(smax);
-  cmin = wave_minmax_u32<false>(cmin);
-  cmax = wave_minmax_u32<true>(cmax);
-  if (lane == 0) {
-    atomicMin(&s_smin, smin);
-    atomicMax(&s_smax, smax);
-    atomicMin(&s_cmin, cmin);
-    atomicMax(&s_cmax, cmax);
-  }
-  lds_barrier();  // slot_of complete; the hash table is dead from here on
 
-  // ---- 3. misses in selection order
+  // ---- 3. misses in selection order (the hash table is dead from here on)
   int my_miss = 0;
   bool miss_here[KPT];
 #pragma unroll
@@ -420,6 +465,18 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
 #pragma unroll
       for (int b = 0; b < GB; ++b) gv[b] = __builtin_nontemporal_load(chunk_src(tid + NT * b));
     }
+  }
+
+  if (INV) {
+    // hit slots (claimed in step 1) and the candidate keys, while the first
+    // host reads are in flight
+#pragma unroll
+    for (int j = 0; j < SPT; ++j) {
+      const int s = s0 + j;
+      if (s < B && ((s_claim[s >> 5] >> (s & 31)) & 1u)) hitmask |= 1u << j;
+    }
+    candidate_keys();
+    lds_barrier();
   }
 
   // ---- 4. victims: the m smallest keys among non-hit slots, by an MSB-first
@@ -518,8 +575,12 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
     return;
   }
 #pragma unroll
-  for (int j = 0; j < SPT; ++j)
-    if ((vmask >> j) & 1u) victim_list[vrank++] = s0 + j;
+  for (int j = 0; j < SPT; ++j) {
+    if ((vmask >> j) & 1u) {
+      victim_old[vrank] = sp[j];  // the position it held, -1 if empty
+      victim_list[vrank++] = s0 + j;
+    }
+  }
   lds_barrier();
 
   // ---- 6. in-place update: fills get 2c - 1, hits get 2c
@@ -530,9 +591,14 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
     const int s = victim_list[r];
     const int i = miss_list[r];
     const int32_t p = miss_pos[r];
+    const int32_t op = victim_old[r];
     d.pos[s] = p;
     d.stamp[s] = 2u * c - 1u;
     slot_of[i] = s;
+    // inverse page table: the evicted position leaves, the fetched one
+    // enters (distinct positions: one is outside the selection, one in it)
+    if (op >= 0) d.inv[op] = -1;
+    d.inv[p] = s;
     // the fetch list is written even when this kernel fetches: buffers of
     // other layers that share this state fetch their own records from it
     d.work[r] = int2v{s, p};
@@ -688,12 +754,16 @@ template <int NT, int SPT, int KPT>
 hipError_t launch_select(const UnitDesc *d_units, int n, const int32_t *d_topk, int k,
                          int hlog2, int rec16, bool gather, size_t lds, int32_t *d_slots,
                          int32_t *d_miss, hipStream_t stream) {
+  // hits through the inverse page table for buffers of more than 1024
+  // slots (two or more per thread), where probing every slot costs more
+  // than the table's dependent read; through the probe below that
+  constexpr bool INV = SPT >= 2;
   trace_begin(HS_TRACE_RESOLVE, stream);
   if (gather)
-    hipLaunchKernelGGL((hs_k_resolve<NT, SPT, KPT, true>), dim3(n), dim3(NT), lds, stream,
+    hipLaunchKernelGGL((hs_k_resolve<NT, SPT, KPT, true, INV>), dim3(n), dim3(NT), lds, stream,
                        d_units, d_topk, k, hlog2, rec16, d_slots, d_miss);
   else
-    hipLaunchKernelGGL((hs_k_resolve<NT, SPT, KPT, false>), dim3(n), dim3(NT), lds, stream,
+    hipLaunchKernelGGL((hs_k_resolve<NT, SPT, KPT, false, INV>), dim3(n), dim3(NT), lds, stream,
                        d_units, d_topk, k, hlog2, rec16, d_slots, d_miss);
   trace_end(stream);
   return hipGetLastError();
@@ -720,7 +790,7 @@ hipError_t launch_select_k(const UnitDesc *d_units, int n, const int32_t *d_topk
 int hash_log2(int k) {
   int h = 2;
   while ((1 << h) < 4 * k) ++h;
-  const size_t region_a = (size_t)(2 * (1 << h) > 5 * k ? 2 * (1 << h) : 5 * k);
+  const size_t region_a = (size_t)(2 * (1 << h) > 6 * k ? 2 * (1 << h) : 6 * k);
   if ((region_a + k) * sizeof(int) > (128u << 10)) --h;
   return h;
 }
@@ -729,7 +799,7 @@ int hash_log2(int k) {
 
 size_t resolve_lds_bytes(int k) {
   const int H = 1 << hash_log2(k);
-  const int regionA = (2 * H > 5 * k) ? 2 * H : 5 * k;
+  const int regionA = (2 * H > 6 * k) ? 2 * H : 6 * k;
   return (size_t)(regionA + k) * sizeof(int);
 }
 
@@ -786,6 +856,33 @@ hipError_t launch_prefetch(const UnitDesc *d_units, int n, int rec_bytes, int wo
   else
     hipLaunchKernelGGL(hs_k_gather<1>, grid, block, 0, stream, d_units, G, rec_bytes / 16);
   trace_end(stream);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(256) void hs_k_inv_clear(int32_t *inv, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    inv[i] = -1;
+}
+
+__global__ __launch_bounds__(256) void hs_k_inv_fill(int32_t *inv, int64_t n,
+                                                     const int32_t *pos, int B) {
+  const int s = blockIdx.x * 256 + threadIdx.x;
+  if (s < B && pos[s] >= 0 && (int64_t)pos[s] < n) inv[pos[s]] = s;
+}
+
+hipError_t launch_inv_clear(int32_t *inv, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+  hipLaunchKernelGGL(hs_k_inv_clear, dim3((unsigned)blocks), dim3(256), 0, stream, inv, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_inv_rebuild(int32_t *inv, int64_t n, const int32_t *pos, int B,
+                              hipStream_t stream) {
+  hipError_t e = launch_inv_clear(inv, n, stream);
+  if (e != hipSuccess || B < 1) return e;
+  hipLaunchKernelGGL(hs_k_inv_fill, dim3((unsigned)((B + 255) / 256)), dim3(256), 0, stream, inv,
+                     n, pos, B);
   return hipGetLastError();
 }
 

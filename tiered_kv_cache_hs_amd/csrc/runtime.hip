@@ -117,6 +117,8 @@ struct hs_buffer_s {
   hs::BufferLayout lay{};
   UnitDesc desc{};
   UnitDesc *d_desc = nullptr;  // single-unit table (state restore)
+  int32_t *d_inv = nullptr;    // inverse page table this buffer owns (not for a
+                               // buffer sharing another's state)
 };
 
 struct hs_batch_s {
@@ -499,12 +501,18 @@ hs_status hs_buffer_create(hs_pool_t p, int32_t req, int32_t layer, int32_t B, v
   d.B = B;
   d.page_shift = p->page_shift;
   d.n_pages = (int32_t)p->max_pages[req];
-  hipError_t e = hipMalloc(&b->d_desc, sizeof(UnitDesc));
+  // the inverse page table covers every position the request can reach
+  d.inv_len = (int32_t)std::max<int64_t>(1, p->max_cap[req]);
+  hipError_t e = hipMalloc(&b->d_inv, sizeof(int32_t) * (size_t)d.inv_len);
+  d.inv = b->d_inv;
+  if (e == hipSuccess) e = hipMalloc(&b->d_desc, sizeof(UnitDesc));
   if (e == hipSuccess)
     e = hipMemcpy(b->d_desc, &b->desc, sizeof(UnitDesc), hipMemcpyHostToDevice);
   if (e == hipSuccess) e = hs::launch_buffer_init(d.pos, d.stamp, d.fsrc, d.ctl, B, S(stream));
+  if (e == hipSuccess) e = hs::launch_inv_clear(d.inv, d.inv_len, S(stream));
   if (e != hipSuccess) {
     if (b->d_desc) (void)hipFree(b->d_desc);
+    if (b->d_inv) (void)hipFree(b->d_inv);
     delete b;
     return hip_fail(e, "buffer create");
   }
@@ -561,6 +569,7 @@ hs_status hs_buffer_destroy(hs_buffer_t b) {
     return fail(HS_E_INVAL, "%d shared buffers still use this buffer's state", b->n_members);
   if (b->base) --b->base->n_members;
   if (b->d_desc) (void)hipFree(b->d_desc);
+  if (b->d_inv) (void)hipFree(b->d_inv);
   delete b;
   return HS_OK;
 }
@@ -710,6 +719,7 @@ hs_status hs_buffer_reset(hs_buffer_t b, void *stream) {
   if (!b) return fail(HS_E_INVAL, "null buffer");
   hipError_t e = hs::launch_buffer_init(b->desc.pos, b->desc.stamp, b->desc.fsrc, b->desc.ctl, b->B,
                                          S(stream));
+  if (e == hipSuccess) e = hs::launch_inv_clear(b->desc.inv, b->desc.inv_len, S(stream));
   if (e != hipSuccess) return hip_fail(e, "buffer reset");
   return HS_OK;
 }
@@ -768,7 +778,9 @@ hs_status hs_buffer_state_set(hs_buffer_t b, const int32_t *pos, const uint32_t 
   HS_HIP(hipMemcpyAsync(b->desc.stamp, stamp, sizeof(uint32_t) * b->B, hipMemcpyHostToDevice,
                         S(stream)));
   HS_HIP(hipMemcpyAsync(b->desc.ctl, ctl, sizeof ctl, hipMemcpyHostToDevice, S(stream)));
-  hipError_t e = hs::launch_regather(b->d_desc, b->B, (int)b->pool->rec, S(stream));
+  hipError_t e = hs::launch_inv_rebuild(b->desc.inv, b->desc.inv_len, b->desc.pos, b->B,
+                                        S(stream));
+  if (e == hipSuccess) e = hs::launch_regather(b->d_desc, b->B, (int)b->pool->rec, S(stream));
   if (e != hipSuccess) return hip_fail(e, "regather");
   HS_HIP(hipStreamSynchronize(S(stream)));
   return HS_OK;
