@@ -393,27 +393,31 @@ __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
     }
   };
 
+  // The loop leaves only at its latch, the remaining steps after it: an
+  // exit between the register rotations gave the compiler a path from the
+  // middle of the loop back to its header on which the loads of the next
+  // step were still in flight, and it waited for them there, at the top of
+  // every iteration (each second step then waited the whole load latency).
+  int st = 0;
   if (DEPTH == 2) {
     Rows R0, R1, R2;
     issue(0, R0);
     issue(1, R1);
-    for (int st = 0;;) {
-      if (st >= n_steps) break;
-      step(st++, R0, R2);
-      if (st >= n_steps) break;
-      step(st++, R1, R0);
-      if (st >= n_steps) break;
-      step(st++, R2, R1);
+    for (; st + 3 <= n_steps; st += 3) {
+      step(st, R0, R2);
+      step(st + 1, R1, R0);
+      step(st + 2, R2, R1);
     }
+    if (st < n_steps) step(st++, R0, R2);
+    if (st < n_steps) step(st, R1, R0);
   } else {
     Rows R0, R1;
     issue(0, R0);
-    for (int st = 0;;) {
-      if (st >= n_steps) break;
-      step(st++, R0, R1);
-      if (st >= n_steps) break;
-      step(st++, R1, R0);
+    for (; st + 2 <= n_steps; st += 2) {
+      step(st, R0, R1);
+      step(st + 1, R1, R0);
     }
+    if (st < n_steps) step(st, R0, R1);
   }
 
   const int any_bad = __syncthreads_or(bad ? 1 : 0);
