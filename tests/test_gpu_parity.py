@@ -105,6 +105,21 @@ def test_latent_heads_per_workgroup(hpw, splits, fused):
         H.hs_set_tuning(0, 0)
 
 
+@pytest.mark.parametrize("hpw", [16, 32, 64])
+@pytest.mark.parametrize("k", [64, 96, 160, 250])
+def test_latent_step_pipeline_tails(hpw, k):
+    """One split over the whole selection, so the chunk is 2, 3, 5 or 8
+    steps of 32 slots (the last one ragged for k = 250): every remainder of
+    the step loop's register rotations (two buffers for 16 and 64 heads per
+    workgroup, three for 32) runs after the loop."""
+    w = _small("latent", I.BF16, 300, k, 3000, 3, 30, R=2, seed=900 + k + hpw, Hq=64)
+    H.hs_set_tuning(1, hpw)
+    try:
+        compare_run(w, 3, fill="full")
+    finally:
+        H.hs_set_tuning(0, 0)
+
+
 def test_multi_request_multi_layer_small():
     w = _small("mha", I.BF16, 600, 200, 3000, 6, 50, R=3, L=2, seed=77, Hkv=2, D=128, Hq=16)
     compare_run(w, 6, fill="full")

@@ -37,7 +37,8 @@
 // tile holds rows 4(l/16)+i, so the lane's 8 P values (2 tiles x 4 rows)
 // are the 8 k-elements of the PV operand, and the V^T words are laid out in
 // that same order. The chunk's slot ids are staged in LDS once; row slices
-// are loaded two steps ahead through three register buffers.
+// are loaded DEPTH steps ahead (one for 16 and 64 heads per workgroup, two
+// for 32) through DEPTH + 1 register buffers.
 //
 // Fetch mode (resolve + attention fused): a selected row that the resolve
 // just assigned to a victim slot has not been copied from the host pool yet;
