@@ -347,17 +347,25 @@ __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
       uint32_t pw[HG];
 #pragma unroll
       for (int i = 0; i < HG; ++i) {
-        // raw scores; the reference maximum is kept in log2 units
-        const float mx = row_max16(fmaxf(sc[0][i], sc[1][i])) * scale_log2;  // finite
+        // raw scores; the reference maximum is kept in log2 units. It moves
+        // to the row maximum when some score exceeds it by more than the
+        // slack: a ballot finds out, and only then is the maximum over the
+        // row's 16 lanes taken (max(x) s = max(x s) for s > 0, so the
+        // decision is the one the row maximum would give)
         const float m_old = m_run[i];
-        if (mx > m_run[i] + LAT_LAZY_LOG2) m_run[i] = mx;
+        const float x = fmaxf(sc[0][i], sc[1][i]);
+        if (__any(x * scale_log2 > m_old + LAT_LAZY_LOG2)) {
+          const float mx = row_max16(x) * scale_log2;  // finite
+          if (mx > m_old + LAT_LAZY_LOG2) m_run[i] = mx;
+        }
         moved |= m_run[i] != m_old;
         alpha[i] = exp2_fast(m_old - m_run[i]);  // 1 when unchanged, 0 at the start
         pw[i] = pack_bf16(exp2_fast(__builtin_fmaf(sc[0][i], scale_log2, -m_run[i])),
                           exp2_fast(__builtin_fmaf(sc[1][i], scale_log2, -m_run[i])));
-        const float ps =
-            row_sum16(__uint_as_float(pw[i] << 16) + __uint_as_float(pw[i] & 0xFFFF0000u));
-        l_run[i] = l_run[i] * alpha[i] + ps;
+        // the lane's share of l (alpha is the same on every lane of the
+        // row); the row sum is taken once, after the last step
+        l_run[i] = l_run[i] * alpha[i] +
+                   (__uint_as_float(pw[i] << 16) + __uint_as_float(pw[i] & 0xFFFF0000u));
       }
       // P^T operand of PV lane (head h, k-group r / 4): word r % 4 holds
       // slots 4(r / 4) + r % 4 of tiles 0 and 1
@@ -429,6 +437,8 @@ __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
     if (st < n_steps) step(st, R0, R1);
   }
 
+#pragma unroll
+  for (int i = 0; i < HG; ++i) l_run[i] = row_sum16(l_run[i]);
   const int any_bad = __syncthreads_or(bad ? 1 : 0);
   if (any_bad && tid == 0) set_error(d.ctl, HS_ERR_SLOT);
   // every wave needs l of every head of the workgroup
