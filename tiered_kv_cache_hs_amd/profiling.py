@@ -464,7 +464,7 @@ def main() -> None:
     ap.add_argument("action", choices=("run", "report", "sq", "sq-report", "bench",
                                        "bench-report"))
     ap.add_argument("--workloads", type=int, nargs="+", default=[3, 4, 5, 6, 7])
-    ap.add_argument("--out", default=os.path.join(ROOT, "gpurun_out", "prof"))
+    ap.add_argument("--out", default=os.path.join(ROOT, "prof_out"))
     ap.add_argument("--limit", type=int, default=240, help="seconds per profiler pass")
     a = ap.parse_args()
     if a.action in ("bench", "bench-report"):
