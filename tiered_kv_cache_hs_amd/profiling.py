@@ -60,6 +60,7 @@ KERNEL_SOURCES = {
     "hs_k_attn_latent": ["attn_latent.hip", "hs_device.h", "runtime.hip"],
     "hs_k_attn_mha": ["attn_mha.hip", "hs_device.h", "runtime.hip"],
     "hs_k_combine": ["attn_mha.hip", "hs_device.h", "runtime.hip"],
+    "hs_k_combine_one_trip": ["attn_mha.hip", "hs_device.h", "runtime.hip"],
 }
 
 
