@@ -296,50 +296,46 @@ __global__ __launch_bounds__(256) void hs_k_combine(const float *__restrict__ ws
   }
 }
 
-// The same merge for S <= COMBINE_ONE_TRIP_S splits in one memory round
-// trip: every thread loads the row's S (m, l) pairs (the same words for all
-// threads of the row) together with its two output elements' partials, and
-// computes the weights itself, so no barrier separates the two loads. Up to
-// 4 splits this is faster (64 MLA requests, 4 splits: 13.6 -> 12.2 us; 32
-// requests, 2 splits: 8.6 -> 8.2); at 8 splits the repeated (m, l) loads
-// cost more than the round trip they save (6.8 -> 7.4 us).
-constexpr int COMBINE_ONE_TRIP_S = 4;
+// The same merge for S <= COMBINE_WAVE_S splits and rows of at most 512
+// elements, in one memory round trip and without LDS or a barrier: lane s of
+// every wave loads split s's (m, l) while each thread loads its two output
+// elements' partials; the weights then come from wave reductions and
+// shuffles, in the same arithmetic as the kernel above (same L tree, same
+// order of the weighted sums), so both give identical results.
+constexpr int COMBINE_WAVE_S = 16;
 
-__global__ __launch_bounds__(256) void hs_k_combine_one_trip(const float *__restrict__ ws_o,
-                                                             const float *__restrict__ ws_ml,
-                                                             int S, int dv,
-                                                             float *__restrict__ out) {
+__global__ __launch_bounds__(256) void hs_k_combine_wave(const float *__restrict__ ws_o,
+                                                         const float *__restrict__ ws_ml, int S,
+                                                         int dv, float *__restrict__ out) {
   const size_t row = blockIdx.x;
-  const float2 *ml = (const float2 *)ws_ml + row * S;
-  const float *src = ws_o + row * S * dv;
-  for (int e = 2 * threadIdx.x; e < dv; e += 2 * blockDim.x) {
-    float2 mlv[COMBINE_ONE_TRIP_S], ov[COMBINE_ONE_TRIP_S];
+  const int lane = threadIdx.x & 63;
+  const int e = 2 * threadIdx.x;  // dv <= 512: at most one pair of elements per thread
+  const bool has = e < dv;
+  const float *src = ws_o + row * S * dv + (has ? e : 0);
+  const float2 my =
+      lane < S ? ((const float2 *)ws_ml)[row * S + lane] : float2{NEG_INF, 0.f};
+  float2 ov[COMBINE_WAVE_S];
 #pragma unroll
-    for (int s = 0; s < COMBINE_ONE_TRIP_S; ++s) {
-      if (s < S) {
-        mlv[s] = ml[s];
-        ov[s] = *(const float2 *)(src + (size_t)s * dv + e);
-      }
-    }
-    float M = NEG_INF;
-    bool nan = false;
+  for (int s = 0; s < COMBINE_WAVE_S; ++s)
+    if (s < S) ov[s] = *(const float2 *)(src + (size_t)s * dv);
+  const bool nan = __any(my.x != my.x);
+  float M = my.x;
 #pragma unroll
-    for (int s = 0; s < COMBINE_ONE_TRIP_S; ++s) {
-      if (s < S) {
-        M = fmaxf(M, mlv[s].x);
-        nan |= mlv[s].x != mlv[s].x;
-      }
-    }
-    float L = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  const float wgt = (my.x == NEG_INF) ? 0.f : exp2_fast(my.x - M);
+  float L = wgt * my.y;
 #pragma unroll
-    for (int s = 0; s < COMBINE_ONE_TRIP_S; ++s) {
-      if (s < S) {
-        const float wgt = (mlv[s].x == NEG_INF) ? 0.f : exp2_fast(mlv[s].x - M);
-        L = fmaf(wgt, mlv[s].y, L);
-        o0 = fmaf(wgt, ov[s].x, o0);
-        o1 = fmaf(wgt, ov[s].y, o1);
-      }
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
+  float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int s = 0; s < COMBINE_WAVE_S; ++s) {
+    if (s < S) {
+      const float ws = __shfl(wgt, s, 64);
+      o0 = fmaf(ws, ov[s].x, o0);
+      o1 = fmaf(ws, ov[s].y, o1);
     }
+  }
+  if (has) {
     const float inv = nan ? __builtin_nanf("") : 1.f / L;
     *(float2 *)(out + row * dv + e) = float2{o0 * inv, o1 * inv};
   }
@@ -388,9 +384,9 @@ hipError_t launch_attn_mha(const AttnMhaArgs &a, hipStream_t stream) {
 hipError_t launch_combine(const float *ws_o, const float *ws_ml, int rows, int splits, int dv,
                           float *out, hipStream_t stream) {
   trace_begin(HS_TRACE_COMBINE, stream);
-  if (splits <= COMBINE_ONE_TRIP_S && dv % 2 == 0)
-    hipLaunchKernelGGL(hs_k_combine_one_trip, dim3(rows), dim3(256), 0, stream, ws_o, ws_ml,
-                       splits, dv, out);
+  if (splits <= COMBINE_WAVE_S && dv % 2 == 0 && dv <= 512)
+    hipLaunchKernelGGL(hs_k_combine_wave, dim3(rows), dim3(256), 0, stream, ws_o, ws_ml, splits,
+                       dv, out);
   else
     hipLaunchKernelGGL(hs_k_combine, dim3(rows), dim3(256), 0, stream, ws_o, ws_ml, splits, dv,
                        out);

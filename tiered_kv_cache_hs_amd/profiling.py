@@ -60,7 +60,7 @@ KERNEL_SOURCES = {
     "hs_k_attn_latent": ["attn_latent.hip", "hs_device.h", "runtime.hip"],
     "hs_k_attn_mha": ["attn_mha.hip", "hs_device.h", "runtime.hip"],
     "hs_k_combine": ["attn_mha.hip", "hs_device.h", "runtime.hip"],
-    "hs_k_combine_one_trip": ["attn_mha.hip", "hs_device.h", "runtime.hip"],
+    "hs_k_combine_wave": ["attn_mha.hip", "hs_device.h", "runtime.hip"],
 }
 
 
@@ -419,7 +419,8 @@ def bench_report(out: str) -> str:
     w = next(I.workload(i) for i in range(1, 8) if I.workload(i).name == bl["config"]["workload"])
     rel = os.path.relpath(out, ROOT)
     cls_of = {"hs_k_resolve": "resolve", "hs_k_gather": "gather", "hs_k_attn_latent": "attn",
-              "hs_k_attn_mha": "attn", "hs_k_combine": "combine"}
+              "hs_k_attn_mha": "attn", "hs_k_combine": "combine",
+              "hs_k_combine_wave": "combine"}
     lines = [f"# Kernel time of the default benchmark: workload {w.name}", "",
              f"{w.n_requests} requests x {w.n_layers} layers, {w.kind} records of "
              f"{w.rec_bytes} bytes, {w.n_q_heads} query heads, k = {w.k}; path "
