@@ -301,8 +301,11 @@ __global__ __launch_bounds__(256) void hs_k_combine(const float *__restrict__ ws
 // every wave loads split s's (m, l) while each thread loads its two output
 // elements' partials; the weights then come from wave reductions and
 // shuffles, in the same arithmetic as the kernel above (same L tree, same
-// order of the weighted sums), so both give identical results.
-constexpr int COMBINE_WAVE_S = 16;
+// order of the weighted sums), so both give identical results. Faster up to
+// 4 splits (2 splits: 8.5 -> 7.2 us; 4: 13.4 -> 11.1), even at 8, slower at
+// 16 (7.8 -> 8.2 us), where the serial chain of 16 shuffles and products
+// costs more than the barrier it saves.
+constexpr int COMBINE_WAVE_S = 8;
 
 __global__ __launch_bounds__(256) void hs_k_combine_wave(const float *__restrict__ ws_o,
                                                          const float *__restrict__ ws_ml, int S,
