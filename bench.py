@@ -3,21 +3,25 @@
 Workload (default): batch 8 requests, 1 layer, context 131072 each, MLA-style
 576-element bf16 latent records shared by 64 query heads, k = 2048 selected
 positions, B = 4096 buffer slots, synthetic 13% Zipf(1.1)-recency drift
-traces. A step is one decode step: per layer, hs_resolve (hash, probe,
-victim select, in-place update, host-to-device miss fetch) then
-hs_sparse_attn (+ split-k combine), all captured once per step in a hipGraph
-and replayed with no host synchronisation. Inputs (pool, selections,
-queries) are resident before the timed region.
+traces. A step is one decode step: hs_stage_run (the step's selections and
+queries copied into fixed device buffers, standing in for the indexer), then
+per layer hs_resolve (hash, probe, victim select, in-place update,
+host-to-device miss fetch) and hs_sparse_attn (+ split-k combine). One
+hipGraph holds the whole step and is replayed for every step with no host
+synchronisation. Inputs (pool, every step's selections and queries) are
+resident in memory before the timed region.
 
-Prints one JSON line with the time per layer, the live event-timed duration
-of each kernel class, the roofline of the dominant kernel, the attention
-kernel's HBM roofline, the miss fetch's host-link rate, and the CPU oracle
-timed on a bounded sample of the same workload.
+Prints one JSON line with the time per layer, the duration of each kernel
+class (HIP events carrying each dispatch's own start and end times, over
+the same steps replayed eagerly), the roofline of the dominant kernel, the
+attention kernel's HBM roofline, the miss fetch's host-link rate, and the
+CPU oracle timed on a bounded sample of the same workload.
 """
 from __future__ import annotations
 
 import argparse
 import json
+import os
 import sys
 import time
 
@@ -202,9 +206,10 @@ def main():
     sess = Session(w, total, fill=fill, fused=fused, share_mode=args.share)
     fused = fused and not sess.grouped  # a group's resolve is planned apart from attention
     sess.capture()
-    print("[bench] graphs captured", file=sys.stderr, flush=True)
+    print("[bench] step graph captured (one graph, replayed every step)", file=sys.stderr,
+          flush=True)
 
-    # ---- timed region: graph replays of steps W .. W+K-1
+    # ---- timed region: K replays of the one graph (steps W .. W+K-1)
     for t in range(W):
         sess.replay(t)
     torch.cuda.synchronize()
@@ -221,27 +226,34 @@ def main():
     print(f"[bench] timed {K} steps: {ms_step * 1000:.1f} us/step (wall {wall * 1e3 / K:.3f} ms/step)",
           file=sys.stderr, flush=True)
 
-    # ---- outside the timed region: every step replayed again from a reset
-    # state with an event pair around each replay (per-step spread; step 0,
-    # the cold all-miss step, reported on its own)
-    sess.reset()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(total)]
-    for t in range(total):
-        evs[t][0].record()
-        sess.replay(t)
-        evs[t][1].record()
-    torch.cuda.synchronize()
-    per_step = np.array([a.elapsed_time(b) * 1000.0 / w.n_layers for a, b in evs])
+    # ---- outside the timed region: the whole trace three times from a reset
+    # state, an event pair around each replay (per-step spread; step 0, the
+    # cold all-miss step, reported on its own)
+    reps = []
+    for rep in range(3):
+        sess.reset()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(total)]
+        for t in range(total):
+            evs[t][0].record()
+            sess.replay(t)
+            evs[t][1].record()
+        torch.cuda.synchronize()
+        reps.append(np.array([a.elapsed_time(b) * 1000.0 / w.n_layers for a, b in evs]))
+    per_step = np.median(np.stack(reps), axis=0)
     warm = per_step[1:]
     step_spread = {"cold_step0": round(float(per_step[0]), 2),
                    "p10": round(float(np.percentile(warm, 10)), 2),
                    "median": round(float(np.median(warm)), 2),
                    "p90": round(float(np.percentile(warm, 90)), 2),
-                   "unit": "us/layer, one event pair per replayed step"}
+                   "median_per_repeat": [round(float(np.median(r[1:])), 2) for r in reps],
+                   "unit": "us/layer, one event pair per replayed step, every step of the trace "
+                           "3 times from a reset state (per-step median over the repeats)"}
     dma = host_dma_rate()
 
-    # ---- the same steps again, eagerly, with each kernel bracketed by events
+    # ---- the same steps again from a reset state, eagerly in the graph's
+    # form (stage + the step over the fixed buffers), each kernel carrying
+    # events that take its dispatch's start and end times
     sess.reset()
     miss_hist = torch.zeros((total, w.n_layers, w.n_requests), dtype=torch.int32, device="cuda")
     for t in range(total):
@@ -249,7 +261,7 @@ def main():
             torch.cuda.synchronize()
             H.hs_trace_enable(True)
             H.hs_trace_read()
-        sess.step(t)
+        sess.staged_step()
         miss_hist[t].copy_(sess.miss)
     tr = H.hs_trace_read()
     H.hs_trace_enable(False)
@@ -327,7 +339,8 @@ def main():
                    "context": w.ctx[0] if len(set(w.ctx)) == 1 else "per-request",
                    "k": w.k, "B": w.B[0] if len(set(w.B)) == 1 else "per-request",
                    "q_heads": w.n_q_heads, "record_bytes": w.rec_bytes, "kind": w.kind,
-                   "graph": "one hipGraph per step",
+                   "graph": "one hipGraph replayed for every step (selections and queries "
+                            "staged into fixed buffers on the device)",
                    "path": ("hs_resolve_attn" if fused else "hs_resolve + hs_sparse_attn")
                    + (f" (layer groups of {w.share}: {sess.share_mode})" if sess.grouped else "")},
         "roofline": dominant,
@@ -349,6 +362,7 @@ def main():
                                                  one_thread_steps=3 if w.n_units <= 8 else 0)
         result["cpu_baseline"] = {
             "value": round(us, 1), "unit": "us/layer", "cores": int(threads), "kind": "oracle",
+            "threads_used": int(threads), "nproc": len(os.sched_getaffinity(0)),
             "cpu_model": cpu_model(),
             "sample": f"first {n_steps} steps of the same trace (step 0 cold, median of the "
                       f"rest), all {w.n_units} units per step, resolve + fp64 attention",

@@ -65,7 +65,8 @@ typedef int32_t hs_status;
 #define HS_E_RANGE (-2)  /* request/layer/position outside the pool */
 #define HS_E_NOMEM (-3)  /* host or device allocation failed */
 #define HS_E_HIP (-4)    /* a HIP runtime call failed */
-#define HS_E_STATE (-5)  /* state given to hs_buffer_state_set is not valid */
+#define HS_E_DEVICE (-5) /* the device reported a data error (hs_batch_status) */
+#define HS_E_STATE (-6)  /* state given to hs_buffer_state_set is not valid */
 
 /* Bits of a unit's device error word. */
 #define HS_ERR_RANGE 1u  /* a selected position was outside [0, pool length) */
@@ -74,6 +75,8 @@ typedef int32_t hs_status;
 #define HS_ERR_SLOT 8u   /* attention got a slot outside [0, B) */
 #define HS_ERR_INTERNAL 16u /* resolve found its victim count inconsistent with
                                the miss count (never expected; state untouched) */
+#define HS_ERR_APPEND 32u /* hs_pool_append_batch found the unit's pool full
+                             (no page allocated at its length); nothing written */
 
 /* Record layouts. HS_KV_MHA: one record per token holds
  * [K: n_kv_heads x head_dim][V: n_kv_heads x head_dim]. HS_KV_LATENT
@@ -121,7 +124,13 @@ typedef struct hs_tuning {
                                    (0 = 64; 1 to 65536) */
   int32_t prefetch_batch;       /* hs_prefetch: host reads in flight per lane
                                    (0 = 1; 1, 2, 4 or 8) */
-  int32_t reserved[4];
+  int32_t gather_bytes_per_lane; /* hs_resolve's miss fetch (the swap-in transfer
+                                   block of HiSparse summary, sections 5 and 8):
+                                   bytes of host reads each lane keeps in flight
+                                   per batch, 16 x {1, 2, 4, 8}; 0 = chosen per
+                                   buffer size (64 for B <= 1024 or B > 8192,
+                                   else 128) */
+  int32_t reserved[3];
 } hs_tuning;
 
 const char *hs_status_str(hs_status s);
@@ -198,6 +207,23 @@ hs_status hs_pool_set_length(hs_pool_t pool, int32_t req, int32_t layer,
 hs_status hs_pool_append(hs_pool_t pool, int32_t req, int32_t layer,
                          int64_t pos, int64_t n, const void *src,
                          int32_t src_on_device, void *stream);
+/* Write-through append at the end, for a decode graph replayed every step
+ * (HiSparse summary, section 3, arrow 5; section 5: the step runs inside the
+ * graph with no host synchronisation). For every unit u of the batch, the
+ * record d_src[u] (device memory, [n][rec_bytes], 16-byte aligned) is
+ * written to position len of u's (request, layer) pool, where len is the
+ * unit's length when the kernel runs, and the length becomes len + 1. The
+ * position is read on the device, so one captured call appends at the next
+ * position on every replay. A unit whose pool has no page allocated at len
+ * is not written and gets HS_ERR_APPEND in its error word (reserve pages
+ * before capture). Only the pool is written. After this call the host no
+ * longer knows the lengths without reading them: a later hs_pool_append of
+ * such a unit synchronises its stream to read the length (and is refused,
+ * HS_E_INVAL, while that stream is being captured). A batch holding two
+ * buffers of one (request, layer) is refused (HS_E_INVAL).
+ * Enqueue only; capture-safe. */
+hs_status hs_pool_append_batch(hs_batch_t batch, const void *d_src,
+                               void *stream);
 
 /* ------------- hot device buffer (HiSparse summary, sections 3-4) ----------
  * A buffer of B record slots for unit (req, layer) with its page table
@@ -300,10 +326,15 @@ hs_status hs_buffer_grow_group(hs_buffer_t base, const hs_buffer_t *members,
 /* ------------------------------- batches -----------------------------------
  * An ordered list of n units (buffers of one pool; buffer sizes may
  * differ). Uploads a device descriptor table. Synchronous; create batches
- * before graph capture. */
+ * before graph capture. The buffers must outlive the batch. */
 hs_status hs_batch_create(const hs_buffer_t *bufs, int32_t n,
                           hs_batch_t *out);
 hs_status hs_batch_destroy(hs_batch_t batch);
+/* Error words of the batch's units after the work enqueued so far: errs[u]
+ * (host array of n, may be NULL) receives unit u's sticky HS_ERR_* bits.
+ * Returns HS_E_DEVICE if any unit has a bit set, else HS_OK. Synchronises
+ * stream; not while it is being captured. */
+hs_status hs_batch_status(hs_batch_t batch, int32_t *errs, void *stream);
 
 /* --------------- RESOLVE (HiSparse summary, sections 4-5) ------------------
  * For every unit u, resolves the selection d_topk[u][0..k) (logical
@@ -387,24 +418,61 @@ hs_status hs_resolve_attn(hs_batch_t batch, const int32_t *d_topk, int32_t k,
  * HS_E_INVAL for a null batch or one made before a buffer of its pool grew. */
 hs_status hs_prefetch(hs_batch_t batch, void *stream);
 
+/* ------------- staging the inputs of a decode step (HiSparse summary, §5) ---
+ * The resolve sits inside the decode step's graph, which reads the indexer's
+ * selection (and the query, and the new token's record) from fixed device
+ * buffers that the step's earlier kernels fill. A stage stands in for those
+ * producers: it copies, for step t, entry t % ring of each region's source
+ * ring into the region's fixed destination, where t is a step counter kept
+ * in device memory and advanced by one on the device after the copy. One
+ * captured hs_stage_run therefore stages a new step on every replay of the
+ * graph, with no host involvement.
+ * hs_stage_create: regions[i] = {d_src, d_dst, bytes, src_stride}: entry j
+ *   of the ring is d_src + j * src_stride; bytes and src_stride multiples of
+ *   16 and pointers 16-byte aligned; destinations must not overlap any
+ *   source or each other. ring >= 1 entries. The step counter starts at 0.
+ *   Uploads a device table; synchronous. HS_E_INVAL for a malformed region.
+ * hs_stage_run: enqueue only; capture-safe. One kernel for every region.
+ * hs_stage_set_step: sets the counter (enqueued; a kernel, not a memset).
+ * hs_stage_get_step: reads the counter; synchronous (waits for the device).
+ */
+typedef struct hs_stage_s *hs_stage_t;
+typedef struct hs_stage_region {
+  const void *d_src;  /* ring of entries, device memory */
+  void *d_dst;        /* fixed destination, device memory */
+  size_t bytes;       /* bytes per entry */
+  size_t src_stride;  /* bytes from one ring entry to the next */
+} hs_stage_region;
+hs_status hs_stage_create(const hs_stage_region *regions, int32_t n,
+                          int32_t ring, hs_stage_t *out);
+hs_status hs_stage_destroy(hs_stage_t stage);
+hs_status hs_stage_run(hs_stage_t stage, void *stream);
+hs_status hs_stage_set_step(hs_stage_t stage, uint32_t step, void *stream);
+hs_status hs_stage_get_step(hs_stage_t stage, uint32_t *step);
+
 /* ------------------------------- tracing -----------------------------------
  * Event timing of individual kernels, for measurement. While enabled, every
- * kernel that hs_resolve and hs_sparse_attn enqueue is bracketed by a pair
- * of HIP events recorded on the same stream (do not enable it around graph
- * capture). hs_trace_read synchronises the device, adds up the elapsed time
- * of every completed pair per kernel class and clears the record. Classes:
+ * kernel that the enqueueing calls launch carries a pair of HIP events that
+ * take the dispatch's own start and end times (hipExtLaunchKernel), so the
+ * elapsed time is the kernel's execution without launch overhead (do not
+ * enable it around graph capture). hs_trace_read synchronises the device,
+ * adds up the elapsed time of every pair per kernel class and clears the
+ * record. Classes:
  * HS_TRACE_RESOLVE (hash, probe, victim select, update; for hs_resolve on
  * batches of 4 or more units also the host-to-device miss fetch),
  * HS_TRACE_GATHER (the miss fetch of hs_resolve on smaller batches, a kernel
  * of its own, and hs_prefetch), HS_TRACE_ATTN (sparse attention; for hs_resolve_attn it
- * includes the miss fetch), HS_TRACE_COMBINE (split-k merge). At most 4096
+ * includes the miss fetch), HS_TRACE_COMBINE (split-k merge), HS_TRACE_STAGE
+ * (hs_stage_run), HS_TRACE_APPEND (device-source appends). At most 4096
  * launches are recorded between reads; later ones are counted in
  * `dropped`. */
 #define HS_TRACE_RESOLVE 0
 #define HS_TRACE_GATHER 1
 #define HS_TRACE_ATTN 2
 #define HS_TRACE_COMBINE 3
-#define HS_TRACE_CLASSES 4
+#define HS_TRACE_STAGE 4
+#define HS_TRACE_APPEND 5
+#define HS_TRACE_CLASSES 6
 typedef struct hs_trace {
   double total_us[HS_TRACE_CLASSES];
   int64_t launches[HS_TRACE_CLASSES];

@@ -404,20 +404,16 @@ typedef struct {
 } oracle_unit;
 
 /* Resolve then attend for every unit; units are independent, so they are
- * spread over n_threads OpenMP threads (<= 0: the runtime default). Returns
- * the number of threads that get work: the team size, at most one thread per
- * unit. */
+ * spread over n_threads OpenMP threads (<= 0: the runtime's default team).
+ * The team is set per call (a num_threads clause), leaving the process-wide
+ * setting alone. Returns the number of threads that get work: the team
+ * size, at most one thread per unit. */
 int oracle_step_batch(int32_t n, const oracle_unit *u, int32_t n_threads) {
   int used = 1;
 #ifdef _OPENMP
-  if (n_threads > 0) omp_set_num_threads(n_threads);
-#pragma omp parallel
-  {
-#pragma omp single
-    used = omp_get_num_threads();
-  }
-  if (used > n) used = n > 0 ? n : 1;
-#pragma omp parallel for schedule(dynamic, 1)
+  const int team = n_threads > 0 ? n_threads : omp_get_max_threads();
+  used = team < n ? team : (n > 0 ? n : 1);
+#pragma omp parallel for num_threads(team) schedule(dynamic, 1)
 #endif
   for (int32_t i = 0; i < n; ++i) {
     const oracle_unit *x = &u[i];

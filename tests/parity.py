@@ -121,7 +121,7 @@ def compare_run(w, steps, traces=None, attn_every=1, rows_every=1, attn_units=No
                 for (r, l), b in list(orc.bufs.items()):
                     orc.bufs[(r, l)] = oracle.grow(b, grow[1][r])
                 if graph:
-                    sess.capture(range(t, steps))
+                    sess.capture()
             if graph:
                 sess.replay(t)
             else:

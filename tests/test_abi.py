@@ -39,9 +39,19 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings_and_tuning_roundtrip():
     assert H.hs_status_str(H.HS_OK) == "ok"
     assert H.hs_status_str(H.HS_E_STATE) == "invalid buffer state"
-    H.hs_set_tuning(4, 32, 96, 2)
+    assert H.hs_status_str(H.HS_E_DEVICE) == "data error reported by the device"
+    assert (H.HS_E_DEVICE, H.HS_E_STATE) == (-5, -6)
+    H.hs_set_tuning(4, 32, 96, 2, 64)
     assert H.hs_get_tuning() == {"attn_splits": 4, "latent_heads_per_wg": 32,
-                                 "prefetch_workgroups": 96, "prefetch_batch": 2}
+                                 "prefetch_workgroups": 96, "prefetch_batch": 2,
+                                 "gather_bytes_per_lane": 64}
+    H.hs_set_tuning(0, 0)
+    for gb in (16, 32, 128):
+        H.hs_set_tuning(gather_bytes_per_lane=gb)
+        assert H.hs_get_tuning()["gather_bytes_per_lane"] == gb
+    for gb in (8, 48, 256, -16):
+        with pytest.raises(H.HsError):
+            H.hs_set_tuning(gather_bytes_per_lane=gb)
     H.hs_set_tuning(0, 0)
     with pytest.raises(H.HsError):
         H.hs_set_tuning(-1, 0)
@@ -72,6 +82,23 @@ def test_null_and_shape_checks_without_device():
     assert L.hs_buffer_create_shared(None, 0, None, 0, None) == H.HS_E_INVAL
     assert L.hs_buffer_grow_group(None, None, 0, 4, None, 0, None, None, None) == H.HS_E_INVAL
     assert L.hs_prefetch(None, None) == H.HS_E_INVAL
+    assert L.hs_pool_append_batch(None, None, None) == H.HS_E_INVAL
+    assert L.hs_batch_status(None, None, None) == H.HS_E_INVAL
+    assert L.hs_stage_create(None, 0, 1, None) == H.HS_E_INVAL
+    assert L.hs_stage_run(None, None) == H.HS_E_INVAL
+    assert L.hs_stage_set_step(None, 0, None) == H.HS_E_INVAL
+    assert L.hs_stage_get_step(None, None) == H.HS_E_INVAL
+    assert L.hs_stage_destroy(None) == H.HS_E_INVAL
+    # stage regions are checked before anything is allocated
+    st = ctypes.c_void_p()
+    bad = [H.StageRegion(0x1000, 0x9000, 24, 32)]  # 24 bytes: not a multiple of 16
+    assert L.hs_stage_create((H.StageRegion * 1)(*bad), 1, 4, ctypes.byref(st)) == H.HS_E_INVAL
+    assert "multiples of 16" in H.hs_last_error()
+    bad = [H.StageRegion(0x1000, 0x1020, 32, 32)]  # destination inside the source ring
+    assert L.hs_stage_create((H.StageRegion * 1)(*bad), 1, 4, ctypes.byref(st)) == H.HS_E_INVAL
+    bad = [H.StageRegion(0x1000, 0x9000, 32, 32), H.StageRegion(0x5000, 0x9010, 32, 32)]
+    assert L.hs_stage_create((H.StageRegion * 2)(*bad), 2, 4, ctypes.byref(st)) == H.HS_E_INVAL
+    assert "overlaps" in H.hs_last_error()
     d = H.PoolDesc(1, 1, 7, H.HS_BF16, 1, 64, 0, 0, (ctypes.c_int64 * 1)(100))
     out = ctypes.c_void_p()
     assert L.hs_pool_create(ctypes.byref(d), ctypes.byref(out)) == H.HS_E_INVAL

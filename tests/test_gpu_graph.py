@@ -1,0 +1,179 @@
+"""GPU: one captured decode-step graph replayed for every step.
+
+The graph's first kernel (hs_stage_run) copies the next step's selections,
+queries and new-token records into fixed device buffers and advances a step
+counter on the device; the resolve, attention and write-through append
+(hs_pool_append_batch, at each pool's device-side length) read only those
+buffers. Replaying that one graph T times must give the oracle's slots,
+miss counts, LRU state, rows and attention at every step, and the pool must
+end with the appended records at the right positions.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from tests.parity import OracleRun, check_attn, small_workload  # noqa: E402
+from tiered_kv_cache_hs_amd import hisparse as H  # noqa: E402
+from tiered_kv_cache_hs_amd import inputs as I  # noqa: E402
+from tiered_kv_cache_hs_amd.session import Session  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    H.lib()
+    H.hs_set_tuning(0, 0)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def test_stage_copies_the_entry_of_the_device_step():
+    ring = 5
+    a = torch.arange(ring * 64, dtype=torch.int32, device="cuda").reshape(ring, 64)
+    b = (torch.arange(ring * 24, dtype=torch.int16, device="cuda") * 3).reshape(ring, 24)
+    da = torch.zeros(64, dtype=torch.int32, device="cuda")
+    db = torch.zeros(24, dtype=torch.int16, device="cuda")
+    st = H.hs_stage_create([(a, da, 256, 256), (b, db, 48, 48)], ring)
+    try:
+        assert H.hs_stage_get_step(st) == 0
+        for t in range(12):  # wraps around the ring twice
+            H.hs_stage_run(st)
+            torch.cuda.synchronize()
+            assert torch.equal(da, a[t % ring]) and torch.equal(db, b[t % ring]), t
+            assert H.hs_stage_get_step(st) == t + 1
+        H.hs_stage_set_step(st, 3)
+        H.hs_stage_run(st)
+        torch.cuda.synchronize()
+        assert torch.equal(da, a[3]) and H.hs_stage_get_step(st) == 4
+        # many workgroups: every one must read the step before it advances
+        big = torch.arange(3 * (1 << 20), dtype=torch.int32, device="cuda").reshape(3, 1 << 20)
+        dbig = torch.zeros(1 << 20, dtype=torch.int32, device="cuda")
+        st2 = H.hs_stage_create([(big, dbig, 4 << 20, 4 << 20)], 3)
+        for t in range(7):
+            H.hs_stage_run(st2)
+            torch.cuda.synchronize()
+            assert torch.equal(dbig, big[t % 3]), t
+        assert H.hs_stage_get_step(st2) == 7
+        H.hs_stage_destroy(st2)
+    finally:
+        H.hs_stage_destroy(st)
+
+
+def _graph_run(w, steps, attn_every=1, rows_every=1, **kw):
+    sess = Session(w, steps, fill="touched", **kw)
+    orc = OracleRun(w, sess.traces, steps)
+    sess.capture()
+    graph = sess.graph
+    worst = {"max_abs": 0.0, "rel_l2": 0.0}
+    try:
+        for t in range(steps):
+            sess.replay(t)
+            assert sess.graph is graph  # the same graph every step
+            torch.cuda.synchronize()
+            slots_g, miss_g = sess.slots.cpu().numpy(), sess.miss.cpu().numpy()
+            out_g = sess.out.cpu().numpy()
+            for l in range(w.n_layers):
+                gl = sess.resolved_layer(l)
+                for r in range(w.n_requests):
+                    so, mo = orc.resolve(t, r, l)
+                    assert np.array_equal(slots_g[gl, r], so), f"slots t={t} r={r} l={l}"
+                    assert int(miss_g[gl, r]) == mo, f"miss t={t} r={r} l={l}"
+                    pos, stamp, clock, err = sess.state(l, r)
+                    ob = orc.bufs[(r, l)]
+                    assert np.array_equal(pos, ob.pos) and np.array_equal(stamp, ob.stamp)
+                    assert clock == int(ob.clock[0]) and err == 0 == int(ob.err[0])
+                    if t % rows_every == 0:
+                        rows = sess.rows(l, r)
+                        occ = ob.pos >= 0
+                        assert np.array_equal(rows[occ], ob.rows[occ]), f"rows t={t} r={r} l={l}"
+                    if t % attn_every == 0:
+                        st = check_attn(w, out_g[l, r], orc.attend(t, r, l, so),
+                                        f"attn t={t} r={r} l={l}")
+                        worst = {k: max(worst[k], st[k]) for k in worst}
+                    if w.append:
+                        orc.append(t, r, l)
+        assert H.hs_stage_get_step(sess.stage) == steps
+        for r in range(w.n_requests):
+            for l in range(w.n_layers):
+                n_len = w.ctx[r] + (steps if w.append else 0)
+                assert H.hs_pool_length(sess.pool, r, l) == n_len
+                if w.append:
+                    got = H.pool_read(sess.pool, r, l, np.arange(w.ctx[r], n_len))
+                    want = orc.pools[(r, l)][w.ctx[r]:n_len]
+                    assert np.array_equal(got, want), f"appended records r={r} l={l}"
+    finally:
+        sess.close()
+    return worst
+
+
+def test_one_graph_every_step_tiny_fp32():
+    w = I.workload(1)
+    say("workload 1: one graph, 32 replays", _graph_run(w, w.steps))
+
+
+def test_one_graph_every_step_gqa_with_appends():
+    """Workload 2's shapes (GQA bf16, one write-through append per step) over
+    64 replays of one graph: the appended positions come from the device."""
+    w = I.workload(2)
+    say("workload 2: one graph, 64 replays", _graph_run(w, 64, attn_every=8, rows_every=16,
+                                                          fused=True))
+
+
+def test_one_graph_every_step_latent_batch8():
+    w = I.workload(3)
+    say("workload 3: one graph, 24 replays", _graph_run(w, 24, attn_every=6, rows_every=12))
+
+
+def test_one_graph_appends_requests_of_different_lengths_and_layers():
+    w = small_workload("mha", I.BF16, 64, 16, 200, 12, 4, R=3, L=2, seed=21, Hkv=2, D=64, Hq=4)
+    w.ctx = [150, 200, 177]
+    w.append = True
+    _graph_run(w, 12, fused=False)
+    _graph_run(w, 12, fused=True)
+
+
+def test_one_graph_layer_groups_prefetch():
+    w = small_workload("latent", I.BF16, 96, 32, 500, 10, 6, R=2, L=4, seed=22, Hq=16, share=2)
+    _graph_run(w, 10, share_mode="prefetch")
+
+
+def test_append_batch_past_the_pool_sets_the_error_bit():
+    """A unit whose pool has no page at its length is not written and reports
+    HS_ERR_APPEND; after a reservation the append lands at that length."""
+    w = small_workload("mha", I.F32, 16, 4, 128, 3, 1, R=2, seed=23)
+    w.append = True  # room for 3 more records per request (pages reserved on demand)
+    sess = Session(w, 3, fill="full", page_tokens=64, reserve="prefill")
+    try:
+        rec = sess.rec
+        src = torch.from_numpy((np.arange(2 * rec) % 251).astype(np.uint8)).to("cuda")
+        H.hs_pool_append_batch(sess.batches[0], src)
+        torch.cuda.synchronize()
+        st, errs = H.hs_batch_status(sess.batches[0], 2)
+        assert st == H.HS_E_DEVICE and all(e & H.HS_ERR_APPEND for e in errs)
+        assert H.hs_pool_length(sess.pool, 0, 0) == 128
+        for r in range(2):
+            H.hs_buffer_reset(sess.bufs[0][r])
+        H.hs_pool_reserve(sess.pool, 0, 129)  # request 0 only
+        H.hs_pool_append_batch(sess.batches[0], src)
+        torch.cuda.synchronize()
+        st, errs = H.hs_batch_status(sess.batches[0], 2)
+        assert errs[0] == 0 and errs[1] & H.HS_ERR_APPEND
+        assert H.hs_pool_length(sess.pool, 0, 0) == 129 and H.hs_pool_length(sess.pool, 1, 0) == 128
+        assert np.array_equal(H.pool_read(sess.pool, 0, 0, [128])[0], src[:rec].cpu().numpy())
+        # the host learns the length again before an explicit-position append
+        H.hs_pool_append_batch(sess.batches[0], src)
+        H.hs_pool_append(sess.pool, 0, 0, 130, np.zeros((1, rec), np.uint8))
+        assert H.hs_pool_length(sess.pool, 0, 0) == 131
+        with pytest.raises(H.HsError):
+            H.hs_pool_append(sess.pool, 0, 0, 132, np.zeros((1, rec), np.uint8))  # a gap
+    finally:
+        sess.close()

@@ -516,14 +516,17 @@ def test_batches_made_before_growth_are_refused():
 
 
 def test_pool_release_and_reuse_of_a_request_index():
-    """A finished request returns its pages; its buffer then reports range
-    errors and reads nothing; after a new reservation, prefill and a buffer
-    reset the request index serves a new request like a fresh one."""
+    """A finished request returns its pages. Its buffer is then refused by
+    the host until reset; a graph captured before the release (no host
+    check) resolves it with range errors and reads nothing. After a new
+    reservation, prefill and a buffer reset the request index serves a new
+    request like a fresh one; without the reset the resolve is refused."""
     w = _small("mha", I.F32, 40, 17, 300, 6, 5, R=2, seed=440)
     sess = Session(w, 6, fill="full", page_tokens=64)
     try:
         for t in range(3):
             sess.step(t)
+        sess.capture()
         torch.cuda.synchronize()
         H.hs_pool_release(sess.pool, 0)
         assert H.hs_pool_capacity(sess.pool, 0)[0] == 0
@@ -531,10 +534,14 @@ def test_pool_release_and_reuse_of_a_request_index():
         assert H.hs_pool_capacity(sess.pool, 1)[0] >= 300  # the other request keeps its pages
         with pytest.raises(H.HsError):
             H.hs_pool_record_ptr(sess.pool, 0, 0, 0)
-        sess.step(3)  # request 0's resolve: every position is out of range now
+        with pytest.raises(H.HsError, match="reset the buffer"):
+            sess.step(3)
+        sess.replay()  # captured before the release: every position is out of range now
         torch.cuda.synchronize()
         assert sess.state(0, 0)[3] & H.HS_ERR_RANGE
         assert sess.state(0, 1)[3] == 0  # request 1 unaffected
+        st, errs = H.hs_batch_status(sess.batches[0], 2)
+        assert st == H.HS_E_DEVICE and errs[0] & H.HS_ERR_RANGE and errs[1] == 0
         # a new request in index 0: pages, prefill, empty buffer
         H.hs_pool_reserve(sess.pool, 0, 300)
         for first, page in H.pool_pages(sess.pool, 0, 0):
@@ -543,8 +550,11 @@ def test_pool_release_and_reuse_of_a_request_index():
                 I.fill_records(w, page.ctypes.data - first * w.rec_bytes, 0, 0,
                                positions=np.arange(first, first + n))
         H.hs_pool_set_length(sess.pool, 0, 0, 300)
+        with pytest.raises(H.HsError, match="reset the buffer"):
+            H.hs_resolve(sess.batches[0], sess.topk[4, 0], w.k, sess.slots[0], sess.miss[0])
         H.hs_buffer_reset(sess.bufs[0][0])
         torch.cuda.synchronize()
+        assert H.hs_batch_status(sess.batches[0], 2)[0] == H.HS_OK
         sel = sess.topk[4, 0, 0].cpu().numpy()
         ob = oracle.OracleBuffer(40, w.rec_bytes, with_rows=True)
         pool = np.zeros((300, w.rec_bytes), np.uint8)

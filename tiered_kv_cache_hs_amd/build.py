@@ -20,7 +20,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libhisparse.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["runtime.hip", "resolve.hip", "attn_mha.hip", "attn_latent.hip"]
+SOURCES = ["runtime.hip", "resolve.hip", "attn_mha.hip", "attn_latent.hip", "stage.hip"]
 ARCH = "gfx950"
 
 

@@ -487,12 +487,9 @@ hipError_t launch_latent_t(const AttnLatentArgs &a, hipStream_t stream) {
   const int HS = a.Hq / (HG * 16);
   if (a.chunk > LAT_MAX_CHUNK || a.chunk % 32) return hipErrorInvalidValue;
   const int grid = ((a.n_units + 7) / 8) * 8 * a.splits * HS;
-  trace_begin(HS_TRACE_ATTN, stream);
-  hipLaunchKernelGGL((hs_k_attn_latent<HG, DEPTH, FETCH, STREAM>), dim3(grid), dim3(LAT_THREADS), 0,
-                     stream, a.units, a.q, a.slots, a.n_units, a.k, a.scale_log2, a.splits, HS,
-                     a.chunk, a.ws_o, a.ws_ml, a.out);
-  trace_end(stream);
-  return hipGetLastError();
+  return launch_k(HS_TRACE_ATTN, hs_k_attn_latent<HG, DEPTH, FETCH, STREAM>, dim3(grid),
+                  dim3(LAT_THREADS), 0, stream, a.units, a.q, a.slots, a.n_units, a.k, a.scale_log2,
+                  a.splits, HS, a.chunk, a.ws_o, a.ws_ml, a.out);
 }
 
 template <bool FETCH, bool STREAM>

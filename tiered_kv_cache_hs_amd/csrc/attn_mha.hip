@@ -347,12 +347,9 @@ __global__ __launch_bounds__(256) void hs_k_combine_wave(const float *__restrict
 template <typename T, int D, int GQ, bool FETCH>
 hipError_t launch_mha_t(const AttnMhaArgs &a, hipStream_t stream) {
   const int grid = a.n_units * a.Hkv * a.splits;
-  trace_begin(HS_TRACE_ATTN, stream);
-  hipLaunchKernelGGL((hs_k_attn_mha<T, D, GQ, FETCH>), dim3(grid), dim3(MHA_THREADS), 0, stream,
-                     a.units, (const T *)a.q, a.slots, a.k, a.Hq, a.Hkv, a.scale_log2,
-                     a.splits, a.chunk, a.rec_bytes, a.ws_o, a.ws_ml, a.out);
-  trace_end(stream);
-  return hipGetLastError();
+  return launch_k(HS_TRACE_ATTN, hs_k_attn_mha<T, D, GQ, FETCH>, dim3(grid), dim3(MHA_THREADS),
+                  0, stream, a.units, (const T *)a.q, a.slots, a.k, a.Hq, a.Hkv, a.scale_log2,
+                  a.splits, a.chunk, a.rec_bytes, a.ws_o, a.ws_ml, a.out);
 }
 
 template <typename T, int D, bool FETCH>
@@ -386,15 +383,11 @@ hipError_t launch_attn_mha(const AttnMhaArgs &a, hipStream_t stream) {
 
 hipError_t launch_combine(const float *ws_o, const float *ws_ml, int rows, int splits, int dv,
                           float *out, hipStream_t stream) {
-  trace_begin(HS_TRACE_COMBINE, stream);
   if (splits <= COMBINE_WAVE_S && dv % 2 == 0 && dv <= 512)
-    hipLaunchKernelGGL(hs_k_combine_wave, dim3(rows), dim3(256), 0, stream, ws_o, ws_ml, splits,
-                       dv, out);
-  else
-    hipLaunchKernelGGL(hs_k_combine, dim3(rows), dim3(256), 0, stream, ws_o, ws_ml, splits, dv,
-                       out);
-  trace_end(stream);
-  return hipGetLastError();
+    return launch_k(HS_TRACE_COMBINE, hs_k_combine_wave, dim3(rows), dim3(256), 0, stream, ws_o,
+                    ws_ml, splits, dv, out);
+  return launch_k(HS_TRACE_COMBINE, hs_k_combine, dim3(rows), dim3(256), 0, stream, ws_o, ws_ml,
+                  splits, dv, out);
 }
 
 }  // namespace hs

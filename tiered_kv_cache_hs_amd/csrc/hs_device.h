@@ -1,6 +1,7 @@
 // Internal definitions shared by the HIP sources of libhisparse (gfx950).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -128,10 +129,25 @@ inline BufferLayout buffer_layout(size_t rec_bytes, int B) {
 }
 
 // ----------------------------------------------------------------- tracing
-// Event pairs around kernel launches while hs_trace_enable(1) is in effect
-// (no-ops otherwise). Defined in runtime.hip.
-void trace_begin(int cls, hipStream_t stream);
-void trace_end(hipStream_t stream);
+// While hs_trace_enable(1) is in effect, a launch of class cls takes the
+// next pair of the tracer's events (defined in runtime.hip); false when
+// tracing is off or the record is full.
+bool trace_claim(int cls, hipEvent_t *start, hipEvent_t *stop);
+
+// Every kernel is launched through this. With tracing on, the start and
+// stop events are those of the dispatch itself (hipExtLaunchKernelGGL):
+// their elapsed time is the kernel's execution, the interval a kernel
+// tracer reports, without the marker packets around it.
+template <typename F, typename... Args>
+inline hipError_t launch_k(int cls, F kernel, dim3 grid, dim3 block, uint32_t lds,
+                           hipStream_t stream, Args... args) {
+  hipEvent_t start = nullptr, stop = nullptr;
+  if (trace_claim(cls, &start, &stop))
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, stream, start, stop, 0u, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+  return hipGetLastError();
+}
 
 // ---------------------------------------------------------------- launches
 // Declared here, defined in the .hip files; all enqueue on `stream` and
@@ -145,9 +161,11 @@ hipError_t launch_buffer_init(int32_t *pos, uint32_t *stamp, int32_t *fsrc, uint
 // kernel of many workgroups per unit (enough host reads in flight when the
 // batch has few units).
 constexpr int FETCH_NONE = 0, FETCH_INLINE = 1, FETCH_KERNEL = 2;
+// gb: the fetch's host-read chunks of 16 bytes per lane per batch (1, 2, 4
+// or 8; 0 = the default for the buffer size).
 hipError_t launch_resolve(const UnitDesc *d_units, int n_units, int max_B,
                           const int32_t *d_topk, int k, int32_t *d_slots,
-                          int32_t *d_miss, int fetch, int rec_bytes,
+                          int32_t *d_miss, int fetch, int gb, int rec_bytes,
                           hipStream_t stream);
 size_t resolve_lds_bytes(int k);
 // Fetch every unit's share of its state's last fetch list (about `workgroups`
@@ -166,6 +184,28 @@ hipError_t launch_inv_rebuild(int32_t *inv, int64_t n, const int32_t *pos, int B
 hipError_t launch_append(const uint64_t *d_pages, int page_shift, int64_t pos, int64_t n,
                          int rec_bytes, const uint8_t *src, int64_t *d_len, int64_t new_len,
                          hipStream_t stream);
+// One record per unit, from src[u] (device, [n][rec_bytes]) to position
+// *len of the unit's pool, then *len + 1; HS_ERR_APPEND where no page is
+// allocated there. One workgroup per unit.
+hipError_t launch_append_batch(const UnitDesc *d_units, int n, int rec_bytes, const uint8_t *src,
+                               hipStream_t stream);
+
+// A stage region: n16 16-byte chunks from src + (t % ring) * stride16 chunks
+// to dst. 32 bytes.
+struct StageRegion {
+  const uint8_t *src;
+  uint8_t *dst;
+  uint64_t n16;
+  uint64_t stride16;
+};
+// Stage control words (device memory): [0] the step counter, [1] the
+// arrivals of the running launch (0 between launches).
+constexpr int STAGE_CTL_WORDS = 64;
+// Copies every region for step ctl[0] and advances ctl[0] by one.
+hipError_t launch_stage(const StageRegion *d_regions, int n, uint64_t total16, uint32_t *d_ctl,
+                        uint32_t ring, hipStream_t stream);
+// ctl[0] = step, ctl[1] = 0.
+hipError_t launch_stage_set(uint32_t *d_ctl, uint32_t step, hipStream_t stream);
 
 struct AttnMhaArgs {
   const UnitDesc *units;

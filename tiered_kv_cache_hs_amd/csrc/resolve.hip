@@ -141,7 +141,7 @@ typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 // host reads is issued as soon as the misses are known, so it overlaps the
 // victim selection. Without GATHER the fetch is left to the attention
 // kernels (fsrc says which rows they must read from the host).
-template <int NT, int SPT, int KPT, bool GATHER, bool INV>
+template <int NT, int SPT, int KPT, bool GATHER, bool INV, int GB>
 __global__ __launch_bounds__(NT) void hs_k_resolve(
     const UnitDesc *__restrict__ units, const int32_t *__restrict__ topk_all,
     int k, int hlog2, int rec16, int32_t *__restrict__ slots_all,
@@ -442,10 +442,10 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   // load or store sits on a lane-dependent path and the waits before each
   // store count exactly the loads it needs (a guarded load made the
   // compiler wait for every earlier load before the next one).
-  // 8 chunks per thread; 4 where registers are short (B > 8192) or where few
-  // misses per buffer are the rule (B <= 1024: the repeated last chunk of
-  // lanes past the end would cost host reads of its own)
-  constexpr int GB = (SPT >= 16 || SPT == 1) ? 4 : 8;
+  // GB chunks per thread per batch (the tuned swap-in block; by default 8,
+  // and 4 where registers are short (B > 8192) or where few misses per
+  // buffer are the rule (B <= 1024: the repeated last chunk of lanes past
+  // the end would cost host reads of its own))
   const size_t rec = (size_t)rec16 * 16;
   const int g_total = m * rec16;
   v4u gv[GB];
@@ -750,39 +750,94 @@ __global__ __launch_bounds__(256) void hs_k_append(const uint64_t *pages, int pa
   if (blockIdx.x == 0 && threadIdx.x == 0 && *len < new_len) *len = new_len;
 }
 
+// Write-through append at the end (a decode graph replayed every step): one
+// workgroup per unit writes src[u] to position *len of the unit's pool and
+// then sets *len + 1. Every thread reads the length (its value addresses the
+// thread's stores, so the read is complete once they are issued) before the
+// LDS barrier, and only thread 0 writes it after, so all of the workgroup's
+// stores go to one position; nothing in the kernel waits for the host
+// writes themselves. A position with no page allocated (entry 0, or past the
+// page table) is not written and sets HS_ERR_APPEND.
+__global__ __launch_bounds__(256) void hs_k_append_next(const UnitDesc *__restrict__ units,
+                                                        int rec16, const uint8_t *__restrict__ src) {
+  const int u = blockIdx.x;
+  const UnitG d = unit_g(units[u]);
+  const HS_GLOBAL v4u *s = (const HS_GLOBAL v4u *)src + (size_t)u * rec16;
+  // the record first: its loads do not depend on the length
+  const bool mine = (int)threadIdx.x < rec16;
+  const v4u v = mine ? s[threadIdx.x] : v4u{0u, 0u, 0u, 0u};
+  const int64_t p = *d.len;
+  const int64_t pg = p >> d.page_shift;
+  const uint64_t page = (p >= 0 && pg < d.n_pages) ? d.pages[pg] : 0ull;
+  if (page != 0ull) {
+    const uint64_t in_page = (uint64_t)p & ((1ull << d.page_shift) - 1ull);
+    HS_GLOBAL v4u *dst =
+        (HS_GLOBAL v4u *)((HS_GLOBAL uint8_t *)page + in_page * (uint64_t)rec16 * 16u);
+    if (mine) dst[threadIdx.x] = v;
+    for (int c = threadIdx.x + 256; c < rec16; c += 256) dst[c] = s[c];
+  }
+  lds_barrier();
+  if (threadIdx.x == 0) {
+    if (page != 0ull)
+      *(HS_GLOBAL int64_t *)d.len = p + 1;
+    else
+      set_error(d.ctl, HS_ERR_APPEND);
+  }
+}
+
+// gb: host-read chunks of 16 bytes per thread per fetch batch (1, 2, 4 or
+// 8; 0 = the default for the buffer size), used when the kernel gathers.
 template <int NT, int SPT, int KPT>
 hipError_t launch_select(const UnitDesc *d_units, int n, const int32_t *d_topk, int k,
-                         int hlog2, int rec16, bool gather, size_t lds, int32_t *d_slots,
+                         int hlog2, int rec16, bool gather, int gb, size_t lds, int32_t *d_slots,
                          int32_t *d_miss, hipStream_t stream) {
   // hits through the inverse page table for buffers of more than 1024
   // slots (two or more per thread), where probing every slot costs more
   // than the table's dependent read; through the probe below that
   constexpr bool INV = SPT >= 2;
-  trace_begin(HS_TRACE_RESOLVE, stream);
-  if (gather)
-    hipLaunchKernelGGL((hs_k_resolve<NT, SPT, KPT, true, INV>), dim3(n), dim3(NT), lds, stream,
-                       d_units, d_topk, k, hlog2, rec16, d_slots, d_miss);
-  else
-    hipLaunchKernelGGL((hs_k_resolve<NT, SPT, KPT, false, INV>), dim3(n), dim3(NT), lds, stream,
-                       d_units, d_topk, k, hlog2, rec16, d_slots, d_miss);
-  trace_end(stream);
-  return hipGetLastError();
+  const dim3 grid(n), block(NT);
+#define HS_RES(G, B)                                                                          \
+  launch_k(HS_TRACE_RESOLVE, hs_k_resolve<NT, SPT, KPT, G, INV, B>, grid, block, (uint32_t)lds, \
+           stream, d_units, d_topk, k, hlog2, rec16, d_slots, d_miss)
+  if (!gather) return HS_RES(false, 1);
+  if (gb == 0) gb = (SPT >= 16 || SPT == 1) ? 4 : 8;
+  switch (gb) {
+    case 1: return HS_RES(true, 1);
+    case 2: return HS_RES(true, 2);
+    case 4: return HS_RES(true, 4);
+    default: return HS_RES(true, 8);
+  }
+#undef HS_RES
 }
 
 // picks per thread: the power of two >= k / NT
 template <int NT, int SPT>
 hipError_t launch_select_k(const UnitDesc *d_units, int n, const int32_t *d_topk, int k,
-                           int hlog2, int rec16, bool gather, size_t lds, int32_t *d_slots,
+                           int hlog2, int rec16, bool gather, int gb, size_t lds, int32_t *d_slots,
                            int32_t *d_miss, hipStream_t stream) {
-#define HS_SEL(KPT)                                                                      \
-  if (k <= NT * KPT)                                                                     \
-    return launch_select<NT, SPT, KPT>(d_units, n, d_topk, k, hlog2, rec16, gather, lds, \
+#define HS_SEL(KPT)                                                                          \
+  if (k <= NT * KPT)                                                                         \
+    return launch_select<NT, SPT, KPT>(d_units, n, d_topk, k, hlog2, rec16, gather, gb, lds, \
                                        d_slots, d_miss, stream);
   HS_SEL(1)
   HS_SEL(2)
 #undef HS_SEL
-  return launch_select<NT, SPT, 4>(d_units, n, d_topk, k, hlog2, rec16, gather, lds, d_slots,
+  return launch_select<NT, SPT, 4>(d_units, n, d_topk, k, hlog2, rec16, gather, gb, lds, d_slots,
                                    d_miss, stream);
+}
+
+template <int BATCH>
+hipError_t launch_gather(const UnitDesc *d_units, int n, int G, int rec16, hipStream_t stream) {
+  return launch_k(HS_TRACE_GATHER, hs_k_gather<BATCH>, dim3(n * G), dim3(GATHER_THREADS), 0,
+                  stream, d_units, G, rec16);
+}
+
+hipError_t launch_gather_b(const UnitDesc *d_units, int n, int G, int rec16, int batch,
+                           hipStream_t stream) {
+  if (batch >= 8) return launch_gather<8>(d_units, n, G, rec16, stream);
+  if (batch >= 4) return launch_gather<4>(d_units, n, G, rec16, stream);
+  if (batch >= 2) return launch_gather<2>(d_units, n, G, rec16, stream);
+  return launch_gather<1>(d_units, n, G, rec16, stream);
 }
 
 // Hash capacity: the power of two >= 4k (load factor <= 1/4, short probe
@@ -804,7 +859,7 @@ size_t resolve_lds_bytes(int k) {
 }
 
 hipError_t launch_resolve(const UnitDesc *d_units, int n, int max_B, const int32_t *d_topk,
-                          int k, int32_t *d_slots, int32_t *d_miss, int fetch,
+                          int k, int32_t *d_slots, int32_t *d_miss, int fetch, int gb,
                           int rec_bytes, hipStream_t stream) {
   const int hlog2 = hash_log2(k);
   const size_t lds = resolve_lds_bytes(k);
@@ -813,28 +868,24 @@ hipError_t launch_resolve(const UnitDesc *d_units, int n, int max_B, const int32
   hipError_t e;
   // 16 waves per unit; each thread owns SPT = B / 1024 consecutive slots
   if (max_B <= 1024)
-    e = launch_select_k<1024, 1>(d_units, n, d_topk, k, hlog2, rec16, inl, lds, d_slots,
+    e = launch_select_k<1024, 1>(d_units, n, d_topk, k, hlog2, rec16, inl, gb, lds, d_slots,
                                  d_miss, stream);
   else if (max_B <= 2048)
-    e = launch_select_k<1024, 2>(d_units, n, d_topk, k, hlog2, rec16, inl, lds, d_slots,
+    e = launch_select_k<1024, 2>(d_units, n, d_topk, k, hlog2, rec16, inl, gb, lds, d_slots,
                                  d_miss, stream);
   else if (max_B <= 4096)
-    e = launch_select_k<1024, 4>(d_units, n, d_topk, k, hlog2, rec16, inl, lds, d_slots,
+    e = launch_select_k<1024, 4>(d_units, n, d_topk, k, hlog2, rec16, inl, gb, lds, d_slots,
                                  d_miss, stream);
   else if (max_B <= 8192)
-    e = launch_select_k<1024, 8>(d_units, n, d_topk, k, hlog2, rec16, inl, lds, d_slots,
+    e = launch_select_k<1024, 8>(d_units, n, d_topk, k, hlog2, rec16, inl, gb, lds, d_slots,
                                  d_miss, stream);
   else
-    e = launch_select_k<1024, 16>(d_units, n, d_topk, k, hlog2, rec16, inl, lds, d_slots,
+    e = launch_select_k<1024, 16>(d_units, n, d_topk, k, hlog2, rec16, inl, gb, lds, d_slots,
                                   d_miss, stream);
   if (e != hipSuccess || fetch != FETCH_KERNEL) return e;
   // enough workgroups that about 512 copy the batch's misses
   const int G = std::max(1, std::min(64, (512 + n - 1) / n));
-  trace_begin(HS_TRACE_GATHER, stream);
-  hipLaunchKernelGGL(hs_k_gather<8>, dim3(n * G), dim3(GATHER_THREADS), 0, stream, d_units, G,
-                     rec16);
-  trace_end(stream);
-  return hipGetLastError();
+  return launch_gather_b(d_units, n, G, rec16, gb > 0 ? gb : 8, stream);
 }
 
 // A prefetch runs beside attention kernels: 64 workgroups keep enough host
@@ -845,18 +896,7 @@ hipError_t launch_prefetch(const UnitDesc *d_units, int n, int rec_bytes, int wo
                            int batch, hipStream_t stream) {
   const int wg = workgroups > 0 ? workgroups : 64;
   const int G = std::max(1, std::min(64, (wg + n - 1) / n));
-  trace_begin(HS_TRACE_GATHER, stream);
-  const dim3 grid(n * G), block(GATHER_THREADS);
-  if (batch >= 8)
-    hipLaunchKernelGGL(hs_k_gather<8>, grid, block, 0, stream, d_units, G, rec_bytes / 16);
-  else if (batch >= 4)
-    hipLaunchKernelGGL(hs_k_gather<4>, grid, block, 0, stream, d_units, G, rec_bytes / 16);
-  else if (batch >= 2)
-    hipLaunchKernelGGL(hs_k_gather<2>, grid, block, 0, stream, d_units, G, rec_bytes / 16);
-  else
-    hipLaunchKernelGGL(hs_k_gather<1>, grid, block, 0, stream, d_units, G, rec_bytes / 16);
-  trace_end(stream);
-  return hipGetLastError();
+  return launch_gather_b(d_units, n, G, rec_bytes / 16, batch, stream);
 }
 
 __global__ __launch_bounds__(256) void hs_k_inv_clear(int32_t *inv, int64_t n) {
@@ -913,9 +953,14 @@ hipError_t launch_append(const uint64_t *d_pages, int page_shift, int64_t pos, i
   int64_t blocks = (n16 + 255) / 256;
   if (blocks > 1024) blocks = 1024;
   if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(hs_k_append, dim3((unsigned)blocks), dim3(256), 0, stream, d_pages,
-                     page_shift, pos, n16, rec_bytes / 16, src, d_len, new_len);
-  return hipGetLastError();
+  return launch_k(HS_TRACE_APPEND, hs_k_append, dim3((unsigned)blocks), dim3(256), 0, stream,
+                  d_pages, page_shift, pos, n16, rec_bytes / 16, src, d_len, new_len);
+}
+
+hipError_t launch_append_batch(const UnitDesc *d_units, int n, int rec_bytes, const uint8_t *src,
+                               hipStream_t stream) {
+  return launch_k(HS_TRACE_APPEND, hs_k_append_next, dim3(n), dim3(256), 0, stream, d_units,
+                  rec_bytes / 16, src);
 }
 
 }  // namespace hs

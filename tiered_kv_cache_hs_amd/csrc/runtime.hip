@@ -44,7 +44,7 @@ hs_status hip_fail(hipError_t e, const char *what) {
     if (e_ != hipSuccess) return hip_fail(e_, #call); \
   } while (0)
 
-hs_tuning g_tuning = {0, 0, 0, 0, {0, 0, 0, 0}};
+hs_tuning g_tuning = {0, 0, 0, 0, 0, {0, 0, 0}};
 
 inline hipStream_t S(void *s) { return (hipStream_t)s; }
 
@@ -54,8 +54,7 @@ struct TraceState {
   bool on = false;
   std::vector<hipEvent_t> begin, end;
   std::vector<int> cls;
-  int n = 0;        // completed pairs recorded
-  int pending = -1; // class of the open pair, -1 if none
+  int n = 0;        // pairs handed to launches
   int64_t dropped = 0;
 };
 TraceState g_trace;
@@ -64,27 +63,17 @@ TraceState g_trace;
 
 namespace hs {
 
-void trace_begin(int cls, hipStream_t stream) {
-  if (!g_trace.on) return;
+bool trace_claim(int cls, hipEvent_t *start, hipEvent_t *stop) {
+  if (!g_trace.on) return false;
   if (g_trace.n >= TRACE_CAP) {
     ++g_trace.dropped;
-    g_trace.pending = -1;
-    return;
+    return false;
   }
-  if (hipEventRecord(g_trace.begin[g_trace.n], stream) != hipSuccess) {
-    g_trace.pending = -1;
-    return;
-  }
-  g_trace.pending = cls;
-}
-
-void trace_end(hipStream_t stream) {
-  if (!g_trace.on || g_trace.pending < 0) return;
-  if (hipEventRecord(g_trace.end[g_trace.n], stream) == hipSuccess) {
-    g_trace.cls[g_trace.n] = g_trace.pending;
-    ++g_trace.n;
-  }
-  g_trace.pending = -1;
+  *start = g_trace.begin[g_trace.n];
+  *stop = g_trace.end[g_trace.n];
+  g_trace.cls[g_trace.n] = cls;
+  ++g_trace.n;
+  return true;
 }
 
 }  // namespace hs
@@ -103,6 +92,9 @@ struct hs_pool_s {
   uint64_t *d_pages = nullptr;      // device page tables of every unit
   int64_t *d_len = nullptr;         // [R * L]
   std::vector<int64_t> shadow;      // lengths as of the calls made so far
+  std::vector<uint8_t> shadow_known; // 0 once a device-position append (whose
+                                     // count of replays the host cannot know) ran
+  std::vector<uint64_t> gen;         // per request: bumped when its pages are released
   uint64_t epoch = 0;               // bumped when a buffer of the pool moves (grows)
   int device = 0;
   int64_t page_records() const { return (int64_t)1 << page_shift; }
@@ -119,12 +111,17 @@ struct hs_buffer_s {
   UnitDesc *d_desc = nullptr;  // single-unit table (state restore)
   int32_t *d_inv = nullptr;    // inverse page table this buffer owns (not for a
                                // buffer sharing another's state)
+  uint64_t gen = 0;            // the request's generation when the state was
+                               // last made empty or restored (state owner only)
+  hs_buffer_s *owner() { return base ? base : this; }
 };
 
 struct hs_batch_s {
   hs_pool_t pool = nullptr;
   int32_t n = 0, min_B = 0, max_B = 0;
   bool shared_twice = false;  // two units share one state (not resolvable)
+  bool unit_twice = false;    // two units of one (request, layer) (no batch append)
+  std::vector<hs_buffer_s *> bufs;
   uint64_t epoch = 0;         // the pool's epoch when the table was made
   UnitDesc *d_units = nullptr;
 };
@@ -138,6 +135,7 @@ const char *hs_status_str(hs_status s) {
     case HS_E_RANGE: return "out of range";
     case HS_E_NOMEM: return "out of memory";
     case HS_E_HIP: return "HIP runtime error";
+    case HS_E_DEVICE: return "data error reported by the device";
     case HS_E_STATE: return "invalid buffer state";
     default: return "unknown status";
   }
@@ -157,6 +155,9 @@ hs_status hs_set_tuning(const hs_tuning *t) {
   const int pb = t->prefetch_batch;
   if (pb != 0 && pb != 1 && pb != 2 && pb != 4 && pb != 8)
     return fail(HS_E_INVAL, "prefetch_batch must be 0, 1, 2, 4 or 8");
+  const int gb = t->gather_bytes_per_lane;
+  if (gb != 0 && gb != 16 && gb != 32 && gb != 64 && gb != 128)
+    return fail(HS_E_INVAL, "gather_bytes_per_lane must be 0, 16, 32, 64 or 128");
   g_tuning = *t;
   return HS_OK;
 }
@@ -302,6 +303,8 @@ hs_status hs_pool_create(const hs_pool_desc *d, hs_pool_t *out) {
   p->max_pages.resize(p->R);
   p->table_off.resize(p->R);
   p->shadow.assign((size_t)p->R * p->L, 0);
+  p->shadow_known.assign((size_t)p->R * p->L, 1);
+  p->gen.assign(p->R, 0);
   (void)hipGetDevice(&p->device);
   size_t entries = 0;
   for (int r = 0; r < p->R; ++r) {
@@ -371,7 +374,9 @@ hs_status hs_pool_release(hs_pool_t p, int32_t req) {
     const size_t ui = (size_t)req * p->L + l;
     HS_HIP(hipMemset(p->d_len + ui, 0, sizeof(int64_t)));
     p->shadow[ui] = 0;
+    p->shadow_known[ui] = 1;
   }
+  ++p->gen[req];  // the request's buffers must be reset before they resolve again
   HS_HIP(hipMemset(unit_table(p, req, 0), 0,
                    sizeof(uint64_t) * (size_t)p->L * (size_t)p->max_pages[req]));
   HS_HIP(hipDeviceSynchronize());
@@ -411,6 +416,9 @@ hs_status hs_pool_length(hs_pool_t p, int32_t req, int32_t layer, int64_t *len) 
   HS_HIP(hipDeviceSynchronize());
   HS_HIP(hipMemcpy(len, p->d_len + (size_t)req * p->L + layer, sizeof(int64_t),
                    hipMemcpyDeviceToHost));
+  const size_t ui = (size_t)req * p->L + layer;
+  p->shadow[ui] = *len;
+  p->shadow_known[ui] = 1;
   return HS_OK;
 }
 
@@ -425,6 +433,7 @@ hs_status hs_pool_set_length(hs_pool_t p, int32_t req, int32_t layer, int64_t le
                    hipMemcpyHostToDevice));
   HS_HIP(hipDeviceSynchronize());
   p->shadow[(size_t)req * p->L + layer] = len;
+  p->shadow_known[(size_t)req * p->L + layer] = 1;
   return HS_OK;
 }
 
@@ -434,6 +443,18 @@ hs_status hs_pool_append(hs_pool_t p, int32_t req, int32_t layer, int64_t pos, i
   if (s) return s;
   if (n < 0 || (n > 0 && !src)) return fail(HS_E_INVAL, "bad source");
   const size_t ui = (size_t)req * p->L + layer;
+  if (!p->shadow_known[ui]) {
+    // device-position appends ran: read the length the device has now
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    HS_HIP(hipStreamIsCapturing(S(stream), &cs));
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(HS_E_INVAL, "unit (%d, %d): length unknown after device-position appends; "
+                              "read it (hs_pool_length) before capture", req, layer);
+    HS_HIP(hipStreamSynchronize(S(stream)));
+    int64_t len = 0;
+    hs_status ls = hs_pool_length(p, req, layer, &len);
+    if (ls) return ls;
+  }
   if (pos < 0 || pos > p->shadow[ui] || n > p->cap[req] || pos + n > p->cap[req])
     return fail(HS_E_RANGE, "append [%lld, %lld) with length %lld, capacity %lld",
                 (long long)pos, (long long)(pos + n), (long long)p->shadow[ui],
@@ -463,6 +484,21 @@ hs_status hs_pool_append(hs_pool_t p, int32_t req, int32_t layer, int64_t pos, i
   return HS_OK;
 }
 
+hs_status hs_pool_append_batch(hs_batch_t b, const void *d_src, void *stream) {
+  if (!b || !d_src) return fail(HS_E_INVAL, "null argument");
+  if (b->epoch != b->pool->epoch)
+    return fail(HS_E_INVAL, "a buffer of the pool grew after this batch was made");
+  if (b->unit_twice) return fail(HS_E_INVAL, "the batch holds two buffers of one unit");
+  if ((uintptr_t)d_src % 16) return fail(HS_E_INVAL, "source must be 16-byte aligned");
+  hs_pool_t p = b->pool;
+  hipError_t e = hs::launch_append_batch(b->d_units, b->n, (int)p->rec, (const uint8_t *)d_src,
+                                         S(stream));
+  if (e != hipSuccess) return hip_fail(e, "append launch");
+  for (int i = 0; i < b->n; ++i)
+    p->shadow_known[(size_t)b->bufs[i]->req * p->L + b->bufs[i]->layer] = 0;
+  return HS_OK;
+}
+
 // ----------------------------------------------------------------- buffers
 
 size_t hs_buffer_bytes(hs_pool_t p, int32_t B) {
@@ -489,6 +525,7 @@ hs_status hs_buffer_create(hs_pool_t p, int32_t req, int32_t layer, int32_t B, v
   b->B = B;
   b->mem = (uint8_t *)d_mem;
   b->lay = lay;
+  b->gen = p->gen[req];
   UnitDesc &d = b->desc;
   d.rows = b->mem + lay.rows;
   d.pos = (int32_t *)(b->mem + lay.pos);
@@ -721,6 +758,7 @@ hs_status hs_buffer_reset(hs_buffer_t b, void *stream) {
                                          S(stream));
   if (e == hipSuccess) e = hs::launch_inv_clear(b->desc.inv, b->desc.inv_len, S(stream));
   if (e != hipSuccess) return hip_fail(e, "buffer reset");
+  b->owner()->gen = b->pool->gen[b->req];
   return HS_OK;
 }
 
@@ -783,6 +821,7 @@ hs_status hs_buffer_state_set(hs_buffer_t b, const int32_t *pos, const uint32_t 
   if (e == hipSuccess) e = hs::launch_regather(b->d_desc, b->B, (int)b->pool->rec, S(stream));
   if (e != hipSuccess) return hip_fail(e, "regather");
   HS_HIP(hipStreamSynchronize(S(stream)));
+  b->owner()->gen = b->pool->gen[b->req];
   return HS_OK;
 }
 
@@ -806,6 +845,10 @@ hs_status hs_batch_create(const hs_buffer_t *bufs, int32_t n, hs_batch_t *out) {
   for (int i = 0; i < n; ++i) states[i] = (uintptr_t)h[i].pos;
   std::sort(states.begin(), states.end());
   const bool shared_twice = std::adjacent_find(states.begin(), states.end()) != states.end();
+  std::vector<int64_t> ids(n);
+  for (int i = 0; i < n; ++i) ids[i] = (int64_t)bufs[i]->req * pool->L + bufs[i]->layer;
+  std::sort(ids.begin(), ids.end());
+  const bool unit_twice = std::adjacent_find(ids.begin(), ids.end()) != ids.end();
   hs_batch_s *bt = new (std::nothrow) hs_batch_s;
   if (!bt) return fail(HS_E_NOMEM, "batch handle");
   bt->pool = pool;
@@ -813,6 +856,8 @@ hs_status hs_batch_create(const hs_buffer_t *bufs, int32_t n, hs_batch_t *out) {
   bt->min_B = min_B;
   bt->max_B = max_B;
   bt->shared_twice = shared_twice;
+  bt->unit_twice = unit_twice;
+  bt->bufs.assign(bufs, bufs + n);
   bt->epoch = pool->epoch;
   hipError_t e = hipMalloc(&bt->d_units, sizeof(UnitDesc) * n);
   if (e == hipSuccess)
@@ -833,11 +878,35 @@ hs_status hs_batch_destroy(hs_batch_t b) {
   return HS_OK;
 }
 
-// A batch made before a buffer of its pool moved describes freed memory.
+// A batch made before a buffer of its pool moved describes freed memory; a
+// buffer of a request whose pages were released since its state was last
+// made empty (or restored) holds positions of the finished request.
 static hs_status check_epoch(hs_batch_t b) {
   if (b->epoch != b->pool->epoch)
     return fail(HS_E_INVAL, "a buffer of the pool grew after this batch was made: create the "
                             "batch again");
+  for (int i = 0; i < b->n; ++i) {
+    hs_buffer_s *x = b->bufs[i];
+    if (x->owner()->gen != b->pool->gen[x->req])
+      return fail(HS_E_INVAL, "unit %d: request %d was released after its buffer's state was "
+                              "set; reset the buffer (hs_buffer_reset) first", i, x->req);
+  }
+  return HS_OK;
+}
+
+hs_status hs_batch_status(hs_batch_t b, int32_t *errs, void *stream) {
+  if (!b) return fail(HS_E_INVAL, "null batch");
+  if (b->epoch != b->pool->epoch)
+    return fail(HS_E_INVAL, "a buffer of the pool grew after this batch was made");
+  HS_HIP(hipStreamSynchronize(S(stream)));
+  bool any = false;
+  for (int i = 0; i < b->n; ++i) {
+    uint32_t e = 0;
+    HS_HIP(hipMemcpy(&e, b->bufs[i]->desc.ctl + hs::CTL_ERR, sizeof e, hipMemcpyDeviceToHost));
+    if (errs) errs[i] = (int32_t)e;
+    any |= e != 0;
+  }
+  if (any) return fail(HS_E_DEVICE, "a unit of the batch has error bits set");
   return HS_OK;
 }
 
@@ -874,7 +943,8 @@ hs_status hs_resolve(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_t *d_
   // link when the batch is small: fetch with a second, wider kernel there
   const int fetch = b->n >= 4 ? hs::FETCH_INLINE : hs::FETCH_KERNEL;
   hipError_t e = hs::launch_resolve(b->d_units, b->n, b->max_B, d_topk, k, d_slots, d_miss,
-                                    fetch, (int)b->pool->rec, S(stream));
+                                    fetch, g_tuning.gather_bytes_per_lane / 16,
+                                    (int)b->pool->rec, S(stream));
   if (e != hipSuccess) return hip_fail(e, "resolve launch");
   return HS_OK;
 }
@@ -1056,7 +1126,7 @@ hs_status hs_resolve_attn(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_
   if (s) return s;
   // resolve without the gather: the attention kernels fetch the misses
   hipError_t e = hs::launch_resolve(b->d_units, b->n, b->max_B, d_topk, k, d_slots, d_miss,
-                                    hs::FETCH_NONE, (int)b->pool->rec, S(stream));
+                                    hs::FETCH_NONE, 0, (int)b->pool->rec, S(stream));
   if (e != hipSuccess) return hip_fail(e, "resolve launch");
   return enqueue_attn(b, d_q, Hq, d_slots, k, sm_scale, d_out, d_ws, pl, 1, stream);
 }
@@ -1074,6 +1144,92 @@ hs_status hs_prefetch(hs_batch_t b, void *stream) {
   return HS_OK;
 }
 
+// ------------------------------------------------------------------- stage
+
+struct hs_stage_s {
+  int32_t n = 0;
+  uint32_t ring = 1;
+  uint64_t total16 = 0;
+  hs::StageRegion *d_regions = nullptr;
+  uint32_t *d_ctl = nullptr;
+};
+
+hs_status hs_stage_create(const hs_stage_region *regions, int32_t n, int32_t ring,
+                          hs_stage_t *out) {
+  if (!regions || !out || n < 1 || ring < 1) return fail(HS_E_INVAL, "need n >= 1 regions, ring >= 1");
+  *out = nullptr;
+  std::vector<hs::StageRegion> h(n);
+  uint64_t total = 0;
+  for (int i = 0; i < n; ++i) {
+    const hs_stage_region &r = regions[i];
+    if (!r.d_src || !r.d_dst || r.bytes == 0)
+      return fail(HS_E_INVAL, "region %d: null pointer or no bytes", i);
+    if (r.bytes % 16 || r.src_stride % 16 || (uintptr_t)r.d_src % 16 || (uintptr_t)r.d_dst % 16)
+      return fail(HS_E_INVAL, "region %d: sizes and pointers must be multiples of 16", i);
+    const size_t span = (size_t)(ring - 1) * r.src_stride + r.bytes;
+    for (int j = 0; j <= i; ++j) {
+      const hs_stage_region &o = regions[j];
+      const size_t ospan = (size_t)(ring - 1) * o.src_stride + o.bytes;
+      if (overlaps(r.d_dst, r.bytes, o.d_src, ospan) || (j < i && overlaps(o.d_dst, o.bytes, r.d_src, span)) ||
+          (j < i && overlaps(r.d_dst, r.bytes, o.d_dst, o.bytes)))
+        return fail(HS_E_INVAL, "region %d overlaps region %d", i, j);
+    }
+    h[i].src = (const uint8_t *)r.d_src;
+    h[i].dst = (uint8_t *)r.d_dst;
+    h[i].n16 = r.bytes / 16;
+    h[i].stride16 = r.src_stride / 16;
+    total += h[i].n16;
+  }
+  hs_stage_s *st = new (std::nothrow) hs_stage_s;
+  if (!st) return fail(HS_E_NOMEM, "stage handle");
+  st->n = n;
+  st->ring = (uint32_t)ring;
+  st->total16 = total;
+  hipError_t e = hipMalloc(&st->d_regions, sizeof(hs::StageRegion) * n);
+  if (e == hipSuccess)
+    e = hipMemcpy(st->d_regions, h.data(), sizeof(hs::StageRegion) * n, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMalloc(&st->d_ctl, sizeof(uint32_t) * hs::STAGE_CTL_WORDS);
+  if (e == hipSuccess) e = hs::launch_stage_set(st->d_ctl, 0u, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    if (st->d_regions) (void)hipFree(st->d_regions);
+    if (st->d_ctl) (void)hipFree(st->d_ctl);
+    delete st;
+    return hip_fail(e, "stage create");
+  }
+  *out = st;
+  return HS_OK;
+}
+
+hs_status hs_stage_destroy(hs_stage_t st) {
+  if (!st) return fail(HS_E_INVAL, "null stage");
+  (void)hipFree(st->d_regions);
+  (void)hipFree(st->d_ctl);
+  delete st;
+  return HS_OK;
+}
+
+hs_status hs_stage_run(hs_stage_t st, void *stream) {
+  if (!st) return fail(HS_E_INVAL, "null stage");
+  hipError_t e = hs::launch_stage(st->d_regions, st->n, st->total16, st->d_ctl, st->ring, S(stream));
+  if (e != hipSuccess) return hip_fail(e, "stage launch");
+  return HS_OK;
+}
+
+hs_status hs_stage_set_step(hs_stage_t st, uint32_t step, void *stream) {
+  if (!st) return fail(HS_E_INVAL, "null stage");
+  hipError_t e = hs::launch_stage_set(st->d_ctl, step, S(stream));
+  if (e != hipSuccess) return hip_fail(e, "stage set");
+  return HS_OK;
+}
+
+hs_status hs_stage_get_step(hs_stage_t st, uint32_t *step) {
+  if (!st || !step) return fail(HS_E_INVAL, "null argument");
+  HS_HIP(hipDeviceSynchronize());
+  HS_HIP(hipMemcpy(step, st->d_ctl, sizeof(uint32_t), hipMemcpyDeviceToHost));
+  return HS_OK;
+}
+
 // ------------------------------------------------------------------ tracing
 
 hs_status hs_trace_enable(int32_t on) {
@@ -1087,7 +1243,6 @@ hs_status hs_trace_enable(int32_t on) {
     }
   }
   g_trace.on = on != 0;
-  g_trace.pending = -1;
   return HS_OK;
 }
 

@@ -1,0 +1,85 @@
+// Staging the inputs of a decode step inside its graph.
+//
+// HiSparse summary (marsggbo.github.io, 2026-09-23), section 5: the resolve
+// is part of the decode step's graph and runs with no host synchronisation,
+// so it reads the indexer's selection from a fixed device buffer that the
+// step's own earlier kernels write. hs_k_stage stands in for those
+// producers (the indexer, the query projection, the new token's record):
+// for step t it copies entry t % ring of each region's source ring into the
+// region's fixed destination, then advances t, all on the device. A graph
+// that captured one launch stages a new step on every replay.
+//
+// The step counter advances once per launch: every workgroup reads it
+// first, copies its share, and arrives on a counter; the last to arrive
+// (all others have read the step by then) writes step + 1 and clears the
+// arrivals, so the control words need no clearing between launches.
+#include "hs_device.h"
+
+namespace hs {
+
+namespace {
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+constexpr int STAGE_THREADS = 256;
+
+// The regions' chunks form one index space (region 0's first, then region
+// 1's, ...); each thread copies chunk c = its global index, then c + the
+// grid's thread count, and so on (one chunk per thread at the usual sizes).
+// Thread 0 reads the step and hands it to the workgroup through LDS; once
+// the workgroup has it, thread 0 arrives (relaxed: only the step's read has
+// to precede the arrival, and its value was already stored to LDS), and the
+// last workgroup to arrive - every other one has its step by then - writes
+// step + 1. The arrival's round trip overlaps the copy, and nothing waits
+// for the copy's stores inside the kernel.
+__global__ __launch_bounds__(STAGE_THREADS) void hs_k_stage(const StageRegion *__restrict__ regs,
+                                                            int n, uint64_t total16, uint32_t *ctl,
+                                                            uint32_t ring) {
+  __shared__ uint32_t s_step;
+  if (threadIdx.x == 0) s_step = __hip_atomic_load(ctl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  lds_barrier();
+  const uint32_t t = s_step;
+  if (threadIdx.x == 0) {
+    const uint32_t before =
+        __hip_atomic_fetch_add(ctl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (before == gridDim.x - 1) {
+      __hip_atomic_store(ctl + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctl, t + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  const uint64_t e = t % ring;
+  const uint64_t stride = (uint64_t)gridDim.x * STAGE_THREADS;
+  for (uint64_t c = (uint64_t)blockIdx.x * STAGE_THREADS + threadIdx.x; c < total16; c += stride) {
+    uint64_t off = c;
+    int i = 0;
+    while (i + 1 < n && off >= regs[i].n16) off -= regs[i++].n16;
+    const StageRegion r = regs[i];
+    ((HS_GLOBAL v4u *)r.dst)[off] = ((const HS_GLOBAL v4u *)r.src)[e * r.stride16 + off];
+  }
+}
+
+__global__ void hs_k_stage_set(uint32_t *ctl, uint32_t step) {
+  if (threadIdx.x == 0) {
+    ctl[0] = step;
+    ctl[1] = 0u;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_stage(const StageRegion *d_regions, int n, uint64_t total16, uint32_t *d_ctl,
+                        uint32_t ring, hipStream_t stream) {
+  // one 16-byte chunk per thread, at most 1024 workgroups
+  uint64_t blocks = (total16 + STAGE_THREADS - 1) / STAGE_THREADS;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 1024) blocks = 1024;
+  return launch_k(HS_TRACE_STAGE, hs_k_stage, dim3((unsigned)blocks), dim3(STAGE_THREADS), 0,
+                  stream, d_regions, n, total16, d_ctl, ring);
+}
+
+hipError_t launch_stage_set(uint32_t *d_ctl, uint32_t step, hipStream_t stream) {
+  hipLaunchKernelGGL(hs_k_stage_set, dim3(1), dim3(64), 0, stream, d_ctl, step);
+  return hipGetLastError();
+}
+
+}  // namespace hs

@@ -22,13 +22,15 @@ HS_E_INVAL = -1
 HS_E_RANGE = -2
 HS_E_NOMEM = -3
 HS_E_HIP = -4
-HS_E_STATE = -5
+HS_E_DEVICE = -5
+HS_E_STATE = -6
 
 HS_ERR_RANGE = 1
 HS_ERR_DUP = 2
 HS_ERR_CLOCK = 4
 HS_ERR_SLOT = 8
 HS_ERR_INTERNAL = 16
+HS_ERR_APPEND = 32
 
 HS_KV_MHA = 0
 HS_KV_LATENT = 1
@@ -42,13 +44,15 @@ EXPORTS = (
     "hs_status_str", "hs_last_error", "hs_set_tuning", "hs_get_tuning",
     "hs_pool_create", "hs_pool_destroy", "hs_pool_record_bytes", "hs_pool_capacity",
     "hs_pool_reserve", "hs_pool_release", "hs_pool_record_ptr", "hs_pool_page_ptr",
-    "hs_pool_length", "hs_pool_set_length", "hs_pool_append",
+    "hs_pool_length", "hs_pool_set_length", "hs_pool_append", "hs_pool_append_batch",
     "hs_buffer_bytes", "hs_buffer_create", "hs_buffer_destroy", "hs_buffer_grow",
     "hs_buffer_reset",
     "hs_buffer_rows", "hs_buffer_state_get", "hs_buffer_state_set",
     "hs_buffer_shared_bytes", "hs_buffer_create_shared", "hs_buffer_grow_group",
-    "hs_batch_create", "hs_batch_destroy", "hs_resolve",
+    "hs_batch_create", "hs_batch_destroy", "hs_batch_status", "hs_resolve",
     "hs_sparse_attn_workspace", "hs_sparse_attn", "hs_resolve_attn", "hs_prefetch",
+    "hs_stage_create", "hs_stage_destroy", "hs_stage_run", "hs_stage_set_step",
+    "hs_stage_get_step",
     "hs_trace_enable", "hs_trace_read",
 )
 
@@ -71,18 +75,23 @@ class PoolDesc(ctypes.Structure):
     ]
 
 
-TRACE_CLASSES = ("resolve", "gather", "attn", "combine")
+TRACE_CLASSES = ("resolve", "gather", "attn", "combine", "stage", "append")
 
 
 class Trace(ctypes.Structure):
-    _fields_ = [("total_us", ctypes.c_double * 4), ("launches", ctypes.c_int64 * 4),
+    _fields_ = [("total_us", ctypes.c_double * 6), ("launches", ctypes.c_int64 * 6),
                 ("dropped", ctypes.c_int64)]
 
 
 class Tuning(ctypes.Structure):
     _fields_ = [("attn_splits", ctypes.c_int32), ("latent_heads_per_wg", ctypes.c_int32),
                 ("prefetch_workgroups", ctypes.c_int32), ("prefetch_batch", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 4)]
+                ("gather_bytes_per_lane", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+
+
+class StageRegion(ctypes.Structure):
+    _fields_ = [("d_src", ctypes.c_void_p), ("d_dst", ctypes.c_void_p),
+                ("bytes", ctypes.c_size_t), ("src_stride", ctypes.c_size_t)]
 
 
 _lib = None
@@ -114,6 +123,7 @@ def lib():
         "hs_pool_length": ([vp, i32, i32, P(i64)], i32),
         "hs_pool_set_length": ([vp, i32, i32, i64], i32),
         "hs_pool_append": ([vp, i32, i32, i64, i64, vp, i32, vp], i32),
+        "hs_pool_append_batch": ([vp, vp, vp], i32),
         "hs_buffer_bytes": ([vp, i32], sz),
         "hs_buffer_create": ([vp, i32, i32, i32, vp, sz, vp, P(vp)], i32),
         "hs_buffer_destroy": ([vp], i32),
@@ -127,11 +137,17 @@ def lib():
         "hs_buffer_grow_group": ([vp, P(vp), i32, i32, vp, sz, P(vp), P(sz), vp], i32),
         "hs_batch_create": ([P(vp), i32, P(vp)], i32),
         "hs_batch_destroy": ([vp], i32),
+        "hs_batch_status": ([vp, vp, vp], i32),
         "hs_resolve": ([vp, vp, i32, vp, vp, vp], i32),
         "hs_sparse_attn_workspace": ([vp, i32, i32], sz),
         "hs_sparse_attn": ([vp, vp, i32, vp, i32, ctypes.c_float, vp, vp, sz, vp], i32),
         "hs_resolve_attn": ([vp, vp, i32, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz, vp], i32),
         "hs_prefetch": ([vp, vp], i32),
+        "hs_stage_create": ([P(StageRegion), i32, i32, P(vp)], i32),
+        "hs_stage_destroy": ([vp], i32),
+        "hs_stage_run": ([vp, vp], i32),
+        "hs_stage_set_step": ([vp, u32, vp], i32),
+        "hs_stage_get_step": ([vp, P(u32)], i32),
         "hs_trace_enable": ([i32], i32),
         "hs_trace_read": ([P(Trace)], i32),
     }
@@ -175,8 +191,10 @@ def hs_last_error() -> str:
 
 
 def hs_set_tuning(attn_splits: int = 0, latent_heads_per_wg: int = 0,
-                  prefetch_workgroups: int = 0, prefetch_batch: int = 0) -> None:
-    t = Tuning(attn_splits, latent_heads_per_wg, prefetch_workgroups, prefetch_batch)
+                  prefetch_workgroups: int = 0, prefetch_batch: int = 0,
+                  gather_bytes_per_lane: int = 0) -> None:
+    t = Tuning(attn_splits, latent_heads_per_wg, prefetch_workgroups, prefetch_batch,
+               gather_bytes_per_lane)
     _check(lib().hs_set_tuning(ctypes.byref(t)))
 
 
@@ -184,7 +202,8 @@ def hs_get_tuning() -> dict:
     t = Tuning()
     _check(lib().hs_get_tuning(ctypes.byref(t)))
     return {"attn_splits": t.attn_splits, "latent_heads_per_wg": t.latent_heads_per_wg,
-            "prefetch_workgroups": t.prefetch_workgroups, "prefetch_batch": t.prefetch_batch}
+            "prefetch_workgroups": t.prefetch_workgroups, "prefetch_batch": t.prefetch_batch,
+            "gather_bytes_per_lane": t.gather_bytes_per_lane}
 
 
 # ------------------------------------------------------------------ pool
@@ -294,6 +313,12 @@ def hs_pool_append(pool: int, req: int, layer: int, pos: int, src, n: Optional[i
                                     _stream(stream)))
 
 
+def hs_pool_append_batch(batch: int, src, stream=None) -> None:
+    """Write-through append of src[u] (device tensor [n][rec_bytes]) at the
+    end of every unit's pool; positions are read on the device."""
+    _check(lib().hs_pool_append_batch(batch, _ptr(src), _stream(stream)))
+
+
 # ------------------------------------------------------------------ buffers
 
 def hs_buffer_bytes(pool: int, B: int) -> int:
@@ -392,6 +417,16 @@ def hs_batch_destroy(batch: int) -> None:
     _check(lib().hs_batch_destroy(batch))
 
 
+def hs_batch_status(batch: int, n: int, stream=None):
+    """(status, error words int32[n]): HS_E_DEVICE when any unit has error
+    bits set (not raised), else HS_OK."""
+    errs = np.zeros(n, dtype=np.int32)
+    st = lib().hs_batch_status(batch, errs.ctypes.data, _stream(stream))
+    if st not in (HS_OK, HS_E_DEVICE):
+        _check(st)
+    return st, errs
+
+
 def hs_resolve(batch: int, topk, k: int, slots, miss=None, stream=None) -> None:
     """topk/slots: int32 device tensors [n][k]; miss: int32 [n] or None."""
     _check(lib().hs_resolve(batch, _ptr(topk), int(k), _ptr(slots), _ptr(miss), _stream(stream)))
@@ -422,6 +457,35 @@ def hs_prefetch(batch: int, stream=None) -> None:
     """Fetch every unit's records of its state's last fetch list (the other
     layers of a group sharing one selection)."""
     _check(lib().hs_prefetch(batch, _stream(stream)))
+
+
+# ------------------------------------------------------------------ stage
+
+def hs_stage_create(regions, ring: int) -> int:
+    """regions: [(src tensor, dst tensor, bytes per entry, src stride bytes)]."""
+    arr = (StageRegion * len(regions))(*[StageRegion(_ptr(s), _ptr(d), int(b), int(st))
+                                         for s, d, b, st in regions])
+    out = ctypes.c_void_p()
+    _check(lib().hs_stage_create(arr, len(regions), int(ring), ctypes.byref(out)))
+    return out.value
+
+
+def hs_stage_destroy(stage: int) -> None:
+    _check(lib().hs_stage_destroy(stage))
+
+
+def hs_stage_run(stage: int, stream=None) -> None:
+    _check(lib().hs_stage_run(stage, _stream(stream)))
+
+
+def hs_stage_set_step(stage: int, step: int, stream=None) -> None:
+    _check(lib().hs_stage_set_step(stage, int(step), _stream(stream)))
+
+
+def hs_stage_get_step(stage: int) -> int:
+    v = ctypes.c_uint32()
+    _check(lib().hs_stage_get_step(stage, ctypes.byref(v)))
+    return v.value
 
 
 # ------------------------------------------------------------------ tracing

@@ -6,9 +6,23 @@ unit, one batch per layer (layers run in sequence within a step, requests of
 a layer together), the per-step selections and queries staged in HBM, and
 the appended-token records for write-through workloads. A decode step is,
 for each layer in order: hs_resolve -> hs_sparse_attn (or the fused
-hs_resolve_attn) -> (write-through) hs_pool_append of that layer's new token. Steps can run eagerly or be
-captured once each into a hipGraph (torch.cuda.CUDAGraph) and replayed with
-no host synchronisation.
+hs_resolve_attn) -> (write-through) append of that layer's new token.
+
+Steps run in one of two ways:
+  eager, step(t): every call takes step t's own arrays (any step, any
+      order), and the append names its position (hs_pool_append);
+  graph, capture() once then replay() every step: one hipGraph
+      (torch.cuda.CUDAGraph) holds a whole step. Its first kernel,
+      hs_stage_run, copies the next step's selections, queries and new
+      records from the per-step arrays into fixed device buffers (the
+      stand-in for the indexer and the other producers of a decode step)
+      and advances a step counter on the device; the rest reads only those
+      fixed buffers, and the append lands at each pool's device-side length
+      (hs_pool_append_batch). The same graph is replayed for every step
+      with no host synchronisation; replays run the steps in order from
+      the counter (reset() sets it back to 0). (Staging the queries on a
+      second stream beside the resolve measured slower: a fork and join
+      inside a graph cost more than the copy.)
 
 Layer groups that reuse one selection (Workload.share > 1; HiSparse summary,
 section 6) run in one of three ways:
@@ -50,10 +64,11 @@ class Session:
         self.device = torch.device(device)
         R, L, k = w.n_requests, w.n_layers, w.k
         self.R, self.L, self.k = R, L, k
-        # traces [steps][n_units (request-major)][k] -> layer-major device copy
+        # traces [steps][n_units (request-major)][k] -> layer-major device copy,
+        # each step's entry padded to 16 bytes (a stage ring entry)
         self.traces = I.gen_traces(w, self.steps) if traces is None else traces
         lm = self.traces.reshape(self.steps, R, L, k).transpose(0, 2, 1, 3)
-        self.topk = torch.from_numpy(np.ascontiguousarray(lm)).to(self.device)  # [T][L][R][k]
+        self.topk = self._ring(torch.from_numpy(np.ascontiguousarray(lm)))  # [T][L][R][k]
 
         # reserve "all": every record the steps will append is allocated up
         # front; "prefill": only the prefill, the rest with hs_pool_reserve
@@ -108,7 +123,7 @@ class Session:
         q = np.stack([I.gen_queries(w, t) for t in range(self.steps)])  # [T][n(req-major)]...
         q = q.reshape(self.steps, R, L, w.n_q_heads, w.q_dim).transpose(0, 2, 1, 3, 4)
         q = np.ascontiguousarray(q)
-        self.q = torch.from_numpy(q.view(np.int16) if qdt == torch.int16 else q).to(self.device)
+        self.q = self._ring(torch.from_numpy(q.view(np.int16) if qdt == torch.int16 else q))
 
         # appended-token records [T][L][R][rec] (write-through workloads)
         self.app = None
@@ -118,7 +133,21 @@ class Session:
                 for l in range(L):
                     pos = np.array([w.ctx[r] + t for t in range(self.steps)], dtype=np.int64)
                     app[:, l, r, :] = I.record_array(w, r, l, pos)
-            self.app = torch.from_numpy(app).to(self.device)
+            self.app = self._ring(torch.from_numpy(app))
+
+        # fixed buffers a captured step reads, filled by its stage kernel from
+        # entry t of the rings above
+        rings = [self.topk, self.q] + ([] if self.app is None else [self.app])
+        fixed = [self._ring(torch.zeros((1,) + tuple(a.shape[1:]), dtype=a.dtype))[0]
+                 for a in rings]
+        self.topk_cur, self.q_cur = fixed[0], fixed[1]
+        self.app_cur = None if self.app is None else fixed[2]
+        # whole padded entries: the ring's stride in bytes
+        self.stage = H.hs_stage_create(
+            [(a, f, self._entry_bytes(a), self._entry_bytes(a)) for a, f in zip(rings, fixed)],
+            self.steps)
+        self._next = 0  # the step the next replay stages (the device counter)
+        self.graph: Optional[torch.cuda.CUDAGraph] = None
 
         self.slots = torch.empty((L, R, k), dtype=torch.int32, device=self.device)
         self.miss = torch.empty((L, R), dtype=torch.int32, device=self.device)
@@ -127,37 +156,63 @@ class Session:
         wsb = max(H.hs_sparse_attn_workspace(self.batches[l], w.n_q_heads, k) for l in range(L))
         self.ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=self.device)
         self.scale = w.sm_scale
-        self.graphs: List[torch.cuda.CUDAGraph] = []
         torch.cuda.synchronize()
+
+    @staticmethod
+    def _entry_bytes(a: torch.Tensor) -> int:
+        """Bytes of one step's entry of a ring made by _ring (padded to 16)."""
+        return -(-a[0].numel() * a.element_size() // 16) * 16
+
+    def _ring(self, a: torch.Tensor) -> torch.Tensor:
+        """a [T][...] on the device with every step's entry starting on a
+        16-byte boundary (a view of a padded [T][stride] array)."""
+        T = a.shape[0]
+        per = a[0].numel()
+        stride = self._entry_bytes(a) // a.element_size()
+        flat = torch.zeros((T, stride), dtype=a.dtype, device=self.device)
+        flat[:, :per].copy_(a.reshape(T, per))
+        return flat[:, :per].unflatten(1, tuple(a.shape[1:]))
 
     # -------------------------------------------------------------- steps
     def resolved_layer(self, l: int) -> int:
         """The layer whose resolve produced layer l's slots and misses."""
         return self.w.group_base(l) if self.grouped else l
 
-    def _append(self, t: int, l: int) -> None:
-        if self.app is not None:
-            for r in range(self.R):
-                H.hs_pool_append(self.pool, r, l, self.w.ctx[r] + t, self.app[t, l, r], n=1)
+    def _inputs(self, t: Optional[int]):
+        """(selections [L][R][k], queries [L][R][Hq][qdim], new records
+        [L][R][rec] or None) of step t, or the fixed staged buffers (t None)."""
+        if t is None:
+            return self.topk_cur, self.q_cur, self.app_cur
+        return self.topk[t], self.q[t], None if self.app is None else self.app[t]
 
-    def _attn(self, t: int, l: int) -> None:
+    def _append(self, t: Optional[int], l: int, app) -> None:
+        if app is None:
+            return
+        if t is None:  # at each pool's device-side length
+            H.hs_pool_append_batch(self.batches[l], app[l])
+            return
+        for r in range(self.R):
+            H.hs_pool_append(self.pool, r, l, self.w.ctx[r] + t, app[l, r], n=1)
+
+    def _attn(self, l: int, q) -> None:
         g = self.resolved_layer(l)
-        H.hs_sparse_attn(self.batches[l], self.q[t, l], self.w.n_q_heads, self.slots[g], self.k,
+        H.hs_sparse_attn(self.batches[l], q[l], self.w.n_q_heads, self.slots[g], self.k,
                          self.scale, self.out[l], self.ws)
 
-    def group(self, t: int, g: int) -> None:
-        """Enqueue step t of the layer group starting at layer g (grouped
-        sessions): one resolve for the group, the later layers' fetches
-        from its plan, every layer's attention."""
+    def _group(self, t: Optional[int], g: int) -> None:
+        """Enqueue the layer group starting at layer g (grouped sessions):
+        one resolve for the group, the later layers' fetches from its plan,
+        every layer's attention."""
         w = self.w
-        H.hs_resolve(self.batches[g], self.topk[t, g], self.k, self.slots[g], self.miss[g])
+        topk, q, app = self._inputs(t)
+        H.hs_resolve(self.batches[g], topk[g], self.k, self.slots[g], self.miss[g])
         if self.share_mode == "serial":
-            self._attn(t, g)
-            self._append(t, g)
+            self._attn(g, q)
+            self._append(t, g, app)
             for l in range(g + 1, g + w.share):
                 H.hs_prefetch(self.batches[l])
-                self._attn(t, l)
-                self._append(t, l)
+                self._attn(l, q)
+                self._append(t, l, app)
             return
         cur = torch.cuda.current_stream()
         self.side.wait_stream(cur)
@@ -165,63 +220,67 @@ class Session:
             for j in range(1, w.share):
                 H.hs_prefetch(self.batches[g + j])
                 self.fetched[j].record(self.side)
-        self._attn(t, g)
-        self._append(t, g)
+        self._attn(g, q)
+        self._append(t, g, app)
         for j in range(1, w.share):
             cur.wait_event(self.fetched[j])
-            self._attn(t, g + j)
-            self._append(t, g + j)
+            self._attn(g + j, q)
+            self._append(t, g + j, app)
 
-    def layer(self, t: int, l: int) -> None:
-        """Enqueue step t of layer l on the current stream."""
+    def _layer(self, t: Optional[int], l: int) -> None:
         w = self.w
+        topk, q, app = self._inputs(t)
         if self.fused:
-            H.hs_resolve_attn(self.batches[l], self.topk[t, l], self.k, self.slots[l],
-                              self.miss[l], self.q[t, l], w.n_q_heads, self.scale, self.out[l],
-                              self.ws)
+            H.hs_resolve_attn(self.batches[l], topk[l], self.k, self.slots[l], self.miss[l],
+                              q[l], w.n_q_heads, self.scale, self.out[l], self.ws)
         else:
-            H.hs_resolve(self.batches[l], self.topk[t, l], self.k, self.slots[l], self.miss[l])
-            H.hs_sparse_attn(self.batches[l], self.q[t, l], w.n_q_heads, self.slots[l], self.k,
+            H.hs_resolve(self.batches[l], topk[l], self.k, self.slots[l], self.miss[l])
+            H.hs_sparse_attn(self.batches[l], q[l], w.n_q_heads, self.slots[l], self.k,
                              self.scale, self.out[l], self.ws)
-        if self.app is not None:
-            for r in range(self.R):
-                H.hs_pool_append(self.pool, r, l, w.ctx[r] + t, self.app[t, l, r], n=1)
+        self._append(t, l, app)
+
+    def _run(self, t: Optional[int]) -> None:
+        if self.grouped:
+            for g in range(0, self.L, self.w.share):
+                self._group(t, g)
+            return
+        for l in range(self.L):
+            self._layer(t, l)
 
     def step(self, t: int) -> None:
+        """Enqueue step t eagerly on the current stream (step t's own arrays)."""
         if self.reserve == "prefill" and self.app is not None:
             # pool pages on demand: room for this step's appended records
             for r in range(self.R):
                 H.hs_pool_reserve(self.pool, r, self.w.ctx[r] + t + 1)
-        if self.grouped:
-            for g in range(0, self.L, self.w.share):
-                self.group(t, g)
-            return
-        for l in range(self.L):
-            self.layer(t, l)
+        self._run(t)
 
-    def capture(self, steps: Optional[range] = None) -> None:
-        """Capture one graph per step (arguments of step t baked in)."""
-        steps = range(self.steps) if steps is None else steps
+    def staged_step(self) -> None:
+        """Enqueue the next step in graph form on the current stream: stage
+        its inputs, then the step over the fixed buffers."""
+        H.hs_stage_run(self.stage)
+        self._run(None)
+
+    def capture(self) -> None:
+        """Capture one graph of staged_step(), replayed for every step."""
         if self.reserve == "prefill" and self.app is not None:
             for r in range(self.R):  # pages cannot be allocated inside a graph
                 H.hs_pool_reserve(self.pool, r, self.w.capacity(r, self.steps))
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
-        self.graphs = [None] * self.steps
-        for t in steps:
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=s):
-                self.step(t)
-            self.graphs[t] = g
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            self.staged_step()
+        self.graph = g
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
 
     def grow(self, new_B: List[int]) -> None:
         """Grow every buffer of request r to new_B[r] slots (hs_buffer_grow, or
-        hs_buffer_grow_group for a layer group) and rebuild the batches;
-        graphs captured before must be captured again."""
+        hs_buffer_grow_group for a layer group) and rebuild the batches; a
+        graph captured before must be captured again."""
         torch.cuda.synchronize()
-        self.graphs = []
+        self.graph = None
         dev = self.device
         for l in range(self.L):
             if self.resolved_layer(l) != l:
@@ -252,12 +311,22 @@ class Session:
             self.ws = torch.empty(wsb, dtype=torch.uint8, device=self.device)
         torch.cuda.synchronize()
 
-    def replay(self, t: int) -> None:
-        self.graphs[t].replay()
+    def replay(self, t: Optional[int] = None) -> None:
+        """Replay the captured step graph; it runs the step the device
+        counter names (t, if given, must be that step)."""
+        if t is not None and t != self._next:
+            raise ValueError(f"the graph runs step {self._next} next, not {t}")
+        if self._next >= self.steps:
+            raise ValueError("every step of the trace has run")
+        self.graph.replay()
+        self._next += 1
 
     def reset(self) -> None:
-        """Every buffer back to empty; pool lengths back to the prefill."""
+        """Every buffer back to empty; pool lengths back to the prefill; the
+        staged step counter back to 0."""
         torch.cuda.synchronize()
+        H.hs_stage_set_step(self.stage, 0)
+        self._next = 0
         for l in range(self.L):
             if self.resolved_layer(l) != l:
                 continue  # a shared state is reset through its group's first layer
@@ -280,7 +349,8 @@ class Session:
 
     def close(self) -> None:
         torch.cuda.synchronize()
-        self.graphs = []
+        self.graph = None
+        H.hs_stage_destroy(self.stage)
         for b in self.batches:
             H.hs_batch_destroy(b)
         for l in reversed(range(self.L)):  # shared buffers before the state they use
