@@ -383,6 +383,25 @@ hs_status hs_sparse_attn(hs_batch_t batch, const void *d_q, int32_t n_q_heads,
                          float *d_out, void *d_ws, size_t ws_bytes,
                          void *stream);
 
+/* Allocation-free sparse attention, for callers that cannot allocate device
+ * memory or pass a workspace: code under graph capture, tight serving loops,
+ * harnesses that forbid allocation. The same computation, kernels and
+ * results as hs_sparse_attn, bit for bit; the split-k partials go to a
+ * scratch array of HS_NOALLOC_SCRATCH_BYTES that the library holds in
+ * device memory on each GPU it runs on, from that GPU's first such call
+ * until the process ends (its address is looked up on that first call, so
+ * make the first call outside graph capture). Calls that would need more
+ * scratch than that are refused (HS_E_INVAL, before anything is enqueued).
+ * Every call on one GPU shares that GPU's array: calls that overlap in
+ * time on one GPU (different streams, or graphs replayed concurrently)
+ * race and give wrong results; order them on one stream. Enqueue only;
+ * capture-safe after the first call; no allocation of any kind. */
+#define HS_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+hs_status hs_sparse_attn_noalloc(hs_batch_t batch, const void *d_q,
+                                 int32_t n_q_heads, const int32_t *d_slots,
+                                 int32_t k, float sm_scale, float *d_out,
+                                 void *stream);
+
 /* ---------- RESOLVE + sparse attention, fused (HiSparse summary, §5) -------
  * The same effect as hs_resolve followed by hs_sparse_attn on the same
  * stream - identical page tables, stamps, clocks, error words, slot vectors,

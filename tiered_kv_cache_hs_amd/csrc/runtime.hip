@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -1114,6 +1115,66 @@ hs_status hs_sparse_attn(hs_batch_t b, const void *d_q, int32_t Hq, const int32_
   hs_status s = check_attn(b, d_q, Hq, d_slots, k, sm_scale, d_out, d_ws, ws_bytes, &pl);
   if (s) return s;
   return enqueue_attn(b, d_q, Hq, d_slots, k, sm_scale, d_out, d_ws, pl, 0, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------- allocation-free attention
+namespace {
+
+// The split-k partials of hs_sparse_attn_noalloc: one array per GPU (each
+// device holds its own copy of a __device__ variable). In host code the
+// name is a host-side stand-in, never a device address: kernels get the
+// address hipGetSymbolAddress returns for the current device.
+__device__ __attribute__((aligned(256))) uint8_t scratch[HS_NOALLOC_SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[SCRATCH_MAX_DEVICES] = {};
+
+// The current device's address of `scratch`, looked up once per device.
+hs_status scratch_address(void **out) {
+  int dev = 0;
+  HS_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= SCRATCH_MAX_DEVICES)
+    return fail(HS_E_INVAL, "device %d beyond the %d this library serves", dev,
+                SCRATCH_MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(HS_E_HIP, "hipGetSymbolAddress(scratch) returned null");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return HS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+hs_status hs_sparse_attn_noalloc(hs_batch_t b, const void *d_q, int32_t Hq,
+                                 const int32_t *d_slots, int32_t k, float sm_scale, float *d_out,
+                                 void *stream) {
+  AttnPlan pl;
+  if (!b) return fail(HS_E_INVAL, "null batch");
+  // the plan alone first: its workspace size is checked against the scratch
+  hs_status s = plan_attn(b, Hq, k, &pl);
+  if (s) return s;
+  if (pl.ws_bytes > HS_NOALLOC_SCRATCH_BYTES)
+    return fail(HS_E_INVAL, "this attention needs %zu bytes of split-k scratch; the "
+                            "allocation-free form holds %zu (use hs_sparse_attn with a workspace)",
+                pl.ws_bytes, (size_t)HS_NOALLOC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  if (pl.ws_bytes > 0) {
+    s = scratch_address(&ws);
+    if (s) return s;
+  }
+  s = check_attn(b, d_q, Hq, d_slots, k, sm_scale, d_out, ws, HS_NOALLOC_SCRATCH_BYTES, &pl);
+  if (s) return s;
+  return enqueue_attn(b, d_q, Hq, d_slots, k, sm_scale, d_out, ws, pl, 0, stream);
 }
 
 hs_status hs_resolve_attn(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_t *d_slots,

@@ -38,6 +38,7 @@ HS_F32 = 0
 HS_BF16 = 1
 HS_MAX_K = 4096
 HS_MAX_B = 16384
+HS_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 # every symbol include/hisparse.h declares
 EXPORTS = (
@@ -50,7 +51,8 @@ EXPORTS = (
     "hs_buffer_rows", "hs_buffer_state_get", "hs_buffer_state_set",
     "hs_buffer_shared_bytes", "hs_buffer_create_shared", "hs_buffer_grow_group",
     "hs_batch_create", "hs_batch_destroy", "hs_batch_status", "hs_resolve",
-    "hs_sparse_attn_workspace", "hs_sparse_attn", "hs_resolve_attn", "hs_prefetch",
+    "hs_sparse_attn_workspace", "hs_sparse_attn", "hs_sparse_attn_noalloc", "hs_resolve_attn",
+    "hs_prefetch",
     "hs_stage_create", "hs_stage_destroy", "hs_stage_run", "hs_stage_set_step",
     "hs_stage_get_step",
     "hs_trace_enable", "hs_trace_read",
@@ -141,6 +143,7 @@ def lib():
         "hs_resolve": ([vp, vp, i32, vp, vp, vp], i32),
         "hs_sparse_attn_workspace": ([vp, i32, i32], sz),
         "hs_sparse_attn": ([vp, vp, i32, vp, i32, ctypes.c_float, vp, vp, sz, vp], i32),
+        "hs_sparse_attn_noalloc": ([vp, vp, i32, vp, i32, ctypes.c_float, vp, vp], i32),
         "hs_resolve_attn": ([vp, vp, i32, vp, vp, vp, i32, ctypes.c_float, vp, vp, sz, vp], i32),
         "hs_prefetch": ([vp, vp], i32),
         "hs_stage_create": ([P(StageRegion), i32, i32, P(vp)], i32),
@@ -441,6 +444,14 @@ def hs_sparse_attn(batch: int, q, n_q_heads: int, slots, k: int, sm_scale: float
     ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().hs_sparse_attn(batch, _ptr(q), int(n_q_heads), _ptr(slots), int(k),
                                 float(sm_scale), _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def hs_sparse_attn_noalloc(batch: int, q, n_q_heads: int, slots, k: int, sm_scale: float, out,
+                           stream=None) -> None:
+    """hs_sparse_attn with its split-k partials in the library's own device
+    scratch (no workspace, no allocation; calls on one GPU must not overlap)."""
+    _check(lib().hs_sparse_attn_noalloc(batch, _ptr(q), int(n_q_heads), _ptr(slots), int(k),
+                                        float(sm_scale), _ptr(out), _stream(stream)))
 
 
 def hs_resolve_attn(batch: int, topk, k: int, slots, miss, q, n_q_heads: int, sm_scale: float,
