@@ -52,6 +52,10 @@ def parse():
                          "split: hs_resolve (which also fetches the misses) then "
                          "hs_sparse_attn; auto: fused for MHA records, split for latent "
                          "records (the faster of the two for each on MI355X)")
+    ap.add_argument("--gather-bytes", type=int, default=0,
+                    help="hs_tuning.gather_bytes_per_lane: bytes of host reads each lane of the "
+                         "resolve's miss fetch keeps in flight (16, 32, 64 or 128; 0 = the "
+                         "library's choice)")
     ap.add_argument("--share", choices=("prefetch", "serial", "none"), default="prefetch",
                     help="layer groups that reuse one selection (workload 6): prefetch = one "
                          "resolve per group, the later layers' fetches on a second stream "
@@ -197,6 +201,7 @@ def main():
     from tiered_kv_cache_hs_amd.session import Session
 
     H.lib()
+    H.hs_set_tuning(gather_bytes_per_lane=args.gather_bytes)
     w = I.workload(args.workload)
     W, K = args.warmup, args.steps
     total = W + K
@@ -320,8 +325,8 @@ def main():
         dominant = roof_host if fetch_us >= attn_us else roof_attn
 
     from tiered_kv_cache_hs_amd.profiling import stored_traffic
-    dominant["traffic"] = stored_traffic(w.name, dominant["kernel"])
-    roof_attn["traffic"] = stored_traffic(w.name, attn_kernel)
+    dominant["traffic"] = stored_traffic(w.name, dominant["kernel"], args.path)
+    roof_attn["traffic"] = stored_traffic(w.name, attn_kernel, args.path)
     result = {
         "metric": METRIC,
         "value": round(ms_step * 1000.0 / w.n_layers, 2),

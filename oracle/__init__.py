@@ -28,7 +28,10 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# HS_ORACLE_LIB names another build of hs_oracle.c to load (the sanitizer
+# test's AddressSanitizer + UndefinedBehaviorSanitizer build)
+_BUILT = os.path.join(_HERE, "liboracle.so")
+_LIB_PATH = os.environ.get("HS_ORACLE_LIB") or _BUILT
 _lib = None
 
 ERR_RANGE = 1
@@ -42,12 +45,32 @@ DT_BF16 = 1
 def build(force: bool = False) -> str:
     """Compile hs_oracle.c into liboracle.so with gcc (OpenMP)."""
     src = os.path.join(_HERE, "hs_oracle.c")
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
-        tmp = _LIB_PATH + ".tmp"
+    if force or not os.path.exists(_BUILT) or os.path.getmtime(_BUILT) < os.path.getmtime(src):
+        tmp = _BUILT + ".tmp"
         subprocess.check_call(["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11",
                                "-fno-fast-math", src, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+        os.replace(tmp, _BUILT)
+    return _BUILT
+
+
+def build_sanitized(out: str) -> str:
+    """hs_oracle.c built with AddressSanitizer and UndefinedBehaviorSanitizer
+    (clang, every check fatal) into out/liboracle_san.so, for a process that
+    preloads the sanitizer runtime (tests/test_sanitizers.py)."""
+    src = os.path.join(_HERE, "hs_oracle.c")
+    lib = os.path.join(out, "liboracle_san.so")
+    subprocess.check_call([SAN_CC, "-O1", "-g", "-fPIC", "-shared", "-fopenmp", "-std=c11",
+                           "-fno-fast-math", "-fno-omit-frame-pointer", *SAN_FLAGS, src, "-o", lib,
+                           "-lm", *SAN_LINK])
+    return lib
+
+
+# The host C compiler of the ROCm LLVM (its sanitizer runtime is the one the
+# sanitized HIP library's host code uses too) and the sanitizer flags.
+SAN_CC = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "llvm", "bin", "clang")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all"]
+# its OpenMP runtime is found next to it
+SAN_LINK = ["-Wl,-rpath," + os.path.join(os.path.dirname(os.path.dirname(SAN_CC)), "lib")]
 
 
 class OracleUnitC(ctypes.Structure):

@@ -60,22 +60,27 @@ def test_stored_traffic_only_while_sources_match(tmp_path, monkeypatch):
 
 
 def test_bench_report_takes_the_launches_the_benchmark_times(tmp_path):
-    """The default-benchmark summary averages, per kernel, the dispatches of
-    the benchmark's last (eager, event-timed) pass: the last K of 3 (W + K)."""
+    """The measured-benchmark summary averages, per kernel, the dispatches of
+    the benchmark's last (eager, dispatch-timed) pass: the last K of 5 (W + K);
+    and recomputes the roofline fraction from those durations."""
     out = str(tmp_path)
     W, K = 2, 4
     kname = "void hs::(anonymous namespace)::hs_k_resolve<1024, 4, 2, true>(hs::UnitDesc const*)"
-    # three passes of W + K steps; durations 10 us in the first two passes,
+    # five passes of W + K steps; durations 10 us in the first four passes,
     # 20 us in the eager pass's warm-up steps and 30 us in its K timed ones
-    durs = [10.0] * (2 * (W + K)) + [20.0] * W + [30.0] * K
+    durs = [10.0] * (4 * (W + K)) + [20.0] * W + [30.0] * K
     _write(f"{out}/trace_bench/h/bench_kernel_trace.csv",
            ["Kernel_Name", "Start_Timestamp", "End_Timestamp"],
            [[kname, 100000 * i, 100000 * i + int(d * 1000)] for i, d in enumerate(durs)])
     line = {"metric": "m", "value": 1.0, "warmup": W, "steps": K,
             "config": {"workload": I.workload(3).name, "path": "p"},
-            "kernels_us": {"resolve": 33.0}, "roofline": {}}
+            "kernels_us": {"resolve": 33.0},
+            "roofline": {"kernel": "hs_k_resolve", "bytes_per_launch": 1_500_000, "peak": 63.0,
+                         "unit": "GB/s", "frac": 0.7, "avg_us": 33.0}}
     os.makedirs(out, exist_ok=True)
     with open(f"{out}/trace_bench.log", "w") as fh:
         fh.write("noise\n" + json.dumps(line) + "\n")
     md = open(P.bench_report(out)).read()
-    assert "| hs_k_resolve<1024, 4, 2, true> | 18 | 30.00 | 30.00 | 33.00 | 10.00 |" in md
+    assert "| hs_k_resolve<1024, 4, 2, true> | 30 | 30.00 | 30.00 | 33.00 | 10.00 |" in md
+    # 1.5 MB / 30 us = 50 GB/s = 0.7937 of 63
+    assert "= 50.00 GB/s, frac 0.7937" in md

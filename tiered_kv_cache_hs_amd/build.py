@@ -48,9 +48,16 @@ FLAGS = [
 EXTRA = {"attn_latent.hip": ["-mno-amdgpu-ieee", "-fno-honor-nans"]}
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-code sanitizers for a CPU-only test build (build_host_sanitized): each
+# flag applies to the host pass only; the device code is built as always.
+HOST_SAN_FLAGS = ["-Xarch_host", "-fsanitize=address,undefined",
+                  "-Xarch_host", "-fno-sanitize-recover=all",
+                  "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, objdir: str = OBJDIR, extra=()) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [hipcc(), *FLAGS, *EXTRA.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     # drop the host pass's notice about the device-only feature
     err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
@@ -75,6 +82,22 @@ def build(verbose: bool = True) -> str:
     if verbose:
         print(f"built {LIB}")
     return LIB
+
+
+def build_host_sanitized(out: str) -> str:
+    """The library with AddressSanitizer and UndefinedBehaviorSanitizer on its
+    host code (argument checks, handles, planning), for CPU tests in a process
+    that preloads the sanitizer runtime: out/libhisparse_san.so."""
+    objdir = os.path.join(out, "obj")
+    os.makedirs(objdir, exist_ok=True)
+    with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, objdir, HOST_SAN_FLAGS), SOURCES))
+    lib = os.path.join(out, "libhisparse_san.so")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", lib]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stderr}")
+    return lib
 
 
 if __name__ == "__main__":

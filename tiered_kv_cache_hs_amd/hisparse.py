@@ -15,7 +15,8 @@ from typing import Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libhisparse.so")
+# HS_LIB names another build to load (the sanitizer test's host-sanitized one)
+LIB_PATH = os.environ.get("HS_LIB") or os.path.join(_HERE, "libhisparse.so")
 
 HS_OK = 0
 HS_E_INVAL = -1

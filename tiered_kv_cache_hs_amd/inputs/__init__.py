@@ -23,7 +23,9 @@ from typing import List, Optional, Sequence, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libhsinputs.so")
+# HS_INPUTS_LIB names another build of fill.c to load (the sanitizer test's)
+_BUILT = os.path.join(_HERE, "libhsinputs.so")
+_LIB_PATH = os.environ.get("HS_INPUTS_LIB") or _BUILT
 _lib = None
 
 F32 = 0
@@ -39,13 +41,25 @@ def build_fill_lib(force: bool = False) -> str:
     import subprocess
 
     src = os.path.join(_HERE, "fill.c")
-    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(src):
-        tmp = _LIB_PATH + ".tmp"
+    if force or not os.path.exists(_BUILT) or os.path.getmtime(_BUILT) < os.path.getmtime(src):
+        tmp = _BUILT + ".tmp"
         subprocess.check_call(
             ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c11", src, "-o", tmp, "-lm"]
         )
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+        os.replace(tmp, _BUILT)
+    return _BUILT
+
+
+def build_sanitized(out: str, cc: str, flags: Sequence[str], link: Sequence[str] = ()) -> str:
+    """fill.c built with the given sanitizer compiler and flags into
+    out/libhsinputs_san.so (tests/test_sanitizers.py)."""
+    import subprocess
+
+    lib = os.path.join(out, "libhsinputs_san.so")
+    subprocess.check_call([cc, "-O1", "-g", "-fPIC", "-shared", "-fopenmp", "-std=c11",
+                           "-fno-omit-frame-pointer", *flags, os.path.join(_HERE, "fill.c"), "-o",
+                           lib, "-lm", *link])
+    return lib
 
 
 def _fill():

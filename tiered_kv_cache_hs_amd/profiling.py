@@ -61,6 +61,8 @@ KERNEL_SOURCES = {
     "hs_k_attn_mha": ["attn_mha.hip", "hs_device.h", "runtime.hip"],
     "hs_k_combine": ["attn_mha.hip", "hs_device.h", "runtime.hip"],
     "hs_k_combine_wave": ["attn_mha.hip", "hs_device.h", "runtime.hip"],
+    "hs_k_stage": ["stage.hip", "hs_device.h", "runtime.hip"],
+    "hs_k_append_next": ["resolve.hip", "hs_device.h", "runtime.hip"],
 }
 
 
@@ -72,17 +74,18 @@ def kernel_sources_sha1(kernel: str) -> str:
     return h.hexdigest()
 
 
-def stored_traffic(workload: str, kernel: str) -> Optional[int]:
-    """HBM bytes per dispatch of `kernel` on `workload` from the committed
-    counter readings, or None when there is none or the kernel's sources
-    changed since it was taken."""
+def stored_traffic(workload: str, kernel: str, path: str = "auto") -> Optional[int]:
+    """HBM bytes per dispatch of `kernel` on `workload` (benchmark --path
+    `path`) from the committed counter readings, or None when there is none
+    or the kernel's sources changed since it was taken."""
     try:
         with open(PMC_FILE) as fh:
             pmc = json.load(fh)
     except (OSError, ValueError):
         return None
     for e in pmc.get("entries", []):
-        if e.get("workload") == workload and e.get("kernel") == kernel:
+        if (e.get("workload") == workload and e.get("kernel") == kernel
+                and e.get("path", "auto") == path):
             if e.get("sources_sha1") != kernel_sources_sha1(kernel):
                 return None
             return int(e["traffic_bytes"])
@@ -123,16 +126,25 @@ def _child(cmd: List[str], log: str, limit: int) -> int:
     return rc
 
 
+# bench.py --path for every run ("auto": the benchmark's own choice per record
+# kind); another path gets its own run directories and summary names
+PATH = "auto"
+
+
+def _tag(wl: int) -> str:
+    return f"wl{wl}" + ("" if PATH == "auto" else f"_{PATH}")
+
+
 def bench_cmd(wl: Optional[int], steps: int, warmup: int) -> List[str]:
     if wl is None:
         return ["python3", "-u", "bench.py", "--copy-calibration"]
     return ["python3", "-u", "bench.py", "--workload", str(wl), "--steps", str(steps),
-            "--warmup", str(warmup), "--no-cpu"]
+            "--warmup", str(warmup), "--no-cpu"] + ([] if PATH == "auto" else ["--path", PATH])
 
 
 def trace_cmd(out: str, wl: int) -> List[str]:
     return ["rocprofv3", "--kernel-trace", "--stats", "--output-format", "csv", "-d",
-            os.path.join(out, f"trace_wl{wl}"), "-o", "bench", "--"] + bench_cmd(wl, 24, 8)
+            os.path.join(out, f"trace_{_tag(wl)}"), "-o", "bench", "--"] + bench_cmd(wl, 24, 8)
 
 
 def pmc_cmd(out: str, tag: str, counter: str, wl: Optional[int]) -> List[str]:
@@ -220,10 +232,10 @@ def run_all(workloads: List[int], out: str, limit: int) -> None:
         if _child(pmc_cmd(out, "copy", c, None), os.path.join(out, f"pmc_copy_{c}.log"), limit):
             raise SystemExit("copy calibration pass failed")
     for wl in workloads:
-        if _child(trace_cmd(out, wl), os.path.join(out, f"trace_wl{wl}.log"), limit):
+        if _child(trace_cmd(out, wl), os.path.join(out, f"trace_{_tag(wl)}.log"), limit):
             raise SystemExit(f"trace pass of workload {wl} failed")
         for c in COUNTERS:
-            if _child(pmc_cmd(out, f"wl{wl}", c, wl), os.path.join(out, f"pmc_wl{wl}_{c}.log"),
+            if _child(pmc_cmd(out, _tag(wl), c, wl), os.path.join(out, f"pmc_{_tag(wl)}_{c}.log"),
                       limit):
                 raise SystemExit(f"{c} pass of workload {wl} failed")
 
@@ -293,10 +305,10 @@ def report(workloads: List[int], out: str) -> None:
     entries = []
     for wl in workloads:
         w = I.workload(wl)
-        pmc = {c: read_counter(os.path.join(out, f"pmc_wl{wl}_{c}")) for c in COUNTERS}
-        stats = read_stats(os.path.join(out, f"trace_wl{wl}"))
-        trace, res = read_trace(os.path.join(out, f"trace_wl{wl}"))
-        bl = bench_line(os.path.join(out, f"trace_wl{wl}.log"))
+        pmc = {c: read_counter(os.path.join(out, f"pmc_{_tag(wl)}_{c}")) for c in COUNTERS}
+        stats = read_stats(os.path.join(out, f"trace_{_tag(wl)}"))
+        trace, res = read_trace(os.path.join(out, f"trace_{_tag(wl)}"))
+        bl = bench_line(os.path.join(out, f"trace_{_tag(wl)}.log"))
         lines = [f"# Kernel time and HBM traffic: workload {w.name}", "",
                  f"{w.n_requests} requests x {w.n_layers} layers, context "
                  f"{w.ctx[0] if len(set(w.ctx)) == 1 else 'per request'}, {w.kind} records of "
@@ -305,15 +317,17 @@ def report(workloads: List[int], out: str) -> None:
                  + (f", layer groups of {w.share}" if w.share > 1 else "") + ".",
                  "", "Made on one MI355X from the repository root by", "",
                  f"    python3 -u -m tiered_kv_cache_hs_amd.profiling run --workloads "
-                 f"{' '.join(str(x) for x in workloads)} --out {rel}", "",
+                 f"{' '.join(str(x) for x in workloads)} --out {rel}"
+                 + ("" if PATH == "auto" else f" --path {PATH}"), "",
                  "which runs these passes for this workload, each under `timeout -s KILL`:", "",
                  "    " + " ".join(trace_cmd(rel, wl)),
                  "    " + " ".join(pmc_cmd(rel, f"wl{wl}", "FETCH_SIZE", wl)),
                  "    " + " ".join(pmc_cmd(rel, f"wl{wl}", "WRITE_SIZE", wl)),
                  "    " + " ".join(pmc_cmd(rel, "copy", "FETCH_SIZE", None)) + "   (and WRITE_SIZE)",
-                 "", "The trace run replays 32 decode steps from their hipGraphs (8 warm-up + 24 "
-                 "timed), then runs them again eagerly with HIP events around every kernel, so "
-                 "each kernel has two dispatches per layer and step.", "",
+                 "", "The trace run replays the step graph for 32 decode steps (8 warm-up + 24 "
+                 "timed), replays the whole trace three more times from a reset state, then "
+                 "runs it once more eagerly with dispatch-timed HIP events on every kernel, so "
+                 "each kernel has five dispatches per layer and step.", "",
                  "## rocprofv3 --stats (all dispatches)", "",
                  "| kernel | calls | avg us | min us | max us | share % |", "|---|---|---|---|---|---|"]
         for r in stats:
@@ -324,13 +338,13 @@ def report(workloads: List[int], out: str) -> None:
                          f"{float(r['Percentage']):.2f} |")
         lines += ["", "## Warm averages (kernel trace, End - Start; each pass's cold first step dropped)",
                   "", "| kernel | dispatches | avg us (warm) | median us (warm) |", "|---|---|---|---|"]
-        steps_per_pass = 32
+        steps_per_pass, passes = 32, BENCH_PASSES
         for name, durs in trace.items():
-            if not name.startswith("hs_k") or "buffer_init" in name:
+            if not name.startswith("hs_k") or "buffer_init" in name or "stage_set" in name:
                 continue
-            per_step = max(1, len(durs) // (2 * steps_per_pass))
-            half = len(durs) // 2
-            warm = durs[per_step:half] + durs[half + per_step:]
+            per_step = max(1, len(durs) // (passes * steps_per_pass))
+            span = per_step * steps_per_pass
+            warm = [d for p0 in range(0, len(durs), span) for d in durs[p0 + per_step:p0 + span]]
             if warm:
                 lines.append(f"| {name[:60]} | {len(warm)} | {statistics.mean(warm):.2f} | "
                              f"{statistics.median(warm):.2f} |")
@@ -347,11 +361,9 @@ def report(workloads: List[int], out: str) -> None:
                              f"{r['Workgroup_Size_X']} | {r['Grid_Size_X']} |")
         if bl:
             lines += ["", "## The benchmark's own timing in the same run", "",
-                      f"Event-timed kernel durations per launch (us): {json.dumps(bl.get('kernels_us'))}; "
-                      f"value {bl.get('value')} us/layer under the profiler; path "
-                      f"{bl.get('config', {}).get('path')}. The event pair adds 2-4 us to a "
-                      "launch, and in a layer group the prefetch runs beside attention, so "
-                      "event times there include the overlap."]
+                      f"Dispatch-timed kernel durations per launch (us): "
+                      f"{json.dumps(bl.get('kernels_us'))}; value {bl.get('value')} us/layer under "
+                      f"the profiler; path {bl.get('config', {}).get('path')}."]
         lines += ["", "## HBM bytes per dispatch (FETCH_SIZE, WRITE_SIZE; separate passes)", "",
                   f"Scale from the 256 MiB copy: FETCH_SIZE reads {copy_kib['FETCH_SIZE']:.1f} KiB "
                   f"(x{scale['FETCH_SIZE']:.4f}), WRITE_SIZE {copy_kib['WRITE_SIZE']:.1f} KiB "
@@ -365,10 +377,12 @@ def report(workloads: List[int], out: str) -> None:
             wv = statistics.median(pmc["WRITE_SIZE"][k])
             b = int(round((f * scale["FETCH_SIZE"] + wv * scale["WRITE_SIZE"]) * 1024))
             lines.append(f"| {k} | {len(pmc['FETCH_SIZE'][k])} | {f:.1f} | {wv:.1f} | {b:,} |")
-            entries.append({"workload": w.name, "kernel": k, "sources_sha1": kernel_sources_sha1(k),
+            entries.append({"workload": w.name, "path": PATH, "kernel": k,
+                            "sources_sha1": kernel_sources_sha1(k),
                             "dispatches": len(pmc["FETCH_SIZE"][k]), "fetch_kib_median": round(f, 1),
                             "write_kib_median": round(wv, 1), "traffic_bytes": b})
-        with open(os.path.join(rep, f"hs_kernels_{w.name}.md"), "w") as fh:
+        suffix = "" if PATH == "auto" else f"_{PATH}"
+        with open(os.path.join(rep, f"hs_kernels_{w.name}{suffix}.md"), "w") as fh:
             fh.write("\n".join(lines) + "\n")
     doc = {"about": "HBM bytes per dispatch from rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE "
                     "(separate passes), median over the dispatches of `python3 -u bench.py "
@@ -387,7 +401,12 @@ def report(workloads: List[int], out: str) -> None:
 
 # --------------------------------------------- the default benchmark command
 
-BENCH_DEFAULT = ["python3", "-u", "bench.py"]
+# The benchmark's passes over the trace: the timed graph replays (W + K
+# steps), three more replays of every step from a reset state, one eager
+# pass with dispatch-timed events (the launches its kernel averages take).
+BENCH_PASSES = 5
+# the command the round's measurement runs
+BENCH_DEFAULT = ["python3", "-u", "bench.py", "--gpus", "1", "--steps", "20", "--warmup", "5"]
 
 
 def bench_trace_cmd(out: str) -> List[str]:
@@ -396,7 +415,7 @@ def bench_trace_cmd(out: str) -> List[str]:
 
 
 def run_bench_trace(out: str, limit: int) -> None:
-    """Kernel trace of exactly the default benchmark command."""
+    """Kernel trace of exactly the measured benchmark command."""
     os.makedirs(out, exist_ok=True)
     os.environ.setdefault("TMPDIR", "/tmp")
     if _child(bench_trace_cmd(out), os.path.join(out, "trace_bench.log"), limit):
@@ -404,11 +423,12 @@ def run_bench_trace(out: str, limit: int) -> None:
 
 
 def bench_report(out: str) -> str:
-    """Summary of the default benchmark's kernel trace: for every kernel, the
-    rocprofv3 durations of the launches the benchmark itself times with HIP
-    events (its last, eager pass: the K steps after the W warm-up steps),
-    beside the benchmark's own event-timed averages from the same run, and
-    the launches of the timed graph replays."""
+    """Summary of the measured benchmark command's kernel trace: for every
+    kernel, the rocprofv3 durations of the launches the benchmark itself
+    times with dispatch events (its last, eager pass: the K steps after the
+    W warm-up steps), beside the benchmark's own averages from the same run,
+    and the launches of the timed graph replays; then the roofline fraction
+    recomputed from the profiler's durations."""
     from . import inputs as I
 
     bl = bench_line(os.path.join(out, "trace_bench.log"))
@@ -420,39 +440,49 @@ def bench_report(out: str) -> str:
     rel = os.path.relpath(out, ROOT)
     cls_of = {"hs_k_resolve": "resolve", "hs_k_gather": "gather", "hs_k_attn_latent": "attn",
               "hs_k_attn_mha": "attn", "hs_k_combine": "combine",
-              "hs_k_combine_wave": "combine"}
+              "hs_k_combine_wave": "combine", "hs_k_stage": "stage", "hs_k_append": "append",
+              "hs_k_append_next": "append"}
     lines = [f"# Kernel time of the default benchmark: workload {w.name}", "",
              f"{w.n_requests} requests x {w.n_layers} layers, {w.kind} records of "
              f"{w.rec_bytes} bytes, {w.n_q_heads} query heads, k = {w.k}; path "
              f"{bl['config'].get('path')}.", "",
              "Made on one MI355X from the repository root by", "",
              f"    python3 -u -m tiered_kv_cache_hs_amd.profiling bench --out {rel}", "",
-             "which runs the benchmark's default command under the kernel tracer:", "",
+             "which runs the measured benchmark command under the kernel tracer:", "",
              "    " + " ".join(bench_trace_cmd(rel)), "",
-             f"The benchmark replays W + K = {W} + {K} steps from their hipGraphs (the timed "
-             "region: the last K), replays them all again with an event pair around each "
-             "step, then runs them eagerly with an event pair around every kernel launch "
-             "(the launches whose average is its `kernels_us` and its roofline `avg_us`). "
-             "Each kernel below has its dispatches in that order; the columns take the "
-             "same launches the benchmark averages.", "",
+             f"The benchmark replays its step graph W + K = {W} + {K} times (the timed "
+             "region: the last K), replays every step three more times from a reset state, "
+             "then runs the steps once more eagerly in the graph's form with events that take "
+             "each dispatch's own start and end (the launches whose average is its "
+             "`kernels_us` and its roofline `avg_us`). Each kernel below has its dispatches "
+             "in that order; the columns take the same launches the benchmark averages.", "",
              "| kernel | dispatches | rocprofv3 avg us (the benchmark's K eager launches) | "
-             "median us | benchmark event-timed avg us | rocprofv3 avg us (timed graph "
+             "median us | benchmark dispatch-timed avg us | rocprofv3 avg us (timed graph "
              "replays) |", "|---|---|---|---|---|---|"]
     ev = bl.get("kernels_us", {})
+    prof_avg = {}
     for name, durs in trace.items():
         base = short_name(name)
         if base not in cls_of:
             continue
-        per_step = max(1, len(durs) // (3 * (W + K)))
+        per_step = max(1, len(durs) // (BENCH_PASSES * (W + K)))
         eager = durs[-K * per_step:]
         timed = durs[W * per_step:(W + K) * per_step]
+        prof_avg[base] = statistics.mean(eager)
         lines.append(f"| {name[:60]} | {len(durs)} | {statistics.mean(eager):.2f} | "
                      f"{statistics.median(eager):.2f} | {ev.get(cls_of[base], 0.0):.2f} | "
                      f"{statistics.mean(timed):.2f} |")
+    roof = bl.get("roofline") or {}
     lines += ["", f"Benchmark line of this run: value {bl['value']} us/layer; roofline "
-              f"{json.dumps(bl.get('roofline'))}.", "",
-              "The event pair around an eager launch also holds the launch's own dispatch "
-              "latency, so event-timed averages read a few us above the kernel's duration."]
+              f"{json.dumps(roof)}."]
+    k = roof.get("kernel")
+    if k in prof_avg and roof.get("bytes_per_launch") and roof.get("peak"):
+        unit = 1e9 if roof.get("unit") == "GB/s" else 1e12
+        ach = roof["bytes_per_launch"] / (prof_avg[k] * 1e-6) / unit
+        lines += ["", f"Roofline from the profiler's durations of the same launches: "
+                  f"{roof['bytes_per_launch']:,} bytes / {prof_avg[k]:.2f} us = {ach:.2f} "
+                  f"{roof.get('unit')}, frac {ach / roof['peak']:.4f} (the line: "
+                  f"{roof.get('frac')}, from {roof.get('avg_us')} us)."]
     os.makedirs(os.path.join(out, "report"), exist_ok=True)
     path = os.path.join(out, "report", f"hs_kernels_bench_default_{w.name}.md")
     with open(path, "w") as fh:
@@ -468,7 +498,11 @@ def main() -> None:
     ap.add_argument("--workloads", type=int, nargs="+", default=[3, 4, 5, 6, 7])
     ap.add_argument("--out", default=os.path.join(ROOT, "prof_out"))
     ap.add_argument("--limit", type=int, default=240, help="seconds per profiler pass")
+    ap.add_argument("--path", choices=("auto", "fused", "split"), default="auto",
+                    help="bench.py --path of every run (run/report)")
     a = ap.parse_args()
+    global PATH
+    PATH = a.path
     if a.action in ("bench", "bench-report"):
         if a.action == "bench":
             run_bench_trace(a.out, a.limit)
