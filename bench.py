@@ -362,7 +362,9 @@ def main():
 
     if not args.no_cpu:
         print("[bench] CPU oracle baseline", file=sys.stderr, flush=True)
-        traces = I.gen_traces(w, total)
+        # the oracle samples the same trace from its start, as far as the
+        # time budget (or the workload's own length) goes
+        traces = I.gen_traces(w, max(total, w.steps))
         us, n_steps, threads, us1 = cpu_baseline(w, traces, args.cpu_seconds,
                                                  one_thread_steps=3 if w.n_units <= 8 else 0)
         result["cpu_baseline"] = {

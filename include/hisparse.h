@@ -119,7 +119,7 @@ typedef struct hs_pool_desc {
 typedef struct hs_tuning {
   int32_t attn_splits;          /* split-k factor of sparse attention */
   int32_t latent_heads_per_wg;  /* latent attention: query heads per workgroup
-                                   (16, 32 or 64, dividing n_q_heads) */
+                                   (32 or 64; 0 = by batch size) */
   int32_t prefetch_workgroups;  /* hs_prefetch: workgroups per launch
                                    (0 = 64; 1 to 65536) */
   int32_t prefetch_batch;       /* hs_prefetch: host reads in flight per lane
@@ -371,6 +371,8 @@ hs_status hs_resolve(hs_batch_t batch, const int32_t *d_topk, int32_t k,
  * HS_KV_LATENT: q [n][n_q_heads][latent_dim + rope_dim] bf16; K is the whole
  *   record, V its latent part; out [n][n_q_heads][latent_dim]. Supported:
  *   bf16, latent_dim 512, rope_dim 64, n_q_heads 16, 32 or 64.
+ *   Attention over the same buffers must not run concurrently with a resolve
+ *   of them.
  * Outputs are fp32 (accumulation is fp32). A slot outside [0, B) makes the
  * unit's output NaN and sets HS_ERR_SLOT. d_ws is scratch of at least
  * hs_sparse_attn_workspace(...) bytes (may be NULL when that is 0); its
@@ -405,12 +407,14 @@ hs_status hs_sparse_attn_noalloc(hs_batch_t batch, const void *d_q,
 /* ---------- RESOLVE + sparse attention, fused (HiSparse summary, §5) -------
  * The same effect as hs_resolve followed by hs_sparse_attn on the same
  * stream - identical page tables, stamps, clocks, error words, slot vectors,
- * miss counts, row bytes and outputs, bit for bit - with one difference in
- * how the misses travel: instead of a separate copy kernel, the attention
- * workgroup that needs a just-resolved miss loads its record straight from
- * the pinned host pool, uses it, and stores it into the slot the resolve
- * assigned, so the host-link transfer overlaps the attention over the
- * resident rows. Every missing byte still crosses the host link once.
+ * miss counts, row bytes and outputs, bit for bit. For HS_KV_MHA records the
+ * misses travel differently: instead of a separate copy kernel, the
+ * attention workgroup that needs a just-resolved miss loads its record
+ * straight from the pinned host pool, uses it, and stores it into the slot
+ * the resolve assigned, so the host-link transfer overlaps the attention over
+ * the resident rows. Every missing byte still crosses the host link once.
+ * For HS_KV_LATENT records it is exactly the two calls (the resolve moves
+ * the misses, its first host reads overlapping its victim selection).
  * Arguments, checks and workspace as for the two calls. Enqueue only;
  * capture-safe. */
 hs_status hs_resolve_attn(hs_batch_t batch, const int32_t *d_topk, int32_t k,
@@ -446,11 +450,11 @@ hs_status hs_prefetch(hs_batch_t batch, void *stream);
  * in device memory and advanced by one on the device after the copy. One
  * captured hs_stage_run therefore stages a new step on every replay of the
  * graph, with no host involvement.
- * hs_stage_create: regions[i] = {d_src, d_dst, bytes, src_stride}: entry j
+ * hs_stage_create: 1 to 8 regions[i] = {d_src, d_dst, bytes, src_stride}: entry j
  *   of the ring is d_src + j * src_stride; bytes and src_stride multiples of
  *   16 and pointers 16-byte aligned; destinations must not overlap any
  *   source or each other. ring >= 1 entries. The step counter starts at 0.
- *   Uploads a device table; synchronous. HS_E_INVAL for a malformed region.
+ *   Synchronous. HS_E_INVAL for a malformed region or more than 8 regions.
  * hs_stage_run: enqueue only; capture-safe. One kernel for every region.
  * hs_stage_set_step: sets the counter (enqueued; a kernel, not a memset).
  * hs_stage_get_step: reads the counter; synchronous (waits for the device).

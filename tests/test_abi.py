@@ -41,26 +41,27 @@ def test_status_strings_and_tuning_roundtrip():
     assert H.hs_status_str(H.HS_E_STATE) == "invalid buffer state"
     assert H.hs_status_str(H.HS_E_DEVICE) == "data error reported by the device"
     assert (H.HS_E_DEVICE, H.HS_E_STATE) == (-5, -6)
-    H.hs_set_tuning(4, 32, 96, 2, 64)
+    H.hs_set_tuning(4, 96, 2, 64, 32)
     assert H.hs_get_tuning() == {"attn_splits": 4, "latent_heads_per_wg": 32,
                                  "prefetch_workgroups": 96, "prefetch_batch": 2,
                                  "gather_bytes_per_lane": 64}
-    H.hs_set_tuning(0, 0)
+    H.hs_set_tuning()
     for gb in (16, 32, 128):
         H.hs_set_tuning(gather_bytes_per_lane=gb)
         assert H.hs_get_tuning()["gather_bytes_per_lane"] == gb
     for gb in (8, 48, 256, -16):
         with pytest.raises(H.HsError):
             H.hs_set_tuning(gather_bytes_per_lane=gb)
-    H.hs_set_tuning(0, 0)
+    H.hs_set_tuning()
     with pytest.raises(H.HsError):
-        H.hs_set_tuning(-1, 0)
+        H.hs_set_tuning(-1)
     with pytest.raises(H.HsError):
-        H.hs_set_tuning(0, 48)
+        H.hs_set_tuning(prefetch_workgroups=-3)
     with pytest.raises(H.HsError):
-        H.hs_set_tuning(0, 0, -3)
-    with pytest.raises(H.HsError):
-        H.hs_set_tuning(0, 0, 0, 3)
+        H.hs_set_tuning(prefetch_batch=3)
+    for hpw in (16, 48, -32):
+        with pytest.raises(H.HsError):
+            H.hs_set_tuning(latent_heads_per_wg=hpw)
     assert H.hs_get_tuning()["prefetch_workgroups"] == 0
 
 
@@ -99,6 +100,9 @@ def test_null_and_shape_checks_without_device():
     bad = [H.StageRegion(0x1000, 0x9000, 32, 32), H.StageRegion(0x5000, 0x9010, 32, 32)]
     assert L.hs_stage_create((H.StageRegion * 2)(*bad), 2, 4, ctypes.byref(st)) == H.HS_E_INVAL
     assert "overlaps" in H.hs_last_error()
+    many = [H.StageRegion(0x1000 * (i + 1), 0x100000 + 0x1000 * i, 32, 32) for i in range(9)]
+    assert L.hs_stage_create((H.StageRegion * 9)(*many), 9, 1, ctypes.byref(st)) == H.HS_E_INVAL
+    assert "1 to 8 regions" in H.hs_last_error()
     d = H.PoolDesc(1, 1, 7, H.HS_BF16, 1, 64, 0, 0, (ctypes.c_int64 * 1)(100))
     out = ctypes.c_void_p()
     assert L.hs_pool_create(ctypes.byref(d), ctypes.byref(out)) == H.HS_E_INVAL

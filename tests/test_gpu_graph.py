@@ -28,7 +28,7 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     H.lib()
-    H.hs_set_tuning(0, 0)
+    H.hs_set_tuning()
 
 
 def say(*a):

@@ -26,9 +26,9 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     H.lib()
-    H.hs_set_tuning(0, 0)
+    H.hs_set_tuning()
     yield
-    H.hs_set_tuning(0, 0)
+    H.hs_set_tuning()
 
 
 def say(*a):
@@ -91,33 +91,36 @@ def test_small_shapes(case):
     compare_run(w, steps, fill="full")
 
 
-@pytest.mark.parametrize("hpw,splits,fused", [(16, 0, False), (32, 0, False), (64, 0, False),
-                                               (16, 3, False), (32, 1, False), (64, 5, False),
-                                               (32, 2, True), (64, 0, True)])
-def test_latent_heads_per_workgroup(hpw, splits, fused):
-    """Latent attention with every head split (16, 32 or 64 heads per
-    workgroup), several split-k factors, a ragged last step of 32 slots."""
-    w = _small("latent", I.BF16, 300, 197, 3000, 4, 40, R=2, seed=50 + hpw + splits, Hq=64)
-    H.hs_set_tuning(splits, hpw)
+@pytest.mark.parametrize("hpw,splits,fused", [(32, 0, False), (32, 1, False), (32, 3, False),
+                                               (64, 0, False), (64, 1, False), (64, 5, False),
+                                               (64, 8, False), (32, 2, True), (64, 0, True)])
+def test_latent_splits(hpw, splits, fused):
+    """Latent attention with 32 and 64 heads per workgroup and several split-k
+    factors (each split a run of 32-entry tiles; k = 197 = 6 * 32 + 5, so the
+    last tile is ragged and, with 32 heads per workgroup and one split, alone
+    in its step) and through the fused entry point."""
+    w = _small("latent", I.BF16, 300, 197, 3000, 4, 40, R=2, seed=50 + splits + hpw, Hq=64)
+    H.hs_set_tuning(splits, latent_heads_per_wg=hpw)
     try:
         compare_run(w, 4, fill="full", fused=fused)
     finally:
-        H.hs_set_tuning(0, 0)
+        H.hs_set_tuning()
 
 
-@pytest.mark.parametrize("hpw", [16, 32, 64])
-@pytest.mark.parametrize("k", [64, 96, 160, 250])
-def test_latent_step_pipeline_tails(hpw, k):
-    """One split over the whole selection, so the chunk is 2, 3, 5 or 8
-    steps of 32 slots (the last one ragged for k = 250): every remainder of
-    the step loop's register rotations (two buffers for 16 and 64 heads per
-    workgroup, three for 32) runs after the loop."""
-    w = _small("latent", I.BF16, 300, k, 3000, 3, 30, R=2, seed=900 + k + hpw, Hq=64)
-    H.hs_set_tuning(1, hpw)
+@pytest.mark.parametrize("hq", [16, 32, 64])
+@pytest.mark.parametrize("k", [1, 15, 16, 17, 47, 64, 100, 250])
+def test_latent_tile_tails(hq, k):
+    """One split over the whole selection: 1 to 8 tiles of 32 entries, with
+    ragged last tiles. 16 or 32 query heads take 32 heads per workgroup (two
+    tiles per step, so the last step may hold one tile and the stream without
+    it merges as an empty state; 16 heads pad the group); 64 heads take 64
+    per workgroup (one tile per step, three step buffers)."""
+    w = _small("latent", I.BF16, 300, k, 3000, 3, min(30, k), R=2, seed=900 + k + hq, Hq=hq)
+    H.hs_set_tuning(1)
     try:
         compare_run(w, 3, fill="full")
     finally:
-        H.hs_set_tuning(0, 0)
+        H.hs_set_tuning()
 
 
 def test_multi_request_multi_layer_small():

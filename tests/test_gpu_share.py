@@ -29,9 +29,9 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     H.lib()
-    H.hs_set_tuning(0, 0, 0)
+    H.hs_set_tuning()
     yield
-    H.hs_set_tuning(0, 0, 0)
+    H.hs_set_tuning()
 
 
 def say(*a):
@@ -94,12 +94,12 @@ def test_prefetch_workgroup_counts():
     w = small_workload("latent", I.BF16, 300, 197, 3000, 4, 40, R=2, L=4, seed=340, Hq=16,
                        share=4)
     for wg, batch in ((1, 1), (7, 2), (96, 4), (4096, 8), (5, 8)):
-        H.hs_set_tuning(0, 0, wg, batch)
+        H.hs_set_tuning(prefetch_workgroups=wg, prefetch_batch=batch)
         try:
             say(f"prefetch_workgroups={wg} prefetch_batch={batch}")
             compare_run(w, 4, fill="full", attn_every=2, share_mode="prefetch")
         finally:
-            H.hs_set_tuning(0, 0, 0, 0)
+            H.hs_set_tuning()
 
 
 def _bitwise_same(a, b, steps, graph):

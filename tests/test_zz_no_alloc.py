@@ -27,9 +27,9 @@ def _gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     H.lib()
-    H.hs_set_tuning(0, 0)
+    H.hs_set_tuning()
     yield
-    H.hs_set_tuning(0, 0)
+    H.hs_set_tuning()
 
 
 def _both(sess, batch, q, slots, k, n_units, Hq, dv):
@@ -126,5 +126,5 @@ def test_noalloc_refuses_more_than_its_scratch():
             H.hs_sparse_attn_noalloc(sess.batches[0], sess.q[0, 0], w.n_q_heads, sess.slots[0],
                                      w.k, sess.scale, sess.out[0])
     finally:
-        H.hs_set_tuning(0, 0)
+        H.hs_set_tuning()
         sess.close()

@@ -35,9 +35,6 @@ def hipcc() -> str:
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # MFMA accumulators in ordinary VGPRs where they fit: no copies between
-    # accumulation and arithmetic registers around the softmax rescale
-    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

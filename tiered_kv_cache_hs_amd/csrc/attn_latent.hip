@@ -10,43 +10,48 @@
 //
 // With 16-64 query heads sharing each row, QK^T is a real dense contraction
 // (heads x 576 by 576 x slots) and PV another (heads x slots by slots x 512),
-// about 111 flop per byte read at 64 heads: bandwidth-bound only if both run
-// on the bf16 matrix cores, so both use v_mfma_f32_16x16x32_bf16.
+// about 111 flop per byte read at 64 heads: both run on the bf16 matrix
+// cores (v_mfma_f32_32x32x16_bf16).
 //
-// Work split. A workgroup (4 waves) owns a chunk of one unit's selection for
-// every query head, walked 32 slots at a time (two 16-row MFMA tiles). The
-// 18 32-wide d-steps of the 576-element key are divided among the waves
-// (wave w: latent d-steps 4w..4w+3, plus rope d-step 16+w for w < 2), so
-// every row byte is loaded once per workgroup and each wave's latent slice is
-// exactly the value slice [128w, 128w+128) it needs for PV. Per 32 slots:
-//   1. each wave multiplies its row slices by the Q^T slices of every head
-//      group of 16 heads (MFMA A = rows, B = Q^T), reusing the loaded rows,
-//      and writes its value slice transposed into its own LDS area (two
-//      slots packed per 32-bit word);
-//   2. the partial score tiles go to LDS (barrier); wave g sums the four
-//      partials of head group g in a fixed order and runs that group's
-//      online softmax (log2 units), rounding P to bf16 (barrier);
-//   3. every wave reads P of every head group and accumulates
-//      O^T[v][head] += V^T[v][slot] P^T[slot][head] with MFMA, each value
-//      tile read once and used by every head group.
-// The running maximum is a lazy reference: it moves only when a score
-// exceeds it by more than 2^8 (log2 units), so P stays in [0, 256] and the
-// accumulators are rescaled only on those rare steps; the partial state
-// (reference max, sum, accumulators) combines exactly as with the true max.
-// The P^T operand is the softmax lane's own score layout: lane l of a 16x16
-// tile holds rows 4(l/16)+i, so the lane's 8 P values (2 tiles x 4 rows)
-// are the 8 k-elements of the PV operand, and the V^T words are laid out in
-// that same order. The chunk's slot ids are staged in LDS once; row slices
-// are loaded DEPTH steps ahead (one for 16 and 64 heads per workgroup, two
-// for 32) through DEPTH + 1 register buffers.
-//
-// Fetch mode (resolve + attention fused): a selected row that the resolve
-// just assigned to a victim slot has not been copied from the host pool yet;
-// the wave that needs it loads its slice straight from pinned host memory,
-// uses it, and stores it into the slot's row, so the host-link transfer
-// overlaps the attention over the resident rows. Each row slice is read by
-// exactly one wave, so every fetched byte crosses the host link once.
+// Work split. A workgroup of 4 waves covers 32 NHG query heads (NHG = 1 or 2)
+// of one (unit, split). The split's selection entries are cut into tiles of
+// 32 rows, processed in steps of 3 - NHG tiles. Wave w = (x, vh), x = w & 1,
+// vh = w >> 1, owns 32 heads x 256 values of the output: with NHG = 2 head
+// group x over every tile; with NHG = 1 the workgroup's 32 heads over tile
+// x of each step (two streams, merged at the end). Per step:
+//   * rows: the 4 waves copy the step's rows from HBM straight into LDS with
+//     global_load_lds (one instruction per row for its 1 KB latent part, one
+//     per 8 rows for their 128-byte rope parts; 9 per wave per tile); the
+//     copies of a later step go out between this step's QK^T MFMAs. The
+//     step buffers rotate (three of 36 KB with NHG = 2, two of 72 KB with
+//     NHG = 1) and one barrier per step tells every wave that the step has
+//     landed and the buffer about to be refilled is free;
+//   * S^T = K Q^T over 36 d-steps of 16: A = the tile's rows (one 1 KB LDS
+//     read per d-step), B = Q^T of the wave's 32 heads (registers, read once
+//     from a query tile that the prologue copies into LDS like a row tile).
+//     A lane ends with 16 slots of one head: the head is the lane's column,
+//     the same column as in the PV accumulators;
+//   * online softmax per head in log2 units with a lazy reference maximum: it
+//     moves only when a score exceeds it by more than 2^8, so P stays in
+//     [0, 256] and the accumulators are rescaled only on those rare steps;
+//     the maximum over a head's 32 slots (two lanes) is taken only when a
+//     ballot says some score passed the slack;
+//   * O^T += V^T P^T: A = V^T read with gfx950's LDS transpose reads
+//     (ds_read_b64_tr_b16, two per operand), B = P^T, the softmax lane's own
+//     16 values rounded to bf16 (8 per k-block of 16 slots); the slot order
+//     inside a k-block follows the score layout, and the transpose reads take
+//     the rows in that same order;
+//   * LDS operand reads run a few MFMAs ahead of their use;
+//   * the accumulators (128 per lane) live in the accumulation registers and
+//     only MFMAs touch them inside the loop; the queries (144 registers) and
+//     everything else fit the ordinary ones, so a compute unit runs one
+//     workgroup.
+// At the end each wave stages its accumulators in LDS and the workgroup
+// stores whole 1 KB row halves: the output, or its split's partial for the
+// split-k combine.
 #include "hs_device.h"
+
+#define HS_LDS __attribute__((address_space(3)))
 
 namespace hs {
 
@@ -57,49 +62,29 @@ constexpr int LAT_DL = 512;
 constexpr int LAT_DR = 64;
 constexpr int LAT_DK = LAT_DL + LAT_DR;            // 576
 constexpr int LAT_REC = LAT_DK * 2;                // 1152 bytes
-constexpr int LAT_VT_STRIDE = 20;                  // words per value row (16 used)
-constexpr int LAT_VT_WORDS = 128 * LAT_VT_STRIDE;  // per wave: 128 value rows
+constexpr int LAT_TILE = 32;                       // rows per tile
+constexpr int LAT_BLOCKS = LAT_REC / 32;           // 36 blocks (= d-steps of 16)
+constexpr int LAT_TILE_BYTES = LAT_BLOCKS * 1024;  // 36 KB
+constexpr int LAT_LDS_BUF = 4 * LAT_TILE_BYTES;     // step buffers: 144 KB
+constexpr int LAT_KPF = 6;                         // K operands read ahead
+constexpr int LAT_VPF = 4;                         // V^T operands read ahead
 constexpr float NEG_INF = -__builtin_huge_valf();
 constexpr float LAT_LAZY_LOG2 = 8.f;               // reference-max slack, log2 units
 // Split partials of at most this many bytes per launch are written with
 // streaming (nontemporal) stores: the kernel then ends without writing back
-// that many dirty L2 lines, and the combine, latency-bound at that size,
-// reads them as fast from memory. Larger partials are read faster by the
-// combine when they were written through the cache. (Batch-8 MLA, 8.4 MB of
-// partials: attention 21.0 -> 19.9 us, combine unchanged; 64 requests,
-// 34 MB: attention +2.2 us, combine +4 us.)
+// that many dirty L2 lines, and the combine reads them as fast from memory.
 constexpr size_t LAT_STREAM_PARTIAL_BYTES = 16u << 20;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short short8 __attribute__((ext_vector_type(8)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Rotation of a value within each row of 16 lanes (DPP row_ror); every
-// lane reads a lane of its own row, so the move folds into the consuming
-// max or add as a DPP operand.
-template <int N>
-__device__ __forceinline__ float row_ror(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x120 + N, 0xF, 0xF, true));
-}
-// Maximum / sum over the 16 lanes of a row, left in every lane of the row.
-__device__ __forceinline__ float row_max16(float x) {
-  x = fmaxf(x, row_ror<8>(x));
-  x = fmaxf(x, row_ror<4>(x));
-  x = fmaxf(x, row_ror<2>(x));
-  return fmaxf(x, row_ror<1>(x));
-}
-__device__ __forceinline__ float row_sum16(float x) {
-  x += row_ror<8>(x);
-  x += row_ror<4>(x);
-  x += row_ror<2>(x);
-  return x + row_ror<1>(x);
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float floatx2 __attribute__((ext_vector_type(2)));
 
 // Two floats rounded to bf16 (nearest even, v_cvt_pk_bf16_f32): a in the
 // low half, b in the high half.
@@ -114,47 +99,90 @@ __device__ __forceinline__ uint32_t nan_bits_if(bool c, float x) {
   return c ? 0x7FC00000u : __float_as_uint(x);
 }
 
-// Word address of value row v (0..127) of a wave's transposed-value area.
-// Rows are 20 words apart (16 used): 16-byte aligned, and 8 (or 16)
-// consecutive rows start in distinct groups of 4 banks, so the 16-byte reads
-// of the PV operand (one row per lane) are free of bank conflicts.
-__device__ __forceinline__ int vt_row(int v) { return LAT_VT_STRIDE * v; }
+// Tile layout (36 KB): the latent part (1 KB) of tile row r at r * 1024, its
+// 16-byte chunk c at position c ^ lat_sw(r); the rope part (128 bytes) of row
+// r at 32768 + 128 r, its chunk c at position c ^ rope_sw(r).
+__device__ __forceinline__ int lat_sw(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+__device__ __forceinline__ int rope_sw(int r) { return (r >> 1) & 7; }
+constexpr int LAT_ROPE_OFF = 32 * 1024;
 
-// A tile row: its slot, and in fetch mode its pool position when it must
-// come from the host (else -1).
-struct RowRef {
-  int slot;
-  int src;
-};
+// One 16-byte global_load_lds per lane: the lane's 16 bytes at src land at
+// LDS byte address lds + 16 * lane (lds wave-uniform, in M0). Written as
+// inline assembly so that the compiler does not track it: its own wait
+// insertion would otherwise wait for every LDS load in flight (the next
+// pair's too) before each LDS read of the pair being computed. Waits for
+// these loads are explicit (wait_vmcnt). The instruction has no output
+// register; its address registers are read at issue; M0 is set in the same
+// statement and declared clobbered (nothing else in this kernel keeps a value
+// in M0). Loads the compiler does not know of can only make its own vmcnt
+// waits stricter: the counter retires in issue order.
+// (The compiler warns that M0 is a reserved register; these kernels use M0
+// nowhere else, which the generated code shows.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_dma16(const HS_GLOBAL uint8_t *src, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"((uint64_t)(uintptr_t)src), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
-// HG head groups of 16 per workgroup; HS workgroups split a unit's Hq =
-// HS * HG * 16 heads; DEPTH steps of row loads in flight ahead of the one
-// computing (1 or 2; the register budget allows 2 up to HG = 2).
-//
-// Score layout: QK^T is computed transposed, S^T[head][slot] = Q x K^T
-// (MFMA A = Q slices, B = row slices), so a lane holds 4 heads x 1 slot per
-// 16-slot tile and the reductions over slots run within a row of 16 lanes
-// (DPP). Every wave issues the same loads in every step (rows past the
-// chunk repeat its last row and are masked), so the number of loads in
-// flight is the same on every path and each step waits only for its own.
-template <int HG, int DEPTH, bool FETCH, bool STREAM>
-__global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
+// Waits until at most N vector-memory operations of this wave are in flight
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt not waited).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// o *= a for accumulators that stay in the accumulation registers: each is
+// moved out, scaled and moved back in one statement, so the compiler never
+// keeps a second copy of the accumulators in ordinary registers (it would
+// otherwise do so around the loop that these multiplies sit in). Used only
+// on the rare moves of the reference maximum, where no MFMA is in flight
+// (their results were read since); the leading and trailing wait states
+// cover the MFMA-to-move and move-to-MFMA distances regardless.
+template <int NVT>
+__device__ __forceinline__ void scale_acc(floatx16 (&o)[NVT], float a) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+#pragma unroll
+  for (int vt = 0; vt < NVT; ++vt) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      float t;
+      asm volatile(
+          "v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+          : "+a"(o[vt][e]), "=&v"(t)
+          : "v"(a));
+    }
+  }
+  asm volatile("s_nop 7");
+}
+
+// Grid: n8 * HS * S workgroups in XCD-aware order (the HS * S workgroups of a
+// unit get block ids equal mod 8, so they run on one XCD and share its L2 for
+// the unit's rows); workgroup (u, head group hh, split sp) covers heads
+// [32 NHG hh, 32 NHG (hh + 1)) of unit u (those below Hq) over selection
+// entries [sp * chunk, min(k, (sp + 1) * chunk)).
+template <int NHG, bool STREAM>
+__global__ __launch_bounds__(LAT_THREADS, 1) void hs_k_attn_latent(
     const UnitDesc *__restrict__ units, const uint16_t *__restrict__ q_all,
-    const int32_t *__restrict__ slots_all, int n_units, int k, float scale_log2, int S,
+    const int32_t *__restrict__ slots_all, int n_units, int k, int Hq, float scale_log2, int S,
     int HS, int chunk, float *__restrict__ ws_o, float *__restrict__ ws_ml,
     float *__restrict__ out) {
-  static_assert(DEPTH == 1 || DEPTH == 2, "prefetch depth 1 or 2");
-  __shared__ uint32_t s_vt[4][LAT_VT_WORDS];
-  __shared__ floatx4 s_part[HG][4][2][64];
-  __shared__ v4u s_p[HG][64];          // PV operand P^T of every lane
-  __shared__ float s_alpha[HG][16];    // per head: rescale factor, then l
-  __shared__ int s_rescale[4];         // per wave: its reference maximum moved
+  constexpr int NVT = LAT_DL / 32 / 2;            // value tiles of 32 per wave
+  constexpr int NST = 3 - NHG;                     // tiles per step
+  constexpr int NBUF = NHG == 2 ? 3 : 2;           // step buffers
+  constexpr int DEPTH = NBUF - 1;                  // steps copied ahead
+  constexpr int STEP_BYTES = NST * LAT_TILE_BYTES;
+  constexpr int CPS = 9 * NST;                     // copies per wave per step
+  static_assert(NBUF * STEP_BYTES <= LAT_LDS_BUF, "step buffers");
+  __shared__ __attribute__((aligned(1024))) uint8_t s_buf[LAT_LDS_BUF];
   __shared__ int s_ids[LAT_MAX_CHUNK];
-  __shared__ int s_src[FETCH ? LAT_MAX_CHUNK : 1];
+  __shared__ floatx2 s_ml[4][32];  // per wave: (m, l) of its 32 heads
+  __shared__ int s_bad;
 
-  // XCD-aware order: the S x HS workgroups of a unit get block ids equal
-  // mod 8, i.e. run on one XCD and share its L2 for the unit's queries and,
-  // across head splits, its rows.
   const int b = blockIdx.x;
   const int xcd = b & 7;
   const int j8 = b >> 3;
@@ -162,344 +190,400 @@ __global__ __launch_bounds__(LAT_THREADS) void hs_k_attn_latent(
   const int hh = (j8 / S) % HS;
   const int u = (j8 / (S * HS)) * 8 + xcd;
   if (u >= n_units) return;
-  const int Hq = HS * HG * 16;
-  const int h0 = hh * HG * 16;  // first head of this workgroup
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
-  const int r = lane & 15;
-  const int q4 = lane >> 4;
+  const int hg = NHG == 2 ? (w & 1) : 0;  // head group of 32 within the workgroup
+  const int st = NHG == 2 ? 0 : (w & 1);  // tile within a step
+  const int vh = w >> 1;                  // value half
+  const int h0 = 32 * NHG * hh;           // the workgroup's first head
+  const int head = h0 + 32 * hg + (lane & 31);  // the lane's column
+  const bool head_ok = head < Hq;
+  const int half = lane >> 5;
 
   const UnitG d = unit_g(units[u]);
   const int B = d.B;
   const int i_begin = sp * chunk;
-  const int i_end = min(k, i_begin + chunk);
-  const int n_rows = i_end - i_begin;
-  // uniform by construction; said so explicitly, or the step loop compiles
-  // as a divergent loop that drains every load at its back edge
-  const int n_steps = __builtin_amdgcn_readfirstlane((n_rows + 31) >> 5);
+  const int n_rows = __builtin_amdgcn_readfirstlane(min(k, i_begin + chunk) - i_begin);
+  const int n_tiles = __builtin_amdgcn_readfirstlane((n_rows + LAT_TILE - 1) / LAT_TILE);
+  const int n_steps = __builtin_amdgcn_readfirstlane((n_tiles + NST - 1) / NST);
   const HS_GLOBAL int32_t *slots = glb(slots_all) + (size_t)u * k;
-  const int64_t pool_len = FETCH ? *d.len : 0;
+  const uint32_t lds0 = (uint32_t)(uintptr_t)&s_buf[0];
+  auto step_buf = [&](int i) { return (i % NBUF) * STEP_BYTES; };
 
-  // the chunk's slot ids (and fetch sources) into LDS; the ids past the
-  // chunk repeat its last row
-  for (int i = tid; i < n_steps * 32; i += LAT_THREADS) {
-    const int j = i_begin + min(i, n_rows - 1);
-    s_ids[i] = slots[j];
-    if (FETCH) s_src[i] = d.fsrc[j];
-  }
-
-  // the wave's d-steps: 4 latent ones, and one rope step for waves 0 and 1.
-  // Waves 2 and 3 load rope slices too and multiply them by a zero query
-  // slice, so every wave runs the same loads and MFMAs (no branch makes the
-  // number of loads in flight differ between paths).
-  const int n_own = w < 2 ? 5 : 4;
-  bf16x8 qb[HG][5];
+  // ---- row copies. Wave w copies, of each 32-row tile, the latent parts of
+  // rows w, w + 4, ..., w + 28 (one instruction per row: the 64 lanes read
+  // the row's 1 KB, 16 bytes each, the swizzle only permuting within it)
+  // and the rope parts of rows 8w .. 8w + 7 (one instruction, 128 bytes from
+  // each of 8 rows): 9 global_load_lds per wave per tile. The queries of the
+  // workgroup's heads are copied the same way (a head's 1152 bytes are laid
+  // out as a row), into tiles of 32 heads.
+  int lofs[4];  // lane part of a latent copy's source, by (row >> 2) & 3
 #pragma unroll
-  for (int hg = 0; hg < HG; ++hg) {
-#pragma unroll
-    for (int jj = 0; jj < 5; ++jj) {
-      const int ds = jj < 4 ? 4 * w + jj : 16 + (w & 1);
-      qb[hg][jj] = *(const HS_GLOBAL bf16x8 *)(q_all + ((size_t)u * Hq + h0 + hg * 16 + r) *
-                                                           LAT_DK + 32 * ds + 8 * q4);
+  for (int m = 0; m < 4; ++m) lofs[m] = 16 * (lane ^ (4 * w + m));
+  const int rope_row = 8 * w + (lane >> 3);
+  const int rofs_src = LAT_DL * 2 + 16 * ((lane & 7) ^ rope_sw(rope_row));
+  // copy m (0..8) of a tile whose row r starts at base(r) (wave-uniform for
+  // the latent copies; per lane, row rope_row, for the rope copy)
+  auto copy_part = [&](int m, const HS_GLOBAL uint8_t *lat_src, const HS_GLOBAL uint8_t *rope_src,
+                       uint32_t tile_dst) {
+    if (m < 8)
+      lds_dma16(lat_src + lofs[m & 3], tile_dst + 1024 * (w + 4 * m));
+    else
+      lds_dma16(rope_src + rofs_src, tile_dst + LAT_ROPE_OFF + 1024 * w);
+  };
+  // the split's slot id at index i (past the split: its last one), checked
+  auto slot_at = [&](int i, bool &flag) {
+    int s = slots[i_begin + min(i, n_rows - 1)];
+    if ((unsigned)s >= (unsigned)B) {
+      flag = true;
+      s = 0;
     }
-    if (w >= 2) qb[hg][4] = __builtin_bit_cast(bf16x8, short8{0, 0, 0, 0, 0, 0, 0, 0});
-  }
+    return s;
+  };
+  // the slot ids a wave's copies of step i need: lanes 8t .. 8t + 7 hold
+  // those of tile t's rows w + 4 (lane & 7); rope[t] that of row rope_row
+  struct CopySrc {
+    int lat;
+    int rope[NST];
+  };
+  auto copy_ids = [&](int i) {
+    CopySrc c;
+    c.lat = s_ids[(NST * i + min((lane >> 3) & 1, NST - 1)) * LAT_TILE + w + 4 * (lane & 7)];
+#pragma unroll
+    for (int t = 0; t < NST; ++t) c.rope[t] = s_ids[(NST * i + t) * LAT_TILE + rope_row];
+    return c;
+  };
+  // copy m (0 .. CPS - 1) of step i
+  const HS_GLOBAL uint8_t *rows = d.rows;
+  auto copy_one = [&](const CopySrc &c, int i, int m) {
+    const int t = m / 9, mm = m % 9;
+    const int slot = __builtin_amdgcn_readlane(c.lat, 8 * t + min(mm, 7));
+    copy_part(mm, rows + (size_t)slot * LAT_REC, rows + (size_t)c.rope[t] * LAT_REC,
+              lds0 + step_buf(i) + t * LAT_TILE_BYTES);
+  };
 
-  floatx4 o[HG][8];
+  // ---- prologue: the queries (into the buffers of steps 1 and 2, or the
+  // second half-buffer) and step 0's rows (slot ids straight from global
+  // memory) are copied first; the split's slot ids load meanwhile
+  const uint32_t q_dst = lds0 + STEP_BYTES * (NHG == 2 ? 1 : 1);
+  {
+    const HS_GLOBAL uint8_t *qb0 = (const HS_GLOBAL uint8_t *)glb(q_all) + (size_t)u * Hq * LAT_REC;
+    const int hmax = Hq - 1;
 #pragma unroll
-  for (int hg = 0; hg < HG; ++hg)
+    for (int g = 0; g < NHG; ++g)
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) o[hg][jj] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // softmax share of wave w: head group hg_w, heads my_h + i (i < HG) of it
-  // for lane (r, q4); they sit in score tile lanes r + 16 (my_h / 4),
-  // elements my_h % 4 + i
-  const int hg_w = w * HG / 4;
-  const int my_h = (w % (4 / HG)) * 4 * HG + HG * q4;
-  const float *part_src =
-      (const float *)&s_part[hg_w][0][0][r + 16 * (my_h >> 2)] + (my_h & 3);
-  float m_run[HG], l_run[HG];
-#pragma unroll
-  for (int i = 0; i < HG; ++i) {
-    m_run[i] = NEG_INF;
-    l_run[i] = 0.f;
+      for (int m = 0; m < 9; ++m)
+        copy_part(m, qb0 + (size_t)min(h0 + 32 * g + w + 4 * m, hmax) * LAT_REC,
+                  qb0 + (size_t)min(h0 + 32 * g + rope_row, hmax) * LAT_REC,
+                  q_dst + g * LAT_TILE_BYTES);
   }
   bool bad = false;
-  uint32_t *vt = s_vt[w];
-  lds_barrier();  // s_ids complete
-
-  struct Rows {
-    v4u a[5], b[5];
-    RowRef ra, rb;
-  };
-  // Loads the wave's slices of a tile row: from its slot in HBM, or (fetch
-  // mode, just-resolved miss) from the host pool. An invalid slot sets the
-  // error and reads row 0 (its output becomes NaN).
-  auto load_row = [&](const RowRef &rf, v4u *dst) {
-    const bool valid = (unsigned)rf.slot < (unsigned)B;
-    const bool from_host = FETCH && valid && rf.src >= 0;
-    const bool host_ok = from_host && (int64_t)rf.src < pool_len;
-    if (!valid || from_host != host_ok) bad = true;
-    // base and row index selected without branches, then one 32 x 32 -> 64
-    // multiply-add
-    const HS_GLOBAL uint8_t *base =
-        host_ok ? (const HS_GLOBAL uint8_t *)d.pages[(uint32_t)rf.src >> d.page_shift] : d.rows;
-    const uint32_t row = host_ok ? ((uint32_t)rf.src & ((1u << d.page_shift) - 1u))
-                                 : (valid && !from_host ? (uint32_t)rf.slot : 0u);
-    const HS_GLOBAL uint8_t *p = base + (uint64_t)row * LAT_REC + 16 * q4;
+  if (n_steps > 0) {
+    CopySrc c0;
+    c0.lat = slot_at(min((lane >> 3) & 1, NST - 1) * LAT_TILE + w + 4 * (lane & 7), bad);
 #pragma unroll
-    for (int jj = 0; jj < 5; ++jj) {
-      const int ds = jj < 4 ? 4 * w + jj : 16 + (w & 1);
-      dst[jj] = *(const HS_GLOBAL v4u *)(p + 64 * ds);
-    }
-  };
-  // fetch mode: the wave's slices of a host-loaded row go to the row's slot
-  auto store_row = [&](const RowRef &rf, const v4u *src) {
-    if (!FETCH) return;
-    if ((unsigned)rf.slot >= (unsigned)B || rf.src < 0 || (int64_t)rf.src >= pool_len) return;
-    HS_GLOBAL uint8_t *p = d.rows + (size_t)rf.slot * LAT_REC + 16 * q4;
+    for (int t = 0; t < NST; ++t) c0.rope[t] = slot_at(t * LAT_TILE + rope_row, bad);
 #pragma unroll
-    for (int jj = 0; jj < 5; ++jj) {
-      const int ds = jj < 4 ? 4 * w + jj : 16 + w;
-      if (jj < n_own) *(HS_GLOBAL v4u *)(p + 64 * ds) = src[jj];
-    }
-  };
-  // loads of step st (clamped to the last step: the tail of the pipeline
-  // re-reads it, and nothing uses those values)
-  auto issue = [&](int st, Rows &R) {
-    const int i = 32 * min(st, n_steps - 1) + r;
-    R.ra.slot = s_ids[i];
-    R.rb.slot = s_ids[i + 16];
-    R.ra.src = FETCH ? s_src[i] : -1;
-    R.rb.src = FETCH ? s_src[i + 16] : -1;
-    load_row(R.ra, R.a);
-    load_row(R.rb, R.b);
-  };
-
-  // One 32-slot step on the rows in `cur`; first starts the loads of the
-  // step DEPTH ahead into `pre`.
-  auto step = [&](int st, Rows &cur, Rows &pre) {
-    issue(st + DEPTH, pre);
-    const int i0 = i_begin + 32 * st;
-
-    // 1. partial S^T tiles of this wave's d-slices, every head group
-    floatx4 acc[HG][2];
-#pragma unroll
-    for (int hg = 0; hg < HG; ++hg) {
-      acc[hg][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-      acc[hg][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int jj = 0; jj < 5; ++jj) {
-        acc[hg][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            qb[hg][jj], __builtin_bit_cast(bf16x8, cur.a[jj]), acc[hg][0], 0, 0, 0);
-        acc[hg][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            qb[hg][jj], __builtin_bit_cast(bf16x8, cur.b[jj]), acc[hg][1], 0, 0, 0);
-      }
-    }
-    store_row(cur.ra, cur.a);
-    store_row(cur.rb, cur.b);
-    // transposed value slice: value row 32jj + 8q4 + e, column r, packed
-    // (tile 0 low half, tile 1 high half) with one v_perm_b32 per word
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t a = cur.a[jj][e], c = cur.b[jj][e];
-        const int v = 32 * jj + 8 * q4 + 2 * e;
-        vt[vt_row(v) + r] = __builtin_amdgcn_perm(c, a, 0x05040100u);
-        vt[vt_row(v + 1) + r] = __builtin_amdgcn_perm(c, a, 0x07060302u);
-      }
-    }
-#pragma unroll
-    for (int hg = 0; hg < HG; ++hg) {
-      s_part[hg][w][0][lane] = acc[hg][0];
-      s_part[hg][w][1][lane] = acc[hg][1];
-    }
-    lds_barrier();
-
-    // 2. online softmax, spread over the four waves: wave w takes heads
-    // hb + HG q4 + i (i < HG) of head group hg_w; lane (r, q4) holds them
-    // for slots i0 + 16t + r. Scores are the four waves' partials summed in
-    // a fixed order; the maximum is a lazy reference.
-    {
-      float sc[2][HG];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int i = 0; i < HG; ++i) {
-          float x = 0.f;
-#pragma unroll
-          for (int ww = 0; ww < 4; ++ww) x += part_src[(ww * 2 + t) * 256 + i];
-          sc[t][i] = x;
-        }
-      }
-      if (i0 + 32 > i_end) {  // the last, partial step: slots past the chunk get -inf
-        const bool in0 = i0 + r < i_end, in1 = i0 + 16 + r < i_end;
-#pragma unroll
-        for (int i = 0; i < HG; ++i) {
-          sc[0][i] = in0 ? sc[0][i] : NEG_INF;
-          sc[1][i] = in1 ? sc[1][i] : NEG_INF;
-        }
-      }
-      bool moved = false;
-      float alpha[HG];
-      uint32_t pw[HG];
-#pragma unroll
-      for (int i = 0; i < HG; ++i) {
-        // raw scores; the reference maximum is kept in log2 units. It moves
-        // to the row maximum when some score exceeds it by more than the
-        // slack: a ballot finds out, and only then is the maximum over the
-        // row's 16 lanes taken (max(x) s = max(x s) for s > 0, so the
-        // decision is the one the row maximum would give)
-        const float m_old = m_run[i];
-        const float x = fmaxf(sc[0][i], sc[1][i]);
-        if (__any(x * scale_log2 > m_old + LAT_LAZY_LOG2)) {
-          const float mx = row_max16(x) * scale_log2;  // finite
-          if (mx > m_old + LAT_LAZY_LOG2) m_run[i] = mx;
-        }
-        moved |= m_run[i] != m_old;
-        alpha[i] = exp2_fast(m_old - m_run[i]);  // 1 when unchanged, 0 at the start
-        pw[i] = pack_bf16(exp2_fast(__builtin_fmaf(sc[0][i], scale_log2, -m_run[i])),
-                          exp2_fast(__builtin_fmaf(sc[1][i], scale_log2, -m_run[i])));
-        // the lane's share of l (alpha is the same on every lane of the
-        // row); the row sum is taken once, after the last step
-        l_run[i] = l_run[i] * alpha[i] +
-                   (__uint_as_float(pw[i] << 16) + __uint_as_float(pw[i] & 0xFFFF0000u));
-      }
-      // P^T operand of PV lane (head h, k-group r / 4): word r % 4 holds
-      // slots 4(r / 4) + r % 4 of tiles 0 and 1
-      uint32_t *pdst = (uint32_t *)&s_p[hg_w][0];
-#pragma unroll
-      for (int i = 0; i < HG; ++i) pdst[((r >> 2) * 16 + my_h + i) * 4 + (r & 3)] = pw[i];
-      // alpha of every head every step (1 where unchanged): a group rescales
-      // all its heads when any of its waves moved
-      if (r == 0) {
-#pragma unroll
-        for (int i = 0; i < HG; ++i) s_alpha[hg_w][my_h + i] = alpha[i];
-      }
-      const bool any_moved = __any(moved);
-      if (lane == 0) s_rescale[w] = any_moved ? 1 : 0;
-    }
-    lds_barrier();
-
-    // 3. PV: each value tile is read once and used by every head group; all
-    // eight tiles are read before the MFMAs so the reads overlap
-    v4u vtile[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) vtile[jj] = *(const v4u *)(vt + vt_row(16 * jj + r) + 4 * q4);
-    bf16x8 pB[HG];
-#pragma unroll
-    for (int hg = 0; hg < HG; ++hg) {
-      pB[hg] = __builtin_bit_cast(bf16x8, s_p[hg][lane]);
-      int moved = 0;  // any wave of the group moved its reference maximum
-#pragma unroll
-      for (int ww = hg * (4 / HG); ww < (hg + 1) * (4 / HG); ++ww) moved |= s_rescale[ww];
-      if (__builtin_amdgcn_readfirstlane(moved)) {
-        const float a = s_alpha[hg][r];
-#pragma unroll
-        for (int jj = 0; jj < 8; ++jj) o[hg][jj] *= a;
-      }
-    }
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-#pragma unroll
-      for (int hg = 0; hg < HG; ++hg)
-        o[hg][jj] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vtile[jj]),
-                                                             pB[hg], o[hg][jj], 0, 0, 0);
-    }
-  };
-
-  // The loop leaves only at its latch, the remaining steps after it: an
-  // exit between the register rotations gave the compiler a path from the
-  // middle of the loop back to its header on which the loads of the next
-  // step were still in flight, and it waited for them there, at the top of
-  // every iteration (each second step then waited the whole load latency).
-  int st = 0;
-  if (DEPTH == 2) {
-    Rows R0, R1, R2;
-    issue(0, R0);
-    issue(1, R1);
-    for (; st + 3 <= n_steps; st += 3) {
-      step(st, R0, R2);
-      step(st + 1, R1, R0);
-      step(st + 2, R2, R1);
-    }
-    if (st < n_steps) step(st++, R0, R2);
-    if (st < n_steps) step(st, R1, R0);
-  } else {
-    Rows R0, R1;
-    issue(0, R0);
-    for (; st + 2 <= n_steps; st += 2) {
-      step(st, R0, R1);
-      step(st + 1, R1, R0);
-    }
-    if (st < n_steps) step(st, R0, R1);
+    for (int m = 0; m < CPS; ++m) copy_one(c0, 0, m);
   }
-
-#pragma unroll
-  for (int i = 0; i < HG; ++i) l_run[i] = row_sum16(l_run[i]);
-  const int any_bad = __syncthreads_or(bad ? 1 : 0);
-  if (any_bad && tid == 0) set_error(d.ctl, HS_ERR_SLOT);
-  // every wave needs l of every head of the workgroup
-  if (r == 0) {
-#pragma unroll
-    for (int i = 0; i < HG; ++i) s_alpha[hg_w][my_h + i] = l_run[i];
-  }
+  // the split's slot ids into LDS, whole steps; entries past the split
+  // repeat its last one (those rows are loaded and masked). An invalid slot
+  // is flagged and replaced by slot 0 (the unit's output becomes NaN).
+  if (tid == 0) s_bad = 0;
+  lds_barrier();
+  for (int i = tid; i < n_steps * NST * LAT_TILE; i += LAT_THREADS) s_ids[i] = slot_at(i, bad);
+  if (bad) s_bad = 1;
+  wait_vmcnt<0>();  // the queries, the ids and step 0's rows have arrived
   lds_barrier();
 
-  // lane holds O^T[v = 128w + 16jj + 4q4 + i][head 16hg + r]
+  // K read of d-step ds from a tile: lane (row r = lane & 31, chunk 2 ds +
+  // half). Latent d-steps: tile + 256 (ds >> 3) + kofs[ds & 7]; rope d-steps
+  // 32 + j: tile + rofs[j]
+  const int kr_row = lane & 31;
+  int kofs[8], rofs[4];
 #pragma unroll
-  for (int hg = 0; hg < HG; ++hg) {
-    const size_t row = (size_t)u * Hq + h0 + hg * 16 + r;
-    if (S == 1) {
-      const float inv = 1.f / s_alpha[hg][r];
+  for (int j = 0; j < 8; ++j) kofs[j] = 1024 * kr_row + 16 * ((2 * j + half) ^ lat_sw(kr_row));
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const floatx4 v = o[hg][jj] * inv;
-        const v4u bits = {nan_bits_if(any_bad, v[0]), nan_bits_if(any_bad, v[1]),
-                          nan_bits_if(any_bad, v[2]), nan_bits_if(any_bad, v[3])};
-        *(HS_GLOBAL v4u *)(out + row * LAT_DL + 128 * w + 16 * jj + 4 * q4) = bits;
+  for (int j = 0; j < 4; ++j)
+    rofs[j] = LAT_ROPE_OFF + 128 * kr_row + 16 * ((2 * j + half) ^ rope_sw(kr_row));
+  auto kread = [&](const HS_LDS uint8_t *tl, int ds) {
+    const int off = ds < 32 ? 256 * (ds >> 3) + kofs[ds & 7] : rofs[ds - 32];
+    return *(const HS_LDS bf16x8 *)(tl + off);
+  };
+
+  // Q^T of the wave's 32 heads (the B operand: lane (head, d 16 ds + 8 half
+  // .. + 7)), read from the query tile like a K operand; padding heads
+  // (Hq = 16) are zero
+  bf16x8 qb[LAT_BLOCKS];
+  {
+    const HS_LDS uint8_t *qt = (const HS_LDS uint8_t *)&s_buf[q_dst - lds0 + hg * LAT_TILE_BYTES];
+    const uint32_t keep = head_ok ? ~0u : 0u;
+#pragma unroll
+    for (int ds = 0; ds < LAT_BLOCKS; ++ds)
+      qb[ds] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(v4u, kread(qt, ds)) & keep);
+  }
+  lds_barrier();  // the query tiles' buffers are free
+  if (DEPTH > 1 && n_steps > 1) {
+    const CopySrc c1 = copy_ids(1);
+#pragma unroll
+    for (int m = 0; m < CPS; ++m) copy_one(c1, 1, m);
+  }
+
+  // transpose read q (0/1) of value tile vt, k-block kb: 16-lane group g
+  // reads rows 16 kb + 8 q + 4 (g >> 1) + 0..3, values 32 vt + 16 (g & 1) +
+  // 0..15 (lane j: row + j / 4, values 4 (j % 4) .. + 3); lane j of the group
+  // receives value 32 vt + 16 (g & 1) + j of those 4 rows. Address: tile +
+  // 16384 kb + 256 (vt >> 2) + tr_off[q][vt & 3].
+  const int g = lane >> 4, jj = lane & 15;
+  int tr_off[2][4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int rb = 8 * q + 4 * (g >> 1) + (jj >> 2);  // row within its k-block
+    const int a = 2 * (g & 1) + ((jj & 3) >> 1);     // chunk within the value tile
+#pragma unroll
+    for (int v3 = 0; v3 < 4; ++v3) {
+      const int pos = 4 * ((v3 ^ (rb & 3)) & 3) + (a ^ ((rb >> 2) & 3));  // = chunk ^ lat_sw
+      tr_off[q][v3] = 1024 * rb + 16 * pos + 8 * (jj & 1);
+    }
+  }
+  // V^T operand m (value tile m / 2 of the wave's half, k-block m % 2)
+  auto vread = [&](const HS_LDS uint8_t *tl, int m) {
+    const int vt = vh * NVT + (m >> 1);
+    const HS_LDS uint8_t *vb = tl + 16384 * (m & 1) + 256 * (vt >> 2);
+    const short4v lo =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((HS_LDS short4v *)(vb + tr_off[0][vt & 3]));
+    const short4v hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((HS_LDS short4v *)(vb + tr_off[1][vt & 3]));
+    return __builtin_bit_cast(bf16x8,
+                              short8v{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+  };
+
+  floatx16 o[NVT];
+#pragma unroll
+  for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[vt][e] = 0.f;
+  float m_run = NEG_INF;  // reference maximum of the lane's head (log2 units)
+  float l_run = 0.f;      // this lane's share of the head's sum
+
+  // LDS operand reads run a few MFMAs ahead of their use (register rings of
+  // LAT_KPF K operands and LAT_VPF V^T operands), so the MFMA pipe does not
+  // wait out an LDS round trip per instruction
+  bf16x8 vring[LAT_VPF];
+  // S^T of the wave's tile: lane (head column, slots 8 (e / 4) + 4 half + e %
+  // 4 of the tile), slots past the split at -inf. The copies of step ci go
+  // out between the MFMAs (one per 36 / CPS d-steps), where their issue cost
+  // overlaps the matrix work; the first V^T operands are read after the last
+  // K operand, so they arrive during the softmax.
+  auto scores = [&](const HS_LDS uint8_t *tl, int tile, bool copy, const CopySrc &cs, int ci) {
+    bf16x8 kring[LAT_KPF];
+#pragma unroll
+    for (int j = 0; j < LAT_KPF; ++j) kring[j] = kread(tl, j);
+    floatx16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+    for (int ds = 0; ds < LAT_BLOCKS; ++ds) {
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kring[ds % LAT_KPF], qb[ds], acc, 0, 0, 0);
+      if (ds + LAT_KPF < LAT_BLOCKS)
+        kring[ds % LAT_KPF] = kread(tl, ds + LAT_KPF);
+      else if (ds + LAT_KPF - LAT_BLOCKS < LAT_VPF)
+        vring[ds + LAT_KPF - LAT_BLOCKS] = vread(tl, ds + LAT_KPF - LAT_BLOCKS);
+      constexpr int every = LAT_BLOCKS / CPS;
+      if (copy && ds % every == 0) copy_one(cs, ci, ds / every);
+      // keep this order: the scheduler would otherwise pull the reads next
+      // to their MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const int valid = __builtin_amdgcn_readfirstlane(n_rows - LAT_TILE * tile);  // in the split
+    if (valid < LAT_TILE) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        acc[e] = 8 * (e >> 2) + 4 * half + (e & 3) < valid ? acc[e] : NEG_INF;
+    }
+    return acc;
+  };
+  // P = 2^(s scale_log2 - m_run) rounded to bf16, the lane's share of l, and
+  // O^T += V^T P^T over the wave's value tiles
+  auto accumulate = [&](const HS_LDS uint8_t *tl, const floatx16 &sc) {
+    // a wave that has seen only masked slots keeps m_run = -inf; its P is 0
+    const float m_ref = fmaxf(m_run, -__FLT_MAX__);
+    uint32_t pw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      pw[e] = pack_bf16(exp2_fast(__builtin_fmaf(sc[2 * e], scale_log2, -m_ref)),
+                        exp2_fast(__builtin_fmaf(sc[2 * e + 1], scale_log2, -m_ref)));
+      l_run += __uint_as_float(pw[e] << 16) + __uint_as_float(pw[e] & 0xFFFF0000u);
+    }
+    // P^T of k-block kb: the lane's scores 8 kb .. 8 kb + 7 (slots 16 kb +
+    // 8 (e / 4) + 4 half + e % 4)
+    const bf16x8 pB0 = __builtin_bit_cast(bf16x8, v4u{pw[0], pw[1], pw[2], pw[3]});
+    const bf16x8 pB1 = __builtin_bit_cast(bf16x8, v4u{pw[4], pw[5], pw[6], pw[7]});
+#pragma unroll
+    for (int m = 0; m < 2 * NVT; ++m) {
+      o[m >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vring[m % LAT_VPF], (m & 1) ? pB1 : pB0,
+                                                          o[m >> 1], 0, 0, 0);
+      if (m + LAT_VPF < 2 * NVT) vring[m % LAT_VPF] = vread(tl, m + LAT_VPF);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // The accumulators are touched only by MFMAs and, on the rare moves of the
+  // reference maximum, by scale_acc, so they stay in their registers across
+  // the loop. Every wave passes the same barriers; the step index and every
+  // branch are wave-uniform (readfirstlane says so; otherwise the loop
+  // compiles to a divergent one under exec masks).
+  for (int i = 0; i < n_steps; ++i) {
+    // this wave's copies of step i have landed (those of the steps after it
+    // may still be in flight), then every wave's have, and every wave is done
+    // with step i - 1, whose buffer step i + DEPTH reuses
+    if (DEPTH > 1 && i + 1 < n_steps)
+      wait_vmcnt<(DEPTH - 1) * CPS>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    const int ci = i + DEPTH;  // the step whose copies go out with QK^T
+    const bool copy = ci < n_steps;
+    const CopySrc cs = copy_ids(copy ? ci : i);
+    // a tile past the split (an odd last tile of a two-tile step) has every
+    // score masked and adds zeros (a skip would give the accumulators a
+    // second path through the loop, which the compiler serves with copies)
+    const int tile = __builtin_amdgcn_readfirstlane(NST * i + st);
+    const HS_LDS uint8_t *tl =
+        (const HS_LDS uint8_t *)&s_buf[step_buf(i) + st * LAT_TILE_BYTES];
+    const floatx16 sc = scores(tl, tile, copy, cs, ci);
+    float x = sc[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) x = fmaxf(x, sc[e]);
+    x *= scale_log2;
+    if (__builtin_amdgcn_readfirstlane(__any(x > m_run + LAT_LAZY_LOG2))) {
+      // max(x) s = max(x s) for s > 0: the decision is the head maximum's
+      const float mx = fmaxf(x, __shfl_xor(x, 32, 64));
+      const float m_new = mx > m_run + LAT_LAZY_LOG2 ? mx : m_run;
+      if (__builtin_amdgcn_readfirstlane(__any(m_run != NEG_INF && m_new != m_run))) {
+        const float alpha = exp2_fast(m_run - m_new);  // 1 where unchanged
+        l_run *= alpha;
+        scale_acc<NVT>(o, alpha);
       }
+      m_run = m_new;
+    }
+    accumulate(tl, sc);
+  }
+
+  // ---- outputs, staged through LDS so that every store writes 1 KB of a
+  // row: each wave puts its accumulators (32 heads x 256 values) and its
+  // heads' (m, l) into its own 32 KB region (every copy has landed and been
+  // read, so the step buffers are free), then each wave stores row halves
+  // (head, value half) from LDS. With two tiles per step (NHG = 1) the two
+  // streams' regions of a value half merge exactly on the way out.
+  // Region layout: head row r at r * 1024, its 16-byte chunk q at position
+  // q ^ (r & 15) (the writes, one head per lane, and the reads, one row per
+  // instruction, are then free of bank conflicts).
+  l_run += __shfl_xor(l_run, 32, 64);
+  wait_vmcnt<0>();
+  __syncthreads();
+  const bool any_bad = s_bad != 0;
+  if (any_bad && tid == 0) set_error(d.ctl, HS_ERR_SLOT);
+  {
+    uint8_t *reg = &s_buf[w * 32768];
+    const int r = lane & 31;
+#pragma unroll
+    for (int vt = 0; vt < NVT; ++vt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int q = 8 * vt + 2 * c + half;
+        *(floatx4 *)(reg + 1024 * r + 16 * (q ^ (r & 15))) =
+            floatx4{o[vt][4 * c], o[vt][4 * c + 1], o[vt][4 * c + 2], o[vt][4 * c + 3]};
+      }
+    if (lane < 32) s_ml[w][lane] = floatx2{m_run, l_run};
+  }
+  __syncthreads();
+  // (m, l) of every head (for the split-k combine, or 1 / l for the output):
+  // lanes 0..31 of waves 0 (and 1 with NHG = 2) take heads h0 + 32 w + lane
+  if (w < NHG && lane < 32 && h0 + 32 * w + lane < Hq) {
+    const floatx2 a = s_ml[w][lane];
+    float M = a[0], L = a[1];
+    if (NHG == 1) {
+      const floatx2 c = s_ml[1][lane];
+      M = fmaxf(a[0], c[0]);
+      L = (a[0] == NEG_INF ? 0.f : a[1] * exp2_fast(a[0] - M)) +
+          (c[0] == NEG_INF ? 0.f : c[1] * exp2_fast(c[0] - M));
+    }
+    const size_t row = (size_t)u * Hq + h0 + 32 * w + lane;
+    if (S > 1) {
+      ((HS_GLOBAL uint32_t *)ws_ml)[(row * S + sp) * 2] = nan_bits_if(any_bad, M);
+      ws_ml[(row * S + sp) * 2 + 1] = L;
     } else {
-      HS_GLOBAL float *dst = glb(ws_o) + (row * S + sp) * LAT_DL + 128 * w + 4 * q4;
+      s_ml[w][lane][1] = L;  // the output's divisor (only its own lane reads it back)
+    }
+  }
+  __syncthreads();
+  // wave w stores 32 (NHG = 2: its region) or 16 (NHG = 1) row halves of
+  // 1 KB, all read from LDS before any is stored
+  constexpr int PIECES = NHG == 2 ? 32 : 16;
+  const int pvh = w >> 1;
+  const int ra = NHG == 2 ? w : 2 * pvh;  // (the first stream's) region
+  auto piece = [&](int pc) {
+    const int r = NHG == 2 ? pc : 16 * (w & 1) + pc;
+    floatx4 v = *(const floatx4 *)&s_buf[ra * 32768 + 1024 * r + 16 * (lane ^ (r & 15))];
+    if (NHG == 1) {
+      const floatx2 m0 = s_ml[ra][r], m1 = s_ml[ra + 1][r];
+      const floatx4 v1 =
+          *(const floatx4 *)&s_buf[(ra + 1) * 32768 + 1024 * r + 16 * (lane ^ (r & 15))];
+      const float M = fmaxf(m0[0], m1[0]);
+      // a stream without tiles has m = -inf: its factor is 0
+      v = v * (m0[0] == NEG_INF ? 0.f : exp2_fast(m0[0] - M)) +
+          v1 * (m1[0] == NEG_INF ? 0.f : exp2_fast(m1[0] - M));
+    }
+    return v;
+  };
+  auto piece_row = [&](int pc) {
+    const int r = NHG == 2 ? pc : 16 * (w & 1) + pc;
+    return h0 + (NHG == 2 ? 32 * (w & 1) : 0) + r;  // the head
+  };
+  const int v0 = 256 * pvh + 4 * lane;
+  // in batches of 16 pieces: every LDS read of a batch, then its stores (the
+  // scheduler would otherwise pair each store with its read and wait out an
+  // LDS round trip per store)
+  constexpr int BATCH = 16;
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
+  for (int p0 = 0; p0 < PIECES; p0 += BATCH) {
+    floatx4 vb[BATCH];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) vb[j] = piece(p0 + j);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int ph = piece_row(p0 + j);
+      if (NHG == 1 && ph >= Hq) continue;
+      if (S == 1) {
+        const float L = s_ml[NHG == 2 ? (w & 1) : 0][ph - h0 - (NHG == 2 ? 32 * (w & 1) : 0)][1];
+        const floatx4 rr = vb[j] * (1.f / L);
+        const v4u bits = {nan_bits_if(any_bad, rr[0]), nan_bits_if(any_bad, rr[1]),
+                          nan_bits_if(any_bad, rr[2]), nan_bits_if(any_bad, rr[3])};
+        *(HS_GLOBAL v4u *)(out + ((size_t)u * Hq + ph) * LAT_DL + v0) = bits;
+      } else {
+        HS_GLOBAL floatx4 *dst =
+            (HS_GLOBAL floatx4 *)(glb(ws_o) + (((size_t)u * Hq + ph) * S + sp) * LAT_DL + v0);
         if (STREAM)
-          __builtin_nontemporal_store(o[hg][jj], (HS_GLOBAL floatx4 *)(dst + 16 * jj));
+          __builtin_nontemporal_store(vb[j], dst);
         else
-          *(HS_GLOBAL floatx4 *)(dst + 16 * jj) = o[hg][jj];
+          *dst = vb[j];
       }
     }
   }
-  if (S > 1 && r == 0) {
-#pragma unroll
-    for (int i = 0; i < HG; ++i) {
-      const size_t row = (size_t)u * Hq + h0 + hg_w * 16 + my_h + i;
-      ((HS_GLOBAL uint32_t *)ws_ml)[(row * S + sp) * 2] = nan_bits_if(any_bad, m_run[i]);
-      ws_ml[(row * S + sp) * 2 + 1] = l_run[i];
-    }
-  }
 }
 
-template <int HG, int DEPTH, bool FETCH, bool STREAM>
+template <int NHG, bool STREAM>
 hipError_t launch_latent_t(const AttnLatentArgs &a, hipStream_t stream) {
-  const int HS = a.Hq / (HG * 16);
-  if (a.chunk > LAT_MAX_CHUNK || a.chunk % 32) return hipErrorInvalidValue;
+  const int HS = (a.Hq + 32 * NHG - 1) / (32 * NHG);
+  if (a.chunk > LAT_MAX_CHUNK || a.chunk % (2 * LAT_TILE)) return hipErrorInvalidValue;
   const int grid = ((a.n_units + 7) / 8) * 8 * a.splits * HS;
-  return launch_k(HS_TRACE_ATTN, hs_k_attn_latent<HG, DEPTH, FETCH, STREAM>, dim3(grid),
-                  dim3(LAT_THREADS), 0, stream, a.units, a.q, a.slots, a.n_units, a.k, a.scale_log2,
-                  a.splits, HS, a.chunk, a.ws_o, a.ws_ml, a.out);
-}
-
-template <bool FETCH, bool STREAM>
-hipError_t launch_latent_f(const AttnLatentArgs &a, hipStream_t stream) {
-  switch (a.hpw / 16) {
-    case 1: return launch_latent_t<1, 1, FETCH, STREAM>(a, stream);
-    case 2: return launch_latent_t<2, 2, FETCH, STREAM>(a, stream);
-    case 4: return launch_latent_t<4, 1, FETCH, STREAM>(a, stream);
-    default: return hipErrorInvalidValue;
-  }
+  return launch_k(HS_TRACE_ATTN, hs_k_attn_latent<NHG, STREAM>, dim3(grid), dim3(LAT_THREADS), 0,
+                  stream, a.units, a.q, a.slots, a.n_units, a.k, a.Hq, a.scale_log2, a.splits, HS,
+                  a.chunk, a.ws_o, a.ws_ml, a.out);
 }
 
 }  // namespace
@@ -507,13 +591,11 @@ hipError_t launch_latent_f(const AttnLatentArgs &a, hipStream_t stream) {
 hipError_t launch_attn_latent(const AttnLatentArgs &a, hipStream_t stream) {
   const bool stream_partials = a.splits > 1 && (size_t)a.n_units * a.Hq * a.splits * LAT_DL *
                                                       sizeof(float) <= LAT_STREAM_PARTIAL_BYTES;
-  hipError_t e;
-  if (a.fetch)
-    e = stream_partials ? launch_latent_f<true, true>(a, stream)
-                        : launch_latent_f<true, false>(a, stream);
-  else
-    e = stream_partials ? launch_latent_f<false, true>(a, stream)
-                        : launch_latent_f<false, false>(a, stream);
+  const hipError_t e =
+      a.hpw == 64 ? (stream_partials ? launch_latent_t<2, true>(a, stream)
+                                   : launch_latent_t<2, false>(a, stream))
+                  : (stream_partials ? launch_latent_t<1, true>(a, stream)
+                                   : launch_latent_t<1, false>(a, stream));
   if (e != hipSuccess || a.splits == 1) return e;
   return launch_combine(a.ws_o, a.ws_ml, a.n_units * a.Hq, a.splits, LAT_DL, a.out, stream);
 }

@@ -198,11 +198,19 @@ struct StageRegion {
   uint64_t n16;
   uint64_t stride16;
 };
+// At most this many regions per stage; the table travels in the kernel's
+// arguments (no device reads before the copy).
+constexpr int STAGE_MAX_REGIONS = 8;
+struct StageTable {
+  StageRegion r[STAGE_MAX_REGIONS];
+  uint64_t end16[STAGE_MAX_REGIONS];  // running sum of n16 up to and including region i
+  int n;
+};
 // Stage control words (device memory): [0] the step counter, [1] the
 // arrivals of the running launch (0 between launches).
 constexpr int STAGE_CTL_WORDS = 64;
-// Copies every region for step ctl[0] and advances ctl[0] by one.
-hipError_t launch_stage(const StageRegion *d_regions, int n, uint64_t total16, uint32_t *d_ctl,
+// Copies entry ctl[0] % ring of every region, then advances ctl[0].
+hipError_t launch_stage(const StageTable &table, uint64_t total16, uint32_t *d_ctl,
                         uint32_t ring, hipStream_t stream);
 // ctl[0] = step, ctl[1] = 0.
 hipError_t launch_stage_set(uint32_t *d_ctl, uint32_t step, hipStream_t stream);
@@ -226,9 +234,8 @@ struct AttnLatentArgs {
   const UnitDesc *units;
   const uint16_t *q;
   const int32_t *slots;
-  int n_units, k, Hq, splits, chunk;
-  int hpw;    // query heads per workgroup (16, 32 or 64; divides Hq)
-  int fetch;  // fused resolve: read just-resolved misses from the host pool
+  int n_units, k, Hq, splits, chunk;  // chunk: a multiple of 64, at most LAT_MAX_CHUNK
+  int hpw;                            // query heads per workgroup: 32 or 64
   float scale_log2;
   float *ws_o, *ws_ml, *out;
 };

@@ -149,8 +149,8 @@ hs_status hs_set_tuning(const hs_tuning *t) {
   if (t->attn_splits < 0 || t->attn_splits > 4096)
     return fail(HS_E_INVAL, "tuning value out of range");
   const int hpw = t->latent_heads_per_wg;
-  if (hpw != 0 && hpw != 16 && hpw != 32 && hpw != 64)
-    return fail(HS_E_INVAL, "latent_heads_per_wg must be 0, 16, 32 or 64");
+  if (hpw != 0 && hpw != 32 && hpw != 64)
+    return fail(HS_E_INVAL, "latent_heads_per_wg must be 0, 32 or 64");
   if (t->prefetch_workgroups < 0 || t->prefetch_workgroups > 65536)
     return fail(HS_E_INVAL, "prefetch_workgroups outside [0, 65536]");
   const int pb = t->prefetch_batch;
@@ -981,31 +981,22 @@ static hs_status plan_attn(hs_batch_t b, int32_t Hq, int32_t k, AttnPlan *pl) {
       return fail(HS_E_INVAL, "latent attention needs bf16, 512 + 64");
     if (Hq != 16 && Hq != 32 && Hq != 64)
       return fail(HS_E_INVAL, "latent attention supports 16, 32 or 64 query heads");
-    // A workgroup covers hpw heads of a (unit, split). Every split writes a
-    // full fp32 (m, l, acc[512]) partial per head, about 2 KB, as much as
-    // two 1152-byte rows: splits shorter than 256 rows write more partial
-    // bytes than they read. So splits stay at 256 rows or more, and the
-    // heads are split instead when that leaves the device short of
-    // workgroups: the largest hpw of 64, 32, 16 (dividing Hq) whose grid
-    // reaches 256 workgroups, else 16 (the rows are then read once per head
-    // group, mostly from L2).
+    // A workgroup covers hpw = 32 or 64 heads (16 pad to 32) of a (unit,
+    // split) and holds a compute unit. With 64 each row is copied once per
+    // (unit, split); with 32 the two head groups copy it apart (the second
+    // time mostly from L2), but a workgroup's epilogue writes half as many
+    // partial bytes and the unit's work spreads over twice the workgroups,
+    // which measured faster on both MLA workloads (batch 8: 21.5 against
+    // 25.7 us with the combine; batch 64: 48.3 against 50.0), so 32 is the
+    // default. Every split writes a 2 KB fp32 partial per head, which the
+    // split-k combine reads back, so splits keep at least 256 rows and are
+    // added until the grid reaches 256 workgroups (batch 8: 32 heads x 8
+    // splits, 128 workgroups; batch 64: 32 x 2, 256).
     const int n8 = (b->n + 7) / 8 * 8;
-    const int split_cap = std::max(1, k / 256);
     int hpw = g_tuning.latent_heads_per_wg;
-    if (hpw <= 0) {
-      hpw = 16;
-      for (int h : {64, 32}) {
-        if (h > Hq || Hq % h) continue;
-        const int bw = n8 * (Hq / h);
-        if (bw * std::min(split_cap, (256 + bw - 1) / bw) >= 256) {
-          hpw = h;
-          break;
-        }
-      }
-    }
-    if (hpw > Hq || Hq % hpw) hpw = Hq;
+    if (hpw <= 0 || Hq <= 32) hpw = 32;
     pl->hpw = hpw;
-    base = n8 * (Hq / hpw);
+    base = n8 * ((Hq + hpw - 1) / hpw);
     min_chunk = 256;
     target = 256;
     pl->dv = p->Dl;
@@ -1017,7 +1008,7 @@ static hs_status plan_attn(hs_batch_t b, int32_t Hq, int32_t k, AttnPlan *pl) {
   if (p->kind == HS_KV_LATENT)
     splits = std::max(splits, (k + hs::LAT_MAX_CHUNK - 1) / hs::LAT_MAX_CHUNK);
   int chunk = (k + splits - 1) / splits;
-  if (p->kind == HS_KV_LATENT) chunk = (chunk + 31) / 32 * 32;
+  if (p->kind == HS_KV_LATENT) chunk = (chunk + 63) / 64 * 64;  // whole pairs of 32-row tiles
   splits = (k + chunk - 1) / chunk;  // every split has at least one slot
   pl->splits = splits;
   pl->chunk = chunk;
@@ -1097,7 +1088,6 @@ static hs_status enqueue_attn(hs_batch_t b, const void *d_q, int32_t Hq, const i
     a.splits = pl.splits;
     a.chunk = pl.chunk;
     a.hpw = pl.hpw;
-    a.fetch = fetch;
     a.scale_log2 = scale_log2;
     a.ws_o = ws_o;
     a.ws_ml = ws_ml;
@@ -1185,6 +1175,13 @@ hs_status hs_resolve_attn(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_
   AttnPlan pl;
   s = check_attn(b, d_q, Hq, d_slots, k, sm_scale, d_out, d_ws, ws_bytes, &pl);
   if (s) return s;
+  if (b->pool->kind == HS_KV_LATENT) {
+    // latent records: the resolve moves the misses (its first host reads
+    // overlap the victim selection) and attention reads resident rows only
+    s = hs_resolve(b, d_topk, k, d_slots, d_miss, stream);
+    if (s) return s;
+    return enqueue_attn(b, d_q, Hq, d_slots, k, sm_scale, d_out, d_ws, pl, 0, stream);
+  }
   // resolve without the gather: the attention kernels fetch the misses
   hipError_t e = hs::launch_resolve(b->d_units, b->n, b->max_B, d_topk, k, d_slots, d_miss,
                                     hs::FETCH_NONE, 0, (int)b->pool->rec, S(stream));
@@ -1208,16 +1205,16 @@ hs_status hs_prefetch(hs_batch_t b, void *stream) {
 // ------------------------------------------------------------------- stage
 
 struct hs_stage_s {
-  int32_t n = 0;
   uint32_t ring = 1;
   uint64_t total16 = 0;
-  hs::StageRegion *d_regions = nullptr;
+  hs::StageTable table{};
   uint32_t *d_ctl = nullptr;
 };
 
 hs_status hs_stage_create(const hs_stage_region *regions, int32_t n, int32_t ring,
                           hs_stage_t *out) {
-  if (!regions || !out || n < 1 || ring < 1) return fail(HS_E_INVAL, "need n >= 1 regions, ring >= 1");
+  if (!regions || !out || n < 1 || n > hs::STAGE_MAX_REGIONS || ring < 1)
+    return fail(HS_E_INVAL, "need 1 to %d regions and ring >= 1", hs::STAGE_MAX_REGIONS);
   *out = nullptr;
   std::vector<hs::StageRegion> h(n);
   uint64_t total = 0;
@@ -1243,17 +1240,19 @@ hs_status hs_stage_create(const hs_stage_region *regions, int32_t n, int32_t rin
   }
   hs_stage_s *st = new (std::nothrow) hs_stage_s;
   if (!st) return fail(HS_E_NOMEM, "stage handle");
-  st->n = n;
   st->ring = (uint32_t)ring;
   st->total16 = total;
-  hipError_t e = hipMalloc(&st->d_regions, sizeof(hs::StageRegion) * n);
-  if (e == hipSuccess)
-    e = hipMemcpy(st->d_regions, h.data(), sizeof(hs::StageRegion) * n, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMalloc(&st->d_ctl, sizeof(uint32_t) * hs::STAGE_CTL_WORDS);
+  st->table.n = n;
+  uint64_t run = 0;
+  for (int i = 0; i < n; ++i) {
+    st->table.r[i] = h[i];
+    run += h[i].n16;
+    st->table.end16[i] = run;
+  }
+  hipError_t e = hipMalloc(&st->d_ctl, sizeof(uint32_t) * hs::STAGE_CTL_WORDS);
   if (e == hipSuccess) e = hs::launch_stage_set(st->d_ctl, 0u, nullptr);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e != hipSuccess) {
-    if (st->d_regions) (void)hipFree(st->d_regions);
     if (st->d_ctl) (void)hipFree(st->d_ctl);
     delete st;
     return hip_fail(e, "stage create");
@@ -1264,7 +1263,6 @@ hs_status hs_stage_create(const hs_stage_region *regions, int32_t n, int32_t rin
 
 hs_status hs_stage_destroy(hs_stage_t st) {
   if (!st) return fail(HS_E_INVAL, "null stage");
-  (void)hipFree(st->d_regions);
   (void)hipFree(st->d_ctl);
   delete st;
   return HS_OK;
@@ -1272,7 +1270,7 @@ hs_status hs_stage_destroy(hs_stage_t st) {
 
 hs_status hs_stage_run(hs_stage_t st, void *stream) {
   if (!st) return fail(HS_E_INVAL, "null stage");
-  hipError_t e = hs::launch_stage(st->d_regions, st->n, st->total16, st->d_ctl, st->ring, S(stream));
+  hipError_t e = hs::launch_stage(st->table, st->total16, st->d_ctl, st->ring, S(stream));
   if (e != hipSuccess) return hip_fail(e, "stage launch");
   return HS_OK;
 }

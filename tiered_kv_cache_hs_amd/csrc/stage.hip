@@ -26,14 +26,15 @@ constexpr int STAGE_THREADS = 256;
 // The regions' chunks form one index space (region 0's first, then region
 // 1's, ...); each thread copies chunk c = its global index, then c + the
 // grid's thread count, and so on (one chunk per thread at the usual sizes).
-// Thread 0 reads the step and hands it to the workgroup through LDS; once
-// the workgroup has it, thread 0 arrives (relaxed: only the step's read has
-// to precede the arrival, and its value was already stored to LDS), and the
-// last workgroup to arrive - every other one has its step by then - writes
-// step + 1. The arrival's round trip overlaps the copy, and nothing waits
-// for the copy's stores inside the kernel.
-__global__ __launch_bounds__(STAGE_THREADS) void hs_k_stage(const StageRegion *__restrict__ regs,
-                                                            int n, uint64_t total16, uint32_t *ctl,
+// The region table is a kernel argument, so the only device read before the
+// copy is the step counter. Thread 0 reads it and hands it to the workgroup
+// through LDS; once the workgroup has it, thread 0 arrives (relaxed: only
+// the step's read has to precede the arrival, and its value was already
+// stored to LDS), and the last workgroup to arrive - every other one has its
+// step by then - writes step + 1. The arrival's round trip overlaps the
+// copy, and nothing waits for the copy's stores inside the kernel.
+__global__ __launch_bounds__(STAGE_THREADS) void hs_k_stage(const StageTable tab,
+                                                            uint64_t total16, uint32_t *ctl,
                                                             uint32_t ring) {
   __shared__ uint32_t s_step;
   if (threadIdx.x == 0) s_step = __hip_atomic_load(ctl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -50,10 +51,13 @@ __global__ __launch_bounds__(STAGE_THREADS) void hs_k_stage(const StageRegion *_
   const uint64_t e = t % ring;
   const uint64_t stride = (uint64_t)gridDim.x * STAGE_THREADS;
   for (uint64_t c = (uint64_t)blockIdx.x * STAGE_THREADS + threadIdx.x; c < total16; c += stride) {
-    uint64_t off = c;
+    // the chunk's region: the first whose running end exceeds c
     int i = 0;
-    while (i + 1 < n && off >= regs[i].n16) off -= regs[i++].n16;
-    const StageRegion r = regs[i];
+#pragma unroll
+    for (int j = 0; j + 1 < STAGE_MAX_REGIONS; ++j)
+      i += (j + 1 < tab.n && c >= tab.end16[j]) ? 1 : 0;
+    const uint64_t off = c - (i ? tab.end16[i - 1] : 0);
+    const StageRegion &r = tab.r[i];
     ((HS_GLOBAL v4u *)r.dst)[off] = ((const HS_GLOBAL v4u *)r.src)[e * r.stride16 + off];
   }
 }
@@ -67,14 +71,14 @@ __global__ void hs_k_stage_set(uint32_t *ctl, uint32_t step) {
 
 }  // namespace
 
-hipError_t launch_stage(const StageRegion *d_regions, int n, uint64_t total16, uint32_t *d_ctl,
+hipError_t launch_stage(const StageTable &table, uint64_t total16, uint32_t *d_ctl,
                         uint32_t ring, hipStream_t stream) {
   // one 16-byte chunk per thread, at most 1024 workgroups
   uint64_t blocks = (total16 + STAGE_THREADS - 1) / STAGE_THREADS;
   if (blocks < 1) blocks = 1;
   if (blocks > 1024) blocks = 1024;
   return launch_k(HS_TRACE_STAGE, hs_k_stage, dim3((unsigned)blocks), dim3(STAGE_THREADS), 0,
-                  stream, d_regions, n, total16, d_ctl, ring);
+                  stream, table, total16, d_ctl, ring);
 }
 
 hipError_t launch_stage_set(uint32_t *d_ctl, uint32_t step, hipStream_t stream) {

@@ -194,9 +194,9 @@ def hs_last_error() -> str:
     return lib().hs_last_error().decode()
 
 
-def hs_set_tuning(attn_splits: int = 0, latent_heads_per_wg: int = 0,
-                  prefetch_workgroups: int = 0, prefetch_batch: int = 0,
-                  gather_bytes_per_lane: int = 0) -> None:
+def hs_set_tuning(attn_splits: int = 0, prefetch_workgroups: int = 0, prefetch_batch: int = 0,
+                  gather_bytes_per_lane: int = 0, latent_heads_per_wg: int = 0) -> None:
+    """Library-wide knobs (0 = the library's choice); see include/hisparse.h."""
     t = Tuning(attn_splits, latent_heads_per_wg, prefetch_workgroups, prefetch_batch,
                gather_bytes_per_lane)
     _check(lib().hs_set_tuning(ctypes.byref(t)))
@@ -206,7 +206,8 @@ def hs_get_tuning() -> dict:
     t = Tuning()
     _check(lib().hs_get_tuning(ctypes.byref(t)))
     return {"attn_splits": t.attn_splits, "latent_heads_per_wg": t.latent_heads_per_wg,
-            "prefetch_workgroups": t.prefetch_workgroups, "prefetch_batch": t.prefetch_batch,
+            "prefetch_workgroups": t.prefetch_workgroups,
+            "prefetch_batch": t.prefetch_batch,
             "gather_bytes_per_lane": t.gather_bytes_per_lane}
 
 

@@ -415,11 +415,14 @@ def bench_trace_cmd(out: str) -> List[str]:
 
 
 def run_bench_trace(out: str, limit: int) -> None:
-    """Kernel trace of exactly the measured benchmark command."""
+    """The measured benchmark command as it runs (no profiler), then again
+    under the kernel tracer."""
     os.makedirs(out, exist_ok=True)
     os.environ.setdefault("TMPDIR", "/tmp")
+    if _child(BENCH_DEFAULT, os.path.join(out, "plain_bench.log"), limit):
+        raise SystemExit("the benchmark failed")
     if _child(bench_trace_cmd(out), os.path.join(out, "trace_bench.log"), limit):
-        raise SystemExit("trace pass of the default benchmark failed")
+        raise SystemExit("trace pass of the benchmark failed")
 
 
 def bench_report(out: str) -> str:
@@ -473,16 +476,26 @@ def bench_report(out: str) -> str:
                      f"{statistics.median(eager):.2f} | {ev.get(cls_of[base], 0.0):.2f} | "
                      f"{statistics.mean(timed):.2f} |")
     roof = bl.get("roofline") or {}
-    lines += ["", f"Benchmark line of this run: value {bl['value']} us/layer; roofline "
-              f"{json.dumps(roof)}."]
+    lines += ["", f"Benchmark line of the traced run: value {bl['value']} us/layer; roofline "
+              f"{json.dumps(roof)}. (Under the tracer every dispatch carries the profiler's "
+              "own bookkeeping, which the benchmark's dispatch events see and the profiler's "
+              "durations do not.)"]
+    plain = bench_line(os.path.join(out, "plain_bench.log"))
+    if plain:
+        pr = plain.get("roofline") or {}
+        lines += ["", f"The same command without the profiler, just before on the same machine: "
+                  f"value {plain['value']} us/layer; kernels_us "
+                  f"{json.dumps(plain.get('kernels_us'))}; roofline {json.dumps(pr)}."]
     k = roof.get("kernel")
     if k in prof_avg and roof.get("bytes_per_launch") and roof.get("peak"):
         unit = 1e9 if roof.get("unit") == "GB/s" else 1e12
         ach = roof["bytes_per_launch"] / (prof_avg[k] * 1e-6) / unit
         lines += ["", f"Roofline from the profiler's durations of the same launches: "
                   f"{roof['bytes_per_launch']:,} bytes / {prof_avg[k]:.2f} us = {ach:.2f} "
-                  f"{roof.get('unit')}, frac {ach / roof['peak']:.4f} (the line: "
-                  f"{roof.get('frac')}, from {roof.get('avg_us')} us)."]
+                  f"{roof.get('unit')}, frac {ach / roof['peak']:.4f} (the traced run's line: "
+                  f"{roof.get('frac')}, from {roof.get('avg_us')} us"
+                  + (f"; the run without the profiler: {pr.get('frac')}, from "
+                     f"{pr.get('avg_us')} us" if plain else "") + ")."]
     os.makedirs(os.path.join(out, "report"), exist_ok=True)
     path = os.path.join(out, "report", f"hs_kernels_bench_default_{w.name}.md")
     with open(path, "w") as fh:
