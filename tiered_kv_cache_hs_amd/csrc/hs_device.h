@@ -206,13 +206,14 @@ struct StageTable {
   uint64_t end16[STAGE_MAX_REGIONS];  // running sum of n16 up to and including region i
   int n;
 };
-// Stage control words (device memory): [0] the step counter, [1] the
-// arrivals of the running launch (0 between launches).
+// Stage control words (device memory, 8-byte aligned): one 64-bit word with
+// the step counter in its high half and the arrivals of the running launch
+// in its low half (0 between launches).
 constexpr int STAGE_CTL_WORDS = 64;
-// Copies entry ctl[0] % ring of every region, then advances ctl[0].
+// Copies entry step % ring of every region, then advances the step.
 hipError_t launch_stage(const StageTable &table, uint64_t total16, uint32_t *d_ctl,
                         uint32_t ring, hipStream_t stream);
-// ctl[0] = step, ctl[1] = 0.
+// Sets the step (arrivals 0).
 hipError_t launch_stage_set(uint32_t *d_ctl, uint32_t step, hipStream_t stream);
 
 struct AttnMhaArgs {

@@ -1285,7 +1285,9 @@ hs_status hs_stage_set_step(hs_stage_t st, uint32_t step, void *stream) {
 hs_status hs_stage_get_step(hs_stage_t st, uint32_t *step) {
   if (!st || !step) return fail(HS_E_INVAL, "null argument");
   HS_HIP(hipDeviceSynchronize());
-  HS_HIP(hipMemcpy(step, st->d_ctl, sizeof(uint32_t), hipMemcpyDeviceToHost));
+  uint64_t w = 0;  // step in the high half, arrivals (0 between launches) in the low
+  HS_HIP(hipMemcpy(&w, st->d_ctl, sizeof(uint64_t), hipMemcpyDeviceToHost));
+  *step = (uint32_t)(w >> 32);
   return HS_OK;
 }
 

@@ -21,34 +21,32 @@ namespace {
 
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
 
-constexpr int STAGE_THREADS = 256;
+constexpr int STAGE_THREADS = 1024;
 
 // The regions' chunks form one index space (region 0's first, then region
 // 1's, ...); each thread copies chunk c = its global index, then c + the
 // grid's thread count, and so on (one chunk per thread at the usual sizes).
-// The region table is a kernel argument, so the only device read before the
-// copy is the step counter. Thread 0 reads it and hands it to the workgroup
-// through LDS; once the workgroup has it, thread 0 arrives (relaxed: only
-// the step's read has to precede the arrival, and its value was already
-// stored to LDS), and the last workgroup to arrive - every other one has its
-// step by then - writes step + 1. The arrival's round trip overlaps the
-// copy, and nothing waits for the copy's stores inside the kernel.
+// The region table is a kernel argument. The control word packs the step
+// (high half) and the arrivals of the running launch (low half): thread 0 of
+// each workgroup arrives with one atomic add, which also returns the step,
+// and hands the step to the workgroup through LDS; the last workgroup to
+// arrive (every other one has its step by then) writes (step + 1, 0). So the
+// only device access before the copy is that one atomic, and the control
+// word needs no clearing between launches.
 __global__ __launch_bounds__(STAGE_THREADS) void hs_k_stage(const StageTable tab,
-                                                            uint64_t total16, uint32_t *ctl,
+                                                            uint64_t total16, uint64_t *ctl,
                                                             uint32_t ring) {
   __shared__ uint32_t s_step;
-  if (threadIdx.x == 0) s_step = __hip_atomic_load(ctl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  lds_barrier();
-  const uint32_t t = s_step;
   if (threadIdx.x == 0) {
-    const uint32_t before =
-        __hip_atomic_fetch_add(ctl + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (before == gridDim.x - 1) {
-      __hip_atomic_store(ctl + 1, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(ctl, t + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    const uint64_t before = __hip_atomic_fetch_add(ctl, (uint64_t)1, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t t = (uint32_t)(before >> 32);
+    s_step = t;
+    if ((uint32_t)before == gridDim.x - 1)
+      __hip_atomic_store(ctl, (uint64_t)(t + 1u) << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  const uint64_t e = t % ring;
+  lds_barrier();
+  const uint64_t e = s_step % ring;
   const uint64_t stride = (uint64_t)gridDim.x * STAGE_THREADS;
   for (uint64_t c = (uint64_t)blockIdx.x * STAGE_THREADS + threadIdx.x; c < total16; c += stride) {
     // the chunk's region: the first whose running end exceeds c
@@ -62,11 +60,8 @@ __global__ __launch_bounds__(STAGE_THREADS) void hs_k_stage(const StageTable tab
   }
 }
 
-__global__ void hs_k_stage_set(uint32_t *ctl, uint32_t step) {
-  if (threadIdx.x == 0) {
-    ctl[0] = step;
-    ctl[1] = 0u;
-  }
+__global__ void hs_k_stage_set(uint64_t *ctl, uint32_t step) {
+  if (threadIdx.x == 0) *ctl = (uint64_t)step << 32;
 }
 
 }  // namespace
@@ -78,11 +73,11 @@ hipError_t launch_stage(const StageTable &table, uint64_t total16, uint32_t *d_c
   if (blocks < 1) blocks = 1;
   if (blocks > 1024) blocks = 1024;
   return launch_k(HS_TRACE_STAGE, hs_k_stage, dim3((unsigned)blocks), dim3(STAGE_THREADS), 0,
-                  stream, table, total16, d_ctl, ring);
+                  stream, table, total16, (uint64_t *)d_ctl, ring);
 }
 
 hipError_t launch_stage_set(uint32_t *d_ctl, uint32_t step, hipStream_t stream) {
-  hipLaunchKernelGGL(hs_k_stage_set, dim3(1), dim3(64), 0, stream, d_ctl, step);
+  hipLaunchKernelGGL(hs_k_stage_set, dim3(1), dim3(64), 0, stream, (uint64_t *)d_ctl, step);
   return hipGetLastError();
 }
 
