@@ -56,6 +56,12 @@ def parse():
                     help="hs_tuning.gather_bytes_per_lane: bytes of host reads each lane of the "
                          "resolve's miss fetch keeps in flight (16, 32, 64 or 128; 0 = the "
                          "library's choice)")
+    ap.add_argument("--fetch", choices=("auto", "inline", "kernel"), default="auto",
+                    help="hs_tuning.resolve_fetch: where hs_resolve moves the misses (inline = in "
+                         "the resolve kernel, its first host reads overlapping the victim "
+                         "selection; kernel = a gather kernel of its own after the resolve, "
+                         "whose duration is the gather phase alone; auto = inline for 4 or more "
+                         "units per batch)")
     ap.add_argument("--share", choices=("prefetch", "serial", "none"), default="prefetch",
                     help="layer groups that reuse one selection (workload 6): prefetch = one "
                          "resolve per group, the later layers' fetches on a second stream "
@@ -201,7 +207,8 @@ def main():
     from tiered_kv_cache_hs_amd.session import Session
 
     H.lib()
-    H.hs_set_tuning(gather_bytes_per_lane=args.gather_bytes)
+    fetch_mode = {"auto": 0, "inline": 1, "kernel": 2}[args.fetch]
+    H.hs_set_tuning(gather_bytes_per_lane=args.gather_bytes, resolve_fetch=fetch_mode)
     w = I.workload(args.workload)
     W, K = args.warmup, args.steps
     total = W + K
@@ -297,7 +304,8 @@ def main():
         cls_bytes = {"attn": lead_bytes + follow_bytes}
     else:
         cls_bytes = {"resolve": 0, "gather": follow_bytes}
-        cls_bytes["resolve" if w.n_requests >= 4 else "gather"] += lead_bytes
+        inline = fetch_mode == 1 or (fetch_mode == 0 and w.n_requests >= 4)
+        cls_bytes["resolve" if inline else "gather"] += lead_bytes
     fetch_class = max(cls_bytes, key=cls_bytes.get)
     fetch_us = per[fetch_class]
     miss_bytes_launch = cls_bytes[fetch_class] / max(1, tr[fetch_class][1])
@@ -346,6 +354,7 @@ def main():
                    "q_heads": w.n_q_heads, "record_bytes": w.rec_bytes, "kind": w.kind,
                    "graph": "one hipGraph replayed for every step (selections and queries "
                             "staged into fixed buffers on the device)",
+                   "fetch": args.fetch,
                    "path": ("hs_resolve_attn" if fused else "hs_resolve + hs_sparse_attn")
                    + (f" (layer groups of {w.share}: {sess.share_mode})" if sess.grouped else "")},
         "roofline": dominant,

@@ -130,7 +130,12 @@ typedef struct hs_tuning {
                                    per batch, 16 x {1, 2, 4, 8}; 0 = chosen per
                                    buffer size (64 for B <= 1024 or B > 8192,
                                    else 128) */
-  int32_t reserved[3];
+  int32_t resolve_fetch;        /* where hs_resolve moves the misses: 0 = by
+                                   batch size (the resolve kernel for 4 or more
+                                   units, else a gather kernel of its own);
+                                   1 = the resolve kernel; 2 = a gather kernel
+                                   of its own (many workgroups per unit) */
+  int32_t reserved[2];
 } hs_tuning;
 
 const char *hs_status_str(hs_status s);

@@ -41,10 +41,10 @@ def test_status_strings_and_tuning_roundtrip():
     assert H.hs_status_str(H.HS_E_STATE) == "invalid buffer state"
     assert H.hs_status_str(H.HS_E_DEVICE) == "data error reported by the device"
     assert (H.HS_E_DEVICE, H.HS_E_STATE) == (-5, -6)
-    H.hs_set_tuning(4, 96, 2, 64, 32)
+    H.hs_set_tuning(4, 96, 2, 64, 32, 2)
     assert H.hs_get_tuning() == {"attn_splits": 4, "latent_heads_per_wg": 32,
                                  "prefetch_workgroups": 96, "prefetch_batch": 2,
-                                 "gather_bytes_per_lane": 64}
+                                 "gather_bytes_per_lane": 64, "resolve_fetch": 2}
     H.hs_set_tuning()
     for gb in (16, 32, 128):
         H.hs_set_tuning(gather_bytes_per_lane=gb)
@@ -62,6 +62,9 @@ def test_status_strings_and_tuning_roundtrip():
     for hpw in (16, 48, -32):
         with pytest.raises(H.HsError):
             H.hs_set_tuning(latent_heads_per_wg=hpw)
+    for rf in (-1, 3):
+        with pytest.raises(H.HsError):
+            H.hs_set_tuning(resolve_fetch=rf)
     assert H.hs_get_tuning()["prefetch_workgroups"] == 0
 
 

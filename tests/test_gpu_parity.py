@@ -123,6 +123,19 @@ def test_latent_tile_tails(hq, k):
         H.hs_set_tuning()
 
 
+@pytest.mark.parametrize("R,fetch", [(4, 2), (5, 2), (2, 1), (1, 1)])
+def test_resolve_fetch_forced(R, fetch):
+    """hs_tuning.resolve_fetch moves the misses in a gather kernel of its own
+    on batches of 4 or more units (2) and inside the resolve kernel on
+    smaller ones (1), against the oracle as always."""
+    w = _small("latent", I.BF16, 300, 197, 3000, 4, 40, R=R, seed=70 + 10 * R + fetch, Hq=32)
+    H.hs_set_tuning(resolve_fetch=fetch)
+    try:
+        compare_run(w, 4, fill="full")
+    finally:
+        H.hs_set_tuning()
+
+
 def test_multi_request_multi_layer_small():
     w = _small("mha", I.BF16, 600, 200, 3000, 6, 50, R=3, L=2, seed=77, Hkv=2, D=128, Hq=16)
     compare_run(w, 6, fill="full")

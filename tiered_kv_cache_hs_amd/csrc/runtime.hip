@@ -45,7 +45,7 @@ hs_status hip_fail(hipError_t e, const char *what) {
     if (e_ != hipSuccess) return hip_fail(e_, #call); \
   } while (0)
 
-hs_tuning g_tuning = {0, 0, 0, 0, 0, {0, 0, 0}};
+hs_tuning g_tuning = {0, 0, 0, 0, 0, 0, {0, 0}};
 
 inline hipStream_t S(void *s) { return (hipStream_t)s; }
 
@@ -159,6 +159,8 @@ hs_status hs_set_tuning(const hs_tuning *t) {
   const int gb = t->gather_bytes_per_lane;
   if (gb != 0 && gb != 16 && gb != 32 && gb != 64 && gb != 128)
     return fail(HS_E_INVAL, "gather_bytes_per_lane must be 0, 16, 32, 64 or 128");
+  if (t->resolve_fetch < 0 || t->resolve_fetch > 2)
+    return fail(HS_E_INVAL, "resolve_fetch must be 0, 1 or 2");
   g_tuning = *t;
   return HS_OK;
 }
@@ -942,7 +944,10 @@ hs_status hs_resolve(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_t *d_
   if (s) return s;
   // one workgroup per unit cannot keep enough host reads in flight for the
   // link when the batch is small: fetch with a second, wider kernel there
-  const int fetch = b->n >= 4 ? hs::FETCH_INLINE : hs::FETCH_KERNEL;
+  const int fetch = g_tuning.resolve_fetch == 1   ? hs::FETCH_INLINE
+                    : g_tuning.resolve_fetch == 2 ? hs::FETCH_KERNEL
+                    : b->n >= 4                   ? hs::FETCH_INLINE
+                                                  : hs::FETCH_KERNEL;
   hipError_t e = hs::launch_resolve(b->d_units, b->n, b->max_B, d_topk, k, d_slots, d_miss,
                                     fetch, g_tuning.gather_bytes_per_lane / 16,
                                     (int)b->pool->rec, S(stream));

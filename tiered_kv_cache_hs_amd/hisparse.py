@@ -89,7 +89,8 @@ class Trace(ctypes.Structure):
 class Tuning(ctypes.Structure):
     _fields_ = [("attn_splits", ctypes.c_int32), ("latent_heads_per_wg", ctypes.c_int32),
                 ("prefetch_workgroups", ctypes.c_int32), ("prefetch_batch", ctypes.c_int32),
-                ("gather_bytes_per_lane", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("gather_bytes_per_lane", ctypes.c_int32), ("resolve_fetch", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2)]
 
 
 class StageRegion(ctypes.Structure):
@@ -195,10 +196,11 @@ def hs_last_error() -> str:
 
 
 def hs_set_tuning(attn_splits: int = 0, prefetch_workgroups: int = 0, prefetch_batch: int = 0,
-                  gather_bytes_per_lane: int = 0, latent_heads_per_wg: int = 0) -> None:
+                  gather_bytes_per_lane: int = 0, latent_heads_per_wg: int = 0,
+                  resolve_fetch: int = 0) -> None:
     """Library-wide knobs (0 = the library's choice); see include/hisparse.h."""
     t = Tuning(attn_splits, latent_heads_per_wg, prefetch_workgroups, prefetch_batch,
-               gather_bytes_per_lane)
+               gather_bytes_per_lane, resolve_fetch)
     _check(lib().hs_set_tuning(ctypes.byref(t)))
 
 
@@ -208,7 +210,7 @@ def hs_get_tuning() -> dict:
     return {"attn_splits": t.attn_splits, "latent_heads_per_wg": t.latent_heads_per_wg,
             "prefetch_workgroups": t.prefetch_workgroups,
             "prefetch_batch": t.prefetch_batch,
-            "gather_bytes_per_lane": t.gather_bytes_per_lane}
+            "gather_bytes_per_lane": t.gather_bytes_per_lane, "resolve_fetch": t.resolve_fetch}
 
 
 # ------------------------------------------------------------------ pool
