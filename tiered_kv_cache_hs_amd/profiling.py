@@ -135,11 +135,19 @@ def _tag(wl: int) -> str:
     return f"wl{wl}" + ("" if PATH == "auto" else f"_{PATH}")
 
 
+def path_args() -> List[str]:
+    """bench.py options of the current path: --path fused / split, or (gather)
+    --fetch kernel, the misses moved by a gather kernel of their own."""
+    if PATH == "auto":
+        return []
+    return ["--fetch", "kernel"] if PATH == "gather" else ["--path", PATH]
+
+
 def bench_cmd(wl: Optional[int], steps: int, warmup: int) -> List[str]:
     if wl is None:
         return ["python3", "-u", "bench.py", "--copy-calibration"]
     return ["python3", "-u", "bench.py", "--workload", str(wl), "--steps", str(steps),
-            "--warmup", str(warmup), "--no-cpu"] + ([] if PATH == "auto" else ["--path", PATH])
+            "--warmup", str(warmup), "--no-cpu"] + path_args()
 
 
 def trace_cmd(out: str, wl: int) -> List[str]:
@@ -321,8 +329,8 @@ def report(workloads: List[int], out: str) -> None:
                  + ("" if PATH == "auto" else f" --path {PATH}"), "",
                  "which runs these passes for this workload, each under `timeout -s KILL`:", "",
                  "    " + " ".join(trace_cmd(rel, wl)),
-                 "    " + " ".join(pmc_cmd(rel, f"wl{wl}", "FETCH_SIZE", wl)),
-                 "    " + " ".join(pmc_cmd(rel, f"wl{wl}", "WRITE_SIZE", wl)),
+                 "    " + " ".join(pmc_cmd(rel, _tag(wl), "FETCH_SIZE", wl)),
+                 "    " + " ".join(pmc_cmd(rel, _tag(wl), "WRITE_SIZE", wl)),
                  "    " + " ".join(pmc_cmd(rel, "copy", "FETCH_SIZE", None)) + "   (and WRITE_SIZE)",
                  "", "The trace run replays the step graph for 32 decode steps (8 warm-up + 24 "
                  "timed), replays the whole trace three more times from a reset state, then "
@@ -394,7 +402,18 @@ def report(workloads: List[int], out: str) -> None:
                      "copy_fetch_kib": round(copy_kib["FETCH_SIZE"], 1),
                      "copy_write_kib": round(copy_kib["WRITE_SIZE"], 1), "copy_bytes": COPY_BYTES},
            "entries": entries}
-    with open(os.path.join(rep, "pmc_traffic.json"), "w") as fh:
+    # readings of other workloads or paths already in the report (earlier
+    # runs into the same directory) are kept
+    path = os.path.join(rep, "pmc_traffic.json")
+    try:
+        with open(path) as fh:
+            old = json.load(fh).get("entries", [])
+    except (OSError, ValueError):
+        old = []
+    mine = {(e["workload"], e["path"], e["kernel"]) for e in entries}
+    doc["entries"] = [e for e in old if (e["workload"], e.get("path", "auto"), e["kernel"])
+                      not in mine] + entries
+    with open(path, "w") as fh:
         json.dump(doc, fh, indent=1)
     print(f"[profiling] report in {rep}", flush=True)
 
@@ -511,8 +530,9 @@ def main() -> None:
     ap.add_argument("--workloads", type=int, nargs="+", default=[3, 4, 5, 6, 7])
     ap.add_argument("--out", default=os.path.join(ROOT, "prof_out"))
     ap.add_argument("--limit", type=int, default=240, help="seconds per profiler pass")
-    ap.add_argument("--path", choices=("auto", "fused", "split"), default="auto",
-                    help="bench.py --path of every run (run/report)")
+    ap.add_argument("--path", choices=("auto", "fused", "split", "gather"), default="auto",
+                    help="bench.py --path of every run (run/report); gather: bench.py --fetch "
+                         "kernel")
     a = ap.parse_args()
     global PATH
     PATH = a.path
