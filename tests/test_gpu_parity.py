@@ -107,6 +107,19 @@ def test_latent_splits(hpw, splits, fused):
         H.hs_set_tuning()
 
 
+@pytest.mark.parametrize("k,splits", [(700, 11), (1000, 16), (1100, 20)])
+def test_latent_many_splits(k, splits):
+    """Latent attention with 11, 16 and 18 splits of 64 entries (ragged last
+    splits): the bf16 split partials merged by the one-pass combine (up to
+    16 splits) and by the two-phase one (18)."""
+    w = _small("latent", I.BF16, k + 100, k, 5000, 3, 60, R=2, seed=70 + splits, Hq=64)
+    H.hs_set_tuning(splits)
+    try:
+        compare_run(w, 3, fill="full")
+    finally:
+        H.hs_set_tuning()
+
+
 @pytest.mark.parametrize("hq", [16, 32, 64])
 @pytest.mark.parametrize("k", [1, 15, 16, 17, 47, 64, 100, 250])
 def test_latent_tile_tails(hq, k):

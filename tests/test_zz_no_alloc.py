@@ -113,8 +113,9 @@ def test_noalloc_in_a_graph_replayed():
 
 
 def test_noalloc_refuses_more_than_its_scratch():
-    # 64 splits of 32 slots for 16 latent units of 64 heads: 134 MB of partials
-    w = small_workload("latent", I.BF16, 2048, 2048, 2100, 1, 10, R=16, seed=64, Hq=64)
+    # 32 splits of 64 slots (latent splits are whole pairs of 32-row tiles) for
+    # 32 latent units of 64 heads: 67 MB of bf16 partials
+    w = small_workload("latent", I.BF16, 2048, 2048, 2100, 1, 10, R=32, seed=64, Hq=64)
     sess = Session(w, 1, fill="touched")
     try:
         sess.step(0)

@@ -47,8 +47,11 @@
 //     everything else fit the ordinary ones, so a compute unit runs one
 //     workgroup.
 // At the end each wave stages its accumulators in LDS and the workgroup
-// stores whole 1 KB row halves: the output, or its split's partial for the
-// split-k combine.
+// stores whole row halves: the output (fp32, 1 KB), or its split's partial
+// for the split-k combine, rounded to bf16 (512 bytes; with (m, l) in fp32).
+// A split's partial is as large as the rows it covers would be in fp32 at
+// 256 rows, and all workgroups write theirs at the same moment, so halving
+// it shortens the kernel's end and the combine's reads.
 #include "hs_device.h"
 
 #define HS_LDS __attribute__((address_space(3)))
@@ -83,6 +86,7 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -169,7 +173,7 @@ template <int NHG, bool STREAM>
 __global__ __launch_bounds__(LAT_THREADS, 1) void hs_k_attn_latent(
     const UnitDesc *__restrict__ units, const uint16_t *__restrict__ q_all,
     const int32_t *__restrict__ slots_all, int n_units, int k, int Hq, float scale_log2, int S,
-    int HS, int chunk, float *__restrict__ ws_o, float *__restrict__ ws_ml,
+    int HS, int chunk, uint16_t *__restrict__ ws_o, float *__restrict__ ws_ml,
     float *__restrict__ out) {
   constexpr int NVT = LAT_DL / 32 / 2;            // value tiles of 32 per wave
   constexpr int NST = 3 - NHG;                     // tiles per step
@@ -520,8 +524,8 @@ __global__ __launch_bounds__(LAT_THREADS, 1) void hs_k_attn_latent(
     }
   }
   __syncthreads();
-  // wave w stores 32 (NHG = 2: its region) or 16 (NHG = 1) row halves of
-  // 1 KB, all read from LDS before any is stored
+  // wave w stores 32 (NHG = 2: its region) or 16 (NHG = 1) row halves, all
+  // read from LDS before any is stored
   constexpr int PIECES = NHG == 2 ? 32 : 16;
   const int pvh = w >> 1;
   const int ra = NHG == 2 ? w : 2 * pvh;  // (the first stream's) region
@@ -565,12 +569,15 @@ __global__ __launch_bounds__(LAT_THREADS, 1) void hs_k_attn_latent(
                           nan_bits_if(any_bad, rr[2]), nan_bits_if(any_bad, rr[3])};
         *(HS_GLOBAL v4u *)(out + ((size_t)u * Hq + ph) * LAT_DL + v0) = bits;
       } else {
-        HS_GLOBAL floatx4 *dst =
-            (HS_GLOBAL floatx4 *)(glb(ws_o) + (((size_t)u * Hq + ph) * S + sp) * LAT_DL + v0);
+        // the split's partial, rounded to bf16 (nearest even): 512 bytes per
+        // instruction
+        HS_GLOBAL v2u *dst =
+            (HS_GLOBAL v2u *)(glb(ws_o) + (((size_t)u * Hq + ph) * S + sp) * LAT_DL + v0);
+        const v2u bits = {pack_bf16(vb[j][0], vb[j][1]), pack_bf16(vb[j][2], vb[j][3])};
         if (STREAM)
-          __builtin_nontemporal_store(vb[j], dst);
+          __builtin_nontemporal_store(bits, dst);
         else
-          *dst = vb[j];
+          *dst = bits;
       }
     }
   }
@@ -590,14 +597,14 @@ hipError_t launch_latent_t(const AttnLatentArgs &a, hipStream_t stream) {
 
 hipError_t launch_attn_latent(const AttnLatentArgs &a, hipStream_t stream) {
   const bool stream_partials = a.splits > 1 && (size_t)a.n_units * a.Hq * a.splits * LAT_DL *
-                                                      sizeof(float) <= LAT_STREAM_PARTIAL_BYTES;
+                                                      sizeof(uint16_t) <= LAT_STREAM_PARTIAL_BYTES;
   const hipError_t e =
       a.hpw == 64 ? (stream_partials ? launch_latent_t<2, true>(a, stream)
                                    : launch_latent_t<2, false>(a, stream))
                   : (stream_partials ? launch_latent_t<1, true>(a, stream)
                                    : launch_latent_t<1, false>(a, stream));
   if (e != hipSuccess || a.splits == 1) return e;
-  return launch_combine(a.ws_o, a.ws_ml, a.n_units * a.Hq, a.splits, LAT_DL, a.out, stream);
+  return launch_combine(a.ws_o, 1, a.ws_ml, a.n_units * a.Hq, a.splits, LAT_DL, a.out, stream);
 }
 
 }  // namespace hs

@@ -264,7 +264,29 @@ __global__ __launch_bounds__(MHA_THREADS) void hs_k_attn_mha(
 // its output elements over the splits with the loads of 8 splits in flight.
 constexpr int COMBINE_MAX_S = 64;
 
-__global__ __launch_bounds__(256) void hs_k_combine(const float *__restrict__ ws_o,
+// Partial element i of a row: fp32, or bf16 widened exactly.
+__device__ __forceinline__ float partial_at(const float *p, size_t i) { return p[i]; }
+__device__ __forceinline__ float partial_at(const uint16_t *p, size_t i) {
+  return __uint_as_float((uint32_t)p[i] << 16);
+}
+// Partial elements i, i + 1 (i even) as loaded, and widened to fp32 (kept
+// apart so that every load of a thread is issued before the first
+// conversion waits for one).
+__device__ __forceinline__ float2 partial_pair_raw(const float *p, size_t i) {
+  return *(const float2 *)(p + i);
+}
+__device__ __forceinline__ uint32_t partial_pair_raw(const uint16_t *p, size_t i) {
+  return *(const uint32_t *)(p + i);
+}
+__device__ __forceinline__ float2 widen_pair(float2 v) { return v; }
+__device__ __forceinline__ float2 widen_pair(uint32_t w) {
+  return float2{__uint_as_float(w << 16), __uint_as_float(w & 0xFFFF0000u)};
+}
+template <typename P>
+using partial_pair_t = decltype(partial_pair_raw((const P *)nullptr, 0));
+
+template <typename P>
+__global__ __launch_bounds__(256) void hs_k_combine(const P *__restrict__ ws_o,
                                                     const float *__restrict__ ws_ml, int S,
                                                     int dv, float *__restrict__ out) {
   __shared__ float s_w[COMBINE_MAX_S];
@@ -287,40 +309,43 @@ __global__ __launch_bounds__(256) void hs_k_combine(const float *__restrict__ ws
   }
   __syncthreads();
   const float inv = s_inv;
-  const float *src = ws_o + row * S * dv;
+  const P *src = ws_o + row * S * dv;
   for (int e = tid; e < dv; e += blockDim.x) {
     float o = 0.f;
 #pragma unroll 8
-    for (int s = 0; s < S; ++s) o = fmaf(s_w[s], src[(size_t)s * dv + e], o);
+    for (int s = 0; s < S; ++s) o = fmaf(s_w[s], partial_at(src, (size_t)s * dv + e), o);
     out[row * dv + e] = o * inv;
   }
 }
 
-// The same merge for S <= COMBINE_WAVE_S splits and rows of at most 512
-// elements, in one memory round trip and without LDS or a barrier: lane s of
-// every wave loads split s's (m, l) while each thread loads its two output
-// elements' partials; the weights then come from wave reductions and
-// shuffles, in the same arithmetic as the kernel above (same L tree, same
-// order of the weighted sums), so both give identical results. Faster up to
-// 4 splits (2 splits: 8.5 -> 7.2 us; 4: 13.4 -> 11.1), even at 8, slower at
-// 16 (7.8 -> 8.2 us), where the serial chain of 16 shuffles and products
-// costs more than the barrier it saves.
+// The same merge for S <= MAXS splits and rows of at most 512 elements, in
+// one memory round trip and without LDS or a barrier: lane s of every wave
+// loads split s's (m, l) while each thread loads its two output elements'
+// partials; the weights then come from wave reductions and shuffles, in the
+// same arithmetic as the kernel above (same L tree, same order of the
+// weighted sums), so both give identical results. With fp32 partials it is
+// faster up to 8 splits (2 splits: 8.5 -> 7.2 us; 4: 13.4 -> 11.1), even at
+// 8, and slower at 16 (7.8 -> 8.2 us), where the serial chain of 16 shuffles
+// and products costs more than the barrier it saves; with bf16 partials it
+// is faster at 16 too (4.7-4.8 -> 4.0-4.3 us for 8 latent units of 64 heads).
 constexpr int COMBINE_WAVE_S = 8;
+constexpr int COMBINE_WAVE_S_BF16 = 16;
 
-__global__ __launch_bounds__(256) void hs_k_combine_wave(const float *__restrict__ ws_o,
+template <typename P, int MAXS>
+__global__ __launch_bounds__(256) void hs_k_combine_wave(const P *__restrict__ ws_o,
                                                          const float *__restrict__ ws_ml, int S,
                                                          int dv, float *__restrict__ out) {
   const size_t row = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int e = 2 * threadIdx.x;  // dv <= 512: at most one pair of elements per thread
   const bool has = e < dv;
-  const float *src = ws_o + row * S * dv + (has ? e : 0);
+  const P *src = ws_o + row * S * dv + (has ? e : 0);
   const float2 my =
       lane < S ? ((const float2 *)ws_ml)[row * S + lane] : float2{NEG_INF, 0.f};
-  float2 ov[COMBINE_WAVE_S];
+  partial_pair_t<P> ov[MAXS];
 #pragma unroll
-  for (int s = 0; s < COMBINE_WAVE_S; ++s)
-    if (s < S) ov[s] = *(const float2 *)(src + (size_t)s * dv);
+  for (int s = 0; s < MAXS; ++s)
+    if (s < S) ov[s] = partial_pair_raw(src, (size_t)s * dv);
   const bool nan = __any(my.x != my.x);
   float M = my.x;
 #pragma unroll
@@ -331,11 +356,12 @@ __global__ __launch_bounds__(256) void hs_k_combine_wave(const float *__restrict
   for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
   float o0 = 0.f, o1 = 0.f;
 #pragma unroll
-  for (int s = 0; s < COMBINE_WAVE_S; ++s) {
+  for (int s = 0; s < MAXS; ++s) {
     if (s < S) {
       const float ws = __shfl(wgt, s, 64);
-      o0 = fmaf(ws, ov[s].x, o0);
-      o1 = fmaf(ws, ov[s].y, o1);
+      const float2 v = widen_pair(ov[s]);
+      o0 = fmaf(ws, v.x, o0);
+      o1 = fmaf(ws, v.y, o1);
     }
   }
   if (has) {
@@ -378,16 +404,30 @@ hipError_t launch_attn_mha(const AttnMhaArgs &a, hipStream_t stream) {
     e = a.D == 64 ? launch_mha_d<uint16_t, 64>(a, stream)
                   : launch_mha_d<uint16_t, 128>(a, stream);
   if (e != hipSuccess || a.splits == 1) return e;
-  return launch_combine(a.ws_o, a.ws_ml, a.n_units * a.Hq, a.splits, a.D, a.out, stream);
+  return launch_combine(a.ws_o, 0, a.ws_ml, a.n_units * a.Hq, a.splits, a.D, a.out, stream);
 }
 
-hipError_t launch_combine(const float *ws_o, const float *ws_ml, int rows, int splits, int dv,
-                          float *out, hipStream_t stream) {
-  if (splits <= COMBINE_WAVE_S && dv % 2 == 0 && dv <= 512)
-    return launch_k(HS_TRACE_COMBINE, hs_k_combine_wave, dim3(rows), dim3(256), 0, stream, ws_o,
-                    ws_ml, splits, dv, out);
-  return launch_k(HS_TRACE_COMBINE, hs_k_combine, dim3(rows), dim3(256), 0, stream, ws_o, ws_ml,
-                  splits, dv, out);
+namespace {
+template <typename P>
+hipError_t launch_combine_t(const P *ws_o, const float *ws_ml, int rows, int splits, int dv,
+                            float *out, hipStream_t stream) {
+  const bool wave_rows = dv % 2 == 0 && dv <= 512;
+  if (wave_rows && splits <= COMBINE_WAVE_S)
+    return launch_k(HS_TRACE_COMBINE, hs_k_combine_wave<P, COMBINE_WAVE_S>, dim3(rows), dim3(256),
+                    0, stream, ws_o, ws_ml, splits, dv, out);
+  if (wave_rows && sizeof(P) == 2 && splits <= COMBINE_WAVE_S_BF16)
+    return launch_k(HS_TRACE_COMBINE, hs_k_combine_wave<P, COMBINE_WAVE_S_BF16>, dim3(rows),
+                    dim3(256), 0, stream, ws_o, ws_ml, splits, dv, out);
+  return launch_k(HS_TRACE_COMBINE, hs_k_combine<P>, dim3(rows), dim3(256), 0, stream, ws_o,
+                  ws_ml, splits, dv, out);
+}
+}  // namespace
+
+hipError_t launch_combine(const void *ws_o, int partial_bf16, const float *ws_ml, int rows,
+                          int splits, int dv, float *out, hipStream_t stream) {
+  return partial_bf16
+             ? launch_combine_t((const uint16_t *)ws_o, ws_ml, rows, splits, dv, out, stream)
+             : launch_combine_t((const float *)ws_o, ws_ml, rows, splits, dv, out, stream);
 }
 
 }  // namespace hs

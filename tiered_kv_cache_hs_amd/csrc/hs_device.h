@@ -238,11 +238,14 @@ struct AttnLatentArgs {
   int n_units, k, Hq, splits, chunk;  // chunk: a multiple of 64, at most LAT_MAX_CHUNK
   int hpw;                            // query heads per workgroup: 32 or 64
   float scale_log2;
-  float *ws_o, *ws_ml, *out;
+  uint16_t *ws_o;  // split partials, bf16
+  float *ws_ml, *out;
 };
 hipError_t launch_attn_latent(const AttnLatentArgs &a, hipStream_t stream);
 
-hipError_t launch_combine(const float *ws_o, const float *ws_ml, int rows,
+// Split-k combine over [rows][splits][dv] partials, fp32 (partial_bf16 = 0)
+// or bf16 (1), and [rows][splits] (m, l) pairs.
+hipError_t launch_combine(const void *ws_o, int partial_bf16, const float *ws_ml, int rows,
                           int splits, int dv, float *out, hipStream_t stream);
 
 }  // namespace hs

@@ -960,7 +960,7 @@ hs_status hs_resolve(hs_batch_t b, const int32_t *d_topk, int32_t k, int32_t *d_
 struct AttnPlan {
   int splits, chunk, dv;
   int hpw;  // latent: query heads per workgroup
-  size_t ws_o_floats, ws_ml_floats, ws_bytes;
+  size_t ws_o_bytes, ws_ml_floats, ws_bytes;
 };
 
 static hs_status plan_attn(hs_batch_t b, int32_t Hq, int32_t k, AttnPlan *pl) {
@@ -993,16 +993,19 @@ static hs_status plan_attn(hs_batch_t b, int32_t Hq, int32_t k, AttnPlan *pl) {
     // partial bytes and the unit's work spreads over twice the workgroups,
     // which measured faster on both MLA workloads (batch 8: 21.5 against
     // 25.7 us with the combine; batch 64: 48.3 against 50.0), so 32 is the
-    // default. Every split writes a 2 KB fp32 partial per head, which the
-    // split-k combine reads back, so splits keep at least 256 rows and are
-    // added until the grid reaches 256 workgroups (batch 8: 32 heads x 8
-    // splits, 128 workgroups; batch 64: 32 x 2, 256).
+    // default. Every split writes a 1 KB bf16 partial per head, which the
+    // split-k combine reads back, so splits keep at least 128 rows and are
+    // added until the grid reaches 256 workgroups (batch 8: 32 heads x 16
+    // splits; batch 64: 32 x 2; 32 requests at k = 512: 32 x 4). Against 256
+    // rows at least (8 and 2 splits on the first and last), attention plus
+    // combine measured 18.6-19.5 against 20.0-20.6 us at batch 8 and 19.6
+    // against 20.9-21.3 us on the 32 requests.
     const int n8 = (b->n + 7) / 8 * 8;
     int hpw = g_tuning.latent_heads_per_wg;
     if (hpw <= 0 || Hq <= 32) hpw = 32;
     pl->hpw = hpw;
     base = n8 * ((Hq + hpw - 1) / hpw);
-    min_chunk = 256;
+    min_chunk = 128;
     target = 256;
     pl->dv = p->Dl;
   }
@@ -1018,13 +1021,15 @@ static hs_status plan_attn(hs_batch_t b, int32_t Hq, int32_t k, AttnPlan *pl) {
   pl->splits = splits;
   pl->chunk = chunk;
   if (splits == 1) {
-    pl->ws_o_floats = pl->ws_ml_floats = 0;
+    pl->ws_o_bytes = pl->ws_ml_floats = 0;
     pl->ws_bytes = 0;
   } else {
     const size_t rows = (size_t)b->n * Hq;
-    pl->ws_o_floats = rows * splits * pl->dv;
+    // partials: fp32 for MHA records, bf16 for latent ones (a latent split
+    // writes 512 values per head, as many bytes in fp32 as two of its rows)
+    pl->ws_o_bytes = rows * splits * pl->dv * (p->kind == HS_KV_LATENT ? 2 : 4);
     pl->ws_ml_floats = rows * splits * 2;
-    pl->ws_bytes = hs::align_up(pl->ws_o_floats * 4, 256) + pl->ws_ml_floats * 4;
+    pl->ws_bytes = hs::align_up(pl->ws_o_bytes, 256) + pl->ws_ml_floats * 4;
   }
   return HS_OK;
 }
@@ -1056,8 +1061,7 @@ static hs_status check_attn(hs_batch_t b, const void *d_q, int32_t Hq, const int
 static hs_status enqueue_attn(hs_batch_t b, const void *d_q, int32_t Hq, const int32_t *d_slots,
                               int32_t k, float sm_scale, float *d_out, void *d_ws,
                               const AttnPlan &pl, int fetch, void *stream) {
-  float *ws_o = (float *)d_ws;
-  float *ws_ml = pl.ws_bytes ? (float *)((uint8_t *)d_ws + hs::align_up(pl.ws_o_floats * 4, 256))
+  float *ws_ml = pl.ws_bytes ? (float *)((uint8_t *)d_ws + hs::align_up(pl.ws_o_bytes, 256))
                              : nullptr;
   const float scale_log2 = sm_scale * 1.4426950408889634f;
   const hs_pool_s *p = b->pool;
@@ -1078,7 +1082,7 @@ static hs_status enqueue_attn(hs_batch_t b, const void *d_q, int32_t Hq, const i
     a.rec_bytes = (int)p->rec;
     a.fetch = fetch;
     a.scale_log2 = scale_log2;
-    a.ws_o = ws_o;
+    a.ws_o = (float *)d_ws;
     a.ws_ml = ws_ml;
     a.out = d_out;
     e = hs::launch_attn_mha(a, S(stream));
@@ -1094,7 +1098,7 @@ static hs_status enqueue_attn(hs_batch_t b, const void *d_q, int32_t Hq, const i
     a.chunk = pl.chunk;
     a.hpw = pl.hpw;
     a.scale_log2 = scale_log2;
-    a.ws_o = ws_o;
+    a.ws_o = (uint16_t *)d_ws;
     a.ws_ml = ws_ml;
     a.out = d_out;
     e = hs::launch_attn_latent(a, S(stream));
