@@ -149,6 +149,19 @@ def test_resolve_fetch_forced(R, fetch):
         H.hs_set_tuning()
 
 
+@pytest.mark.parametrize("R,fetch", [(4, 0), (1, 1)])
+def test_large_buffer_inline_fetch(R, fetch):
+    """Buffers of more than 8192 slots with the misses fetched inside the
+    resolve kernel (16 slots per thread, fewer host reads in flight per lane):
+    by default on a batch of 4 units, forced on a single unit."""
+    w = _small("mha", I.F32, 16384, 4096, 40000, 3, 1000, R=R, seed=90 + R)
+    H.hs_set_tuning(resolve_fetch=fetch)
+    try:
+        compare_run(w, 3, fill="full")
+    finally:
+        H.hs_set_tuning()
+
+
 def test_multi_request_multi_layer_small():
     w = _small("mha", I.BF16, 600, 200, 3000, 6, 50, R=3, L=2, seed=77, Hkv=2, D=128, Hq=16)
     compare_run(w, 6, fill="full")
