@@ -237,15 +237,6 @@ __global__ __launch_bounds__(LAT_THREADS, 1) void hs_k_attn_latent(
     else
       lds_dma16(rope_src + rofs_src, tile_dst + LAT_ROPE_OFF + 1024 * w);
   };
-  // the split's slot id at index i (past the split: its last one), checked
-  auto slot_at = [&](int i, bool &flag) {
-    int s = slots[i_begin + min(i, n_rows - 1)];
-    if ((unsigned)s >= (unsigned)B) {
-      flag = true;
-      s = 0;
-    }
-    return s;
-  };
   // the slot ids a wave's copies of step i need: lanes 8t .. 8t + 7 hold
   // those of tile t's rows w + 4 (lane & 7); rope[t] that of row rope_row
   struct CopySrc {
@@ -268,10 +259,48 @@ __global__ __launch_bounds__(LAT_THREADS, 1) void hs_k_attn_latent(
               lds0 + step_buf(i) + t * LAT_TILE_BYTES);
   };
 
-  // ---- prologue: the queries (into the buffers of steps 1 and 2, or the
-  // second half-buffer) and step 0's rows (slot ids straight from global
-  // memory) are copied first; the split's slot ids load meanwhile
-  const uint32_t q_dst = lds0 + STEP_BYTES * (NHG == 2 ? 1 : 1);
+  // ---- prologue, in two memory round trips. First the loads the compiler
+  // waits for: the unit's descriptor and every slot id of the split (a wait
+  // for them issued after the row copies would wait for the copies too, the
+  // counter retiring in issue order). Then the copies of the queries (into
+  // the buffer of step 1, or of steps 1 and 2) and of step 0's rows, back
+  // to back; the queries land first and are read while step 0's rows are
+  // still arriving.
+  if (tid == 0) s_bad = 0;
+  // the split's slot ids in whole steps (entries past the split repeat its
+  // last one: those rows are loaded and masked)
+  const int n_ids = n_steps * NST * LAT_TILE;
+  constexpr int IDS_PT = LAT_MAX_CHUNK / LAT_THREADS;
+  int ids[IDS_PT];
+#pragma unroll
+  for (int j = 0; j < IDS_PT; ++j) {
+    const int i = tid + j * LAT_THREADS;
+    ids[j] = i < n_ids ? slots[i_begin + min(i, n_rows - 1)] : 0;
+  }
+  CopySrc c0;  // step 0's, straight from global memory
+  if (n_steps > 0) {
+    c0.lat = slots[i_begin + min(min((lane >> 3) & 1, NST - 1) * LAT_TILE + w + 4 * (lane & 7),
+                                 n_rows - 1)];
+#pragma unroll
+    for (int t = 0; t < NST; ++t)
+      c0.rope[t] = slots[i_begin + min(t * LAT_TILE + rope_row, n_rows - 1)];
+  }
+  // an invalid slot is flagged and replaced by slot 0 (the unit's output
+  // becomes NaN)
+  bool bad = false;
+  auto checked = [&](int sl) {
+    if ((unsigned)sl >= (unsigned)B) {
+      bad = true;
+      sl = 0;
+    }
+    return sl;
+  };
+#pragma unroll
+  for (int j = 0; j < IDS_PT; ++j) {
+    const int i = tid + j * LAT_THREADS;
+    if (i < n_ids) s_ids[i] = checked(ids[j]);
+  }
+  const uint32_t q_dst = lds0 + STEP_BYTES;
   {
     const HS_GLOBAL uint8_t *qb0 = (const HS_GLOBAL uint8_t *)glb(q_all) + (size_t)u * Hq * LAT_REC;
     const int hmax = Hq - 1;
@@ -283,23 +312,21 @@ __global__ __launch_bounds__(LAT_THREADS, 1) void hs_k_attn_latent(
                   qb0 + (size_t)min(h0 + 32 * g + rope_row, hmax) * LAT_REC,
                   q_dst + g * LAT_TILE_BYTES);
   }
-  bool bad = false;
   if (n_steps > 0) {
-    CopySrc c0;
-    c0.lat = slot_at(min((lane >> 3) & 1, NST - 1) * LAT_TILE + w + 4 * (lane & 7), bad);
+    c0.lat = checked(c0.lat);
 #pragma unroll
-    for (int t = 0; t < NST; ++t) c0.rope[t] = slot_at(t * LAT_TILE + rope_row, bad);
+    for (int t = 0; t < NST; ++t) c0.rope[t] = checked(c0.rope[t]);
 #pragma unroll
     for (int m = 0; m < CPS; ++m) copy_one(c0, 0, m);
   }
-  // the split's slot ids into LDS, whole steps; entries past the split
-  // repeat its last one (those rows are loaded and masked). An invalid slot
-  // is flagged and replaced by slot 0 (the unit's output becomes NaN).
-  if (tid == 0) s_bad = 0;
-  lds_barrier();
-  for (int i = tid; i < n_steps * NST * LAT_TILE; i += LAT_THREADS) s_ids[i] = slot_at(i, bad);
+  lds_barrier();  // s_bad's initial value is visible to every wave
   if (bad) s_bad = 1;
-  wait_vmcnt<0>();  // the queries, the ids and step 0's rows have arrived
+  // this wave's query copies have landed (step 0's may still be in flight),
+  // then every wave's have
+  if (n_steps > 0)
+    wait_vmcnt<CPS>();
+  else
+    wait_vmcnt<0>();
   lds_barrier();
 
   // K read of d-step ds from a tile: lane (row r = lane & 31, chunk 2 ds +
@@ -328,7 +355,10 @@ __global__ __launch_bounds__(LAT_THREADS, 1) void hs_k_attn_latent(
     for (int ds = 0; ds < LAT_BLOCKS; ++ds)
       qb[ds] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(v4u, kread(qt, ds)) & keep);
   }
-  lds_barrier();  // the query tiles' buffers are free
+  // step 0's rows have landed, and every wave's; the query tiles' buffers
+  // are free; the slot ids and s_bad are visible
+  wait_vmcnt<0>();
+  lds_barrier();
   if (DEPTH > 1 && n_steps > 1) {
     const CopySrc c1 = copy_ids(1);
 #pragma unroll
