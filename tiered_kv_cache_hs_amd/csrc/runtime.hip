@@ -999,7 +999,11 @@ static hs_status plan_attn(hs_batch_t b, int32_t Hq, int32_t k, AttnPlan *pl) {
     // splits; batch 64: 32 x 2; 32 requests at k = 512: 32 x 4). Against 256
     // rows at least (8 and 2 splits on the first and last), attention plus
     // combine measured 18.6-19.5 against 20.0-20.6 us at batch 8 and 19.6
-    // against 20.9-21.3 us on the 32 requests.
+    // against 20.9-21.3 us on the 32 requests. With bf16 partials 64 heads x
+    // 4 splits beat 32 x 2 at batch 64 when the same step's attention is
+    // timed alone (44.0 against 46.3-47.7 us) but not inside the decode step
+    // (47.7 against 47.6, the resolve having just written 45 MB of rows), and
+    // lost at 8, 16 and 32 requests, so 32 stays the default.
     const int n8 = (b->n + 7) / 8 * 8;
     int hpw = g_tuning.latent_heads_per_wg;
     if (hpw <= 0 || Hq <= 32) hpw = 32;
