@@ -378,8 +378,11 @@ hs_status hs_resolve(hs_batch_t batch, const int32_t *d_topk, int32_t k,
  *   bf16, latent_dim 512, rope_dim 64, n_q_heads 16, 32 or 64.
  *   Attention over the same buffers must not run concurrently with a resolve
  *   of them.
- * Outputs are fp32 (accumulation is fp32). A slot outside [0, B) makes the
- * unit's output NaN and sets HS_ERR_SLOT. d_ws is scratch of at least
+ * Outputs are fp32 (accumulation is fp32; for latent records the split-k
+ * partials in the workspace are rounded to bf16, their (m, l) kept in fp32,
+ * which the relative-L2 bound of 4e-3 on bf16 records covers). A slot
+ * outside [0, B) makes the unit's output NaN and sets HS_ERR_SLOT. d_ws is
+ * scratch of at least
  * hs_sparse_attn_workspace(...) bytes (may be NULL when that is 0); its
  * contents need no initialisation. Enqueue only; capture-safe.
  * HS_E_INVAL for unsupported shapes or a small workspace. */
