@@ -277,14 +277,23 @@ __global__ __launch_bounds__(LAT_THREADS, 1) void hs_k_attn_latent(
     const int i = tid + j * LAT_THREADS;
     ids[j] = i < n_ids ? slots[i_begin + min(i, n_rows - 1)] : 0;
   }
-  CopySrc c0;  // step 0's, straight from global memory
-  if (n_steps > 0) {
-    c0.lat = slots[i_begin + min(min((lane >> 3) & 1, NST - 1) * LAT_TILE + w + 4 * (lane & 7),
-                                 n_rows - 1)];
+  // step 0's copy ids, and with two tiles per step step 1's, straight from
+  // global memory (step 1's second tile goes to the second half of the
+  // buffer whose first half takes the queries, so it is copied now)
+  auto load_ids = [&](int i) {
+    CopySrc c;
+    c.lat = slots[i_begin + min((NST * i + min((lane >> 3) & 1, NST - 1)) * LAT_TILE + w +
+                                    4 * (lane & 7),
+                                n_rows - 1)];
 #pragma unroll
     for (int t = 0; t < NST; ++t)
-      c0.rope[t] = slots[i_begin + min(t * LAT_TILE + rope_row, n_rows - 1)];
-  }
+      c.rope[t] = slots[i_begin + min((NST * i + t) * LAT_TILE + rope_row, n_rows - 1)];
+    return c;
+  };
+  const bool early1 = NHG == 1 && n_steps > 1;  // wave-uniform
+  CopySrc c0, c1;
+  if (n_steps > 0) c0 = load_ids(0);
+  if (early1) c1 = load_ids(1);
   // an invalid slot is flagged and replaced by slot 0 (the unit's output
   // becomes NaN)
   bool bad = false;
@@ -319,11 +328,19 @@ __global__ __launch_bounds__(LAT_THREADS, 1) void hs_k_attn_latent(
 #pragma unroll
     for (int m = 0; m < CPS; ++m) copy_one(c0, 0, m);
   }
+  if (early1) {
+    c1.lat = checked(c1.lat);
+    c1.rope[NST - 1] = checked(c1.rope[NST - 1]);
+#pragma unroll
+    for (int m = 9; m < CPS; ++m) copy_one(c1, 1, m);
+  }
   lds_barrier();  // s_bad's initial value is visible to every wave
   if (bad) s_bad = 1;
-  // this wave's query copies have landed (step 0's may still be in flight),
-  // then every wave's have
-  if (n_steps > 0)
+  // this wave's query copies have landed (the later ones may still be in
+  // flight), then every wave's have
+  if (early1)
+    wait_vmcnt<CPS + 9>();
+  else if (n_steps > 0)
     wait_vmcnt<CPS>();
   else
     wait_vmcnt<0>();
@@ -355,9 +372,13 @@ __global__ __launch_bounds__(LAT_THREADS, 1) void hs_k_attn_latent(
     for (int ds = 0; ds < LAT_BLOCKS; ++ds)
       qb[ds] = __builtin_bit_cast(bf16x8, __builtin_bit_cast(v4u, kread(qt, ds)) & keep);
   }
-  // step 0's rows have landed, and every wave's; the query tiles' buffers
-  // are free; the slot ids and s_bad are visible
-  wait_vmcnt<0>();
+  // step 0's rows have landed (step 1's second tile may still be in
+  // flight), and every wave's; the query tiles' buffers are free; the slot
+  // ids and s_bad are visible
+  if (early1)
+    wait_vmcnt<9>();
+  else
+    wait_vmcnt<0>();
   lds_barrier();
   if (DEPTH > 1 && n_steps > 1) {
     const CopySrc c1 = copy_ids(1);
@@ -426,7 +447,9 @@ __global__ __launch_bounds__(LAT_THREADS, 1) void hs_k_attn_latent(
       else if (ds + LAT_KPF - LAT_BLOCKS < LAT_VPF)
         vring[ds + LAT_KPF - LAT_BLOCKS] = vread(tl, ds + LAT_KPF - LAT_BLOCKS);
       constexpr int every = LAT_BLOCKS / CPS;
-      if (copy && ds % every == 0) copy_one(cs, ci, ds / every);
+      // (step 1's second tile went out in the prologue)
+      if (copy && ds % every == 0 && !(NHG == 1 && ci == 1 && ds / every >= 9))
+        copy_one(cs, ci, ds / every);
       // keep this order: the scheduler would otherwise pull the reads next
       // to their MFMAs
       __builtin_amdgcn_sched_barrier(0);
@@ -475,6 +498,8 @@ __global__ __launch_bounds__(LAT_THREADS, 1) void hs_k_attn_latent(
     // with step i - 1, whose buffer step i + DEPTH reuses
     if (DEPTH > 1 && i + 1 < n_steps)
       wait_vmcnt<(DEPTH - 1) * CPS>();
+    else if (early1 && i == 0)
+      wait_vmcnt<9>();  // step 1's second tile, copied in the prologue
     else
       wait_vmcnt<0>();
     __syncthreads();
