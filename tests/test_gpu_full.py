@@ -11,8 +11,9 @@ steps: the resident row bytes of sampled units, and attention outputs of
 sampled units; at one warm step, the attention of every unit (max abs 1e-5
 for fp32 records; max abs 1e-2 and relative L2 4e-3 for bf16 records, per
 unit and over the whole step's output tensor), the oracle computing the
-units in parallel host threads. The worst margins of each workload (and
-where they occur) are written to gpurun_out/parity_margins.md.
+units in parallel host threads. With HS_PARITY_MARGINS_OUT set to a
+directory, the worst margins of each workload (and where they occur) are
+written there: one JSON file per workload and parity_margins.md.
 """
 import json
 import os
@@ -32,8 +33,7 @@ from tiered_kv_cache_hs_amd.session import Session  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-MARGINS_DIR = os.path.join(ROOT, "gpurun_out", "parity_margins")
+MARGINS_OUT = os.environ.get("HS_PARITY_MARGINS_OUT", "")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -141,8 +141,10 @@ def test_full_size_workload(wl):
         sess.close()
     say(f"workload {wl}: all {w.steps} steps bit-exact; worst attention {worst}; "
         f"whole-step rel L2 at step {all_step}: {step_rel}; {time.time() - t0:.1f}s")
-    os.makedirs(MARGINS_DIR, exist_ok=True)
-    with open(os.path.join(MARGINS_DIR, f"wl{wl}.json"), "w") as fh:
+    if not MARGINS_OUT:
+        return
+    os.makedirs(MARGINS_OUT, exist_ok=True)
+    with open(os.path.join(MARGINS_OUT, f"wl{wl}.json"), "w") as fh:
         json.dump({"workload": wl, "name": w.name, "dtype": "f32" if w.dtype == I.F32 else "bf16",
                    "units": w.n_units, "steps": w.steps, "unit_checks": n_checked,
                    "all_units_step": all_step, "worst_max_abs": worst["max_abs"][0],
@@ -151,17 +153,18 @@ def test_full_size_workload(wl):
 
 
 def _write_margins_summary():
-    if not os.path.isdir(MARGINS_DIR):
+    if not MARGINS_OUT or not os.path.isdir(MARGINS_OUT):
         return
     rows = []
     for wl in sorted(PLAN):
-        f = os.path.join(MARGINS_DIR, f"wl{wl}.json")
+        f = os.path.join(MARGINS_OUT, f"wl{wl}.json")
         if os.path.exists(f):
             rows.append(json.load(open(f)))
     if not rows:
         return
     lines = ["# Attention parity margins at full size", "",
-             "Written by `python -u -m pytest tests/test_gpu_full.py -m gpu` (one MI355X): for every "
+             "Written by `HS_PARITY_MARGINS_OUT=<dir> python -u -m pytest tests/test_gpu_full.py -m "
+             "gpu` (one MI355X): for every "
              "workload, the worst per-unit attention error against the oracle over every checked "
              "(step, unit) - the sampled units at the sampled steps and every unit at one warm "
              "step - and the relative L2 error over the whole output tensor of that warm step. "
@@ -178,5 +181,5 @@ def _write_margins_summary():
                      f"{d['unit_checks']} | {d['worst_max_abs']:.3e} | {fa} | "
                      f"{d['worst_rel_l2']:.3e} | {fb} | {d['step_rel_l2']:.3e} "
                      f"({d['all_units_step']}) |")
-    with open(os.path.join(os.path.dirname(MARGINS_DIR), "parity_margins.md"), "w") as fh:
+    with open(os.path.join(MARGINS_OUT, "parity_margins.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
