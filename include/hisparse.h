@@ -127,9 +127,7 @@ typedef struct hs_tuning {
   int32_t gather_bytes_per_lane; /* hs_resolve's miss fetch (the swap-in transfer
                                    block of HiSparse summary, sections 5 and 8):
                                    bytes of host reads each lane keeps in flight
-                                   per batch, 16 x {1, 2, 4, 8}; 0 = chosen per
-                                   buffer size (64 for B <= 1024 or B > 8192,
-                                   else 128) */
+                                   per batch, 16 x {1, 2, 4, 8}; 0 = 64 */
   int32_t resolve_fetch;        /* where hs_resolve moves the misses: 0 = by
                                    batch size (the resolve kernel for 4 or more
                                    units, else a gather kernel of its own);

@@ -38,8 +38,8 @@
 //    stops at the first digit whose bucket is taken whole.
 //  * The fetch (batched gather): with 4 or more units per launch it runs in
 //    the same workgroup: each thread reads 16-byte chunks of the missed
-//    records with non-temporal loads from the device-mapped host pool, up to
-//    8 per thread in flight, the first batch issued as soon as the miss list
+//    records with non-temporal loads from the device-mapped host pool, 4 per
+//    thread in flight by default, the first batch issued as soon as the miss list
 //    is known, so host-link latency overlaps the victim selection. One
 //    compute unit keeps only so many host reads in flight, so smaller
 //    batches fetch with hs_k_gather instead: many workgroups per unit copy
@@ -442,10 +442,12 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
   // load or store sits on a lane-dependent path and the waits before each
   // store count exactly the loads it needs (a guarded load made the
   // compiler wait for every earlier load before the next one).
-  // GB chunks per thread per batch (the tuned swap-in block; by default 8,
-  // and 4 where registers are short (B > 8192) or where few misses per
-  // buffer are the rule (B <= 1024: the repeated last chunk of lanes past
-  // the end would cost host reads of its own))
+  // GB chunks per thread per batch (the tuned swap-in block; by default 4:
+  // with 8 the waves stay blocked at the issue of their first batch for
+  // longer before the victim selection can run, and the batch-8 MLA step
+  // measured 74.1-74.4 against 75.4-75.5 us per layer with 4 (the 64-request
+  // one 852-853 against 854-855); with fewer than 4 the link is not kept
+  // full (75.8-76.6))
   const size_t rec = (size_t)rec16 * 16;
   const int g_total = m * rec16;
   v4u gv[GB];
@@ -800,7 +802,7 @@ hipError_t launch_select(const UnitDesc *d_units, int n, const int32_t *d_topk, 
   launch_k(HS_TRACE_RESOLVE, hs_k_resolve<NT, SPT, KPT, G, INV, B>, grid, block, (uint32_t)lds, \
            stream, d_units, d_topk, k, hlog2, rec16, d_slots, d_miss)
   if (!gather) return HS_RES(false, 1);
-  if (gb == 0) gb = (SPT >= 16 || SPT == 1) ? 4 : 8;
+  if (gb == 0) gb = 4;
   switch (gb) {
     case 1: return HS_RES(true, 1);
     case 2: return HS_RES(true, 2);
