@@ -278,6 +278,26 @@ __global__ __launch_bounds__(NT) void hs_k_resolve(
     else if (!INV || slot_of[k0 + j] < 0)
       pend |= 1u << j;
   }
+  // INV: only the misses are inserted, so the table is nearly empty and an
+  // insert almost always takes its hashed entry: one compare-and-swap there
+  // first, without reading the bucket (one LDS round trip instead of two on
+  // the path to the first host read; the batch-8 MLA step measured 73.1-73.4
+  // against 74.0-74.5 us per layer). The rest probe on below.
+  if (INV) {
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) {
+      if (!((pend >> j) & 1u)) continue;
+      const int old = atomicCAS(&hkey[hcur[j]], EMPTY_KEY, tk[j]);
+      if (old == EMPTY_KEY) {
+        pend &= ~(1u << j);
+      } else if (old == tk[j]) {
+        myflag |= HS_ERR_DUP;
+        pend &= ~(1u << j);
+      } else {
+        hcur[j] = (hcur[j] + 1u) & (uint32_t)(H - 1);
+      }
+    }
+  }
   // Linear probing, read 4 entries (one 16-byte aligned bucket) at a time:
   // entries before the first empty one are taken for good (nothing is ever
   // removed), so skipping them equals failed compare-and-swaps on them.
